@@ -1,0 +1,317 @@
+/*
+ * CPU oracle for the quantised GEMV / expert-MLP path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  The tests, the smoke check and the benchmark's
+ * CPU-baseline leg are the only callers.  The product path never loads this
+ * library.  It shares no code, header, table or helper with the HIP path.
+ *
+ * Plain and slow on purpose.  Each quantity comes straight from its
+ * definition, in double precision.  Outputs are computed one at a time, and
+ * every sum runs in input order.  The only concurrency is OpenMP over
+ * independent outputs, which reorders no sum.
+ *
+ * Sources (page title, then the passage):
+ *  [G]  "colibri Vulkan compute backend complete guide" (xdnf.cn): the
+ *       shader-level details section (formats: int8; int4 with two per byte
+ *       and value nibble-8; int3-g64 with two planes and one f32 scale per
+ *       64 inputs; MXFP4 e2m1 nibble with bit 3 the sign and f32 scales per
+ *       32 inputs that the host expands), the API contract section (gate_up
+ *       is silu(gate(x))*up(x); the expert group is the whole fused MLP of a
+ *       batch) and the correctness section (int4 is offset binary,
+ *       nibble - 8).
+ *  [V]  "colibri -- Vulkan backend (docs/vulkan.md)": the arithmetic
+ *       paragraph (the device multiplies the CPU's weights by f32
+ *       activations, so the two differ only in summation order); the
+ *       expert-tier engine table (format numbers 1, 2, 4, 5, 7 and SwiGLU);
+ *       the tier's list of properties (each expert's output joins its row in
+ *       routing order) and the GLM-5.2 paragraph (routed experts in rank
+ *       order, then the shared expert).
+ *  [OCP] The OCP Microscaling (MX) Formats specification v1.0, FP4 E2M1:
+ *       1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit, subnormal
+ *       when the exponent field is 0.
+ *
+ * Readings taken where the pages are silent (each is a listed reading, not
+ * a page fact):
+ *  - int4 and MXFP4 pairs: the low nibble of byte j holds input 2j and the
+ *    high nibble input 2j+1 (by analogy with f16 rows, whose low half is the
+ *    even column, in the f16-rows paragraph of [V]).
+ *  - groups are gs consecutive inputs of one row; scales are row-major
+ *    [O][K/gs].
+ *  - int3-g64: the low plane holds 2 bits per input, 16 inputs per
+ *    little-endian 32-bit word (input k at bits 2*(k mod 16)); the high
+ *    plane holds 1 bit per input, 32 inputs per word (bit k mod 32);
+ *    code = low | high << 2, value = code - 4.
+ *  - a weight is the real product value * scale; the materialised f32
+ *    weight is that product rounded once to nearest-even.
+ *  - router weights multiply each expert's down output; the shared expert
+ *    is added last with weight 1.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <omp.h>
+
+typedef struct {
+    int fmt;               /* 1 int8/row, 2 int4/row, 4 int4/gs, 5 int3-g64, 7 MXFP4 */
+    long O, K, gs;         /* rows, inputs per row, inputs per scale */
+    const void *q;         /* codes (fmt 5: the 2-bit plane) */
+    const void *q2;        /* fmt 5: the 1-bit plane; otherwise unused */
+    const float *scales;   /* [O][K/gs] */
+} orc_matrix;
+
+/* ------------------------------------------------------------------ */
+/* Code values, from the format definitions.                            */
+/* ------------------------------------------------------------------ */
+
+/* One nibble of a packed pair: even input in the low nibble. */
+static int nibble_at(const uint8_t *row, long k)
+{
+    uint8_t byte = row[k / 2];
+    if (k % 2 == 0)
+        return byte & 0x0F;
+    return byte >> 4;
+}
+
+/* FP4 E2M1 value of a 4-bit code, from its bit fields [OCP]. */
+double orc_e2m1(int code)
+{
+    int sign = (code >> 3) & 1;
+    int expo = (code >> 1) & 3;
+    int mant = code & 1;
+    double mag;
+    if (expo == 0)
+        mag = 0.5 * mant;                       /* 2^(1-1) * (mant / 2) */
+    else
+        mag = ldexp(1.0 + 0.5 * mant, expo - 1);   /* 2^(expo-1) * (1 + mant/2) */
+    return sign ? -mag : mag;
+}
+
+/* int3 code 0..7 of input k from the two planes. */
+static int int3_code(const uint32_t *low_row, const uint32_t *high_row, long k)
+{
+    int low = (int)((low_row[k / 16] >> (2 * (k % 16))) & 3u);
+    int high = (int)((high_row[k / 32] >> (k % 32)) & 1u);
+    return low | (high << 2);
+}
+
+/* The signed value v of weight (o, k) before scaling. */
+double orc_code_value(const orc_matrix *m, long o, long k)
+{
+    switch (m->fmt) {
+    case 1: {
+        const int8_t *row = (const int8_t *)m->q + o * m->K;
+        return (double)row[k];
+    }
+    case 2:
+    case 4: {
+        const uint8_t *row = (const uint8_t *)m->q + o * (m->K / 2);
+        return (double)(nibble_at(row, k) - 8);
+    }
+    case 5: {
+        const uint32_t *low_row = (const uint32_t *)m->q + o * (m->K / 16);
+        const uint32_t *high_row = (const uint32_t *)m->q2 + o * (m->K / 32);
+        return (double)(int3_code(low_row, high_row, k) - 4);
+    }
+    case 7: {
+        const uint8_t *row = (const uint8_t *)m->q + o * (m->K / 2);
+        return orc_e2m1(nibble_at(row, k));
+    }
+    }
+    return NAN;
+}
+
+/* The scale that applies to weight (o, k). */
+double orc_scale(const orc_matrix *m, long o, long k)
+{
+    long groups = m->K / m->gs;
+    return (double)m->scales[o * groups + k / m->gs];
+}
+
+/* Weight (o, k) as a real number: v * s.  Exact in double (v has at most
+   8 significant bits, s has 24). */
+double orc_weight(const orc_matrix *m, long o, long k)
+{
+    return orc_code_value(m, o, k) * orc_scale(m, o, k);
+}
+
+/* ------------------------------------------------------------------ */
+/* Dequantisation: f32 weights, v * s rounded once to nearest-even.     */
+/* ------------------------------------------------------------------ */
+
+void orc_dequant(const orc_matrix *m, float *out)
+{
+    long o;
+#pragma omp parallel for schedule(static)
+    for (o = 0; o < m->O; o++)
+        for (long k = 0; k < m->K; k++)
+            out[o * m->K + k] = (float)orc_weight(m, o, k);
+}
+
+/* ------------------------------------------------------------------ */
+/* GEMV: y[s][o] = sum_k w[o][k] * x[s][k], in double, k in order.      */
+/* absn[s][o] = sum_k |w[o][k] * x[s][k]|, the per-row normaliser.      */
+/* ------------------------------------------------------------------ */
+
+static void row_dot(const orc_matrix *m, long o, const float *xf, const double *xd,
+                    double *y, double *absn)
+{
+    double sum = 0.0, mag = 0.0;
+    for (long k = 0; k < m->K; k++) {
+        double xk = xf ? (double)xf[k] : xd[k];
+        double term = orc_weight(m, o, k) * xk;
+        sum += term;
+        mag += fabs(term);
+    }
+    *y = sum;
+    if (absn)
+        *absn = mag;
+}
+
+void orc_gemv(const orc_matrix *m, const float *x, long S, double *y, double *absn)
+{
+    long idx;
+#pragma omp parallel for schedule(static)
+    for (idx = 0; idx < S * m->O; idx++) {
+        long s = idx / m->O, o = idx % m->O;
+        row_dot(m, o, x + s * m->K, NULL, &y[s * m->O + o], absn ? &absn[s * m->O + o] : NULL);
+    }
+}
+
+/* Same with double inputs (used for the down projection of h). */
+void orc_gemv_f64(const orc_matrix *m, const double *x, long S, double *y, double *absn)
+{
+    long idx;
+#pragma omp parallel for schedule(static)
+    for (idx = 0; idx < S * m->O; idx++) {
+        long s = idx / m->O, o = idx % m->O;
+        row_dot(m, o, NULL, x + s * m->K, &y[s * m->O + o], absn ? &absn[s * m->O + o] : NULL);
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* SwiGLU: h = silu(g) * u with silu(z) = z / (1 + exp(-z)).            */
+/* ------------------------------------------------------------------ */
+
+double orc_silu(double z)
+{
+    return z / (1.0 + exp(-z));
+}
+
+/* d silu / dz = sigma(z) * (1 + z * (1 - sigma(z))). */
+static double silu_slope(double z)
+{
+    double sig = 1.0 / (1.0 + exp(-z));
+    return sig * (1.0 + z * (1.0 - sig));
+}
+
+/*
+ * gate_up over S tokens: g = G x, u = U x, h = silu(g) * u, each [S][I].
+ * nh[s][i] bounds how far an f32 evaluation of h may move when g and u
+ * carry errors proportional to their own normalisers (first order):
+ *   nh = |silu'(g)| * absn_g * |u| + |silu(g)| * absn_u.
+ * Any output pointer may be NULL except h.
+ */
+void orc_gate_up(const orc_matrix *G, const orc_matrix *U, const float *x, long S,
+                 double *h, double *nh, double *g_out, double *u_out,
+                 double *ag_out, double *au_out)
+{
+    long I = G->O, idx;
+#pragma omp parallel for schedule(static)
+    for (idx = 0; idx < S * I; idx++) {
+        long s = idx / I, i = idx % I;
+        double g, u, ag, au;
+        row_dot(G, i, x + s * G->K, NULL, &g, &ag);
+        row_dot(U, i, x + s * U->K, NULL, &u, &au);
+        h[idx] = orc_silu(g) * u;
+        if (nh)
+            nh[idx] = fabs(silu_slope(g)) * ag * fabs(u) + fabs(orc_silu(g)) * au;
+        if (g_out) g_out[idx] = g;
+        if (u_out) u_out[idx] = u;
+        if (ag_out) ag_out[idx] = ag;
+        if (au_out) au_out[idx] = au;
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Expert group.                                                        */
+/*   y[t] = sum_{r=0..k-1} w[t][r] * MLP_{ids[t][r]}(x[t])   (rank order) */
+/*        + MLP_shared(x[t])                       (if shared >= 0)       */
+/*   MLP_e(x) = down_e * (silu(gate_e x) * (up_e x)).                     */
+/* absn[t][o] = sum over the terms of |weight| * sum_k |down[o][k]| *     */
+/*   (|h[k]| + nh[k]): the down row's own normaliser plus the first-order */
+/*   reach of the errors h may carry.                                    */
+/* ids outside [0, n_experts) make the token's row NaN.                  */
+/* ------------------------------------------------------------------ */
+
+static void mlp_one(const orc_matrix *gate, const orc_matrix *up, const orc_matrix *down,
+                    const float *x, double *h, double *nh, double *dy, double *dabs)
+{
+    long I = gate->O, H = down->O;
+    orc_gate_up(gate, up, x, 1, h, nh, NULL, NULL, NULL, NULL);
+    long o;
+#pragma omp parallel for schedule(static)
+    for (o = 0; o < H; o++) {
+        double sum = 0.0, mag = 0.0;
+        for (long k = 0; k < I; k++) {
+            double wk = orc_weight(down, o, k);
+            sum += wk * h[k];
+            mag += fabs(wk) * (fabs(h[k]) + nh[k]);
+        }
+        dy[o] = sum;
+        dabs[o] = mag;
+    }
+}
+
+void orc_expert_group(const orc_matrix *gates, const orc_matrix *ups, const orc_matrix *downs,
+                      long n_experts, long S, long k, const int32_t *ids, const float *w,
+                      long shared, const float *x, double *y, double *absn,
+                      double *h_work /* [I] */, double *nh_work /* [I] */,
+                      double *dy_work /* [H] */, double *dabs_work /* [H] */)
+{
+    long H = downs[0].O;
+    for (long t = 0; t < S; t++) {
+        double *yt = y + t * H, *at = absn + t * H;
+        for (long o = 0; o < H; o++) {
+            yt[o] = 0.0;
+            at[o] = 0.0;
+        }
+        for (long r = 0; r < k; r++) {
+            long e = ids[t * k + r];
+            if (e < 0 || e >= n_experts) {
+                for (long o = 0; o < H; o++)
+                    yt[o] = NAN;
+                continue;
+            }
+            double wr = (double)w[t * k + r];
+            mlp_one(&gates[e], &ups[e], &downs[e], x + t * gates[e].K, h_work, nh_work,
+                    dy_work, dabs_work);
+            for (long o = 0; o < H; o++) {
+                yt[o] += wr * dy_work[o];
+                at[o] += fabs(wr) * dabs_work[o];
+            }
+        }
+        if (shared >= 0) {
+            mlp_one(&gates[shared], &ups[shared], &downs[shared], x + t * gates[shared].K,
+                    h_work, nh_work, dy_work, dabs_work);
+            for (long o = 0; o < H; o++) {
+                yt[o] += dy_work[o];
+                at[o] += dabs_work[o];
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------ */
+/* Threads.                                                             */
+/* ------------------------------------------------------------------ */
+
+void orc_set_threads(int n)
+{
+    if (n > 0)
+        omp_set_num_threads(n);
+}
+
+int orc_get_threads(void)
+{
+    return omp_get_max_threads();
+}

@@ -1,0 +1,219 @@
+"""ctypes wrapper over liboracle.so (test infrastructure only).
+
+Matrices are any objects with the fields of ``synth.QMatrix`` (fmt, O, K,
+gs, q, q2, scales) holding host numpy arrays.  Every result is float64
+except ``dequant`` (float32, the materialised weights).
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+
+from . import build as _build
+
+
+class _Mat(C.Structure):
+    _fields_ = [("fmt", C.c_int), ("O", C.c_long), ("K", C.c_long), ("gs", C.c_long),
+                ("q", C.c_void_p), ("q2", C.c_void_p), ("scales", C.c_void_p)]
+
+
+_P = C.c_void_p
+_L = C.c_long
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _check_matrix(m) -> None:
+    for name in ("q", "scales"):
+        a = getattr(m, name)
+        if not a.flags["C_CONTIGUOUS"]:
+            raise ValueError(f"{name} must be C-contiguous")
+    if m.scales.dtype != np.float32:
+        raise ValueError("scales must be float32")
+    if m.K % m.gs:
+        raise ValueError("K must be a multiple of gs")
+    if m.fmt == 5 and m.q2 is None:
+        raise ValueError("fmt 5 needs its 1-bit plane")
+
+
+def _mat(m) -> _Mat:
+    _check_matrix(m)
+    return _Mat(int(m.fmt), int(m.O), int(m.K), int(m.gs), _ptr(m.q), _ptr(m.q2), _ptr(m.scales))
+
+
+def _f32(x) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+class OracleLib:
+    """One loaded copy of the oracle (the default build, or a test's mutant)."""
+
+    def __init__(self, path: str):
+        self.path = path
+        lib = C.CDLL(path)
+        lib.orc_e2m1.restype = C.c_double
+        lib.orc_e2m1.argtypes = [C.c_int]
+        lib.orc_code_value.restype = C.c_double
+        lib.orc_code_value.argtypes = [C.POINTER(_Mat), _L, _L]
+        lib.orc_weight.restype = C.c_double
+        lib.orc_weight.argtypes = [C.POINTER(_Mat), _L, _L]
+        lib.orc_dequant.restype = None
+        lib.orc_dequant.argtypes = [C.POINTER(_Mat), _P]
+        lib.orc_gemv.restype = None
+        lib.orc_gemv.argtypes = [C.POINTER(_Mat), _P, _L, _P, _P]
+        lib.orc_gemv_f64.restype = None
+        lib.orc_gemv_f64.argtypes = [C.POINTER(_Mat), _P, _L, _P, _P]
+        lib.orc_silu.restype = C.c_double
+        lib.orc_silu.argtypes = [C.c_double]
+        lib.orc_gate_up.restype = None
+        lib.orc_gate_up.argtypes = [C.POINTER(_Mat), C.POINTER(_Mat), _P, _L, _P, _P, _P, _P, _P, _P]
+        lib.orc_expert_group.restype = None
+        lib.orc_expert_group.argtypes = [_P, _P, _P, _L, _L, _L, _P, _P, _L, _P, _P, _P, _P, _P, _P, _P]
+        lib.orc_set_threads.restype = None
+        lib.orc_set_threads.argtypes = [C.c_int]
+        lib.orc_get_threads.restype = C.c_int
+        lib.orc_get_threads.argtypes = []
+        self.lib = lib
+
+    # -- scalar helpers ---------------------------------------------------
+    def e2m1(self, code: int) -> float:
+        return self.lib.orc_e2m1(int(code))
+
+    def silu(self, z: float) -> float:
+        return self.lib.orc_silu(float(z))
+
+    def set_threads(self, n: int) -> None:
+        self.lib.orc_set_threads(int(n))
+
+    def get_threads(self) -> int:
+        return self.lib.orc_get_threads()
+
+    # -- matrices -----------------------------------------------------------
+    def code_values(self, m) -> np.ndarray:
+        """Signed code values v[o][k] (float64), one call per element."""
+        mm = _mat(m)
+        out = np.empty((m.O, m.K), dtype=np.float64)
+        for o in range(m.O):
+            for k in range(m.K):
+                out[o, k] = self.lib.orc_code_value(C.byref(mm), o, k)
+        return out
+
+    def dequant(self, m) -> np.ndarray:
+        out = np.empty((m.O, m.K), dtype=np.float32)
+        self.lib.orc_dequant(C.byref(_mat(m)), _ptr(out))
+        return out
+
+    def gemv(self, m, x) -> tuple:
+        """y[S][O] and its normaliser sum_k |w*x|, for x f32 [S][K] (or f64)."""
+        x = np.atleast_2d(x)
+        S = x.shape[0]
+        if x.shape[1] != m.K:
+            raise ValueError("x has the wrong width")
+        y = np.empty((S, m.O), dtype=np.float64)
+        a = np.empty((S, m.O), dtype=np.float64)
+        if x.dtype == np.float64:
+            xx = np.ascontiguousarray(x)
+            self.lib.orc_gemv_f64(C.byref(_mat(m)), _ptr(xx), S, _ptr(y), _ptr(a))
+        else:
+            xx = _f32(x)
+            self.lib.orc_gemv(C.byref(_mat(m)), _ptr(xx), S, _ptr(y), _ptr(a))
+        return y, a
+
+    def gate_up(self, G, U, x) -> dict:
+        x = _f32(np.atleast_2d(x))
+        S, I = x.shape[0], G.O
+        if G.K != x.shape[1] or U.K != x.shape[1] or U.O != I:
+            raise ValueError("gate/up/x shapes disagree")
+        out = {n: np.empty((S, I), dtype=np.float64) for n in ("h", "nh", "g", "u", "ag", "au")}
+        self.lib.orc_gate_up(C.byref(_mat(G)), C.byref(_mat(U)), _ptr(x), S,
+                             *[_ptr(out[n]) for n in ("h", "nh", "g", "u", "ag", "au")])
+        return out
+
+    def expert_group(self, experts: Sequence, ids, w, shared: Optional[int], x) -> tuple:
+        """y[S][H] and its normaliser for a token batch.
+
+        ``experts`` is a sequence of objects with gate/up/down matrices,
+        indexed by expert id.  Only the experts that ``ids`` and ``shared``
+        name are handed to the C code (the others are never read).
+        """
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        w = _f32(w)
+        x = _f32(np.atleast_2d(x))
+        S, k = ids.shape
+        used = sorted({int(e) for e in ids.ravel() if 0 <= int(e) < len(experts)}
+                      | ({int(shared)} if shared is not None and shared >= 0 else set()))
+        remap = {e: i for i, e in enumerate(used)}
+        # an id outside the table stays outside the compact table too
+        cids = np.array([[remap.get(int(e), -1) for e in row] for row in ids], dtype=np.int32)
+        cshared = remap[int(shared)] if shared is not None and shared >= 0 else -1
+        n = len(used)
+        gates = (_Mat * max(n, 1))(*[_mat(experts[e].gate) for e in used])
+        ups = (_Mat * max(n, 1))(*[_mat(experts[e].up) for e in used])
+        downs = (_Mat * max(n, 1))(*[_mat(experts[e].down) for e in used])
+        H = experts[used[0]].down.O
+        I = experts[used[0]].gate.O
+        y = np.empty((S, H), dtype=np.float64)
+        a = np.empty((S, H), dtype=np.float64)
+        hw = np.empty(I, dtype=np.float64)
+        nw = np.empty(I, dtype=np.float64)
+        dw = np.empty(H, dtype=np.float64)
+        aw = np.empty(H, dtype=np.float64)
+        self.lib.orc_expert_group(C.cast(gates, C.c_void_p), C.cast(ups, C.c_void_p),
+                                  C.cast(downs, C.c_void_p), n, S, k, _ptr(cids), _ptr(w),
+                                  cshared, _ptr(x), _ptr(y), _ptr(a), _ptr(hw), _ptr(nw),
+                                  _ptr(dw), _ptr(aw))
+        return y, a
+
+
+_default: Optional[OracleLib] = None
+
+
+def load(path: Optional[str] = None) -> OracleLib:
+    """The default oracle (built on demand), or the library at ``path``."""
+    global _default
+    if path is not None:
+        return OracleLib(path)
+    if _default is None:
+        _default = OracleLib(_build.ensure_built())
+    return _default
+
+
+def e2m1(code):
+    return load().e2m1(code)
+
+
+def silu(z):
+    return load().silu(z)
+
+
+def set_threads(n):
+    load().set_threads(n)
+
+
+def get_threads():
+    return load().get_threads()
+
+
+def code_values(m):
+    return load().code_values(m)
+
+
+def dequant(m):
+    return load().dequant(m)
+
+
+def gemv(m, x):
+    return load().gemv(m, x)
+
+
+def gate_up(G, U, x):
+    return load().gate_up(G, U, x)
+
+
+def expert_group(experts, ids, w, shared, x):
+    return load().expert_group(experts, ids, w, shared, x)

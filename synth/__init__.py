@@ -1,0 +1,202 @@
+"""Seeded synthetic inputs for the quantised GEMV / expert-MLP path.
+
+This module is shared by the tests, the benchmark and the oracle's callers.
+It only draws random storage words, scales, activations and routings with
+the shapes and value distributions of the workloads; it holds none of the
+method's arithmetic (no decoding, no dot products, no activation).
+
+Storage forms (one per weight format; the format numbers are colibri's
+device formats as listed in the expert-tier engine table of "colibri --
+Vulkan backend (docs/vulkan.md)"):
+
+  fmt 1  int8, one f32 scale per row
+         q: int8 [O][K]                     scales: f32 [O][1]
+  fmt 2  int4 pairs, one f32 scale per row
+         q: uint8 [O][K/2]                  scales: f32 [O][1]
+  fmt 4  int4 pairs, one f32 scale per gs inputs
+         q: uint8 [O][K/2]                  scales: f32 [O][K/gs]
+  fmt 5  int3, one group per 64 inputs, two bit planes
+         q: uint32 [O][K/16] (2-bit plane)  q2: uint32 [O][K/32] (1-bit plane)
+         scales: f32 [O][K/64]
+  fmt 7  MXFP4: e2m1 nibbles, f32 scale per 32 inputs (pre-expanded e8m0)
+         q: uint8 [O][K/2]                  scales: f32 [O][K/32]
+
+Uniform random words give uniform codes in every field, so drawing words is
+the same as drawing codes; no bit of any code is computed here.
+"""
+from __future__ import annotations
+
+import dataclasses
+from concurrent.futures import ThreadPoolExecutor
+from typing import Optional
+
+import numpy as np
+
+FMT_I8_ROW = 1
+FMT_I4_ROW = 2
+FMT_I4_GS = 4
+FMT_I3_G64 = 5
+FMT_MXFP4 = 7
+
+FORMATS = (FMT_I8_ROW, FMT_I4_ROW, FMT_I4_GS, FMT_I3_G64, FMT_MXFP4)
+
+BASE_SEED = 20261202
+
+
+@dataclasses.dataclass
+class QMatrix:
+    """Host copy of one quantised matrix in its storage form."""
+    fmt: int
+    O: int
+    K: int
+    gs: int
+    q: np.ndarray
+    q2: Optional[np.ndarray]
+    scales: np.ndarray
+
+    @property
+    def nbytes(self) -> int:
+        n = self.q.nbytes + self.scales.nbytes
+        if self.q2 is not None:
+            n += self.q2.nbytes
+        return n
+
+
+def group_size(fmt: int, K: int, gs: Optional[int] = None) -> int:
+    """Inputs per scale for a format (the whole row for the per-row forms)."""
+    if fmt in (FMT_I8_ROW, FMT_I4_ROW):
+        return K
+    if fmt == FMT_I3_G64:
+        return 64
+    if fmt == FMT_MXFP4:
+        return 32
+    if fmt == FMT_I4_GS:
+        if gs is None:
+            raise ValueError("fmt 4 needs a group size")
+        return gs
+    raise ValueError(f"unknown format {fmt}")
+
+
+def storage_shapes(fmt: int, O: int, K: int, gs: int):
+    """(q shape, q dtype, q2 shape or None, scales shape) of a format."""
+    if fmt == FMT_I8_ROW:
+        return (O, K), np.int8, None, (O, 1)
+    if fmt in (FMT_I4_ROW, FMT_I4_GS, FMT_MXFP4):
+        return (O, K // 2), np.uint8, None, (O, K // gs)
+    if fmt == FMT_I3_G64:
+        return (O, K // 16), np.uint32, (O, K // 32), (O, K // 64)
+    raise ValueError(f"unknown format {fmt}")
+
+
+def rng_for(*key: int) -> np.random.Generator:
+    """Independent PCG64 stream for a tuple of integers (seed, ids...)."""
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(key))))
+
+
+def _scales(rng: np.random.Generator, fmt: int, shape, kind: str) -> np.ndarray:
+    if kind == "pow2":
+        # e8m0 scales pre-expanded to f32: 2^e with e uniform in {-10..-6}
+        e = rng.integers(-10, -5, size=shape)
+        return np.ldexp(np.ones(shape, dtype=np.float32), e).astype(np.float32)
+    if kind == "row_int8":
+        lo, hi = 1e-3, 1e-2
+    else:
+        lo, hi = 1e-3, 2e-2
+    return rng.uniform(lo, hi, size=shape).astype(np.float32)
+
+
+def default_scale_kind(fmt: int) -> str:
+    if fmt == FMT_I8_ROW:
+        return "row_int8"
+    if fmt == FMT_MXFP4:
+        return "pow2"
+    return "uniform"
+
+
+def matrix(fmt: int, O: int, K: int, gs: Optional[int], *key: int,
+           scale_kind: Optional[str] = None) -> QMatrix:
+    """Draw one quantised matrix from the stream named by ``key``.
+
+    int8 codes are uniform in [-127, 127]; every other format's fields are
+    uniform over all their codes.  Scales: int8 rows U[1e-3, 1e-2], int4 and
+    int3 groups U[1e-3, 2e-2], MXFP4 powers of two 2^U{-10..-6}.
+    """
+    gs = group_size(fmt, K, gs)
+    if K % gs:
+        raise ValueError("K must be a multiple of the group size")
+    qshape, qdtype, q2shape, sshape = storage_shapes(fmt, O, K, gs)
+    rng = rng_for(*key)
+    if fmt == FMT_I8_ROW:
+        q = rng.integers(-127, 128, size=qshape, dtype=np.int8)
+    elif qdtype == np.uint8:
+        q = rng.integers(0, 256, size=qshape, dtype=np.uint8)
+    else:
+        q = rng.integers(0, 2**32, size=qshape, dtype=np.uint32)
+    q2 = None
+    if q2shape is not None:
+        q2 = rng.integers(0, 2**32, size=q2shape, dtype=np.uint32)
+    s = _scales(rng, fmt, sshape, scale_kind or default_scale_kind(fmt))
+    return QMatrix(fmt, O, K, gs, q, q2, s)
+
+
+def activations(S: int, K: int, *key: int) -> np.ndarray:
+    """x[S][K] f32, entries N(0, 1)."""
+    return rng_for(*key).standard_normal(size=(S, K)).astype(np.float32)
+
+
+def routing(S: int, n_experts: int, k: int, *key: int):
+    """Top-k routing of S tokens.
+
+    ids[t]: k expert indices drawn uniformly without replacement.
+    w[t]: softmax of the token's k standard-normal logits (f64, shifted by
+    the max, stored f32).  These stand in for a router's output.
+    """
+    rng = rng_for(*key)
+    ids = np.empty((S, k), dtype=np.int32)
+    w = np.empty((S, k), dtype=np.float32)
+    for t in range(S):
+        ids[t] = rng.choice(n_experts, size=k, replace=False)
+        logits = rng.standard_normal(k)
+        e = np.exp(logits - logits.max())
+        w[t] = (e / e.sum()).astype(np.float32)
+    return ids, w
+
+
+@dataclasses.dataclass
+class Expert:
+    gate: QMatrix   # [I x H]
+    up: QMatrix     # [I x H]
+    down: QMatrix   # [H x I]
+
+
+def expert(fmt: int, H: int, I: int, gs: Optional[int], seed: int, index: int,
+           down_fmt: Optional[int] = None, down_gs: Optional[int] = None) -> Expert:
+    """Expert ``index`` of a seeded set: gate, up [I x H] and down [H x I]."""
+    dfmt = fmt if down_fmt is None else down_fmt
+    dgs = gs if down_gs is None else down_gs
+    if dfmt in (FMT_I8_ROW, FMT_I4_ROW):
+        dgs = None
+    return Expert(matrix(fmt, I, H, gs, seed, index, 0),
+                  matrix(fmt, I, H, gs, seed, index, 1),
+                  matrix(dfmt, H, I, dgs, seed, index, 2))
+
+
+def experts(fmt: int, H: int, I: int, gs: Optional[int], seed: int, n: int,
+            threads: int = 8, **kw) -> list:
+    """n experts, drawn in parallel (each from its own stream)."""
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        return list(ex.map(lambda i: expert(fmt, H, I, gs, seed, i, **kw), range(n)))
+
+
+# Workloads.  Shapes and distributions of the five configurations the path
+# is measured on; seeds are BASE_SEED + workload index.
+WORKLOADS = {
+    "int8_gemv_256x512": dict(kind="gemv", fmt=FMT_I8_ROW, O=256, K=512, gs=None, S=(1,), seed=BASE_SEED + 0),
+    "int4g32_gemv_6144x6144": dict(kind="gemv", fmt=FMT_I4_GS, O=6144, K=6144, gs=32, S=(1, 4), seed=BASE_SEED + 1),
+    "int4g32_expert_6144x2048": dict(kind="expert", fmt=FMT_I4_GS, H=6144, I=2048, gs=32, S=(1,), seed=BASE_SEED + 2),
+    "int4g32_expert_group_256top8_shared": dict(kind="group", fmt=FMT_I4_GS, H=6144, I=2048, gs=32, E=256, k=8,
+                                                shared=True, S=(1, 2, 4), seed=BASE_SEED + 3),
+    "mxfp4_expert_group_384top8_s8": dict(kind="group", fmt=FMT_MXFP4, H=7168, I=2048, gs=32, E=384, k=8,
+                                          shared=False, S=(8,), seed=BASE_SEED + 4),
+    "int3g64_gemv_6144x16384": dict(kind="gemv", fmt=FMT_I3_G64, O=6144, K=16384, gs=64, S=(1,), seed=BASE_SEED + 5),
+}

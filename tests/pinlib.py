@@ -1,0 +1,503 @@
+"""Pins of the CPU oracle: checks against what the pages and mathematics fix.
+
+Each ``pin_*`` function takes an ``oracle.OracleLib`` and raises
+AssertionError when the oracle disagrees with:
+  - hand-written fixtures under tests/golden/ (code tables and byte layouts,
+    each citing the passage or reading it follows);
+  - closed forms (constant codes, one-hot inputs, zero scales, powers of two);
+  - exact rational brute force on tiny inputs;
+  - a library routine where the operation reduces to one (scipy's expit);
+  - invariants of the expert group (zero weights, one expert, permutations).
+The same pins run against source-patched mutants of the oracle in
+test_oracle_mutants.py, each of which some pin must reject.
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------------------
+# fixtures
+# ---------------------------------------------------------------------------
+
+def _rows(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                yield line.split()
+
+
+def golden_e2m1():
+    return {int(r[0]): float(r[2]) for r in _rows("e2m1_values.txt")}
+
+
+def golden_pairs(name):
+    """[(byte, value_even, value_odd)] from a pair fixture."""
+    return [(int(r[0], 16), float(r[1]), float(r[2])) for r in _rows(name)]
+
+
+def golden_int8():
+    return [(int(r[0], 16), int(r[1])) for r in _rows("int8_rows.txt")]
+
+
+def golden_int3():
+    low, high, values = None, None, []
+    for r in _rows("int3_planes.txt"):
+        if r[0] == "low":
+            low = [int(v, 16) for v in r[1:]]
+        elif r[0] == "high":
+            high = [int(v, 16) for v in r[1:]]
+        elif r[0] == "values":
+            values += [int(v) for v in r[1:]]
+    return low, high, values
+
+
+def _same_bits(a, b) -> bool:
+    return np.float64(a).tobytes() == np.float64(b).tobytes()
+
+
+def _qm(fmt, O, K, gs, q, scales, q2=None):
+    return synth.QMatrix(fmt, O, K, gs, np.ascontiguousarray(q),
+                         None if q2 is None else np.ascontiguousarray(q2),
+                         np.ascontiguousarray(scales, dtype=np.float32))
+
+
+# ---------------------------------------------------------------------------
+# decode: code tables and layouts
+# ---------------------------------------------------------------------------
+
+def pin_e2m1_table(lib):
+    table = golden_e2m1()
+    assert len(table) == 16
+    for code, val in table.items():
+        got = lib.e2m1(code)
+        assert _same_bits(got, val), f"e2m1({code}) = {got!r}, expected {val!r}"
+
+
+def pin_int4_pairs(lib):
+    for fmt in (synth.FMT_I4_GS, synth.FMT_I4_ROW):
+        rows = golden_pairs("int4_pairs.txt")
+        q = np.array([[b for b, _, _ in rows]], dtype=np.uint8)
+        K = 2 * q.shape[1]
+        m = _qm(fmt, 1, K, K, q, np.ones((1, 1), np.float32))
+        got = lib.code_values(m)[0]
+        want = np.array([v for _, a, b in rows for v in (a, b)])
+        assert np.array_equal(got, want), f"fmt {fmt}: {got} != {want}"
+
+
+def pin_mxfp4_pairs(lib):
+    rows = golden_pairs("mxfp4_pairs.txt")
+    pad = (-len(rows)) % 16                 # whole groups of 32 inputs
+    q = np.array([[b for b, _, _ in rows] + [0] * pad], dtype=np.uint8)
+    K = 2 * q.shape[1]
+    m = _qm(synth.FMT_MXFP4, 1, K, 32, q, np.ones((1, K // 32), np.float32))
+    got = lib.code_values(m)[0]
+    want = [v for _, a, b in rows for v in (a, b)]
+    for k, v in enumerate(want):
+        assert _same_bits(got[k], v), f"k={k}: {got[k]!r} != {v!r}"
+
+
+def pin_int8_rows(lib):
+    rows = golden_int8()
+    q = np.array([[b for b, _ in rows]], dtype=np.uint8).view(np.int8)
+    m = _qm(synth.FMT_I8_ROW, 1, q.shape[1], q.shape[1], q, np.ones((1, 1), np.float32))
+    got = lib.code_values(m)[0]
+    assert np.array_equal(got, [v for _, v in rows]), got
+
+
+def pin_int3_planes(lib):
+    low, high, values = golden_int3()
+    m = _qm(synth.FMT_I3_G64, 1, 64, 64, np.array([low], dtype=np.uint32),
+            np.ones((1, 1), np.float32), q2=np.array([high], dtype=np.uint32))
+    got = lib.code_values(m)[0]
+    assert np.array_equal(got, values), f"{got} != {values}"
+
+
+def pin_exhaustive_codes(lib):
+    """Every code of every format decodes to its closed form (value * 1)."""
+    # int8: all 256 bytes, two's complement
+    q = np.arange(256, dtype=np.uint8).view(np.int8).reshape(1, 256)
+    m = _qm(1, 1, 256, 256, q, np.ones((1, 1), np.float32))
+    assert np.array_equal(lib.code_values(m)[0], np.arange(256, dtype=np.uint8).view(np.int8))
+    # int4: byte b holds (b & 15, b >> 4) -> all 256 combinations
+    q = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    m = _qm(4, 1, 512, 32, q, np.ones((1, 16), np.float32))
+    v = lib.code_values(m)[0]
+    b = np.arange(256)
+    assert np.array_equal(v[0::2], (b & 15) - 8) and np.array_equal(v[1::2], (b >> 4) - 8)
+    # int3: each of the 8 codes at each of the 64 positions of a group
+    for code in range(8):
+        lo_word = (code & 3) * 0x55555555
+        hi_word = 0xFFFFFFFF if code & 4 else 0
+        m = _qm(5, 1, 64, 64, np.full((1, 4), lo_word, np.uint32), np.ones((1, 1), np.float32),
+                q2=np.full((1, 2), hi_word, np.uint32))
+        assert np.array_equal(lib.code_values(m)[0], np.full(64, code - 4)), code
+
+
+# ---------------------------------------------------------------------------
+# an independent NumPy decoder (vectorised), pinned to the same fixtures,
+# used to check the oracle's row and word indexing on large random matrices
+# ---------------------------------------------------------------------------
+
+def numpy_values(m) -> np.ndarray:
+    O, K = m.O, m.K
+    if m.fmt == 1:
+        return m.q.astype(np.float64)
+    if m.fmt in (2, 4, 7):
+        lo = (m.q & 0x0F).astype(np.int64)
+        hi = (m.q >> 4).astype(np.int64)
+        nib = np.stack([lo, hi], axis=-1).reshape(O, K)
+        if m.fmt == 7:
+            table = golden_e2m1()
+            return np.vectorize(lambda c: table[int(c)])(nib).astype(np.float64)
+        return (nib - 8).astype(np.float64)
+    if m.fmt == 5:
+        shifts2 = np.arange(16, dtype=np.uint32) * 2
+        lo = ((m.q[:, :, None] >> shifts2) & 3).reshape(O, K).astype(np.int64)
+        shifts1 = np.arange(32, dtype=np.uint32)
+        hi = ((m.q2[:, :, None] >> shifts1) & 1).reshape(O, K).astype(np.int64)
+        return (lo + 4 * hi - 4).astype(np.float64)
+    raise ValueError(m.fmt)
+
+
+def numpy_scales(m) -> np.ndarray:
+    return np.repeat(m.scales.astype(np.float64), m.gs, axis=1)
+
+
+def pin_numpy_decoder_matches_fixtures(lib):
+    """The NumPy decoder itself agrees with every fixture (so it can judge)."""
+    rows = golden_pairs("int4_pairs.txt")
+    q = np.array([[b for b, _, _ in rows]], dtype=np.uint8)
+    m = _qm(4, 1, 2 * q.shape[1], 2 * q.shape[1], q, np.ones((1, 1), np.float32))
+    assert np.array_equal(numpy_values(m)[0], [v for _, a, b in rows for v in (a, b)])
+    low, high, values = golden_int3()
+    m = _qm(5, 1, 64, 64, np.array([low], np.uint32), np.ones((1, 1), np.float32),
+            q2=np.array([high], np.uint32))
+    assert np.array_equal(numpy_values(m)[0], values)
+
+
+def _random_matrices():
+    yield synth.matrix(1, 5, 96, None, 11, 1)
+    yield synth.matrix(2, 5, 96, None, 11, 2)
+    yield synth.matrix(4, 5, 128, 32, 11, 3)
+    yield synth.matrix(4, 3, 256, 64, 11, 4)
+    yield synth.matrix(5, 4, 192, 64, 11, 5)
+    yield synth.matrix(7, 5, 128, 32, 11, 6)
+
+
+def pin_random_layouts(lib):
+    """Oracle decode == NumPy decode on random multi-row matrices."""
+    for m in _random_matrices():
+        got = lib.code_values(m)
+        want = numpy_values(m)
+        assert np.array_equal(got, want), f"fmt {m.fmt}: layout mismatch"
+
+
+def pin_dequant_rounding_and_scale_index(lib):
+    """dequant[o][k] == RNE_f32(v * s[o][k // gs]), with every group's scale distinct."""
+    for m in _random_matrices():
+        groups = m.K // m.gs
+        # distinct scales per (row, group): identifiable if mis-indexed
+        s = (1.0 + np.arange(m.O * groups, dtype=np.float64) / 64.0) * 1e-3
+        m.scales = s.reshape(m.O, groups).astype(np.float32)
+        want = (numpy_values(m) * numpy_scales(m)).astype(np.float32)   # exact product, one rounding
+        got = lib.dequant(m)
+        assert got.tobytes() == want.tobytes(), f"fmt {m.fmt}: dequant bits differ"
+
+
+def pin_signed_zero(lib):
+    """A zero code times a negative scale gives -0; MXFP4 code 8 gives -0."""
+    q = np.full((1, 16), 0x88, np.uint8)            # int4 nibble 8 -> value 0
+    m = _qm(4, 1, 32, 32, q, np.full((1, 1), -0.5, np.float32))
+    d = lib.dequant(m)
+    assert all(math.copysign(1.0, v) < 0 for v in d[0]), "0 * negative scale must be -0"
+    m = _qm(7, 1, 32, 32, q, np.full((1, 1), 0.5, np.float32))
+    d = lib.dequant(m)
+    assert all(v == 0 and math.copysign(1.0, v) < 0 for v in d[0]), "MXFP4 code 8 must be -0"
+
+
+# ---------------------------------------------------------------------------
+# GEMV
+# ---------------------------------------------------------------------------
+
+def pin_one_hot_selects_column(lib):
+    """x = e_k gives y[o] = w[o][k] exactly, so RNE_f32(y) == dequant.
+
+    Compared by value: a sum of signed zeros starting from +0 is +0, so a
+    -0 weight reads back as +0 here (outputs compare equal across signs).
+    """
+    for m in _random_matrices():
+        x = np.eye(m.K, dtype=np.float32)
+        y, a = lib.gemv(m, x)                  # y[k][o]
+        d = lib.dequant(m)                     # [o][k]
+        assert np.array_equal(y.T.astype(np.float32), d), f"fmt {m.fmt}"
+        assert np.array_equal(a.T, np.abs(y.T))
+
+
+def pin_fraction_brute_force(lib):
+    """Tiny shapes: oracle y within f64 rounding of the exact rational sum."""
+    for m in _random_matrices():
+        O, K = min(m.O, 3), m.K
+        x = synth.activations(2, K, 99, m.fmt)
+        y, a = lib.gemv(m, x)
+        v = numpy_values(m)
+        sc = numpy_scales(m)
+        for s in range(2):
+            for o in range(O):
+                exact = sum(Fraction(v[o, k]) * Fraction(float(sc[o, k])) * Fraction(float(x[s, k]))
+                            for k in range(K))
+                mag = sum(abs(Fraction(v[o, k]) * Fraction(float(sc[o, k])) * Fraction(float(x[s, k])))
+                          for k in range(K))
+                assert abs(Fraction(y[s, o]) - exact) <= mag * Fraction(2 * K, 2**53), (m.fmt, s, o)
+                assert abs(Fraction(a[s, o]) - mag) <= mag * Fraction(2 * K, 2**53), (m.fmt, s, o)
+
+
+def _group_sums(x, gs):
+    return [math.fsum(float(v) for v in x[g * gs:(g + 1) * gs]) for g in range(len(x) // gs)]
+
+
+def pin_constant_codes_closed_form(lib):
+    """All codes equal c: y[o] = value(c) * sum_g s[o][g] * sum_{k in g} x_k."""
+    K = 256
+    x = synth.activations(1, K, 77, 1)[0]
+    e2m1 = golden_e2m1()
+    cases = []
+    for c in range(16):   # int4, gs 32 and gs 64
+        for gs in (32, 64):
+            cases.append((4, gs, np.full((3, K // 2), c | (c << 4), np.uint8), None, c - 8))
+    for c in range(16):
+        cases.append((7, 32, np.full((3, K // 2), c | (c << 4), np.uint8), None, e2m1[c]))
+    for c in (-127, -1, 0, 5, 127):
+        cases.append((1, K, np.full((3, K), c, np.int8), None, c))
+    for c in range(8):
+        cases.append((5, 64, np.full((3, K // 16), (c & 3) * 0x55555555, np.uint32),
+                      np.full((3, K // 32), 0xFFFFFFFF if c & 4 else 0, np.uint32), c - 4))
+    for fmt, gs, q, q2, val in cases:
+        G = K // gs
+        s = synth.rng_for(5, fmt, gs).uniform(1e-3, 2e-2, size=(3, G)).astype(np.float32)
+        m = _qm(fmt, 3, K, gs, q, s, q2=q2)
+        y, _ = lib.gemv(m, x[None, :])
+        xs = _group_sums(x, gs)
+        xa = _group_sums(np.abs(x), gs)
+        for o in range(3):
+            want = val * math.fsum(float(s[o, g]) * xs[g] for g in range(G))
+            ref = abs(val) * math.fsum(float(s[o, g]) * xa[g] for g in range(G))
+            assert abs(y[0, o] - want) <= 2 * K * 2.0**-52 * ref, (fmt, gs, val, o, y[0, o], want)
+
+
+def pin_zero_scales(lib):
+    for m in _random_matrices():
+        m.scales = np.zeros_like(m.scales)
+        y, a = lib.gemv(m, synth.activations(2, m.K, 3))
+        assert np.all(y == 0) and np.all(a == 0), m.fmt
+
+
+def pin_power_of_two_scaling(lib):
+    """Scaling x by 2^j scales y by 2^j bit for bit (no rounding changes)."""
+    for m in _random_matrices():
+        x = synth.activations(2, m.K, 4)
+        y0, _ = lib.gemv(m, x)
+        for j in (3, -5):
+            y1, _ = lib.gemv(m, np.ldexp(x, j).astype(np.float32))
+            assert np.array_equal(y1, np.ldexp(y0, j)), (m.fmt, j)
+
+
+def pin_normaliser_bounds(lib):
+    for m in _random_matrices():
+        y, a = lib.gemv(m, synth.activations(3, m.K, 5))
+        assert np.all(a >= np.abs(y)) and np.all(a > 0)
+
+
+def pin_token_rows_independent(lib):
+    """Row s of a batch equals the single-token result for x[s] (no transposition)."""
+    for m in _random_matrices():
+        x = synth.activations(3, m.K, 6)
+        y, a = lib.gemv(m, x)
+        for s in range(3):
+            y1, a1 = lib.gemv(m, x[s:s + 1])
+            assert np.array_equal(y[s], y1[0]) and np.array_equal(a[s], a1[0]), (m.fmt, s)
+
+
+# ---------------------------------------------------------------------------
+# SwiGLU and gate_up
+# ---------------------------------------------------------------------------
+
+def pin_silu(lib):
+    from scipy.special import expit
+    assert lib.silu(0.0) == 0.0
+    for z in np.linspace(-30, 30, 241):
+        want = z * expit(z)
+        got = lib.silu(z)
+        assert abs(got - want) <= 4e-16 * max(abs(want), 1e-300) + 1e-300, (z, got, want)
+        # silu(z) - silu(-z) = z
+        assert abs(lib.silu(z) - lib.silu(-z) - z) <= 1e-15 * max(abs(z), 1.0)
+    assert abs(lib.silu(50.0) - 50.0) < 1e-18 * 50
+    assert lib.silu(-800.0) == 0.0 or abs(lib.silu(-800.0)) < 1e-300
+
+
+def pin_gate_up_one_hot(lib):
+    """x = e_k: g = w_gate[i][k], u = w_up[i][k], h = g * expit(g) * u."""
+    from scipy.special import expit
+    for fmt, gs in ((4, 32), (7, 32), (1, None), (5, 64)):
+        K = 128
+        G = synth.matrix(fmt, 6, K, gs, 21, fmt, 0)
+        U = synth.matrix(fmt, 6, K, gs, 21, fmt, 1)
+        # larger scales so silu works away from its linear part
+        G.scales = (G.scales * 200).astype(np.float32)
+        dg = lib.dequant(G).astype(np.float64)
+        du = lib.dequant(U).astype(np.float64)
+        for k in (0, 1, 31, 64, 127):
+            x = np.zeros((1, K), np.float32)
+            x[0, k] = 1.0
+            r = lib.gate_up(G, U, x)
+            g = lib.gemv(G, x)[0][0]
+            assert np.allclose(r["g"][0], g, rtol=0, atol=0)
+            assert np.allclose(np.float32(r["g"][0]), dg[:, k], rtol=0, atol=0)
+            assert np.allclose(np.float32(r["u"][0]), du[:, k], rtol=0, atol=0)
+            want = r["g"][0] * expit(r["g"][0]) * r["u"][0]
+            assert np.allclose(r["h"][0], want, rtol=1e-15, atol=0), (fmt, k)
+
+
+def pin_gate_up_zero(lib):
+    G = synth.matrix(4, 8, 64, 32, 22, 0)
+    U = synth.matrix(4, 8, 64, 32, 22, 1)
+    x = synth.activations(2, 64, 22)
+    Gz = _qm(4, 8, 64, 32, G.q, np.zeros_like(G.scales))
+    Uz = _qm(4, 8, 64, 32, U.q, np.zeros_like(U.scales))
+    assert np.all(lib.gate_up(Gz, U, x)["h"] == 0)
+    assert np.all(lib.gate_up(G, Uz, x)["h"] == 0)
+    r = lib.gate_up(G, U, x)
+    assert np.all(r["nh"] >= 0)
+
+
+def pin_gate_up_rows(lib):
+    """h[s][i] uses gate row i and up row i with token s (gate and up not swapped)."""
+    from scipy.special import expit
+    G = synth.matrix(4, 8, 64, 32, 23, 0)
+    U = synth.matrix(4, 8, 64, 32, 23, 1)
+    G.scales = (G.scales * 50).astype(np.float32)
+    x = synth.activations(3, 64, 23)
+    r = lib.gate_up(G, U, x)
+    g, _ = lib.gemv(G, x)
+    u, _ = lib.gemv(U, x)
+    assert np.array_equal(r["g"], g) and np.array_equal(r["u"], u)
+    assert np.allclose(r["h"], g * expit(g) * u, rtol=1e-14, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# expert group
+# ---------------------------------------------------------------------------
+
+def _tiny_experts(n, fmt=4, gs=32, H=64, I=32, seed=31):
+    return [synth.expert(fmt, H, I, gs, seed, i) for i in range(n)]
+
+
+def _mlp(lib, ex, x):
+    h = lib.gate_up(ex.gate, ex.up, x)["h"]
+    y, _ = lib.gemv(ex.down, h)
+    return y
+
+
+def pin_group_shared_only(lib):
+    exs = _tiny_experts(6)
+    x = synth.activations(2, 64, 32)
+    ids = np.array([[0, 1, 2], [3, 4, 1]], np.int32)
+    w = np.zeros((2, 3), np.float32)
+    y, a = lib.expert_group(exs, ids, w, 5, x)
+    want = _mlp(lib, exs[5], x)
+    assert np.allclose(y, want, rtol=1e-13, atol=1e-15)
+    y0, _ = lib.expert_group(exs, ids, w, -1, x)
+    assert np.all(y0 == 0)
+
+
+def pin_group_single_expert(lib):
+    exs = _tiny_experts(6)
+    x = synth.activations(2, 64, 33)
+    ids = np.array([[0, 1, 2], [3, 4, 1]], np.int32)
+    for t, r in ((0, 1), (1, 2)):
+        w = np.zeros((2, 3), np.float32)
+        w[t, r] = 1.0
+        y, _ = lib.expert_group(exs, ids, w, 5, x)
+        want = _mlp(lib, exs[5], x)
+        want[t] += _mlp(lib, exs[int(ids[t, r])], x[t:t + 1])[0]
+        assert np.allclose(y, want, rtol=1e-13, atol=1e-15), (t, r)
+
+
+def pin_group_weights_scale_outputs(lib):
+    """w[t][r] multiplies expert r's output: doubling one weight adds that output once more."""
+    exs = _tiny_experts(5)
+    x = synth.activations(1, 64, 34)
+    ids = np.array([[4, 0, 2]], np.int32)
+    w = np.array([[0.25, 0.5, 0.125]], np.float32)
+    y1, _ = lib.expert_group(exs, ids, w, -1, x)
+    w2 = w.copy()
+    w2[0, 1] *= 2
+    y2, _ = lib.expert_group(exs, ids, w2, -1, x)
+    d = _mlp(lib, exs[0], x)[0] * 0.5
+    assert np.allclose(y2[0] - y1[0], d, rtol=1e-12, atol=1e-15)
+
+
+def pin_group_identical_experts(lib):
+    """Every expert the same: y = (sum w) * MLP(x) + MLP_shared(x)."""
+    base = _tiny_experts(1)[0]
+    shared = _tiny_experts(1, seed=35)[0]
+    exs = [base] * 7 + [shared]
+    S, k = 3, 4
+    ids, w = synth.routing(S, 7, k, 36)
+    x = synth.activations(S, 64, 36)
+    y, _ = lib.expert_group(exs, ids, w, 7, x)
+    want = w.astype(np.float64).sum(axis=1)[:, None] * _mlp(lib, base, x) + _mlp(lib, shared, x)
+    assert np.allclose(y, want, rtol=1e-12, atol=1e-15)
+
+
+def pin_group_permutation(lib):
+    exs = _tiny_experts(9)
+    S, k = 2, 4
+    ids, w = synth.routing(S, 8, k, 37)
+    x = synth.activations(S, 64, 37)
+    y, a = lib.expert_group(exs, ids, w, 8, x)
+    perm = [2, 0, 3, 1]
+    y2, a2 = lib.expert_group(exs, ids[:, perm], w[:, perm], 8, x)
+    assert np.all(np.abs(y - y2) <= 1e-13 * a)
+    assert np.allclose(a, a2, rtol=1e-13)
+
+
+def pin_group_tokens_independent(lib):
+    """Token t of a batch equals the batch of just token t."""
+    exs = _tiny_experts(9)
+    S, k = 3, 4
+    ids, w = synth.routing(S, 8, k, 38)
+    x = synth.activations(S, 64, 38)
+    y, a = lib.expert_group(exs, ids, w, 8, x)
+    for t in range(S):
+        y1, a1 = lib.expert_group(exs, ids[t:t + 1], w[t:t + 1], 8, x[t:t + 1])
+        assert np.array_equal(y[t], y1[0]) and np.array_equal(a[t], a1[0]), t
+
+
+def pin_group_bad_id_is_nan(lib):
+    exs = _tiny_experts(4)
+    x = synth.activations(2, 64, 39)
+    ids = np.array([[0, 9], [1, 2]], np.int32)
+    w = np.full((2, 2), 0.5, np.float32)
+    y, _ = lib.expert_group(exs, ids, w, 3, x)
+    assert np.all(np.isnan(y[0])) and np.all(np.isfinite(y[1]))
+
+
+def pin_group_normaliser(lib):
+    exs = _tiny_experts(9)
+    ids, w = synth.routing(2, 8, 4, 40)
+    x = synth.activations(2, 64, 40)
+    y, a = lib.expert_group(exs, ids, w, 8, x)
+    assert np.all(a >= np.abs(y)) and np.all(a > 0)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -1,0 +1,86 @@
+"""Mutation tests of the pins: each plausible mistake planted in the oracle's
+source (on the CPU, in a temporary copy) must make at least one pin fail.
+
+Mutants follow the silent failure modes the correctness section of "colibri
+Vulkan compute backend complete guide" names (a mis-decoded nibble, a
+reversed group direction, scrambled scale order) plus dropped terms, wrong
+signs, swapped operands and transposed indexes.  Every mutant keeps all
+memory accesses in bounds.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle import build as obuild
+import pinlib
+
+SRC = open(obuild.SRC).read()
+
+MUTANTS = {
+    "nibble_order_swapped": ("    if (k % 2 == 0)\n        return byte & 0x0F;",
+                             "    if (k % 2 != 0)\n        return byte & 0x0F;"),
+    "int4_offset_dropped": ("return (double)(nibble_at(row, k) - 8);", "return (double)(nibble_at(row, k));"),
+    "int4_offset_wrong": ("return (double)(nibble_at(row, k) - 8);", "return (double)(nibble_at(row, k) - 7);"),
+    "int4_row_stride": ("        const uint8_t *row = (const uint8_t *)m->q + o * (m->K / 2);\n"
+                        "        return (double)(nibble_at(row, k) - 8);",
+                        "        const uint8_t *row = (const uint8_t *)m->q + o * (m->K / 4);\n"
+                        "        return (double)(nibble_at(row, k) - 8);"),
+    "group_direction_reversed": ("return (double)m->scales[o * groups + k / m->gs];",
+                                 "return (double)m->scales[o * groups + (m->K - 1 - k) / m->gs];"),
+    "scale_index_shifted": ("return (double)m->scales[o * groups + k / m->gs];",
+                            "return (double)m->scales[o * groups + (k / m->gs + 1) % groups];"),
+    "scale_row_ignored": ("return (double)m->scales[o * groups + k / m->gs];",
+                          "return (double)m->scales[k / m->gs];"),
+    "e2m1_bias_wrong": ("mag = ldexp(1.0 + 0.5 * mant, expo - 1);", "mag = ldexp(1.0 + 0.5 * mant, expo);"),
+    "e2m1_subnormal_wrong": ("mag = 0.5 * mant;", "mag = 1.0 * mant;"),
+    "e2m1_sign_ignored": ("return sign ? -mag : mag;", "return (void)sign, mag;"),
+    "int3_planes_swapped": ("return low | (high << 2);", "return (low << 1) | high;"),
+    "int3_offset_wrong": ("return (double)(int3_code(low_row, high_row, k) - 4);",
+                          "return (double)(int3_code(low_row, high_row, k) - 3);"),
+    "int3_low_bits_reversed": ("(low_row[k / 16] >> (2 * (k % 16)))", "(low_row[k / 16] >> (30 - 2 * (k % 16)))"),
+    "int3_high_bits_reversed": ("(high_row[k / 32] >> (k % 32))", "(high_row[k / 32] >> (31 - k % 32))"),
+    "int8_unsigned": ("return (double)row[k];", "return (double)(uint8_t)row[k];"),
+    "dot_first_term_dropped": ("        sum += term;", "        sum += (k == 0) ? 0.0 : term;"),
+    "dot_sign_flipped": ("        double term = orc_weight(m, o, k) * xk;", "        double term = -orc_weight(m, o, k) * xk;"),
+    "normaliser_not_absolute": ("        mag += fabs(term);", "        mag += term;"),
+    "gemv_output_transposed": ("row_dot(m, o, x + s * m->K, NULL, &y[s * m->O + o]",
+                               "row_dot(m, o, x + s * m->K, NULL, &y[o * S + s]"),
+    "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
+    "silu_missing_z": ("return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
+    "gate_up_swapped": ("h[idx] = orc_silu(g) * u;", "h[idx] = orc_silu(u) * g;"),
+    "router_weight_dropped": ("yt[o] += wr * dy_work[o];", "yt[o] += dy_work[o];"),
+    "shared_expert_dropped": ("                yt[o] += dy_work[o];", "                yt[o] += 0.0 * dy_work[o];"),
+    "down_uses_gate_rows": ("mlp_one(&gates[e], &ups[e], &downs[e],", "mlp_one(&gates[e], &ups[e], &downs[(e + 1) % n_experts],"),
+    "token_x_not_advanced": ("mlp_one(&gates[e], &ups[e], &downs[e], x + t * gates[e].K,",
+                             "mlp_one(&gates[e], &ups[e], &downs[e], x,"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    search, replace = MUTANTS[name]
+    assert SRC.count(search) == 1, f"mutant {name}: patch site not unique"
+    src = tmp_path / "mutant.c"
+    src.write_text(SRC.replace(search, replace))
+    lib_path = str(tmp_path / "libmutant.so")
+    obuild.build(str(src), lib_path, extra=("-w",))
+    lib = oracle.load(lib_path)
+    failed = []
+    for pin in pinlib.ALL_PINS:
+        try:
+            pin(lib)
+        except AssertionError:
+            failed.append(pin.__name__)
+    assert failed, f"mutant {name} passed every pin"
+
+
+def test_unmutated_copy_passes(tmp_path):
+    """The same build route with no patch passes every pin (the harness is fair)."""
+    src = tmp_path / "same.c"
+    src.write_text(SRC)
+    lib_path = str(tmp_path / "libsame.so")
+    obuild.build(str(src), lib_path)
+    lib = oracle.load(lib_path)
+    for pin in pinlib.ALL_PINS:
+        pin(lib)
