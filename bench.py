@@ -1,0 +1,243 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed expert group (the hot path) on one MI355X.
+
+A step is one dqg_expert_group call: stage x, stream every needed weight
+byte of the token batch's routed experts and the shared expert, decode,
+dot, SwiGLU, down projection and the rank-order weighted combine, y written.
+The default workload is the int4-g32 group: 256 resident experts of
+H = 6144, I = 2048 plus a shared expert, top-8 routing, 1 token.
+
+Inputs are resident in HBM before timing.  Every step takes a fresh
+routing (ids uniform without replacement, weights the softmax of N(0,1)
+logits) and a fresh x from a seeded pool, and the shared expert rotates
+over several copies, so the 256 MB Infinity Cache cannot serve a step's
+weights from the previous steps.
+
+Prints one JSON line: the metric is weight-stream GB/s (algorithmic bytes:
+codes + scales of each distinct expert the step needs, once, plus x and
+y) over wall time; `roofline` is the dominant kernel (the gate/up launch)
+timed with HIP events on its stream; `cpu_baseline` is the CPU oracle on a
+bounded sample of the same steps.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "quant GEMV weight-stream GB/s (% of HBM peak); µs per top-8 expert MLP"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def matrix_bytes(m) -> int:
+    n = m.q.nbytes + m.scales.nbytes
+    if m.q2 is not None:
+        n += m.q2.nbytes
+    return n
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--workload", default="int4g32_expert_group_256top8_shared")
+    ap.add_argument("--tokens", type=int, default=None, help="token batch (default: the workload's first)")
+    ap.add_argument("--pool", type=int, default=1024, help="distinct routings drawn")
+    ap.add_argument("--shared-copies", type=int, default=12)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the path is measured "
+              "on one GPU's share; see DESIGN.md for how it would shard)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import synth
+    import dequant_gemv_expert_amd as dq
+    from dequant_gemv_expert_amd import _lib as L
+
+    c = synth.WORKLOADS[args.workload]
+    if c["kind"] != "group":
+        raise SystemExit("bench.py times the routed expert group workloads")
+    S = args.tokens or c["S"][0]
+    E, k, H, I, fmt, gs, seed = c["E"], c["k"], c["H"], c["I"], c["fmt"], c["gs"], c["seed"]
+    n_shared = args.shared_copies if c["shared"] else 0
+    torch.cuda.set_device(0)
+    dev_name = torch.cuda.get_device_name(0)
+
+    # -- resident experts ------------------------------------------------
+    t0 = time.time()
+    from concurrent.futures import ThreadPoolExecutor
+    n_total = E + n_shared
+    experts = [None] * n_total
+    exp_bytes = gu_bytes = down_bytes = 0
+    with ThreadPoolExecutor(16) as ex:
+        for b0 in range(0, n_total, 16):
+            idx = list(range(b0, min(n_total, b0 + 16)))
+            hs = list(ex.map(lambda i: synth.expert(fmt, H, I, gs, seed, i), idx))
+            for i, h in zip(idx, hs):
+                experts[i] = dq.Expert.upload(h)
+                if i == 0:
+                    gu_bytes = matrix_bytes(h.gate) + matrix_bytes(h.up)
+                    down_bytes = matrix_bytes(h.down)
+                    exp_bytes = gu_bytes + down_bytes
+    table = dq.ExpertTable(experts)
+    torch.cuda.synchronize()
+    log(f"[bench] {dev_name}: {n_total} experts resident ({n_total * exp_bytes / 1e9:.2f} GB) "
+        f"in {time.time() - t0:.1f}s")
+
+    # -- routing and activation pool ---------------------------------------
+    P = args.pool
+    ids = np.empty((P, S, k), np.int32)
+    w = np.empty((P, S, k), np.float32)
+    for p in range(P):
+        ids[p], w[p] = synth.routing(S, E, k, seed, 7, S, p)
+    x = synth.activations(P * S, H, seed, 8, S).reshape(P, S, H)
+    union = np.array([len(np.unique(ids[p])) for p in range(P)])
+    ids_d = torch.from_numpy(ids).cuda()
+    w_d = torch.from_numpy(w).cuda()
+    x_d = torch.from_numpy(x).cuda()
+    y_d = torch.empty((S, H), dtype=torch.float32, device="cuda")
+    scratch = table.scratch(S, k)
+    lib = L.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    nbytes_scratch = scratch.numel()
+    shared_of = (lambda i: E + i % n_shared) if n_shared else (lambda i: -1)
+    n_sh = 1 if n_shared else 0
+
+    def call_args(i):
+        p = i % P
+        return (table.handle, S, k, ids_d[p].data_ptr(), w_d[p].data_ptr(), shared_of(i),
+                x_d[p].data_ptr(), y_d.data_ptr(), scratch.data_ptr(), nbytes_scratch, stream)
+
+    plan = [call_args(i) for i in range(args.warmup + args.steps)]
+    io_bytes = S * H * 4 * 2                       # x read, y written
+    h_bytes = (S * k + S * n_sh) * I * 4           # h written by gate/up, read by down
+
+    def step_bytes(i):
+        units = union[i % P] + n_sh
+        return units * exp_bytes + io_bytes
+
+    def step_bytes_gate_up(i):
+        return (union[i % P] + n_sh) * gu_bytes + S * H * 4 + h_bytes
+
+    # -- warmup ------------------------------------------------------------
+    fn = lib.dqg_expert_group
+    for i in range(args.warmup):
+        rc = fn(*plan[i])
+        if rc:
+            raise RuntimeError(dq.dqg_last_error())
+    torch.cuda.synchronize()
+
+    # -- timed region (HIP events around each kernel, on its stream) --------
+    K = args.steps
+    dq.dqg_prof_begin(2 * K)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.warmup, args.warmup + K):
+        rc = fn(*plan[i])
+        if rc:
+            raise RuntimeError(dq.dqg_last_error())
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_start
+    prof = dq.dqg_prof_end()
+
+    total_bytes = sum(step_bytes(i) for i in range(args.warmup, args.warmup + K))
+    gu_total = sum(step_bytes_gate_up(i) for i in range(args.warmup, args.warmup + K))
+    ms_per_step = t_wall * 1e3 / K
+    value = total_bytes / t_wall / 1e9
+    n_a, ms_a = prof.get("group_gate_up", (0, 0.0))
+    n_b, ms_b = prof.get("group_down", (0, 0.0))
+    achieved = gu_total / (ms_a * 1e-3) / 1e9 if ms_a > 0 else None
+    down_total = sum((union[i % P] + n_sh) * down_bytes + h_bytes + S * H * 4
+                     for i in range(args.warmup, args.warmup + K))
+    log(f"[bench] {K} steps: {ms_per_step * 1e3:.1f} us/step wall, {value:.0f} GB/s; "
+        f"gate_up kernel {ms_a / max(n_a, 1) * 1e3:.1f} us avg ({achieved or 0:.0f} GB/s), "
+        f"down kernel {ms_b / max(n_b, 1) * 1e3:.1f} us avg "
+        f"({down_total / (ms_b * 1e-3) / 1e9 if ms_b else 0:.0f} GB/s); "
+        f"mean union {union.mean():.2f} experts + {n_sh} shared")
+
+    # -- CPU oracle on a bounded sample -------------------------------------
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        cache = {}
+
+        def host_expert(e):
+            if e not in cache:
+                cache[e] = synth.expert(fmt, H, I, gs, seed, e)
+            return cache[e]
+
+        class View:
+            def __len__(self):
+                return n_total
+
+            def __getitem__(self, e):
+                return host_expert(int(e))
+
+        threads = oracle.get_threads()
+        spent, calls, cbytes = 0.0, 0, 0
+        while spent < args.cpu_seconds and calls < P:
+            i = args.warmup + calls
+            p = i % P
+            for e in set(ids[p].ravel().tolist()) | ({shared_of(i)} if n_shared else set()):
+                host_expert(e)   # drawn before the clock starts
+            t = time.perf_counter()
+            oracle.expert_group(View(), ids[p], w[p], shared_of(i), x[p])
+            spent += time.perf_counter() - t
+            calls += 1
+            cbytes += step_bytes(i)
+            if len(cache) > 64:
+                cache.clear()
+        cpu = {"value": round(cbytes / spent / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+               "sample": f"{calls} expert-group calls ({S} token(s), top-{k} of {E}"
+                         f"{' + shared' if n_sh else ''}) from the same routing pool, {spent:.1f} s",
+               "us_per_call": round(spent / calls * 1e6, 1)}
+        log(f"[bench] cpu oracle: {cpu['value']} GB/s on {threads} threads ({calls} calls)")
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_call": round(ms_per_step * 1e3, 2),
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": S, "top_k": k, "experts": E,
+                   "shared_expert": bool(n_sh), "H": H, "I": I, "format": f"fmt {fmt}, gs {gs}",
+                   "routing_pool": P, "shared_copies": n_shared, "device": dev_name},
+        "roofline": {"kernel": "group_gate_up", "bound": "hbm",
+                     "achieved": round(achieved, 1) if achieved else None, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
+                     "traffic": None, "avg_us": round(ms_a / max(n_a, 1) * 1e3, 2),
+                     "bytes_per_launch": round(gu_total / K)},
+        "roofline_down": {"kernel": "group_down", "avg_us": round(ms_b / max(n_b, 1) * 1e3, 2),
+                          "achieved": round(down_total / (ms_b * 1e-3) / 1e9, 1) if ms_b else None,
+                          "bytes_per_launch": round(down_total / K)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    table.close()
+
+
+if __name__ == "__main__":
+    main()

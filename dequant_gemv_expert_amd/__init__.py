@@ -1,0 +1,15 @@
+"""Quantised GEMV and expert-MLP kernels for AMD Instinct MI355X (gfx950).
+
+The work happens in libdqg.so (hand-written HIP kernels behind the C ABI of
+include/dqg.h); this package is its Python binding.
+"""
+from ._lib import (DQG_I3_G64, DQG_I4_GS, DQG_I4_ROW, DQG_I8_ROW, DQG_MXFP4, DqgError, Expert,
+                   ExpertTable, Matrix, dqg_dequant, dqg_expert_group, dqg_expert_group_issue,
+                   dqg_expert_group_take, dqg_gate_up, dqg_last_error, dqg_matmul, dqg_prof_begin,
+                   dqg_prof_end, dqg_stats, dqg_stats_reset, load)
+
+__all__ = ["DQG_I3_G64", "DQG_I4_GS", "DQG_I4_ROW", "DQG_I8_ROW", "DQG_MXFP4", "DqgError", "Expert",
+           "ExpertTable", "Matrix", "dqg_dequant", "dqg_expert_group", "dqg_expert_group_issue",
+           "dqg_expert_group_take", "dqg_gate_up", "dqg_last_error", "dqg_matmul", "dqg_prof_begin",
+           "dqg_prof_end", "dqg_stats",
+           "dqg_stats_reset", "load"]

@@ -1,0 +1,275 @@
+"""ctypes binding of libdqg.so: the C ABI of include/dqg.h, one Python
+function per C entry point, with the same names.
+
+Argument marshalling only: every step of the path runs in the library's
+HIP kernels.  PyTorch supplies device memory and the current stream.  There
+is no fallback: a missing library or a tensor that is not on a GPU raises.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Optional, Sequence
+
+import torch
+
+from . import build as _build
+
+DQG_OK = 0
+STATUS = {0: "DQG_OK", -1: "DQG_EINVAL", -2: "DQG_EFORMAT", -3: "DQG_ESHAPE", -4: "DQG_EDEVICE",
+          -5: "DQG_ELAUNCH", -6: "DQG_ENOMEM", -7: "DQG_EROUTE"}
+
+DQG_I8_ROW, DQG_I4_ROW, DQG_I4_GS, DQG_I3_G64, DQG_MXFP4 = 1, 2, 4, 5, 7
+
+
+class DqgError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{STATUS.get(code, code)}: {message}")
+        self.code = code
+
+
+class dqg_matrix(C.Structure):
+    _fields_ = [("fmt", C.c_int32), ("O", C.c_int32), ("K", C.c_int32), ("gs", C.c_int32),
+                ("q", C.c_void_p), ("q2", C.c_void_p), ("scales", C.c_void_p)]
+
+
+class dqg_expert(C.Structure):
+    _fields_ = [("gate", dqg_matrix), ("up", dqg_matrix), ("down", dqg_matrix)]
+
+
+class dqg_ticket(C.Structure):
+    _fields_ = [("event", C.c_void_p), ("flag", C.c_void_p), ("status", C.c_int32)]
+
+
+class dqg_counters(C.Structure):
+    _fields_ = [("calls_matmul", C.c_uint64), ("calls_gate_up", C.c_uint64),
+                ("calls_dequant", C.c_uint64), ("calls_expert_group", C.c_uint64),
+                ("launches", C.c_uint64), ("bytes", C.c_uint64)]
+
+
+class dqg_prof_record(C.Structure):
+    _fields_ = [("kernel", C.c_char * 32), ("launches", C.c_int64), ("total_ms", C.c_double)]
+
+
+# Every symbol the header declares, with its ctypes signature.
+_P, _I32, _SZ = C.c_void_p, C.c_int32, C.c_size_t
+SIGNATURES = {
+    "dqg_matmul": (C.c_int, [C.POINTER(dqg_matrix), _P, _I32, _P, _P]),
+    "dqg_gate_up": (C.c_int, [C.POINTER(dqg_matrix), C.POINTER(dqg_matrix), _P, _I32, _P, _P]),
+    "dqg_dequant": (C.c_int, [C.POINTER(dqg_matrix), _P, _P]),
+    "dqg_expert_table_create": (C.c_int, [C.POINTER(dqg_expert), _I32, C.POINTER(C.c_void_p)]),
+    "dqg_expert_table_destroy": (None, [_P]),
+    "dqg_expert_group_scratch_bytes": (_SZ, [_P, _I32, _I32]),
+    "dqg_expert_group": (C.c_int, [_P, _I32, _I32, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
+    "dqg_expert_group_issue": (C.c_int, [_P, _I32, _I32, _P, _P, _I32, _P, _P, _P, _SZ, _P,
+                                         C.POINTER(dqg_ticket)]),
+    "dqg_expert_group_take": (C.c_int, [C.POINTER(dqg_ticket)]),
+    "dqg_prof_begin": (C.c_int, [_I32]),
+    "dqg_prof_end": (C.c_int, [C.POINTER(dqg_prof_record), _I32, C.POINTER(_I32)]),
+    "dqg_last_error": (C.c_char_p, []),
+    "dqg_stats": (None, [C.POINTER(dqg_counters)]),
+    "dqg_stats_reset": (None, []),
+}
+
+_lib = None
+
+
+def library_path() -> str:
+    return os.environ.get("DQG_LIBRARY", _build.LIB)
+
+
+def load() -> C.CDLL:
+    """Load libdqg.so (built in-tree by __graft_entry__.build()); raise if absent."""
+    global _lib
+    if _lib is None:
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"libdqg.so is not built ({path}); run __graft_entry__.build()")
+        lib = C.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != DQG_OK:
+        raise DqgError(rc, load().dqg_last_error().decode())
+
+
+def _dev(t: Optional[torch.Tensor], name: str, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+class Matrix:
+    """A resident quantised matrix: device tensors q, q2 (fmt 5), scales."""
+
+    def __init__(self, fmt: int, O: int, K: int, gs: int, q: torch.Tensor,
+                 scales: torch.Tensor, q2: Optional[torch.Tensor] = None):
+        self.fmt, self.O, self.K, self.gs = int(fmt), int(O), int(K), int(gs)
+        self.q, self.q2, self.scales = q, q2, scales
+        self.struct = dqg_matrix(self.fmt, self.O, self.K, self.gs, _dev(q, "q"),
+                                 _dev(q2, "q2"), _dev(scales, "scales", torch.float32))
+
+    @classmethod
+    def upload(cls, m, device="cuda") -> "Matrix":
+        """Copy a host matrix (fields fmt, O, K, gs, q, q2, scales as numpy) to the GPU."""
+        to = lambda a: None if a is None else torch.from_numpy(a).to(device)
+        return cls(m.fmt, m.O, m.K, m.gs, to(m.q), to(m.scales), to(m.q2))
+
+    @property
+    def nbytes(self) -> int:
+        n = self.q.numel() * self.q.element_size() + self.scales.numel() * 4
+        if self.q2 is not None:
+            n += self.q2.numel() * self.q2.element_size()
+        return n
+
+
+def dqg_matmul(W: Matrix, x: torch.Tensor, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    S = x.shape[0]
+    if y is None:
+        y = torch.empty((S, W.O), dtype=torch.float32, device=x.device)
+    _check(load().dqg_matmul(C.byref(W.struct), _dev(x, "x", torch.float32), S,
+                             _dev(y, "y", torch.float32), _stream(stream)))
+    return y
+
+
+def dqg_gate_up(G: Matrix, U: Matrix, x: torch.Tensor, h: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    S = x.shape[0]
+    if h is None:
+        h = torch.empty((S, G.O), dtype=torch.float32, device=x.device)
+    _check(load().dqg_gate_up(C.byref(G.struct), C.byref(U.struct), _dev(x, "x", torch.float32), S,
+                              _dev(h, "h", torch.float32), _stream(stream)))
+    return h
+
+
+def dqg_dequant(W: Matrix, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty((W.O, W.K), dtype=torch.float32, device=W.q.device)
+    _check(load().dqg_dequant(C.byref(W.struct), _dev(out, "out", torch.float32), _stream(stream)))
+    return out
+
+
+class Expert:
+    def __init__(self, gate: Matrix, up: Matrix, down: Matrix):
+        self.gate, self.up, self.down = gate, up, down
+
+    @classmethod
+    def upload(cls, e, device="cuda") -> "Expert":
+        return cls(Matrix.upload(e.gate, device), Matrix.upload(e.up, device), Matrix.upload(e.down, device))
+
+    @property
+    def nbytes(self) -> int:
+        return self.gate.nbytes + self.up.nbytes + self.down.nbytes
+
+
+class ExpertTable:
+    """dqg_expert_table_create / _destroy.  Keeps the experts' tensors alive."""
+
+    def __init__(self, experts: Sequence[Expert]):
+        self.experts = list(experts)
+        arr = (dqg_expert * len(self.experts))(*[dqg_expert(e.gate.struct, e.up.struct, e.down.struct)
+                                                  for e in self.experts])
+        handle = C.c_void_p()
+        _check(load().dqg_expert_table_create(arr, len(self.experts), C.byref(handle)))
+        self.handle = handle
+        self.H = self.experts[0].gate.K
+        self.I = self.experts[0].gate.O
+
+    def close(self) -> None:
+        if self.handle:
+            load().dqg_expert_table_destroy(self.handle)
+            self.handle = C.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def scratch_bytes(self, S: int, k: int) -> int:
+        return load().dqg_expert_group_scratch_bytes(self.handle, S, k)
+
+    def scratch(self, S: int, k: int, device="cuda") -> torch.Tensor:
+        return torch.empty(self.scratch_bytes(S, k), dtype=torch.uint8, device=device)
+
+
+def _group_args(table: ExpertTable, ids, w, shared, x, y, scratch):
+    S, k = ids.shape
+    if y is None:
+        y = torch.empty((S, table.H), dtype=torch.float32, device=x.device)
+    if scratch is None:
+        scratch = table.scratch(S, k, x.device)
+    args = (table.handle, S, k, _dev(ids, "ids", torch.int32), _dev(w, "w", torch.float32),
+            -1 if shared is None else int(shared), _dev(x, "x", torch.float32),
+            _dev(y, "y", torch.float32), _dev(scratch, "scratch"),
+            scratch.numel() * scratch.element_size())
+    return args, y, scratch
+
+
+def dqg_expert_group(table: ExpertTable, ids: torch.Tensor, w: torch.Tensor, shared: Optional[int],
+                     x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                     scratch: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    args, y, _ = _group_args(table, ids, w, shared, x, y, scratch)
+    _check(load().dqg_expert_group(*args, _stream(stream)))
+    return y
+
+
+def dqg_expert_group_issue(table: ExpertTable, ids: torch.Tensor, w: torch.Tensor,
+                           shared: Optional[int], x: torch.Tensor, y: Optional[torch.Tensor] = None,
+                           scratch: Optional[torch.Tensor] = None, stream=None):
+    """Returns (ticket, y, scratch); keep scratch alive until the ticket is taken."""
+    args, y, scratch = _group_args(table, ids, w, shared, x, y, scratch)
+    ticket = dqg_ticket()
+    _check(load().dqg_expert_group_issue(*args, _stream(stream), C.byref(ticket)))
+    return ticket, y, scratch
+
+
+def dqg_expert_group_take(ticket: dqg_ticket) -> None:
+    _check(load().dqg_expert_group_take(C.byref(ticket)))
+
+
+def dqg_last_error() -> str:
+    return load().dqg_last_error().decode()
+
+
+def dqg_stats() -> dict:
+    c = dqg_counters()
+    load().dqg_stats(C.byref(c))
+    return {name: getattr(c, name) for name, _ in dqg_counters._fields_}
+
+
+def dqg_stats_reset() -> None:
+    load().dqg_stats_reset()
+
+
+def dqg_prof_begin(capacity: int) -> None:
+    """Time the next ``capacity`` launches with HIP events on their streams."""
+    _check(load().dqg_prof_begin(int(capacity)))
+
+
+def dqg_prof_end() -> dict:
+    """{kernel name: (launches, total device ms)} of the launches timed since dqg_prof_begin."""
+    recs = (dqg_prof_record * 16)()
+    n = C.c_int32()
+    _check(load().dqg_prof_end(recs, 16, C.byref(n)))
+    return {recs[i].kernel.decode(): (recs[i].launches, recs[i].total_ms) for i in range(n.value)}

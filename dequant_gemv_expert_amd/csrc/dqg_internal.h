@@ -1,0 +1,68 @@
+// Internal declarations shared by the C-ABI layer (dqg_api.cpp) and the
+// kernels (dqg_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dqg {
+
+// Row pointers of one matrix row: codes, high plane (int3 only), scales.
+struct RowPtrs {
+    const uint8_t *q;
+    const uint8_t *q2;
+    const float *s;
+};
+
+// A matrix as the kernels see it.
+struct MatDev {
+    const uint8_t *q;
+    const uint8_t *q2;
+    const float *s;
+    int32_t O, K;
+    int32_t qstride;    // bytes of codes per row
+    int32_t q2stride;   // bytes of the high plane per row (fmt 5)
+    int32_t sstride;    // scales per row
+    int32_t shift;      // chunk index >> shift = scale index (31 for one scale a row)
+};
+
+// One expert's matrices in the device table.
+struct ExpertDev {
+    MatDev gate, up, down;
+};
+
+// Codec family a format decodes with (fmt 2 and 4 share the int4 codec).
+enum Codec : int { C_I8 = 1, C_I4 = 4, C_I3 = 5, C_FP4 = 7 };
+
+// Launch parameters of the grouped expert call.
+struct GroupArgs {
+    const ExpertDev *table;
+    int32_t n_experts;
+    int32_t S, k;
+    const int32_t *ids;
+    const float *w;
+    int32_t shared;      // expert index or -1
+    const float *x;      // [S][H]
+    float *y;            // [S][H]
+    float *h;            // [S*k + S][I]
+    int32_t *flag;       // cleared by the gate_up launch, set by the down launch
+                         // when an id is out of range
+    int32_t H, I;
+};
+
+// Optional event timing of launches (dqg_api.cpp): when timing is on,
+// prof_slot hands out the start/stop events the next launch of `kernel`
+// records (hipExtLaunchKernelGGL attaches them to the dispatch itself);
+// otherwise it returns false and the launch carries no events.
+bool prof_slot(const char *kernel, hipEvent_t *start, hipEvent_t *stop);
+
+// Host launchers (dqg_kernels.hip).  Return hipSuccess or the launch error.
+hipError_t launch_matmul(int codec, const MatDev &m, const float *x, int S, float *y,
+                         hipStream_t st);
+hipError_t launch_gate_up(int codec, const MatDev &g, const MatDev &u, const float *x, int S,
+                          float *h, hipStream_t st);
+hipError_t launch_dequant(int codec, const MatDev &m, float *out, hipStream_t st);
+hipError_t launch_group(int codec_gu, int codec_down, const GroupArgs &a, hipStream_t st,
+                        int *launches);
+
+}  // namespace dqg

@@ -1,0 +1,787 @@
+// Quantised GEMV, SwiGLU gate_up and routed-expert kernels for gfx950 (CDNA4).
+//
+// What is computed (pages: "colibri Vulkan compute backend complete guide",
+// shader-level and API-contract sections; "colibri -- Vulkan backend
+// (docs/vulkan.md)", arithmetic paragraph and expert-tier properties):
+// weights are decoded from their packed codes and multiplied by f32
+// activations; gate_up is silu(gate(x)) * up(x); the expert group sums each
+// token's routed experts in rank order, weighted by the router, then adds
+// the shared expert.
+//
+// How, on CDNA4 (prior-art shaders used one subgroup per row, x staged in
+// shared memory and one subgroupAdd per row; this keeps the parts that
+// hold on a wave64 part with 16-byte loads and DPP):
+//  * One wave owns R rows (R rows of gate plus R of up for gate_up).  Lane
+//    l streams 16-byte chunks l, l+64, l+128, ... of each row, so a wave's
+//    loads of one chunk index are one fully coalesced 1 KiB read per row.
+//    All R rows' chunks are issued before any is decoded.
+//  * A chunk is decoded in registers into unsigned codes (v_perm and
+//    v_cvt_f32_ubyte) and dotted with the matching slice of x for every
+//    token of the batch; each decoded weight serves all tokens.  The offset
+//    (8 for int4, 4 for int3, 128 for int8 read as offset binary) is folded
+//    out once per chunk as OFF * sum(x slice), and the group scale is
+//    applied once per chunk, not once per weight.
+//  * Per-lane partial sums are reduced across the wave with DPP (quad
+//    permutes, row rotates, row broadcasts): no LDS, no barrier.
+//  * Every output's arithmetic is the same whatever the batch size, so a
+//    token's results have the same bits alone or in a batch.
+#include "dqg_internal.h"
+
+#include <hip/hip_ext.h>
+
+namespace dqg {
+namespace {
+
+constexpr int WAVE = 64;
+
+// Global-memory loads: base pointers are wave-uniform, offsets 32-bit, so
+// the address is one SGPR pair plus one VGPR (no per-row 64-bit math).
+#define GLOBAL __attribute__((address_space(1)))
+typedef const GLOBAL uint8_t *gbytes;
+typedef const GLOBAL float *gfloats;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld16(gbytes base, uint32_t off) {
+    const u32x4 v = *(const GLOBAL u32x4 *)(base + off);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint2 ld8(gbytes base, uint32_t off) {
+    const u32x2 v = *(const GLOBAL u32x2 *)(base + off);
+    return make_uint2(v.x, v.y);
+}
+// idx counts floats; the byte offset is formed in 32 bits
+__device__ __forceinline__ float4 ldf4(gfloats base, uint32_t idx) {
+    const f32x4 v = *(const GLOBAL f32x4 *)((gbytes)base + (idx << 2));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ float ldf(gfloats base, uint32_t idx) {
+    return *(const GLOBAL float *)((gbytes)base + (idx << 2));
+}
+
+// A wave-uniform global pointer, held in SGPRs.
+__device__ __forceinline__ uint64_t uniform_bits(const void *p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ gbytes gb(const void *p) { return (gbytes)uniform_bits(p); }
+__device__ __forceinline__ gfloats gf(const void *p) { return (gfloats)uniform_bits(p); }
+
+// Row pointers as the kernels use them (global address space, uniform).
+struct GRow {
+    gbytes q, q2;
+    gfloats s;
+};
+
+// Hides a value's known bits from the optimiser (no instruction).
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+    asm("" : "+v"(x));
+    return x;
+}
+
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// acc + f16(pair half) * x: the f16 -> f32 widening folds into v_fma_mix_f32.
+__device__ __forceinline__ float fma_lo(uint32_t pair, float x, float acc) {
+    return fmaf((float)__builtin_bit_cast(half2_t, pair).x, x, acc);
+}
+__device__ __forceinline__ float fma_hi(uint32_t pair, float x, float acc) {
+    return fmaf((float)__builtin_bit_cast(half2_t, pair).y, x, acc);
+}
+
+// ---------------------------------------------------------------------------
+// Codecs.  A chunk is the 16 bytes of codes (plus 8 of high plane for int3)
+// one lane reads per step, covering CW inputs.  decode(ch, u, pr) turns the
+// UW codes of unit u into UW/2 pairs of f16 bit patterns; half h of pair p
+// multiplies x[unit base + IDX[2p + h]].
+//
+// The f16 patterns are exact multiples of the weight values:
+//  - a non-negative integer code n below 1024 placed in the low bits of an
+//    f16 is the subnormal n * 2^-24 (int8 read as offset binary n = q + 128,
+//    int4 nibbles, int3 codes);
+//  - an e2m1 code with its three magnitude bits at f16 bits 9..11 and its
+//    sign at bit 15 is e2m1 * 2^-14, subnormal case included, because both
+//    formats put the implicit one and the exponent bias in the same places.
+// So weight = (pattern - OFF * 2^-24) * VMUL with VMUL a power of two that
+// folds into the scale; f16 and f32 denormals are kept (IEEE mode).
+// ---------------------------------------------------------------------------
+template <int C>
+struct Codec;
+
+// int8 rows: byte = two's complement q; q ^ 0x80 = q + 128 as an unsigned
+// byte; v_perm drops bytes into the low byte of each f16 half.
+template <>
+struct Codec<C_I8> {
+    static constexpr int CW = 16, UNITS = 4, UW = 4;
+    static constexpr float VMUL = 16777216.f, OFFS = 128.f / 16777216.f;
+    static constexpr int IDX[UW] = {0, 2, 1, 3};
+    struct Chunk { uint32_t w[4]; };
+    __device__ static Chunk load(const GRow &r, uint32_t c) {
+        uint4 v = ld16(r.q, c * 16u);
+        return {{v.x, v.y, v.z, v.w}};
+    }
+    __device__ static void decode(const Chunk &ch, int u, uint32_t (&pr)[UW / 2]) {
+        const uint32_t w = ch.w[u] ^ 0x80808080u;
+        pr[0] = __builtin_amdgcn_perm(0u, w, 0x0C020C00u);   // inputs 0, 2
+        pr[1] = __builtin_amdgcn_perm(0u, w, 0x0C030C01u);   // inputs 1, 3
+    }
+};
+
+// int4 pairs: nibble i of word u is input 8u + i; pair j = nibbles j, j+4,
+// which sit at the same offset of the two 16-bit halves.
+template <>
+struct Codec<C_I4> {
+    static constexpr int CW = 32, UNITS = 4, UW = 8;
+    static constexpr float VMUL = 16777216.f, OFFS = 8.f / 16777216.f;
+    static constexpr int IDX[UW] = {0, 4, 1, 5, 2, 6, 3, 7};
+    struct Chunk { uint32_t w[4]; };
+    __device__ static Chunk load(const GRow &r, uint32_t c) {
+        uint4 v = ld16(r.q, c * 16u);
+        return {{v.x, v.y, v.z, v.w}};
+    }
+    __device__ static void decode(const Chunk &ch, int u, uint32_t (&pr)[UW / 2]) {
+        const uint32_t w = ch.w[u];
+        pr[0] = w & 0x000F000Fu;
+        pr[1] = (w >> 4) & 0x000F000Fu;
+        pr[2] = (w >> 8) & 0x000F000Fu;
+        pr[3] = (w >> 12) & 0x000F000Fu;
+    }
+};
+
+// MXFP4: e2m1 nibbles in int4 order.  The f16 high byte of code c is
+// ((c & 7) << 1) | ((c & 8) << 4); it is built for the four even and four
+// odd codes of a word at once, then v_perm pairs each even code with the
+// next odd one over zero low bytes.
+template <>
+struct Codec<C_FP4> {
+    static constexpr int CW = 32, UNITS = 4, UW = 8;
+    static constexpr float VMUL = 16384.f, OFFS = 0.f;
+    static constexpr int IDX[UW] = {0, 1, 2, 3, 4, 5, 6, 7};
+    struct Chunk { uint32_t w[4]; };
+    __device__ static Chunk load(const GRow &r, uint32_t c) {
+        uint4 v = ld16(r.q, c * 16u);
+        return {{v.x, v.y, v.z, v.w}};
+    }
+    __device__ static void decode(const Chunk &ch, int u, uint32_t (&pr)[UW / 2]) {
+        const uint32_t w = ch.w[u];
+        const uint32_t he = ((w << 1) & 0x0E0E0E0Eu) | ((w << 4) & 0x80808080u);   // codes 0,2,4,6
+        const uint32_t ho = ((w >> 3) & 0x0E0E0E0Eu) | (w & 0x80808080u);          // codes 1,3,5,7
+        pr[0] = __builtin_amdgcn_perm(ho, he, 0x040C000Cu);
+        pr[1] = __builtin_amdgcn_perm(ho, he, 0x050C010Cu);
+        pr[2] = __builtin_amdgcn_perm(ho, he, 0x060C020Cu);
+        pr[3] = __builtin_amdgcn_perm(ho, he, 0x070C030Cu);
+    }
+};
+
+// int3-g64: a chunk is one group of 64 inputs: 16 bytes of the 2-bit plane
+// (words L0..L3, 16 inputs each) and 8 bytes of the 1-bit plane (H0, H1, 32
+// inputs each).  Unit u is inputs 32u..32u+31: L(2u), L(2u+1), H(u).  For
+// m = 0..7, byte b of q_m is the 3-bit code of input 8b + m: the 2-bit
+// fields are gathered with one v_perm per four m, the high bits with a
+// shift, the two joined with a shift-or, and v_perm pairs bytes (0, 1) and
+// (2, 3) of q_m into f16 halves.
+template <>
+struct Codec<C_I3> {
+    static constexpr int CW = 64, UNITS = 2, UW = 32;
+    static constexpr float VMUL = 16777216.f, OFFS = 4.f / 16777216.f;
+    // pair 2m: inputs m, 8+m; pair 2m+1: inputs 16+m, 24+m
+    static constexpr int IDX[UW] = {0, 8, 16, 24, 1, 9, 17, 25, 2, 10, 18, 26, 3, 11, 19, 27,
+                                    4, 12, 20, 28, 5, 13, 21, 29, 6, 14, 22, 30, 7, 15, 23, 31};
+    struct Chunk { uint32_t l[4]; uint32_t h[2]; };
+    __device__ static Chunk load(const GRow &r, uint32_t c) {
+        uint4 lv = ld16(r.q, c * 16u);
+        uint2 hv = ld8(r.q2, c * 8u);
+        return {{lv.x, lv.y, lv.z, lv.w}, {hv.x, hv.y}};
+    }
+    __device__ static void decode(const Chunk &ch, int u, uint32_t (&pr)[UW / 2]) {
+        const uint32_t L0 = ch.l[2 * u], L1 = ch.l[2 * u + 1], H = ch.h[u];
+        // za = [L0.b0, L0.b2, L1.b0, L1.b2]: fields of inputs m, 8+m, 16+m, 24+m (m < 4)
+        // zb = [L0.b1, L0.b3, L1.b1, L1.b3]: the same for m >= 4
+        const uint32_t za = __builtin_amdgcn_perm(L1, L0, 0x06040200u);
+        const uint32_t zb = __builtin_amdgcn_perm(L1, L0, 0x07050301u);
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const uint32_t z = m < 4 ? za : zb;
+            const uint32_t lo = (z >> (2 * (m & 3))) & 0x03030303u;
+            const uint32_t hi = (H >> m) & 0x01010101u;
+            const uint32_t q = lo | (hi << 2);
+            pr[2 * m] = __builtin_amdgcn_perm(0u, q, 0x0C010C00u);
+            pr[2 * m + 1] = __builtin_amdgcn_perm(0u, q, 0x0C030C02u);
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// Wave64 sum with DPP.  Quad permutes and row rotates give every lane its
+// row's sum; two row broadcasts carry rows 0..2 into row 3.  The total is
+// read from lane 63 (uniform result).  The order of the additions is fixed.
+// ---------------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_rows(float v) {
+    // rows outside ROW_MASK read 0
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROW_MASK, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_mov<0xB1>(v);        // quad_perm [1,0,3,2]
+    v += dpp_mov<0x4E>(v);        // quad_perm [2,3,0,1]
+    v += dpp_mov<0x124>(v);       // row_ror:4
+    v += dpp_mov<0x128>(v);       // row_ror:8
+    v += dpp_rows<0x142, 0xA>(v); // row_bcast:15 into rows 1 and 3
+    v += dpp_rows<0x143, 0xC>(v); // row_bcast:31 into rows 2 and 3
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+__device__ __forceinline__ int wave_id() {
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / WAVE));
+}
+
+__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+
+// ---------------------------------------------------------------------------
+// The row-set dot product.  acc[r][s] (per lane) = this lane's share of
+// sum_k W_r[k] * x_s[k]; reduce with wave_sum.  Per chunk and row:
+// p = sum(pattern * x) over the chunk, then acc += scale * VMUL *
+// (p - OFFS * sum(x)): the code offset is removed once per chunk and the
+// scale applied once per chunk.
+// ---------------------------------------------------------------------------
+template <int C, int NR, int SM>
+__device__ __forceinline__ void dot_rows(const GRow (&rows)[NR], int nch, int shift,
+                                         const gfloats (&xp)[SM], float (&acc)[NR][SM]) {
+    using Cd = Codec<C>;
+    const int lane = threadIdx.x & (WAVE - 1);
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int s = 0; s < SM; ++s) acc[r][s] = 0.f;
+
+    for (int c = lane; c < nch; c += WAVE) {
+        // Every load of the step first (codes and scales of all rows, then
+        // x), kept ahead of the arithmetic by a scheduling barrier so that a
+        // wave has all its requests in flight before it waits.  The chunk
+        // index is hidden from loop strength reduction so that each load is
+        // one SGPR base plus a 32-bit lane offset.
+        const uint32_t cu = opaque((uint32_t)c);
+        typename Cd::Chunk ch[NR];
+        float sc[NR];
+        const uint32_t si = cu >> shift;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            ch[r] = Cd::load(rows[r], cu);
+            sc[r] = ldf(rows[r].s, si);
+        }
+        float xv[SM][Cd::CW];
+#pragma unroll
+        for (int s = 0; s < SM; ++s)
+#pragma unroll
+            for (int i = 0; i < Cd::CW / 4; ++i) {
+                const float4 t = ldf4(xp[s], cu * Cd::CW + 4 * i);
+                xv[s][4 * i] = t.x; xv[s][4 * i + 1] = t.y; xv[s][4 * i + 2] = t.z; xv[s][4 * i + 3] = t.w;
+            }
+        __builtin_amdgcn_sched_barrier(0);
+        float p[NR][SM], xs[SM];
+#pragma unroll
+        for (int s = 0; s < SM; ++s) {
+            xs[s] = 0.f;
+            if (Cd::OFFS != 0.f) {
+#pragma unroll
+                for (int i = 0; i < Cd::CW; ++i) xs[s] += xv[s][i];
+            }
+#pragma unroll
+            for (int r = 0; r < NR; ++r) p[r][s] = 0.f;
+        }
+#pragma unroll
+        for (int u = 0; u < Cd::UNITS; ++u) {
+#pragma unroll
+            for (int r = 0; r < NR; ++r) {
+                uint32_t pr[Cd::UW / 2];
+                Cd::decode(ch[r], u, pr);
+#pragma unroll
+                for (int s = 0; s < SM; ++s)
+#pragma unroll
+                    for (int q = 0; q < Cd::UW / 2; ++q) {
+                        p[r][s] = fma_lo(pr[q], xv[s][u * Cd::UW + Cd::IDX[2 * q]], p[r][s]);
+                        p[r][s] = fma_hi(pr[q], xv[s][u * Cd::UW + Cd::IDX[2 * q + 1]], p[r][s]);
+                    }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < NR; ++r)
+#pragma unroll
+            for (int s = 0; s < SM; ++s)
+                acc[r][s] = fmaf(sc[r] * Cd::VMUL, fmaf(-Cd::OFFS, xs[s], p[r][s]), acc[r][s]);
+    }
+}
+
+__device__ __forceinline__ GRow row_ptrs(const MatDev &m, int row) {
+    return {gb(m.q + (size_t)row * m.qstride), gb(m.q2 + (size_t)row * m.q2stride),
+            gf(m.s + (size_t)row * m.sstride)};
+}
+
+// Pointers of a row that may differ from lane to lane (the dequant kernel).
+__device__ __forceinline__ GRow lane_row_ptrs(const MatDev &m, int row) {
+    return {(gbytes)(m.q + (size_t)row * m.qstride), (gbytes)(m.q2 + (size_t)row * m.q2stride),
+            (gfloats)(m.s + (size_t)row * m.sstride)};
+}
+
+// ---------------------------------------------------------------------------
+// dqg_matmul: y[s][o] = W[o] . x[s]
+// ---------------------------------------------------------------------------
+template <int C, int R, int SM>
+__global__ void __launch_bounds__(256) k_matmul(MatDev m, const float *__restrict__ x, int S,
+                                                float *__restrict__ y) {
+    const int wave = blockIdx.x * (blockDim.x / WAVE) + wave_id();
+    const int row0 = wave * R;
+    if (row0 >= m.O) return;
+    const int lane = threadIdx.x & (WAVE - 1);
+    GRow rows[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) rows[r] = row_ptrs(m, min(row0 + r, m.O - 1));
+    const int nch = m.K / Codec<C>::CW;
+    for (int s0 = 0; s0 < S; s0 += SM) {
+        gfloats xp[SM];
+#pragma unroll
+        for (int s = 0; s < SM; ++s) xp[s] = gf(x + (size_t)min(s0 + s, S - 1) * m.K);
+        float acc[R][SM];
+        dot_rows<C, R, SM>(rows, nch, m.shift, xp, acc);
+        float out = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int s = 0; s < SM; ++s) {
+                const float t = wave_sum(acc[r][s]);
+                if (lane == r * SM + s) out = t;
+            }
+        const int r = lane / SM, s = lane % SM;
+        if (lane < R * SM && row0 + r < m.O && s0 + s < S) y[(size_t)(s0 + s) * m.O + row0 + r] = out;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dqg_gate_up: h[s][i] = silu(G[i] . x[s]) * (U[i] . x[s])
+// ---------------------------------------------------------------------------
+template <int C, int R, int SM>
+__global__ void __launch_bounds__(256) k_gate_up(MatDev g, MatDev u, const float *__restrict__ x,
+                                                 int S, float *__restrict__ h) {
+    const int I = g.O;
+    const int wave = blockIdx.x * (blockDim.x / WAVE) + wave_id();
+    const int row0 = wave * R;
+    if (row0 >= I) return;
+    const int lane = threadIdx.x & (WAVE - 1);
+    GRow rows[2 * R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        rows[r] = row_ptrs(g, min(row0 + r, I - 1));
+        rows[R + r] = row_ptrs(u, min(row0 + r, I - 1));
+    }
+    const int nch = g.K / Codec<C>::CW;
+    for (int s0 = 0; s0 < S; s0 += SM) {
+        gfloats xp[SM];
+#pragma unroll
+        for (int s = 0; s < SM; ++s) xp[s] = gf(x + (size_t)min(s0 + s, S - 1) * g.K);
+        float acc[2 * R][SM];
+        dot_rows<C, 2 * R, SM>(rows, nch, g.shift, xp, acc);
+        float gv = 0.f, uv = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int s = 0; s < SM; ++s) {
+                const float tg = wave_sum(acc[r][s]);
+                const float tu = wave_sum(acc[R + r][s]);
+                if (lane == r * SM + s) { gv = tg; uv = tu; }
+            }
+        const int r = lane / SM, s = lane % SM;
+        if (lane < R * SM && row0 + r < I && s0 + s < S) h[(size_t)(s0 + s) * I + row0 + r] = silu(gv) * uv;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// dqg_dequant: out[o][k] = value * scale with value = (pattern - OFFS) *
+// VMUL exactly, then one rounding.  One thread per chunk.
+// ---------------------------------------------------------------------------
+template <int C>
+__global__ void __launch_bounds__(256) k_dequant(MatDev m, float *__restrict__ out) {
+    using Cd = Codec<C>;
+    const int nch = m.K / Cd::CW;
+    const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= (size_t)m.O * nch) return;
+    const int row = (int)(idx / nch), c = (int)(idx % nch);
+    const GRow rp = lane_row_ptrs(m, row);
+    const typename Cd::Chunk ch = Cd::load(rp, (uint32_t)c);
+    const float sc = ldf(rp.s, (uint32_t)c >> m.shift);
+    float *o = out + (size_t)row * m.K + (size_t)c * Cd::CW;
+#pragma unroll
+    for (int u = 0; u < Cd::UNITS; ++u) {
+        uint32_t pr[Cd::UW / 2];
+        Cd::decode(ch, u, pr);
+        float v[Cd::UW];
+#pragma unroll
+        for (int q = 0; q < Cd::UW / 2; ++q) {
+            const half2_t h = __builtin_bit_cast(half2_t, pr[q]);
+            v[Cd::IDX[2 * q]] = (((float)h.x - Cd::OFFS) * Cd::VMUL) * sc;
+            v[Cd::IDX[2 * q + 1]] = (((float)h.y - Cd::OFFS) * Cd::VMUL) * sc;
+        }
+#pragma unroll
+        for (int i = 0; i < Cd::UW; i += 4)
+            *reinterpret_cast<float4 *>(o + u * Cd::UW + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Routed expert group.
+//
+// Units: routed slot q = t*k + r (q < S*k) and, with a shared expert, unit
+// S*k.  A routed unit whose expert appears at an earlier slot is skipped;
+// the first slot of an expert (its owner) serves every slot that names it,
+// so each distinct expert's rows are read once per call.  Slot lists come
+// from wave ballots over ids; no host round trip.
+// ---------------------------------------------------------------------------
+struct SlotBatch {
+    int n;          // 1..4 valid entries; unused entries repeat entry 0
+    int slot[4];
+    int token[4];
+};
+
+// Is unit q the first slot naming expert e?  (wave-uniform)
+__device__ __forceinline__ bool owns(const int32_t *ids, int q, int e) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    for (int base = 0; base < q; base += WAVE) {
+        const int i = base + lane;
+        const bool hit = i < q && ids[i] == e;
+        if (__ballot(hit)) return false;
+    }
+    return true;
+}
+
+// Calls f(batch) for batches of up to CAP (<= 4) (slot, token) pairs that
+// use unit q's expert e: every slot >= q naming e, or every token's shared
+// slot.  All indexes into a batch are compile-time constants.
+template <int CAP, typename F>
+__device__ __forceinline__ void for_slots(const GroupArgs &a, int q, int e, F &&f) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int nr = a.S * a.k;
+    if (q >= nr) {   // shared expert: token t's slot is nr + t
+        for (int t0 = 0; t0 < a.S; t0 += CAP) {
+            SlotBatch b;
+            b.n = min(CAP, a.S - t0);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int t = t0 + (j < b.n ? j : 0);
+                b.slot[j] = nr + t;
+                b.token[j] = t;
+            }
+            f(b);
+        }
+        return;
+    }
+    for (int base = q; base < nr; base += WAVE) {
+        const int i = base + lane;
+        uint64_t mask = __ballot(i < nr && a.ids[i] == e);
+        while (mask) {
+            SlotBatch b;
+            b.n = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (j < CAP && mask) {
+                    const int slot = base + __builtin_ctzll(mask);
+                    mask &= mask - 1;
+                    b.slot[j] = slot;
+                    b.token[j] = slot / a.k;
+                    b.n = j + 1;
+                } else {
+                    b.slot[j] = b.slot[0];
+                    b.token[j] = b.token[0];
+                }
+            }
+            f(b);
+        }
+    }
+}
+
+// gate_up of R rows (row0..) of expert e for a batch of SM slots.
+template <int C, int R, int SM>
+__device__ __forceinline__ void group_gu_batch(const GroupArgs &a, const ExpertDev &ex, int row0,
+                                               const SlotBatch &b) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    GRow rows[2 * R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        rows[r] = row_ptrs(ex.gate, min(row0 + r, a.I - 1));
+        rows[R + r] = row_ptrs(ex.up, min(row0 + r, a.I - 1));
+    }
+    gfloats xp[SM];
+#pragma unroll
+    for (int s = 0; s < SM; ++s) xp[s] = gf(a.x + (size_t)b.token[s] * a.H);
+    float acc[2 * R][SM];
+    dot_rows<C, 2 * R, SM>(rows, ex.gate.K / Codec<C>::CW, ex.gate.shift, xp, acc);
+    float gv = 0.f, uv = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int s = 0; s < SM; ++s) {
+            const float tg = wave_sum(acc[r][s]);
+            const float tu = wave_sum(acc[R + r][s]);
+            if (lane == r * SM + s) { gv = tg; uv = tu; }
+        }
+    const int r = lane / SM, s = lane % SM;
+    if (lane < R * SM && row0 + r < a.I && s < b.n) {
+        int slot = b.slot[0];
+#pragma unroll
+        for (int j = 1; j < SM; ++j)
+            if (s == j) slot = b.slot[j];
+        a.h[(size_t)slot * a.I + row0 + r] = silu(gv) * uv;
+    }
+}
+
+// Kernel A: grid (row blocks of I, units).  Clears the error flag.  CAP is
+// the largest token batch the launch needs (1 when S = 1), so that a
+// launch only carries the register footprint of the batches it can see.
+template <int C, int R, int CAP>
+__global__ void __launch_bounds__(256) k_group_gate_up(GroupArgs a) {
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.flag = 0;
+    const int q = blockIdx.y;
+    const int nr = a.S * a.k;
+    const int e = __builtin_amdgcn_readfirstlane(q < nr ? a.ids[q] : a.shared);
+    if (e < 0 || e >= a.n_experts) return;         // reported by kernel B
+    if (q < nr && !owns(a.ids, q, e)) return;
+    const int wave = blockIdx.x * (blockDim.x / WAVE) + wave_id();
+    const int row0 = wave * R;
+    if (row0 >= a.I) return;
+    const ExpertDev &ex = a.table[e];
+    for_slots<CAP>(a, q, e, [&](const SlotBatch &b) {
+        if (CAP == 1 || b.n == 1) group_gu_batch<C, R, 1>(a, ex, row0, b);
+        else if (CAP == 2 || b.n == 2) group_gu_batch<C, R, 2>(a, ex, row0, b);
+        else group_gu_batch<C, R, 4>(a, ex, row0, b);
+    });
+}
+
+// down rows row0.. of expert e applied to a batch of slots' h -> d (LDS)
+template <int C, int R, int SM>
+__device__ __forceinline__ void group_down_batch(const GroupArgs &a, const ExpertDev &ex, int row0,
+                                                 const SlotBatch &b, float *d) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    GRow rows[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) rows[r] = row_ptrs(ex.down, min(row0 + r, a.H - 1));
+    gfloats xp[SM];
+#pragma unroll
+    for (int s = 0; s < SM; ++s) xp[s] = gf(a.h + (size_t)b.slot[s] * a.I);
+    float acc[R][SM];
+    dot_rows<C, R, SM>(rows, ex.down.K / Codec<C>::CW, ex.down.shift, xp, acc);
+    float out = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int s = 0; s < SM; ++s) {
+            const float t = wave_sum(acc[r][s]);
+            if (lane == r * SM + s) out = t;
+        }
+    const int r = lane / SM, s = lane % SM;
+    if (lane < R * SM && s < b.n) {
+        int slot = b.slot[0];
+#pragma unroll
+        for (int j = 1; j < SM; ++j)
+            if (s == j) slot = b.slot[j];
+        d[slot * R + r] = out;
+    }
+}
+
+// Kernel B: one block per R rows of H.  Waves share the units; each unit's
+// outputs go to LDS d[slot][R]; then y[t][row] = sum_r w[t][r] * d[t*k+r]
+// in rank order, plus the shared slot.  Sets the flag for a bad id.
+// Block size: one wave per unit up to 16 waves when every batch is one slot
+// (small register footprint), up to 8 otherwise.
+template <int CAP>
+constexpr int down_max_waves() { return CAP == 1 ? 16 : 8; }
+
+template <int C, int R, int CAP>
+__global__ void __launch_bounds__(WAVE * down_max_waves<CAP>()) k_group_down(GroupArgs a) {
+    extern __shared__ float d[];
+    const int row0 = blockIdx.x * R;
+    const int nr = a.S * a.k;
+    const int nunits = nr + (a.shared >= 0 ? 1 : 0);
+    const int nw = blockDim.x / WAVE;
+    const int lane = threadIdx.x & (WAVE - 1);
+    for (int q = wave_id(); q < nunits; q += nw) {
+        const int e = __builtin_amdgcn_readfirstlane(q < nr ? a.ids[q] : a.shared);
+        if (e < 0 || e >= a.n_experts) {
+            if (lane < R) d[q * R + lane] = __int_as_float(0x7FC00000);   // quiet NaN
+            if (lane == 0) *a.flag = 1;
+            continue;
+        }
+        if (q < nr && !owns(a.ids, q, e)) continue;
+        const ExpertDev &ex = a.table[e];
+        for_slots<CAP>(a, q, e, [&](const SlotBatch &b) {
+            if (CAP == 1 || b.n == 1) group_down_batch<C, R, 1>(a, ex, row0, b, d);
+            else if (CAP == 2 || b.n == 2) group_down_batch<C, R, 2>(a, ex, row0, b, d);
+            else group_down_batch<C, R, 4>(a, ex, row0, b, d);
+        });
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < a.S * R; j += blockDim.x) {
+        const int t = j / R, r = j % R;
+        if (row0 + r >= a.H) continue;
+        float acc = 0.f;
+        for (int rk = 0; rk < a.k; ++rk) acc = fmaf(a.w[t * a.k + rk], d[(t * a.k + rk) * R + r], acc);
+        if (a.shared >= 0) acc += d[(nr + t) * R + r];
+        a.y[(size_t)t * a.H + row0 + r] = acc;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Host launchers
+// ---------------------------------------------------------------------------
+constexpr int WPB = 4;   // waves per block for the row kernels
+
+// Launch, with start/stop events attached to the dispatch when timing is on.
+template <typename K, typename... Args>
+void launch(const char *name, K kernel, dim3 grid, dim3 block, size_t lds, hipStream_t st, Args... args) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (prof_slot(name, &e0, &e1))
+        hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)lds, st, e0, e1, 0, args...);
+    else
+        hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+}
+
+template <int C, int R, int SM>
+hipError_t go_matmul(const MatDev &m, const float *x, int S, float *y, hipStream_t st) {
+    const int rows_per_block = R * WPB;
+    dim3 grid((m.O + rows_per_block - 1) / rows_per_block);
+    launch("matmul", (k_matmul<C, R, SM>), grid, dim3(WAVE * WPB), 0, st, m, x, S, y);
+    return hipGetLastError();
+}
+
+template <int C>
+hipError_t matmul_c(const MatDev &m, const float *x, int S, float *y, hipStream_t st) {
+    if (S >= 8) return go_matmul<C, 2, 8>(m, x, S, y, st);
+    if (S >= 4) return go_matmul<C, 4, 4>(m, x, S, y, st);
+    if (S >= 2) return go_matmul<C, 8, 2>(m, x, S, y, st);
+    return go_matmul<C, 8, 1>(m, x, S, y, st);
+}
+
+template <int C, int R, int SM>
+hipError_t go_gate_up(const MatDev &g, const MatDev &u, const float *x, int S, float *h, hipStream_t st) {
+    const int rows_per_block = R * WPB;
+    dim3 grid((g.O + rows_per_block - 1) / rows_per_block);
+    launch("gate_up", (k_gate_up<C, R, SM>), grid, dim3(WAVE * WPB), 0, st, g, u, x, S, h);
+    return hipGetLastError();
+}
+
+template <int C>
+hipError_t gate_up_c(const MatDev &g, const MatDev &u, const float *x, int S, float *h, hipStream_t st) {
+    if (S >= 8) return go_gate_up<C, 1, 8>(g, u, x, S, h, st);
+    if (S >= 4) return go_gate_up<C, 2, 4>(g, u, x, S, h, st);
+    if (S >= 2) return go_gate_up<C, 4, 2>(g, u, x, S, h, st);
+    return go_gate_up<C, 4, 1>(g, u, x, S, h, st);
+}
+
+template <int C>
+hipError_t dequant_c(const MatDev &m, float *out, hipStream_t st) {
+    const size_t n = (size_t)m.O * (m.K / Codec<C>::CW);
+    dim3 grid((unsigned)((n + 255) / 256));
+    launch("dequant", (k_dequant<C>), grid, dim3(256), 0, st, m, out);
+    return hipGetLastError();
+}
+
+constexpr int RA = 4;   // rows of gate (and of up) per wave in kernel A
+constexpr int RB = 8;   // rows of down per block in kernel B
+
+template <int C, int CAP>
+hipError_t group_a_cap(const GroupArgs &a, hipStream_t st) {
+    const int units = a.S * a.k + (a.shared >= 0 ? 1 : 0);
+    const int rows_per_block = RA * WPB;
+    dim3 grid((a.I + rows_per_block - 1) / rows_per_block, units);
+    launch("group_gate_up", (k_group_gate_up<C, RA, CAP>), grid, dim3(WAVE * WPB), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int C, int CAP>
+hipError_t group_b_cap(const GroupArgs &a, hipStream_t st) {
+    const int units = a.S * a.k + (a.shared >= 0 ? 1 : 0);
+    const int slots = a.S * a.k + (a.shared >= 0 ? a.S : 0);
+    const int waves = units < down_max_waves<CAP>() ? units : down_max_waves<CAP>();
+    dim3 grid((a.H + RB - 1) / RB);
+    const size_t lds = (size_t)slots * RB * sizeof(float);
+    launch("group_down", (k_group_down<C, RB, CAP>), grid, dim3(WAVE * waves), lds, st, a);
+    return hipGetLastError();
+}
+
+// Batch capacity: one token needs single-slot batches only.
+template <int C>
+hipError_t group_a(const GroupArgs &a, hipStream_t st) {
+    if (a.S == 1) return group_a_cap<C, 1>(a, st);
+    if (a.S == 2) return group_a_cap<C, 2>(a, st);
+    return group_a_cap<C, 4>(a, st);
+}
+
+template <int C>
+hipError_t group_b(const GroupArgs &a, hipStream_t st) {
+    if (a.S == 1) return group_b_cap<C, 1>(a, st);
+    if (a.S == 2) return group_b_cap<C, 2>(a, st);
+    return group_b_cap<C, 4>(a, st);
+}
+
+}  // namespace
+
+hipError_t launch_matmul(int codec, const MatDev &m, const float *x, int S, float *y, hipStream_t st) {
+    switch (codec) {
+    case C_I8: return matmul_c<C_I8>(m, x, S, y, st);
+    case C_I4: return matmul_c<C_I4>(m, x, S, y, st);
+    case C_I3: return matmul_c<C_I3>(m, x, S, y, st);
+    case C_FP4: return matmul_c<C_FP4>(m, x, S, y, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_gate_up(int codec, const MatDev &g, const MatDev &u, const float *x, int S,
+                          float *h, hipStream_t st) {
+    switch (codec) {
+    case C_I8: return gate_up_c<C_I8>(g, u, x, S, h, st);
+    case C_I4: return gate_up_c<C_I4>(g, u, x, S, h, st);
+    case C_I3: return gate_up_c<C_I3>(g, u, x, S, h, st);
+    case C_FP4: return gate_up_c<C_FP4>(g, u, x, S, h, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_dequant(int codec, const MatDev &m, float *out, hipStream_t st) {
+    switch (codec) {
+    case C_I8: return dequant_c<C_I8>(m, out, st);
+    case C_I4: return dequant_c<C_I4>(m, out, st);
+    case C_I3: return dequant_c<C_I3>(m, out, st);
+    case C_FP4: return dequant_c<C_FP4>(m, out, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_group(int codec_gu, int codec_down, const GroupArgs &a, hipStream_t st, int *launches) {
+    hipError_t e = hipErrorInvalidValue;
+    switch (codec_gu) {
+    case C_I8: e = group_a<C_I8>(a, st); break;
+    case C_I4: e = group_a<C_I4>(a, st); break;
+    case C_I3: e = group_a<C_I3>(a, st); break;
+    case C_FP4: e = group_a<C_FP4>(a, st); break;
+    }
+    if (e != hipSuccess) return e;
+    ++*launches;
+    e = hipErrorInvalidValue;
+    switch (codec_down) {
+    case C_I8: e = group_b<C_I8>(a, st); break;
+    case C_I4: e = group_b<C_I4>(a, st); break;
+    case C_I3: e = group_b<C_I3>(a, st); break;
+    case C_FP4: e = group_b<C_FP4>(a, st); break;
+    }
+    if (e == hipSuccess) ++*launches;
+    return e;
+}
+
+}  // namespace dqg

@@ -1,0 +1,228 @@
+/*
+ * dqg.h -- quantised GEMV and expert-MLP kernels for AMD Instinct MI355X
+ * (gfx950), C ABI.
+ *
+ * The operations are the decode-time calls over resident quantised weights
+ * that the API-contract section of "colibri Vulkan compute backend complete
+ * guide" (xdnf.cn) lists:
+ *   - a single quantised GEMV (its coli_vk_matmul);
+ *   - the first half of an expert MLP, silu(gate(x)) * up(x), with x read
+ *     once (its coli_vk_gate_up);
+ *   - the whole fused MLP of a batch of routed experts, hidden state kept
+ *     on the device, synchronous or issued and joined later (its
+ *     coli_vk_expert_group, _issue and _take).
+ *
+ * Weight formats are the device formats of colibri's expert tier ("colibri
+ * -- Vulkan backend (docs/vulkan.md)", expert-tier engine table; values and
+ * packing from the shader-level section of the guide above):
+ *   DQG_I8_ROW  (1)  int8, two's complement, one f32 scale per row
+ *   DQG_I4_ROW  (2)  int4 pairs, value = nibble - 8, one f32 scale per row
+ *   DQG_I4_GS   (4)  int4 pairs, value = nibble - 8, one f32 scale per gs inputs
+ *   DQG_I3_G64  (5)  int3 in two bit planes, value = code - 4, one f32 scale per 64
+ *   DQG_MXFP4   (7)  e2m1 nibbles, bit 3 the sign, one f32 scale per 32
+ *                    (the e8m0 scale pre-expanded to f32 by the host)
+ *
+ * Storage of one matrix W with O rows of K inputs (all row-major):
+ *   fmt 1:        q = int8 [O][K]                          scales = f32 [O]
+ *   fmt 2, 4, 7:  q = uint8 [O][K/2]; byte j of a row holds input 2j in its
+ *                 low nibble and input 2j+1 in its high nibble
+ *                                                          scales = f32 [O][K/gs]
+ *   fmt 5:        q  = uint32 [O][K/16]: 2 bits per input, input k at bits
+ *                      2*(k mod 16) of word k/16;
+ *                 q2 = uint32 [O][K/32]: 1 bit per input, input k at bit
+ *                      (k mod 32) of word k/32;
+ *                 code = low | high << 2               scales = f32 [O][K/64]
+ * (The pages do not fix nibble order or plane bit order; these are the
+ * readings this library and its tests use.)
+ *
+ * A weight is value * scale.  y[s][o] = sum_k W[o][k] * x[s][k] in f32.
+ * Results match a double-precision evaluation of that sum to within 1e-5
+ * of sum_k |W[o][k] * x[s][k]| per row; dequantised weights match the
+ * f32 rounding of value * scale bit for bit.
+ *
+ * Conventions for every call:
+ *   - Every array argument is a DEVICE pointer owned by the caller; nothing
+ *     is copied to or from the host.  The library owns only an expert
+ *     table's device descriptor array.
+ *   - Base pointers of q, q2, x, y, h and scratch must be 16-byte aligned;
+ *     scales 4-byte aligned.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue
+ *     kernels and return without synchronising the host, except
+ *     dqg_expert_group_take, dqg_expert_table_create/destroy.
+ *   - Arguments are validated before anything is enqueued.  On a non-zero
+ *     return nothing was launched and no output was written; the reason is
+ *     in dqg_last_error() (per thread).
+ *   - Work on one stream is ordered as usual; calls on different streams
+ *     that write the same buffers race.
+ */
+#ifndef DQG_H
+#define DQG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    DQG_OK = 0,
+    DQG_EINVAL = -1,   /* NULL or misaligned pointer, bad count or option */
+    DQG_EFORMAT = -2,  /* unknown format, or a group size the format does not have */
+    DQG_ESHAPE = -3,   /* shapes that disagree or do not divide into whole groups */
+    DQG_EDEVICE = -4,  /* a HIP runtime call failed */
+    DQG_ELAUNCH = -5,  /* a kernel launch failed (or DQG_FAULT injected a failure) */
+    DQG_ENOMEM = -6,   /* scratch too small, or a device allocation failed */
+    DQG_EROUTE = -7    /* dqg_expert_group_take: an expert id was out of range */
+} dqg_status;
+
+enum {
+    DQG_I8_ROW = 1,
+    DQG_I4_ROW = 2,
+    DQG_I4_GS = 4,
+    DQG_I3_G64 = 5,
+    DQG_MXFP4 = 7
+};
+
+/* One resident quantised matrix (device pointers, caller-owned).
+ * gs: inputs per scale; K for fmt 1 and 2, a power of two >= 32 dividing K
+ * for fmt 4, 64 for fmt 5, 32 for fmt 7.  K must be a multiple of 16
+ * (fmt 1), 32 (fmt 2, 4, 7) or 64 (fmt 5).  q2 is used by fmt 5 only. */
+typedef struct {
+    int32_t fmt;
+    int32_t O;
+    int32_t K;
+    int32_t gs;
+    const void *q;
+    const void *q2;
+    const float *scales;
+} dqg_matrix;
+
+/* One expert's three matrices: gate and up are [I x H], down is [H x I]. */
+typedef struct {
+    dqg_matrix gate;
+    dqg_matrix up;
+    dqg_matrix down;
+} dqg_expert;
+
+/* Opaque: a device copy of the experts' descriptors (owned by the library). */
+typedef struct dqg_expert_table dqg_expert_table;
+
+/* Handle of an issued expert-group call. */
+typedef struct {
+    void *event;          /* hipEvent_t recorded after the call's kernels */
+    const int32_t *flag;  /* device word the kernels set when an id was out of range */
+    int32_t status;       /* DQG_OK until dqg_expert_group_take reports otherwise */
+} dqg_ticket;
+
+/* Counters of calls, launches and host-known algorithmic bytes. */
+typedef struct {
+    uint64_t calls_matmul;
+    uint64_t calls_gate_up;
+    uint64_t calls_dequant;
+    uint64_t calls_expert_group;
+    uint64_t launches;
+    uint64_t bytes;   /* weight codes + scales + x + y of matmul, gate_up, dequant */
+} dqg_counters;
+
+/*
+ * y[s][o] = sum_k W[o][k] * x[s][k] for s < S.
+ * Quantised GEMV (the guide's API-contract section, coli_vk_matmul; the
+ * shader-level section for the decode).  x: f32 [S][K]; y: f32 [S][O].
+ * S >= 1; every token's row has the same bits whatever S is.
+ */
+int dqg_matmul(const dqg_matrix *W, const float *x, int32_t S, float *y, void *stream);
+
+/*
+ * h[s][i] = silu(G[i] . x[s]) * (U[i] . x[s]), silu(z) = z / (1 + e^-z).
+ * The SwiGLU half of an expert MLP in one launch with x read once (the
+ * guide's API-contract section, coli_vk_gate_up).  G and U: [I x H] of one
+ * format; x: f32 [S][H]; h: f32 [S][I].
+ */
+int dqg_gate_up(const dqg_matrix *G, const dqg_matrix *U, const float *x, int32_t S, float *h,
+                void *stream);
+
+/*
+ * out[o][k] = value(o, k) * scale(o, k), rounded once to f32.
+ * Materialises the dequantised weights (for bit-exact checks of the decode
+ * that the other calls do in registers).  out: f32 [O][K].
+ */
+int dqg_dequant(const dqg_matrix *W, float *out, void *stream);
+
+/*
+ * Build the device descriptor table of n_experts experts (all with the same
+ * gate/up format, group size and [I x H] shape, and the same down format,
+ * group size and [H x I] shape).  Synchronous (one small host-to-device
+ * copy on the current device).  The pointed-to weights stay caller-owned
+ * and must outlive the table.  The resident-expert table stands for the
+ * device registry of the guide's "what runs on the GPU" section.
+ */
+int dqg_expert_table_create(const dqg_expert *experts, int32_t n_experts, dqg_expert_table **out);
+void dqg_expert_table_destroy(dqg_expert_table *table);
+
+/* Scratch bytes dqg_expert_group needs for S tokens of top-k routing:
+ * the hidden state h of every (token, rank) and shared slot, plus a flag. */
+size_t dqg_expert_group_scratch_bytes(const dqg_expert_table *table, int32_t S, int32_t k);
+
+/*
+ * y[t] = sum_{r<k} w[t][r] * MLP_{ids[t][r]}(x[t]) + MLP_shared(x[t])
+ * with MLP_e(x) = down_e . (silu(gate_e . x) * (up_e . x)).
+ * The whole batch of routed experts in two launches with h kept in device
+ * scratch (the guide's API-contract section, coli_vk_expert_group); the
+ * routed outputs join each token in rank order and the shared expert last
+ * ("colibri -- Vulkan backend (docs/vulkan.md)", the tier's properties and
+ * the GLM-5.2 paragraph).  An expert used by several tokens is read once.
+ *   ids: int32 [S][k] device; w: f32 [S][k] device; shared: an expert index
+ *   or -1 for none; x: f32 [S][H]; y: f32 [S][H]; scratch: device buffer of
+ *   at least dqg_expert_group_scratch_bytes(table, S, k) bytes.  After the
+ *   call its first bytes hold h, f32 [S*k + S][I]: slot t*k + r for
+ *   (token t, rank r), slot S*k + t for token t's shared expert.
+ * An id outside [0, n_experts) makes its token's row of y NaN and sets the
+ * scratch flag that dqg_expert_group_take reports.  No host sync.
+ */
+int dqg_expert_group(const dqg_expert_table *table, int32_t S, int32_t k, const int32_t *ids,
+                     const float *w, int32_t shared, const float *x, float *y, void *scratch,
+                     size_t scratch_bytes, void *stream);
+
+/* As dqg_expert_group, then records an event in `ticket` (the async form,
+ * coli_vk_expert_group_issue in the guide's API-contract section).  The
+ * scratch must stay untouched until the ticket is taken. */
+int dqg_expert_group_issue(const dqg_expert_table *table, int32_t S, int32_t k,
+                           const int32_t *ids, const float *w, int32_t shared, const float *x,
+                           float *y, void *scratch, size_t scratch_bytes, void *stream,
+                           dqg_ticket *ticket);
+
+/* Join an issued call: waits for its event, then reads its flag.  Returns
+ * DQG_OK, DQG_EROUTE (an id was out of range) or DQG_EDEVICE.  Releases
+ * the event; a ticket is taken once. */
+int dqg_expert_group_take(dqg_ticket *ticket);
+
+/* Per-kernel device time, measured with HIP events that the library
+ * records on the launch stream around each kernel it enqueues.
+ * dqg_prof_begin(capacity) creates `capacity` event pairs (host-blocking,
+ * call it outside timed regions); the next `capacity` launches are timed.
+ * dqg_prof_end waits for the recorded events, fills up to `max` records
+ * (one per kernel name, in first-launch order), stores their count in *n
+ * and releases the events.  Kernel names: "matmul", "gate_up", "dequant",
+ * "group_gate_up", "group_down". */
+typedef struct {
+    char kernel[32];
+    int64_t launches;
+    double total_ms;
+} dqg_prof_record;
+
+int dqg_prof_begin(int32_t capacity);
+int dqg_prof_end(dqg_prof_record *out, int32_t max, int32_t *n);
+
+/* Text of the calling thread's last error (never NULL). */
+const char *dqg_last_error(void);
+
+/* Snapshot and reset of the process-wide counters. */
+void dqg_stats(dqg_counters *out);
+void dqg_stats_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DQG_H */

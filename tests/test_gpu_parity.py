@@ -1,0 +1,354 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI.
+
+Bars: dequantised weights bit for bit; outputs within 1e-5 of the per-row
+normaliser sum_k |w*x| (for the expert group, the oracle's propagated
+normaliser: each down row's own plus the first-order reach of the errors
+its h may carry, weighted by |router weight|).
+"""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pinlib
+import synth
+from gpu_helpers import (HostExperts, TOL, assert_close, dev_f32, dev_i32, host, log,
+                         upload_experts)
+
+pytestmark = pytest.mark.gpu
+
+if torch.cuda.is_available():
+    import dequant_gemv_expert_amd as dq
+else:   # collected on CPU-only hosts, never run there
+    dq = None
+
+
+@pytest.fixture(autouse=True)
+def _announce(request):
+    log(f"[gpu] start {request.node.nodeid}")
+    yield
+    torch.cuda.synchronize()
+    log(f"[gpu] done  {request.node.nodeid}")
+
+
+def up(m):
+    return dq.Matrix.upload(m)
+
+
+def bits_equal(a: np.ndarray, b: np.ndarray) -> bool:
+    return a.view(np.uint32).tobytes() == b.view(np.uint32).tobytes()
+
+
+SMALL = [  # (fmt, O, K, gs)
+    (1, 1, 16, None), (1, 77, 512, None), (1, 33, 2064, None),
+    (2, 45, 96, None), (2, 300, 2240, None),
+    (4, 1, 32, 32), (4, 77, 2240, 32), (4, 130, 4128, 32), (4, 64, 2048, 64), (4, 50, 1024, 128),
+    (5, 3, 64, 64), (5, 77, 4160, 64), (5, 129, 8192, 64),
+    (7, 1, 32, 32), (7, 77, 2240, 32), (7, 300, 4128, 32),
+]
+
+
+def _small(i, spec):
+    fmt, O, K, gs = spec
+    return synth.matrix(fmt, O, K, gs, 1000 + i, fmt)
+
+
+# ---------------------------------------------------------------------------
+# dequant: bits
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("i,spec", list(enumerate(SMALL)), ids=[f"fmt{s[0]}_{s[1]}x{s[2]}" for s in SMALL])
+def test_dequant_bits_random(i, spec):
+    m = _small(i, spec)
+    got = host(dq.dqg_dequant(up(m)))
+    want = oracle.dequant(m)
+    assert bits_equal(got, want), f"{spec}: dequant bits differ"
+
+
+def test_dequant_bits_all_codes_and_signed_zero():
+    cases = []
+    q = np.tile(np.arange(256, dtype=np.uint8), (2, 1))                  # every byte, K = 512
+    for fmt, gs in ((4, 32), (4, 64), (2, 512), (7, 32)):
+        s = synth.rng_for(3, fmt).uniform(-2e-2, 2e-2, size=(2, 512 // gs)).astype(np.float32)
+        cases.append(synth.QMatrix(fmt, 2, 512, gs, q.copy(), None, s))
+    q8 = np.tile(np.arange(256, dtype=np.uint8).view(np.int8), (2, 1))  # int8, with -128
+    cases.append(synth.QMatrix(1, 2, 256, 256, q8, None, np.array([[3e-3], [-7e-3]], np.float32)))
+    for code in range(8):                                                 # int3, every code
+        lo = np.full((2, 4), (code & 3) * 0x55555555, np.uint32)
+        hi = np.full((2, 2), 0xFFFFFFFF if code & 4 else 0, np.uint32)
+        cases.append(synth.QMatrix(5, 2, 64, 64, lo, hi, np.array([[1e-2], [-1e-2]], np.float32)))
+    low, high, _ = pinlib.golden_int3()
+    cases.append(synth.QMatrix(5, 1, 64, 64, np.array([low], np.uint32), np.array([high], np.uint32),
+                               np.array([[0.25]], np.float32)))
+    for m in cases:
+        got = host(dq.dqg_dequant(up(m)))
+        want = oracle.dequant(m)
+        assert bits_equal(got, want), f"fmt {m.fmt}: dequant bits differ"
+
+
+# ---------------------------------------------------------------------------
+# GEMV
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("i,spec", list(enumerate(SMALL)), ids=[f"fmt{s[0]}_{s[1]}x{s[2]}" for s in SMALL])
+def test_one_hot_is_exact(i, spec):
+    """x = e_k: the GPU's y[o] equals the dequantised weight exactly."""
+    m = _small(i, spec)
+    K = m.K
+    ks = sorted(set([0, 1, K - 1, K // 2] + list(synth.rng_for(4, i).integers(0, K, 12))))
+    x = np.zeros((len(ks), K), np.float32)
+    for j, k in enumerate(ks):
+        x[j, k] = 1.0
+    y = host(dq.dqg_matmul(up(m), dev_f32(x)))
+    d = oracle.dequant(m)
+    for j, k in enumerate(ks):
+        assert np.array_equal(y[j], d[:, k]), f"{spec}: column {k}"
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 5, 8, 9, 13])
+@pytest.mark.parametrize("i,spec", list(enumerate(SMALL)), ids=[f"fmt{s[0]}_{s[1]}x{s[2]}" for s in SMALL])
+def test_matmul_matches_oracle(i, spec, S):
+    m = _small(i, spec)
+    x = synth.activations(S, m.K, 2000 + i, S)
+    y = host(dq.dqg_matmul(up(m), dev_f32(x)))
+    yr, a = oracle.gemv(m, x)
+    assert_close(y, yr, a, f"matmul {spec} S={S}")
+
+
+def test_matmul_batch_invariant():
+    """Each token's row has the same bits alone and inside a batch."""
+    for i, spec in enumerate(SMALL[::3]):
+        m = _small(i, spec)
+        W = up(m)
+        x = synth.activations(9, m.K, 2100 + i)
+        yb = host(dq.dqg_matmul(W, dev_f32(x)))
+        for t in range(9):
+            y1 = host(dq.dqg_matmul(W, dev_f32(x[t:t + 1])))
+            assert bits_equal(yb[t], y1[0]), (spec, t)
+
+
+def test_zero_scales_give_zero():
+    for i, spec in enumerate(SMALL[::2]):
+        m = _small(i, spec)
+        m.scales = np.zeros_like(m.scales)
+        y = host(dq.dqg_matmul(up(m), dev_f32(synth.activations(3, m.K, 5))))
+        assert np.all(y == 0), spec
+
+
+# ---------------------------------------------------------------------------
+# gate_up
+# ---------------------------------------------------------------------------
+
+GU = [(4, 64, 2048, 32), (4, 77, 96, 32), (7, 130, 2240, 32), (1, 50, 512, None), (5, 33, 4160, 64),
+      (4, 2048, 6144, 32)]
+
+
+@pytest.mark.parametrize("S", [1, 2, 4, 5, 8])
+@pytest.mark.parametrize("spec", GU, ids=[f"fmt{s[0]}_{s[1]}x{s[2]}" for s in GU])
+def test_gate_up_matches_oracle(spec, S):
+    fmt, I, H, gs = spec
+    G = synth.matrix(fmt, I, H, gs, 3000, 0)
+    U = synth.matrix(fmt, I, H, gs, 3000, 1)
+    x = synth.activations(S, H, 3001, S)
+    h = host(dq.dqg_gate_up(up(G), up(U), dev_f32(x)))
+    r = oracle.gate_up(G, U, x)
+    assert_close(h, r["h"], r["nh"], f"gate_up {spec} S={S}")
+
+
+# ---------------------------------------------------------------------------
+# expert group (small)
+# ---------------------------------------------------------------------------
+
+def _small_group(n, fmt=4, gs=32, H=256, I=128, seed=4000, **kw):
+    hs = [synth.expert(fmt, H, I, gs, seed, i, **kw) for i in range(n)]
+    table = dq.ExpertTable([dq.Expert.upload(h) for h in hs])
+    return hs, table
+
+
+def _check_group(hs, table, ids, w, shared, x, what):
+    S, k = ids.shape
+    scratch = table.scratch(S, k)
+    y = host(dq.dqg_expert_group(table, dev_i32(ids), dev_f32(w), shared, dev_f32(x), scratch=scratch))
+    yr, a = oracle.expert_group(hs, ids, w, shared, x)
+    worst = assert_close(y, yr, a, what)
+    # stage check: h of every valid slot in scratch
+    I = table.I
+    hdev = host(scratch[: (S * k + S) * I * 4].view(torch.float32)).reshape(S * k + S, I)
+    for t in range(S):
+        for r in range(k):
+            e = int(ids[t, r])
+            if 0 <= e < len(hs):
+                o = oracle.gate_up(hs[e].gate, hs[e].up, x[t:t + 1])
+                assert_close(hdev[t * k + r][None], o["h"], o["nh"], f"{what} h[{t},{r}]")
+        if shared is not None and shared >= 0:
+            o = oracle.gate_up(hs[shared].gate, hs[shared].up, x[t:t + 1])
+            assert_close(hdev[S * k + t][None], o["h"], o["nh"], f"{what} h[shared {t}]")
+    return y, worst
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 4, 5, 8])
+@pytest.mark.parametrize("shared", [True, False])
+def test_group_small(S, shared):
+    E, k = 12, 4
+    hs, table = _small_group(E + 1)
+    ids, w = synth.routing(S, E, k, 4100 + S)
+    x = synth.activations(S, 256, 4200 + S)
+    _check_group(hs, table, ids, w, E if shared else None, x, f"group S={S} shared={shared}")
+
+
+@pytest.mark.parametrize("fmts", [(7, 32, 4, 32), (4, 64, 1, None), (1, None, 7, 32), (5, 64, 4, 32)])
+def test_group_mixed_formats(fmts):
+    fmt, gs, dfmt, dgs = fmts
+    hs, table = _small_group(7, fmt=fmt, gs=gs, down_fmt=dfmt, down_gs=dgs, seed=4300)
+    ids, w = synth.routing(3, 6, 3, 4301)
+    x = synth.activations(3, 256, 4302)
+    _check_group(hs, table, ids, w, 6, x, f"group mixed {fmts}")
+
+
+def test_group_many_slots():
+    """S*k > 64: the dedup ballots span several windows."""
+    hs, table = _small_group(20)
+    ids, w = synth.routing(20, 19, 8, 4400)
+    x = synth.activations(20, 256, 4401)
+    _check_group(hs, table, ids, w, 19, x, "group S=20 k=8")
+
+
+def test_group_repeated_id_in_a_token():
+    hs, table = _small_group(8)
+    ids = np.array([[3, 3, 5, 7], [5, 1, 3, 3]], np.int32)
+    w = np.array([[0.4, 0.3, 0.2, 0.1], [0.25, 0.25, 0.25, 0.25]], np.float32)
+    x = synth.activations(2, 256, 4500)
+    _check_group(hs, table, ids, w, 0, x, "group repeated ids")
+
+
+def test_group_batch_invariant():
+    hs, table = _small_group(13)
+    ids, w = synth.routing(5, 12, 4, 4600)
+    x = synth.activations(5, 256, 4601)
+    yb = host(dq.dqg_expert_group(table, dev_i32(ids), dev_f32(w), 12, dev_f32(x)))
+    for t in range(5):
+        y1 = host(dq.dqg_expert_group(table, dev_i32(ids[t:t + 1]), dev_f32(w[t:t + 1]), 12,
+                                      dev_f32(x[t:t + 1])))
+        assert bits_equal(yb[t], y1[0]), t
+
+
+def test_group_bad_id_is_reported():
+    hs, table = _small_group(6)
+    ids = np.array([[0, 1, 2], [1, 99, 4]], np.int32)
+    w = np.full((2, 3), 1 / 3, np.float32)
+    x = synth.activations(2, 256, 4700)
+    ticket, y, scratch = dq.dqg_expert_group_issue(table, dev_i32(ids), dev_f32(w), 5, dev_f32(x))
+    with pytest.raises(dq.DqgError) as ei:
+        dq.dqg_expert_group_take(ticket)
+    assert ei.value.code == -7
+    yh = host(y)
+    assert np.all(np.isnan(yh[1])) and np.all(np.isfinite(yh[0]))
+    yr, a = oracle.expert_group(hs, ids[:1], w[:1], 5, x[:1])
+    assert_close(yh[:1], yr, a, "row beside a bad id")
+    # the next good call clears the flag
+    ids[1, 1] = 3
+    ticket, y, scratch = dq.dqg_expert_group_issue(table, dev_i32(ids), dev_f32(w), 5, dev_f32(x),
+                                                   scratch=scratch)
+    dq.dqg_expert_group_take(ticket)
+
+
+def test_group_zero_weights_and_no_shared():
+    hs, table = _small_group(6)
+    ids, _ = synth.routing(2, 5, 3, 4800)
+    w = np.zeros((2, 3), np.float32)
+    x = synth.activations(2, 256, 4801)
+    y = host(dq.dqg_expert_group(table, dev_i32(ids), dev_f32(w), None, dev_f32(x)))
+    assert np.all(y == 0)
+
+
+# ---------------------------------------------------------------------------
+# the measured workloads at full size
+# ---------------------------------------------------------------------------
+
+def test_workload_int8_gemv_256x512():
+    c = synth.WORKLOADS["int8_gemv_256x512"]
+    m = synth.matrix(c["fmt"], c["O"], c["K"], c["gs"], c["seed"], 0)
+    x = synth.activations(1, c["K"], c["seed"], 1)
+    y = host(dq.dqg_matmul(up(m), dev_f32(x)))
+    yr, a = oracle.gemv(m, x)
+    log(f"  worst normalised error {assert_close(y, yr, a, 'int8 256x512'):.2e}")
+
+
+@pytest.mark.parametrize("S", [1, 4])
+def test_workload_int4g32_gemv_6144(S):
+    c = synth.WORKLOADS["int4g32_gemv_6144x6144"]
+    m = synth.matrix(c["fmt"], c["O"], c["K"], c["gs"], c["seed"], 0)
+    x = synth.activations(S, c["K"], c["seed"], S)
+    y = host(dq.dqg_matmul(up(m), dev_f32(x)))
+    yr, a = oracle.gemv(m, x)
+    log(f"  worst normalised error {assert_close(y, yr, a, f'int4 6144 S={S}'):.2e}")
+
+
+def test_workload_int3g64_gemv_6144x16384():
+    c = synth.WORKLOADS["int3g64_gemv_6144x16384"]
+    m = synth.matrix(c["fmt"], c["O"], c["K"], c["gs"], c["seed"], 0)
+    x = synth.activations(1, c["K"], c["seed"], 1)
+    y = host(dq.dqg_matmul(up(m), dev_f32(x)))
+    yr, a = oracle.gemv(m, x)
+    log(f"  worst normalised error {assert_close(y, yr, a, 'int3 6144x16384'):.2e}")
+
+
+def test_workload_single_expert_mlp():
+    c = synth.WORKLOADS["int4g32_expert_6144x2048"]
+    e = synth.expert(c["fmt"], c["H"], c["I"], c["gs"], c["seed"], 0)
+    x = synth.activations(1, c["H"], c["seed"], 1)
+    d = dq.Expert.upload(e)
+    h = dq.dqg_gate_up(d.gate, d.up, dev_f32(x))
+    y = host(dq.dqg_matmul(d.down, h))
+    yr, a = oracle.expert_group([e], np.zeros((1, 1), np.int32), np.ones((1, 1), np.float32), None, x)
+    log(f"  worst normalised error {assert_close(y, yr, a, 'expert MLP'):.2e}")
+    table = dq.ExpertTable([d])
+    y2 = host(dq.dqg_expert_group(table, dev_i32([[0]]), dev_f32([[1.0]]), None, dev_f32(x)))
+    assert_close(y2, yr, a, "expert MLP via expert_group")
+
+
+@pytest.fixture(scope="module")
+def group256():
+    c = synth.WORKLOADS["int4g32_expert_group_256top8_shared"]
+    routes = {S: synth.routing(S, c["E"], c["k"], c["seed"], S) for S in c["S"]}
+    keep = set(np.concatenate([r[0].ravel() for r in routes.values()]).tolist()) | {c["E"]}
+    log(f"  drawing {c['E'] + 1} experts ({len(keep)} kept on the host)")
+    dev, hosts = upload_experts(c["fmt"], c["H"], c["I"], c["gs"], c["seed"], c["E"] + 1, keep=keep)
+    table = dq.ExpertTable(dev)
+    yield c, routes, table, HostExperts(c["E"] + 1, hosts)
+    table.close()
+    del dev, table
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("S", [1, 2, 4])
+def test_workload_group_256top8_shared(group256, S):
+    c, routes, table, hosts = group256
+    ids, w = routes[S]
+    x = synth.activations(S, c["H"], c["seed"], 100 + S)
+    y = host(dq.dqg_expert_group(table, dev_i32(ids), dev_f32(w), c["E"], dev_f32(x)))
+    yr, a = oracle.expert_group(hosts, ids, w, c["E"], x)
+    log(f"  worst normalised error {assert_close(y, yr, a, f'group256 S={S}'):.2e}")
+
+
+def test_workload_mxfp4_group_384top8_s8():
+    c = synth.WORKLOADS["mxfp4_expert_group_384top8_s8"]
+    S = 8
+    ids, w = synth.routing(S, c["E"], c["k"], c["seed"], S)
+    sample = [0, 5]   # tokens checked by the oracle (token rows are independent)
+    keep = set(ids[sample].ravel().tolist())
+    log(f"  drawing {c['E']} MXFP4 experts")
+    dev, hosts = upload_experts(c["fmt"], c["H"], c["I"], c["gs"], c["seed"], c["E"], keep=keep)
+    table = dq.ExpertTable(dev)
+    x = synth.activations(S, c["H"], c["seed"], 200)
+    y = host(dq.dqg_expert_group(table, dev_i32(ids), dev_f32(w), None, dev_f32(x)))
+    yr, a = oracle.expert_group(HostExperts(c["E"], hosts), ids[sample], w[sample], None, x[sample])
+    log(f"  worst normalised error {assert_close(y[sample], yr, a, 'mxfp4 group S=8'):.2e}")
+    assert np.all(np.isfinite(y))
+    table.close()
+    del dev, table
+    gc.collect()
+    torch.cuda.empty_cache()
