@@ -36,6 +36,38 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+KERNEL_SOURCES = ["dequant_gemv_expert_amd/csrc/dqg_kernels.hip", "dequant_gemv_expert_amd/csrc/dqg_api.cpp",
+                  "dequant_gemv_expert_amd/csrc/dqg_internal.h"]
+TRAFFIC_PROFILE = "profiles/group_int4g32_s1_traffic.md"
+
+
+def kernel_sources_sha256() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, TRAFFIC_PROFILE)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("traffic:"):
+                key, _, val = line[len("traffic:"):].strip().partition("=")
+                fields[key.strip()] = val.strip()
+    if fields.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None
+    v = fields.get(f"bytes_per_launch.{kernel}")
+    return int(float(v)) if v else None
+
+
 def matrix_bytes(m) -> int:
     n = m.q.nbytes + m.scales.nbytes
     if m.q2 is not None:
@@ -54,6 +86,9 @@ def main():
     ap.add_argument("--shared-copies", type=int, default=12)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (torch) 5 times, the reference "
+                         "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -63,6 +98,17 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "copies": 5}), flush=True)
+        return
 
     import synth
     import dequant_gemv_expert_amd as dq
@@ -228,7 +274,9 @@ def main():
         "roofline": {"kernel": "group_gate_up", "bound": "hbm",
                      "achieved": round(achieved, 1) if achieved else None, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
-                     "traffic": None, "avg_us": round(ms_a / max(n_a, 1) * 1e3, 2),
+                     "traffic": profiled_traffic("group_gate_up") if (S == 1 and args.workload ==
+                                "int4g32_expert_group_256top8_shared") else None,
+                     "avg_us": round(ms_a / max(n_a, 1) * 1e3, 2),
                      "bytes_per_launch": round(gu_total / K)},
         "roofline_down": {"kernel": "group_down", "avg_us": round(ms_b / max(n_b, 1) * 1e3, 2),
                           "achieved": round(down_total / (ms_b * 1e-3) / 1e9, 1) if ms_b else None,

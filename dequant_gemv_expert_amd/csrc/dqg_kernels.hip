@@ -34,6 +34,27 @@ namespace {
 
 constexpr int WAVE = 64;
 
+// Tile shapes of the grouped launches (compile-time; the defaults are the
+// measured best on MI355X for the int4-g32 group at 1-4 tokens).
+#ifndef DQG_RA
+#define DQG_RA 4
+#endif
+#ifndef DQG_WPB_A
+#define DQG_WPB_A 4
+#endif
+#ifndef DQG_RB
+#define DQG_RB 8
+#endif
+#ifndef DQG_CAP_A
+#define DQG_CAP_A 2   // largest token batch of the gate/up launch (x rows staged in LDS)
+#endif
+#ifndef DQG_CAP_B
+#define DQG_CAP_B 1   // largest slot batch of the down launch
+#endif
+constexpr int RA = DQG_RA;        // rows of gate (and of up) per wave in kernel A
+constexpr int WPB_A = DQG_WPB_A;  // waves per block in kernel A
+constexpr int RB = DQG_RB;        // rows of down per block in kernel B
+
 // Global-memory loads: base pointers are wave-uniform, offsets 32-bit, so
 // the address is one SGPR pair plus one VGPR (no per-row 64-bit math).
 #define GLOBAL __attribute__((address_space(1)))
@@ -44,8 +65,14 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+#ifndef DQG_NT
+#define DQG_NT 0
+#endif
+// Weight codes are read once per call: DQG_NT=1 marks those loads
+// non-temporal so that they do not displace x and h in the caches.
 __device__ __forceinline__ uint4 ld16(gbytes base, uint32_t off) {
-    const u32x4 v = *(const GLOBAL u32x4 *)(base + off);
+    const GLOBAL u32x4 *p = (const GLOBAL u32x4 *)(base + off);
+    const u32x4 v = DQG_NT ? __builtin_nontemporal_load(p) : *p;
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ uint2 ld8(gbytes base, uint32_t off) {
@@ -60,6 +87,23 @@ __device__ __forceinline__ float4 ldf4(gfloats base, uint32_t idx) {
 __device__ __forceinline__ float ldf(gfloats base, uint32_t idx) {
     return *(const GLOBAL float *)((gbytes)base + (idx << 2));
 }
+
+// Where a step reads x from: global memory (L2) or the block's LDS copy.
+#define LDS __attribute__((address_space(3)))
+typedef LDS float *lfloats_w;
+typedef const LDS float *lfloats;
+
+struct XGlobal {
+    gfloats p;
+    __device__ __forceinline__ float4 load4(uint32_t idx) const { return ldf4(p, idx); }
+};
+struct XLds {
+    lfloats p;
+    __device__ __forceinline__ float4 load4(uint32_t idx) const {
+        const f32x4 v = *(const LDS f32x4 *)(p + idx);
+        return make_float4(v.x, v.y, v.z, v.w);
+    }
+};
 
 // A wave-uniform global pointer, held in SGPRs.
 __device__ __forceinline__ uint64_t uniform_bits(const void *p) {
@@ -253,75 +297,113 @@ __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 // p = sum(pattern * x) over the chunk, then acc += scale * VMUL *
 // (p - OFFS * sum(x)): the code offset is removed once per chunk and the
 // scale applied once per chunk.
+//
+// A step issues every load of one chunk (codes and scales of all rows,
+// then x) before any arithmetic, held ahead by a scheduling barrier, so a
+// wave has all its requests in flight before it waits.  The chunk index
+// is hidden from loop strength reduction so that each load is one SGPR
+// base plus a 32-bit lane offset.  With DQG_PIPE the next chunk's loads
+// are issued before the current chunk is computed.
 // ---------------------------------------------------------------------------
 template <int C, int NR, int SM>
-__device__ __forceinline__ void dot_rows(const GRow (&rows)[NR], int nch, int shift,
-                                         const gfloats (&xp)[SM], float (&acc)[NR][SM]) {
+struct Step {
+    typename Codec<C>::Chunk ch[NR];
+    float sc[NR];
+    float xv[SM][Codec<C>::CW];
+};
+
+template <int C, int NR, int SM, typename XP>
+__device__ __forceinline__ void step_load(Step<C, NR, SM> &st, const GRow (&rows)[NR], int shift,
+                                          const XP (&xp)[SM], uint32_t cu) {
     using Cd = Codec<C>;
+    const uint32_t si = cu >> shift;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        st.ch[r] = Cd::load(rows[r], cu);
+        st.sc[r] = ldf(rows[r].s, si);
+    }
+#pragma unroll
+    for (int s = 0; s < SM; ++s)
+#pragma unroll
+        for (int i = 0; i < Cd::CW / 4; ++i) {
+            const float4 t = xp[s].load4(cu * Cd::CW + 4 * i);
+            st.xv[s][4 * i] = t.x; st.xv[s][4 * i + 1] = t.y; st.xv[s][4 * i + 2] = t.z; st.xv[s][4 * i + 3] = t.w;
+        }
+}
+
+template <int C, int NR, int SM>
+__device__ __forceinline__ void step_compute(const Step<C, NR, SM> &st, float (&acc)[NR][SM]) {
+    using Cd = Codec<C>;
+    float p[NR][SM], xs[SM];
+#pragma unroll
+    for (int s = 0; s < SM; ++s) {
+        xs[s] = 0.f;
+        if (Cd::OFFS != 0.f) {
+#pragma unroll
+            for (int i = 0; i < Cd::CW; ++i) xs[s] += st.xv[s][i];
+        }
+#pragma unroll
+        for (int r = 0; r < NR; ++r) p[r][s] = 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < Cd::UNITS; ++u) {
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            uint32_t pr[Cd::UW / 2];
+            Cd::decode(st.ch[r], u, pr);
+#pragma unroll
+            for (int s = 0; s < SM; ++s)
+#pragma unroll
+                for (int q = 0; q < Cd::UW / 2; ++q) {
+                    p[r][s] = fma_lo(pr[q], st.xv[s][u * Cd::UW + Cd::IDX[2 * q]], p[r][s]);
+                    p[r][s] = fma_hi(pr[q], st.xv[s][u * Cd::UW + Cd::IDX[2 * q + 1]], p[r][s]);
+                }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int s = 0; s < SM; ++s)
+            acc[r][s] = fmaf(st.sc[r] * Cd::VMUL, fmaf(-Cd::OFFS, xs[s], p[r][s]), acc[r][s]);
+}
+
+#ifndef DQG_PIPE
+#define DQG_PIPE 0
+#endif
+
+template <int C, int NR, int SM, bool PIPE = DQG_PIPE, typename XP = XGlobal>
+__device__ __forceinline__ void dot_rows(const GRow (&rows)[NR], int nch, int shift,
+                                         const XP (&xp)[SM], float (&acc)[NR][SM]) {
     const int lane = threadIdx.x & (WAVE - 1);
 #pragma unroll
     for (int r = 0; r < NR; ++r)
 #pragma unroll
         for (int s = 0; s < SM; ++s) acc[r][s] = 0.f;
-
-    for (int c = lane; c < nch; c += WAVE) {
-        // Every load of the step first (codes and scales of all rows, then
-        // x), kept ahead of the arithmetic by a scheduling barrier so that a
-        // wave has all its requests in flight before it waits.  The chunk
-        // index is hidden from loop strength reduction so that each load is
-        // one SGPR base plus a 32-bit lane offset.
-        const uint32_t cu = opaque((uint32_t)c);
-        typename Cd::Chunk ch[NR];
-        float sc[NR];
-        const uint32_t si = cu >> shift;
-#pragma unroll
-        for (int r = 0; r < NR; ++r) {
-            ch[r] = Cd::load(rows[r], cu);
-            sc[r] = ldf(rows[r].s, si);
+    if (!PIPE) {
+        for (int c = lane; c < nch; c += WAVE) {
+            Step<C, NR, SM> st;
+            step_load(st, rows, shift, xp, opaque((uint32_t)c));
+            __builtin_amdgcn_sched_barrier(0);
+            step_compute(st, acc);
         }
-        float xv[SM][Cd::CW];
-#pragma unroll
-        for (int s = 0; s < SM; ++s)
-#pragma unroll
-            for (int i = 0; i < Cd::CW / 4; ++i) {
-                const float4 t = ldf4(xp[s], cu * Cd::CW + 4 * i);
-                xv[s][4 * i] = t.x; xv[s][4 * i + 1] = t.y; xv[s][4 * i + 2] = t.z; xv[s][4 * i + 3] = t.w;
-            }
+        return;
+    }
+    int c = lane;
+    Step<C, NR, SM> cur, nxt;
+    if (c < nch) step_load(cur, rows, shift, xp, opaque((uint32_t)c));
+    while (c < nch) {
+        const int cn = c + WAVE;
+        if (cn < nch) step_load(nxt, rows, shift, xp, opaque((uint32_t)cn));
         __builtin_amdgcn_sched_barrier(0);
-        float p[NR][SM], xs[SM];
-#pragma unroll
-        for (int s = 0; s < SM; ++s) {
-            xs[s] = 0.f;
-            if (Cd::OFFS != 0.f) {
-#pragma unroll
-                for (int i = 0; i < Cd::CW; ++i) xs[s] += xv[s][i];
-            }
-#pragma unroll
-            for (int r = 0; r < NR; ++r) p[r][s] = 0.f;
-        }
-#pragma unroll
-        for (int u = 0; u < Cd::UNITS; ++u) {
-#pragma unroll
-            for (int r = 0; r < NR; ++r) {
-                uint32_t pr[Cd::UW / 2];
-                Cd::decode(ch[r], u, pr);
-#pragma unroll
-                for (int s = 0; s < SM; ++s)
-#pragma unroll
-                    for (int q = 0; q < Cd::UW / 2; ++q) {
-                        p[r][s] = fma_lo(pr[q], xv[s][u * Cd::UW + Cd::IDX[2 * q]], p[r][s]);
-                        p[r][s] = fma_hi(pr[q], xv[s][u * Cd::UW + Cd::IDX[2 * q + 1]], p[r][s]);
-                    }
-            }
-        }
-#pragma unroll
-        for (int r = 0; r < NR; ++r)
-#pragma unroll
-            for (int s = 0; s < SM; ++s)
-                acc[r][s] = fmaf(sc[r] * Cd::VMUL, fmaf(-Cd::OFFS, xs[s], p[r][s]), acc[r][s]);
+        step_compute(cur, acc);
+        cur = nxt;
+        c = cn;
     }
 }
 
+// Pointers of one row.  Rows are wave-uniform in every kernel but dequant;
+// readfirstlane keeps them in SGPRs even when the matrix came from a table
+// read with vector loads.
 __device__ __forceinline__ GRow row_ptrs(const MatDev &m, int row) {
     return {gb(m.q + (size_t)row * m.qstride), gb(m.q2 + (size_t)row * m.q2stride),
             gf(m.s + (size_t)row * m.sstride)};
@@ -348,9 +430,9 @@ __global__ void __launch_bounds__(256) k_matmul(MatDev m, const float *__restric
     for (int r = 0; r < R; ++r) rows[r] = row_ptrs(m, min(row0 + r, m.O - 1));
     const int nch = m.K / Codec<C>::CW;
     for (int s0 = 0; s0 < S; s0 += SM) {
-        gfloats xp[SM];
+        XGlobal xp[SM];
 #pragma unroll
-        for (int s = 0; s < SM; ++s) xp[s] = gf(x + (size_t)min(s0 + s, S - 1) * m.K);
+        for (int s = 0; s < SM; ++s) xp[s] = {gf(x + (size_t)min(s0 + s, S - 1) * m.K)};
         float acc[R][SM];
         dot_rows<C, R, SM>(rows, nch, m.shift, xp, acc);
         float out = 0.f;
@@ -385,9 +467,9 @@ __global__ void __launch_bounds__(256) k_gate_up(MatDev g, MatDev u, const float
     }
     const int nch = g.K / Codec<C>::CW;
     for (int s0 = 0; s0 < S; s0 += SM) {
-        gfloats xp[SM];
+        XGlobal xp[SM];
 #pragma unroll
-        for (int s = 0; s < SM; ++s) xp[s] = gf(x + (size_t)min(s0 + s, S - 1) * g.K);
+        for (int s = 0; s < SM; ++s) xp[s] = {gf(x + (size_t)min(s0 + s, S - 1) * g.K)};
         float acc[2 * R][SM];
         dot_rows<C, 2 * R, SM>(rows, nch, g.shift, xp, acc);
         float gv = 0.f, uv = 0.f;
@@ -507,22 +589,40 @@ __device__ __forceinline__ void for_slots(const GroupArgs &a, int q, int e, F &&
     }
 }
 
-// gate_up of R rows (row0..) of expert e for a batch of SM slots.
+// Copies the batch's token rows of x into the block's LDS (all threads).
+template <int SM>
+__device__ __forceinline__ void stage_x(const GroupArgs &a, const SlotBatch &b, lfloats_w xs) {
+    __syncthreads();   // the previous batch's readers are done
+    const int n4 = a.H / 4;
+    for (int i = threadIdx.x; i < SM * n4; i += blockDim.x) {
+        const int s = i / n4, k4 = i - s * n4;
+        int t = b.token[0];
+#pragma unroll
+        for (int j = 1; j < SM; ++j)
+            if (s == j) t = b.token[j];
+        const f32x4 v = *(const GLOBAL f32x4 *)(gf(a.x) + (size_t)t * a.H + 4 * k4);
+        *(LDS f32x4 *)(xs + (size_t)s * a.H + 4 * k4) = v;
+    }
+    __syncthreads();
+}
+
+// gate_up of R rows (row0..) of expert e for a batch of SM slots, x from LDS.
 template <int C, int R, int SM>
 __device__ __forceinline__ void group_gu_batch(const GroupArgs &a, const ExpertDev &ex, int row0,
-                                               const SlotBatch &b) {
+                                               const SlotBatch &b, lfloats_w xs) {
     const int lane = threadIdx.x & (WAVE - 1);
+    stage_x<SM>(a, b, xs);
     GRow rows[2 * R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         rows[r] = row_ptrs(ex.gate, min(row0 + r, a.I - 1));
         rows[R + r] = row_ptrs(ex.up, min(row0 + r, a.I - 1));
     }
-    gfloats xp[SM];
+    XLds xp[SM];
 #pragma unroll
-    for (int s = 0; s < SM; ++s) xp[s] = gf(a.x + (size_t)b.token[s] * a.H);
+    for (int s = 0; s < SM; ++s) xp[s] = {xs + (size_t)s * a.H};
     float acc[2 * R][SM];
-    dot_rows<C, 2 * R, SM>(rows, ex.gate.K / Codec<C>::CW, ex.gate.shift, xp, acc);
+    dot_rows<C, 2 * R, SM, DQG_PIPE, XLds>(rows, ex.gate.K / Codec<C>::CW, ex.gate.shift, xp, acc);
     float gv = 0.f, uv = 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -545,8 +645,13 @@ __device__ __forceinline__ void group_gu_batch(const GroupArgs &a, const ExpertD
 // Kernel A: grid (row blocks of I, units).  Clears the error flag.  CAP is
 // the largest token batch the launch needs (1 when S = 1), so that a
 // launch only carries the register footprint of the batches it can see.
+// The block stages each batch's x rows in LDS (CAP * H floats) once; its
+// waves read their slices from there.  Every wave of a block stays to the
+// end (block barriers), with rows past I clamped and their outputs dropped.
 template <int C, int R, int CAP>
-__global__ void __launch_bounds__(256) k_group_gate_up(GroupArgs a) {
+__global__ void __launch_bounds__(WAVE * WPB_A) k_group_gate_up(GroupArgs a) {
+    extern __shared__ float x_lds_raw[];
+    lfloats_w xs = (lfloats_w)x_lds_raw;
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.flag = 0;
     const int q = blockIdx.y;
     const int nr = a.S * a.k;
@@ -554,13 +659,12 @@ __global__ void __launch_bounds__(256) k_group_gate_up(GroupArgs a) {
     if (e < 0 || e >= a.n_experts) return;         // reported by kernel B
     if (q < nr && !owns(a.ids, q, e)) return;
     const int wave = blockIdx.x * (blockDim.x / WAVE) + wave_id();
-    const int row0 = wave * R;
-    if (row0 >= a.I) return;
+    const int row0 = wave * R;   // rows past I are clamped in row_ptrs, outputs dropped
     const ExpertDev &ex = a.table[e];
     for_slots<CAP>(a, q, e, [&](const SlotBatch &b) {
-        if (CAP == 1 || b.n == 1) group_gu_batch<C, R, 1>(a, ex, row0, b);
-        else if (CAP == 2 || b.n == 2) group_gu_batch<C, R, 2>(a, ex, row0, b);
-        else group_gu_batch<C, R, 4>(a, ex, row0, b);
+        if (CAP == 1 || b.n == 1) group_gu_batch<C, R, 1>(a, ex, row0, b, xs);
+        else if (CAP == 2 || b.n == 2) group_gu_batch<C, R, 2>(a, ex, row0, b, xs);
+        else group_gu_batch<C, R, 4>(a, ex, row0, b, xs);
     });
 }
 
@@ -572,11 +676,11 @@ __device__ __forceinline__ void group_down_batch(const GroupArgs &a, const Exper
     GRow rows[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) rows[r] = row_ptrs(ex.down, min(row0 + r, a.H - 1));
-    gfloats xp[SM];
+    XGlobal xp[SM];
 #pragma unroll
-    for (int s = 0; s < SM; ++s) xp[s] = gf(a.h + (size_t)b.slot[s] * a.I);
+    for (int s = 0; s < SM; ++s) xp[s] = {gf(a.h + (size_t)b.slot[s] * a.I)};
     float acc[R][SM];
-    dot_rows<C, R, SM>(rows, ex.down.K / Codec<C>::CW, ex.down.shift, xp, acc);
+    dot_rows<C, R, SM, false>(rows, ex.down.K / Codec<C>::CW, ex.down.shift, xp, acc);
     float out = 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -692,15 +796,14 @@ hipError_t dequant_c(const MatDev &m, float *out, hipStream_t st) {
     return hipGetLastError();
 }
 
-constexpr int RA = 4;   // rows of gate (and of up) per wave in kernel A
-constexpr int RB = 8;   // rows of down per block in kernel B
 
 template <int C, int CAP>
 hipError_t group_a_cap(const GroupArgs &a, hipStream_t st) {
     const int units = a.S * a.k + (a.shared >= 0 ? 1 : 0);
-    const int rows_per_block = RA * WPB;
+    const int rows_per_block = RA * WPB_A;
     dim3 grid((a.I + rows_per_block - 1) / rows_per_block, units);
-    launch("group_gate_up", (k_group_gate_up<C, RA, CAP>), grid, dim3(WAVE * WPB), 0, st, a);
+    const size_t lds = (size_t)CAP * a.H * sizeof(float);
+    launch("group_gate_up", (k_group_gate_up<C, RA, CAP>), grid, dim3(WAVE * WPB_A), lds, st, a);
     return hipGetLastError();
 }
 
@@ -715,19 +818,21 @@ hipError_t group_b_cap(const GroupArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Batch capacity: one token needs single-slot batches only.
+// Batch capacity: one token needs single-slot batches only.  Tokens that
+// share an expert beyond the capacity take further passes over its rows,
+// which the caches then serve.
 template <int C>
 hipError_t group_a(const GroupArgs &a, hipStream_t st) {
-    if (a.S == 1) return group_a_cap<C, 1>(a, st);
-    if (a.S == 2) return group_a_cap<C, 2>(a, st);
-    return group_a_cap<C, 4>(a, st);
+    if constexpr (DQG_CAP_A == 1) return group_a_cap<C, 1>(a, st);
+    else if constexpr (DQG_CAP_A == 2) return a.S == 1 ? group_a_cap<C, 1>(a, st) : group_a_cap<C, 2>(a, st);
+    else return a.S == 1 ? group_a_cap<C, 1>(a, st) : a.S == 2 ? group_a_cap<C, 2>(a, st) : group_a_cap<C, 4>(a, st);
 }
 
 template <int C>
 hipError_t group_b(const GroupArgs &a, hipStream_t st) {
-    if (a.S == 1) return group_b_cap<C, 1>(a, st);
-    if (a.S == 2) return group_b_cap<C, 2>(a, st);
-    return group_b_cap<C, 4>(a, st);
+    if constexpr (DQG_CAP_B == 1) return group_b_cap<C, 1>(a, st);
+    else if constexpr (DQG_CAP_B == 2) return a.S == 1 ? group_b_cap<C, 1>(a, st) : group_b_cap<C, 2>(a, st);
+    else return a.S == 1 ? group_b_cap<C, 1>(a, st) : a.S == 2 ? group_b_cap<C, 2>(a, st) : group_b_cap<C, 4>(a, st);
 }
 
 }  // namespace
