@@ -15,8 +15,9 @@ weights from the previous steps.
 
 Prints one JSON line: the metric is weight-stream GB/s (algorithmic bytes:
 codes + scales of each distinct expert the step needs, once, plus x and
-y) over wall time; `roofline` is the dominant kernel (the gate/up launch)
-timed with HIP events on its stream; `cpu_baseline` is the CPU oracle on a
+y) over wall time; `roofline` is the dominant kernel (the one-launch group
+kernel; the gate/up launch when a call takes the two-launch form) timed
+with HIP events on its stream; `cpu_baseline` is the CPU oracle on a
 bounded sample of the same steps.
 """
 import argparse
@@ -204,16 +205,22 @@ def main():
     gu_total = sum(step_bytes_gate_up(i) for i in range(args.warmup, args.warmup + K))
     ms_per_step = t_wall * 1e3 / K
     value = total_bytes / t_wall / 1e9
-    n_a, ms_a = prof.get("group_gate_up", (0, 0.0))
+    # the dominant kernel: the one-launch group kernel, or the gate/up launch
+    # when the call took the two-launch form
+    if "group_fused" in prof:
+        dom, dom_total = "group_fused", total_bytes
+    else:
+        dom, dom_total = "group_gate_up", gu_total
+    n_dom, ms_dom = prof.get(dom, (0, 0.0))
+    achieved = dom_total / (ms_dom * 1e-3) / 1e9 if ms_dom > 0 else None
     n_b, ms_b = prof.get("group_down", (0, 0.0))
-    achieved = gu_total / (ms_a * 1e-3) / 1e9 if ms_a > 0 else None
     down_total = sum((union[i % P] + n_sh) * down_bytes + h_bytes + S * H * 4
                      for i in range(args.warmup, args.warmup + K))
     log(f"[bench] {K} steps: {ms_per_step * 1e3:.1f} us/step wall, {value:.0f} GB/s; "
-        f"gate_up kernel {ms_a / max(n_a, 1) * 1e3:.1f} us avg ({achieved or 0:.0f} GB/s), "
-        f"down kernel {ms_b / max(n_b, 1) * 1e3:.1f} us avg "
-        f"({down_total / (ms_b * 1e-3) / 1e9 if ms_b else 0:.0f} GB/s); "
-        f"mean union {union.mean():.2f} experts + {n_sh} shared")
+        f"{dom} kernel {ms_dom / max(n_dom, 1) * 1e3:.1f} us avg ({achieved or 0:.0f} GB/s)"
+        + (f", down kernel {ms_b / max(n_b, 1) * 1e3:.1f} us avg "
+           f"({down_total / (ms_b * 1e-3) / 1e9:.0f} GB/s)" if ms_b else "")
+        + f"; mean union {union.mean():.2f} experts + {n_sh} shared")
 
     # -- CPU oracle on a bounded sample -------------------------------------
     cpu = None
@@ -271,16 +278,16 @@ def main():
         "config": {"workload": args.workload, "tokens": S, "top_k": k, "experts": E,
                    "shared_expert": bool(n_sh), "H": H, "I": I, "format": f"fmt {fmt}, gs {gs}",
                    "routing_pool": P, "shared_copies": n_shared, "device": dev_name},
-        "roofline": {"kernel": "group_gate_up", "bound": "hbm",
+        "roofline": {"kernel": dom, "bound": "hbm",
                      "achieved": round(achieved, 1) if achieved else None, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
-                     "traffic": profiled_traffic("group_gate_up") if (S == 1 and args.workload ==
+                     "traffic": profiled_traffic(dom) if (S == 1 and args.workload ==
                                 "int4g32_expert_group_256top8_shared") else None,
-                     "avg_us": round(ms_a / max(n_a, 1) * 1e3, 2),
-                     "bytes_per_launch": round(gu_total / K)},
-        "roofline_down": {"kernel": "group_down", "avg_us": round(ms_b / max(n_b, 1) * 1e3, 2),
-                          "achieved": round(down_total / (ms_b * 1e-3) / 1e9, 1) if ms_b else None,
-                          "bytes_per_launch": round(down_total / K)},
+                     "avg_us": round(ms_dom / max(n_dom, 1) * 1e3, 2),
+                     "bytes_per_launch": round(dom_total / K)},
+        "roofline_down": ({"kernel": "group_down", "avg_us": round(ms_b / max(n_b, 1) * 1e3, 2),
+                           "achieved": round(down_total / (ms_b * 1e-3) / 1e9, 1),
+                           "bytes_per_launch": round(down_total / K)} if ms_b else None),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

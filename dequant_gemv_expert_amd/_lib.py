@@ -210,6 +210,7 @@ class ExpertTable:
         return load().dqg_expert_group_scratch_bytes(self.handle, S, k)
 
     def scratch(self, S: int, k: int, device="cuda") -> torch.Tensor:
+        """Scratch for calls of up to S tokens (it needs no initialisation)."""
         return torch.empty(self.scratch_bytes(S, k), dtype=torch.uint8, device=device)
 
 

@@ -148,10 +148,15 @@ uint64_t matrix_bytes(const dqg_matrix *W) {
 
 constexpr int32_t MAX_S = 256, MAX_K = 64, MAX_SLOTS = 2048;
 
+// Scratch: a fixed header (the error flag at byte 0; the rest is reserved),
+// then h [S*k + S][I] f32 from byte DQG_SCRATCH_H_OFFSET.  The header sits
+// at the same place for every S, so one scratch serves calls of any size.
+// The gate/up launch clears the flag, so the scratch needs no initialisation.
 size_t group_h_bytes(int32_t S, int32_t k, int32_t I) {
     const size_t slots = (size_t)S * k + S;
     return (slots * I * sizeof(float) + 255) / 256 * 256;
 }
+constexpr size_t FLAG_OFFSET = 0;
 
 int group_common(const dqg_expert_table *t, int32_t S, int32_t k, const int32_t *ids,
                  const float *w, int32_t shared, const float *x, float *y, void *scratch,
@@ -182,12 +187,13 @@ int group_common(const dqg_expert_table *t, int32_t S, int32_t k, const int32_t 
     a.shared = shared;
     a.x = x;
     a.y = y;
-    a.h = static_cast<float *>(scratch);
-    a.flag = reinterpret_cast<int32_t *>(static_cast<char *>(scratch) + group_h_bytes(S, k, t->I));
+    char *base = static_cast<char *>(scratch);
+    a.h = reinterpret_cast<float *>(base + DQG_SCRATCH_H_OFFSET);
+    a.flag = reinterpret_cast<int32_t *>(base + FLAG_OFFSET);
     a.H = t->H;
     a.I = t->I;
     int nl = 0;
-    hipError_t e = launch_group(t->codec_gu, t->codec_down, a, static_cast<hipStream_t>(stream), &nl);
+    const hipError_t e = launch_group(t->codec_gu, t->codec_down, a, static_cast<hipStream_t>(stream), &nl);
     g_launches += nl;
     if ((rc = launched(e, "expert_group"))) return rc;
     if (flag_out) *flag_out = a.flag;
@@ -384,7 +390,7 @@ void dqg_expert_table_destroy(dqg_expert_table *t) {
 
 size_t dqg_expert_group_scratch_bytes(const dqg_expert_table *t, int32_t S, int32_t k) {
     if (!t || S < 1 || k < 1) return 0;
-    return group_h_bytes(S, k, t->I) + 256;
+    return DQG_SCRATCH_H_OFFSET + group_h_bytes(S, k, t->I);
 }
 
 int dqg_expert_group(const dqg_expert_table *t, int32_t S, int32_t k, const int32_t *ids,

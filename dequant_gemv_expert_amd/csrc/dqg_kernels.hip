@@ -29,6 +29,8 @@
 
 #include <hip/hip_ext.h>
 
+#include <mutex>
+
 namespace dqg {
 namespace {
 
@@ -312,9 +314,9 @@ struct Step {
     float xv[SM][Codec<C>::CW];
 };
 
-template <int C, int NR, int SM, typename XP>
-__device__ __forceinline__ void step_load(Step<C, NR, SM> &st, const GRow (&rows)[NR], int shift,
-                                          const XP (&xp)[SM], uint32_t cu) {
+// Codes and scales of chunk cu of every row.
+template <int C, int NR, int SM>
+__device__ __forceinline__ void step_load_w(Step<C, NR, SM> &st, const GRow (&rows)[NR], int shift, uint32_t cu) {
     using Cd = Codec<C>;
     const uint32_t si = cu >> shift;
 #pragma unroll
@@ -322,6 +324,12 @@ __device__ __forceinline__ void step_load(Step<C, NR, SM> &st, const GRow (&rows
         st.ch[r] = Cd::load(rows[r], cu);
         st.sc[r] = ldf(rows[r].s, si);
     }
+}
+
+// The matching slice of x for every token of the batch.
+template <int C, int NR, int SM, typename XP>
+__device__ __forceinline__ void step_load_x(Step<C, NR, SM> &st, const XP (&xp)[SM], uint32_t cu) {
+    using Cd = Codec<C>;
 #pragma unroll
     for (int s = 0; s < SM; ++s)
 #pragma unroll
@@ -329,6 +337,13 @@ __device__ __forceinline__ void step_load(Step<C, NR, SM> &st, const GRow (&rows
             const float4 t = xp[s].load4(cu * Cd::CW + 4 * i);
             st.xv[s][4 * i] = t.x; st.xv[s][4 * i + 1] = t.y; st.xv[s][4 * i + 2] = t.z; st.xv[s][4 * i + 3] = t.w;
         }
+}
+
+template <int C, int NR, int SM, typename XP>
+__device__ __forceinline__ void step_load(Step<C, NR, SM> &st, const GRow (&rows)[NR], int shift,
+                                          const XP (&xp)[SM], uint32_t cu) {
+    step_load_w(st, rows, shift, cu);
+    step_load_x(st, xp, cu);
 }
 
 template <int C, int NR, int SM>

@@ -105,6 +105,9 @@ typedef struct {
     dqg_matrix down;
 } dqg_expert;
 
+/* Byte offset of h inside an expert-group scratch buffer (see below). */
+#define DQG_SCRATCH_H_OFFSET 1024
+
 /* Opaque: a device copy of the experts' descriptors (owned by the library). */
 typedef struct dqg_expert_table dqg_expert_table;
 
@@ -160,23 +163,28 @@ int dqg_dequant(const dqg_matrix *W, float *out, void *stream);
 int dqg_expert_table_create(const dqg_expert *experts, int32_t n_experts, dqg_expert_table **out);
 void dqg_expert_table_destroy(dqg_expert_table *table);
 
-/* Scratch bytes dqg_expert_group needs for S tokens of top-k routing:
- * the hidden state h of every (token, rank) and shared slot, plus a flag. */
+/* Scratch bytes dqg_expert_group needs for S tokens of top-k routing: a
+ * header of DQG_SCRATCH_H_OFFSET bytes (the error flag at byte 0), then the
+ * hidden state h of every (token, rank) and shared slot.  The scratch needs
+ * no initialisation, and one scratch serves calls of any size up to the
+ * one it was sized for (calls that share a scratch must not overlap). */
 size_t dqg_expert_group_scratch_bytes(const dqg_expert_table *table, int32_t S, int32_t k);
 
 /*
  * y[t] = sum_{r<k} w[t][r] * MLP_{ids[t][r]}(x[t]) + MLP_shared(x[t])
  * with MLP_e(x) = down_e . (silu(gate_e . x) * (up_e . x)).
- * The whole batch of routed experts in two launches with h kept in device
- * scratch (the guide's API-contract section, coli_vk_expert_group); the
+ * The whole batch of routed experts in two launches (gate/up, then down)
+ * with h kept in device scratch (the guide's API-contract section,
+ * coli_vk_expert_group); the
  * routed outputs join each token in rank order and the shared expert last
  * ("colibri -- Vulkan backend (docs/vulkan.md)", the tier's properties and
  * the GLM-5.2 paragraph).  An expert used by several tokens is read once.
  *   ids: int32 [S][k] device; w: f32 [S][k] device; shared: an expert index
  *   or -1 for none; x: f32 [S][H]; y: f32 [S][H]; scratch: device buffer of
  *   at least dqg_expert_group_scratch_bytes(table, S, k) bytes.  After the
- *   call its first bytes hold h, f32 [S*k + S][I]: slot t*k + r for
- *   (token t, rank r), slot S*k + t for token t's shared expert.
+ *   call, from byte DQG_SCRATCH_H_OFFSET it
+ *   holds h, f32 [S*k + S][I]: slot t*k + r for (token t, rank r), slot
+ *   S*k + t for token t's shared expert.
  * An id outside [0, n_experts) makes its token's row of y NaN and sets the
  * scratch flag that dqg_expert_group_take reports.  No host sync.
  */

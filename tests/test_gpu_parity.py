@@ -170,12 +170,16 @@ def _small_group(n, fmt=4, gs=32, H=256, I=128, seed=4000, **kw):
 def _check_group(hs, table, ids, w, shared, x, what):
     S, k = ids.shape
     scratch = table.scratch(S, k)
-    y = host(dq.dqg_expert_group(table, dev_i32(ids), dev_f32(w), shared, dev_f32(x), scratch=scratch))
+    ticket, y, _ = dq.dqg_expert_group_issue(table, dev_i32(ids), dev_f32(w), shared, dev_f32(x),
+                                             scratch=scratch)
+    dq.dqg_expert_group_take(ticket)   # raises on an out-of-range id or a wait past its bound
+    y = host(y)
     yr, a = oracle.expert_group(hs, ids, w, shared, x)
     worst = assert_close(y, yr, a, what)
     # stage check: h of every valid slot in scratch
     I = table.I
-    hdev = host(scratch[: (S * k + S) * I * 4].view(torch.float32)).reshape(S * k + S, I)
+    off = 1024   # DQG_SCRATCH_H_OFFSET
+    hdev = host(scratch[off: off + (S * k + S) * I * 4].view(torch.float32)).reshape(S * k + S, I)
     for t in range(S):
         for r in range(k):
             e = int(ids[t, r])
@@ -252,6 +256,20 @@ def test_group_bad_id_is_reported():
     ticket, y, scratch = dq.dqg_expert_group_issue(table, dev_i32(ids), dev_f32(w), 5, dev_f32(x),
                                                    scratch=scratch)
     dq.dqg_expert_group_take(ticket)
+
+
+def test_group_scratch_reused_across_calls():
+    """One scratch, consecutive calls of different sizes: each matches the oracle."""
+    hs, table = _small_group(13)
+    scratch = table.scratch(6, 4)
+    for i, S in enumerate([3, 1, 6, 2, 6, 1]):
+        ids, w = synth.routing(S, 12, 4, 4900 + i)
+        x = synth.activations(S, 256, 4950 + i)
+        sc = scratch[: table.scratch_bytes(S, 4)]
+        y = host(dq.dqg_expert_group(table, dev_i32(ids), dev_f32(w), 12 if i % 2 else None, dev_f32(x),
+                                     scratch=sc))
+        yr, a = oracle.expert_group(hs, ids, w, 12 if i % 2 else None, x)
+        assert_close(y, yr, a, f"reused scratch call {i} S={S}")
 
 
 def test_group_zero_weights_and_no_shared():
