@@ -416,6 +416,26 @@ __device__ __forceinline__ void dot_rows(const GRow (&rows)[NR], int nch, int sh
     }
 }
 
+// As dot_rows (without DQG_PIPE), when the caller has already issued the
+// codes and scales of this lane's first chunk into st (have: this lane has
+// a first chunk), e.g. before staging x, so that both latencies overlap.
+template <int C, int NR, int SM, typename XP>
+__device__ __forceinline__ void dot_rows_from(Step<C, NR, SM> &st, bool have, const GRow (&rows)[NR], int nch,
+                                              int shift, const XP (&xp)[SM], float (&acc)[NR][SM]) {
+    const int lane = threadIdx.x & (WAVE - 1);
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int s = 0; s < SM; ++s) acc[r][s] = 0.f;
+    for (int c = lane; c < nch; c += WAVE) {
+        const uint32_t cu = opaque((uint32_t)c);
+        if (!(have && c == lane)) step_load_w(st, rows, shift, cu);
+        step_load_x(st, xp, cu);
+        __builtin_amdgcn_sched_barrier(0);
+        step_compute(st, acc);
+    }
+}
+
 // Pointers of one row.  Rows are wave-uniform in every kernel but dequant;
 // readfirstlane keeps them in SGPRs even when the matrix came from a table
 // read with vector loads.
@@ -605,18 +625,33 @@ __device__ __forceinline__ void for_slots(const GroupArgs &a, int q, int e, F &&
 }
 
 // Copies the batch's token rows of x into the block's LDS (all threads).
+// Each thread issues up to 8 loads (4 for batches of several tokens, whose
+// kernels hold more registers) before its first LDS write, so the copy
+// costs one round trip per batch of loads, not one per load.
 template <int SM>
 __device__ __forceinline__ void stage_x(const GroupArgs &a, const SlotBatch &b, lfloats_w xs) {
+    constexpr int U = SM == 1 ? 8 : 4;
     __syncthreads();   // the previous batch's readers are done
-    const int n4 = a.H / 4;
-    for (int i = threadIdx.x; i < SM * n4; i += blockDim.x) {
-        const int s = i / n4, k4 = i - s * n4;
-        int t = b.token[0];
+    const int n4 = a.H / 4, total = SM * n4;
+    for (int i0 = threadIdx.x; i0 < total; i0 += U * blockDim.x) {
+        f32x4 v[U];
 #pragma unroll
-        for (int j = 1; j < SM; ++j)
-            if (s == j) t = b.token[j];
-        const f32x4 v = *(const GLOBAL f32x4 *)(gf(a.x) + (size_t)t * a.H + 4 * k4);
-        *(LDS f32x4 *)(xs + (size_t)s * a.H + 4 * k4) = v;
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * (int)blockDim.x;
+            if (i < total) {
+                const int s = i / n4, k4 = i - s * n4;
+                int t = b.token[0];
+#pragma unroll
+                for (int j = 1; j < SM; ++j)
+                    if (s == j) t = b.token[j];
+                v[u] = *(const GLOBAL f32x4 *)(gf(a.x) + (size_t)t * a.H + 4 * k4);
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = i0 + u * (int)blockDim.x;
+            if (i < total) *(LDS f32x4 *)(xs + 4 * (size_t)i) = v[u];
+        }
     }
     __syncthreads();
 }
@@ -626,18 +661,34 @@ template <int C, int R, int SM>
 __device__ __forceinline__ void group_gu_batch(const GroupArgs &a, const ExpertDev &ex, int row0,
                                                const SlotBatch &b, lfloats_w xs) {
     const int lane = threadIdx.x & (WAVE - 1);
-    stage_x<SM>(a, b, xs);
-    GRow rows[2 * R];
+    const int nch = ex.gate.K / Codec<C>::CW;
+    const auto row_set = [&](GRow (&rows)[2 * R]) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        rows[r] = row_ptrs(ex.gate, min(row0 + r, a.I - 1));
-        rows[R + r] = row_ptrs(ex.up, min(row0 + r, a.I - 1));
-    }
+        for (int r = 0; r < R; ++r) {
+            rows[r] = row_ptrs(ex.gate, min(row0 + r, a.I - 1));
+            rows[R + r] = row_ptrs(ex.up, min(row0 + r, a.I - 1));
+        }
+    };
     XLds xp[SM];
 #pragma unroll
     for (int s = 0; s < SM; ++s) xp[s] = {xs + (size_t)s * a.H};
     float acc[2 * R][SM];
-    dot_rows<C, 2 * R, SM, DQG_PIPE, XLds>(rows, ex.gate.K / Codec<C>::CW, ex.gate.shift, xp, acc);
+    GRow rows[2 * R];
+    if constexpr (SM == 1) {
+        // one token: the first chunk's weights are requested before x is
+        // staged (with several tokens the registers this holds cost more
+        // than it saves)
+        row_set(rows);
+        Step<C, 2 * R, SM> st;
+        const bool have = lane < nch;
+        if (have) step_load_w(st, rows, ex.gate.shift, opaque((uint32_t)lane));
+        stage_x<SM>(a, b, xs);
+        dot_rows_from<C, 2 * R, SM, XLds>(st, have, rows, nch, ex.gate.shift, xp, acc);
+    } else {
+        stage_x<SM>(a, b, xs);
+        row_set(rows);
+        dot_rows<C, 2 * R, SM, DQG_PIPE, XLds>(rows, nch, ex.gate.shift, xp, acc);
+    }
     float gv = 0.f, uv = 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -717,10 +768,13 @@ __device__ __forceinline__ void group_down_batch(const GroupArgs &a, const Exper
 // Kernel B: one block per R rows of H.  Waves share the units; each unit's
 // outputs go to LDS d[slot][R]; then y[t][row] = sum_r w[t][r] * d[t*k+r]
 // in rank order, plus the shared slot.  Sets the flag for a bad id.
-// Block size: one wave per unit up to 16 waves when every batch is one slot
-// (small register footprint), up to 8 otherwise.
+// Block size: one wave per unit, at most 8 waves (2 per SIMD, so that two
+// blocks share a CU; blocks of 9 or more waves were measured to hold one).
+#ifndef DQG_BW1
+#define DQG_BW1 8
+#endif
 template <int CAP>
-constexpr int down_max_waves() { return CAP == 1 ? 16 : 8; }
+constexpr int down_max_waves() { return CAP == 1 ? DQG_BW1 : 8; }
 
 template <int C, int R, int CAP>
 __global__ void __launch_bounds__(WAVE * down_max_waves<CAP>()) k_group_down(GroupArgs a) {
