@@ -416,23 +416,58 @@ __device__ __forceinline__ void dot_rows(const GRow (&rows)[NR], int nch, int sh
     }
 }
 
-// As dot_rows (without DQG_PIPE), when the caller has already issued the
-// codes and scales of this lane's first chunk into st (have: this lane has
-// a first chunk), e.g. before staging x, so that both latencies overlap.
-template <int C, int NR, int SM, typename XP>
-__device__ __forceinline__ void dot_rows_from(Step<C, NR, SM> &st, bool have, const GRow (&rows)[NR], int nch,
-                                              int shift, const XP (&xp)[SM], float (&acc)[NR][SM]) {
+// step_compute for one token with x in LDS: x is read per decode unit (UW
+// values) as the unit is used, so only UW values of x are live at a time
+// instead of the chunk's CW; the register budget this frees lets more waves
+// share a SIMD.
+template <int C, int NR>
+__device__ __forceinline__ void step_compute_lds(const Step<C, NR, 1> &st, lfloats x, uint32_t cu,
+                                                 float (&acc)[NR][1]) {
+    using Cd = Codec<C>;
+    float p[NR], xs = 0.f;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) p[r] = 0.f;
+#pragma unroll
+    for (int u = 0; u < Cd::UNITS; ++u) {
+        float xv[Cd::UW];
+#pragma unroll
+        for (int i = 0; i < Cd::UW / 4; ++i) {
+            const f32x4 t = *(const LDS f32x4 *)(x + cu * Cd::CW + u * Cd::UW + 4 * i);
+            xv[4 * i] = t.x; xv[4 * i + 1] = t.y; xv[4 * i + 2] = t.z; xv[4 * i + 3] = t.w;
+        }
+        if (Cd::OFFS != 0.f) {
+#pragma unroll
+            for (int i = 0; i < Cd::UW; ++i) xs += xv[i];
+        }
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+            uint32_t pr[Cd::UW / 2];
+            Cd::decode(st.ch[r], u, pr);
+#pragma unroll
+            for (int q = 0; q < Cd::UW / 2; ++q) {
+                p[r] = fma_lo(pr[q], xv[Cd::IDX[2 * q]], p[r]);
+                p[r] = fma_hi(pr[q], xv[Cd::IDX[2 * q + 1]], p[r]);
+            }
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) acc[r][0] = fmaf(st.sc[r] * Cd::VMUL, fmaf(-Cd::OFFS, xs, p[r]), acc[r][0]);
+}
+
+// dot_rows for one token with x in LDS, when the caller has already issued
+// the codes and scales of this lane's first chunk into st (have: this lane
+// has a first chunk), e.g. before staging x, so that both latencies overlap.
+template <int C, int NR>
+__device__ __forceinline__ void dot_rows_lds1(Step<C, NR, 1> &st, bool have, const GRow (&rows)[NR], int nch,
+                                              int shift, lfloats x, float (&acc)[NR][1]) {
     const int lane = threadIdx.x & (WAVE - 1);
 #pragma unroll
-    for (int r = 0; r < NR; ++r)
-#pragma unroll
-        for (int s = 0; s < SM; ++s) acc[r][s] = 0.f;
+    for (int r = 0; r < NR; ++r) acc[r][0] = 0.f;
     for (int c = lane; c < nch; c += WAVE) {
         const uint32_t cu = opaque((uint32_t)c);
         if (!(have && c == lane)) step_load_w(st, rows, shift, cu);
-        step_load_x(st, xp, cu);
         __builtin_amdgcn_sched_barrier(0);
-        step_compute(st, acc);
+        step_compute_lds(st, x, cu, acc);
     }
 }
 
@@ -683,7 +718,7 @@ __device__ __forceinline__ void group_gu_batch(const GroupArgs &a, const ExpertD
         const bool have = lane < nch;
         if (have) step_load_w(st, rows, ex.gate.shift, opaque((uint32_t)lane));
         stage_x<SM>(a, b, xs);
-        dot_rows_from<C, 2 * R, SM, XLds>(st, have, rows, nch, ex.gate.shift, xp, acc);
+        dot_rows_lds1<C, 2 * R>(st, have, rows, nch, ex.gate.shift, xs, acc);
     } else {
         stage_x<SM>(a, b, xs);
         row_set(rows);
@@ -715,7 +750,7 @@ __device__ __forceinline__ void group_gu_batch(const GroupArgs &a, const ExpertD
 // waves read their slices from there.  Every wave of a block stays to the
 // end (block barriers), with rows past I clamped and their outputs dropped.
 template <int C, int R, int CAP>
-__global__ void __launch_bounds__(WAVE * WPB_A) k_group_gate_up(GroupArgs a) {
+__device__ __forceinline__ void group_gate_up(const GroupArgs &a) {
     extern __shared__ float x_lds_raw[];
     lfloats_w xs = (lfloats_w)x_lds_raw;
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.flag = 0;
@@ -733,6 +768,18 @@ __global__ void __launch_bounds__(WAVE * WPB_A) k_group_gate_up(GroupArgs a) {
         else group_gu_batch<C, R, 4>(a, ex, row0, b, xs);
     });
 }
+
+template <int C, int R, int CAP>
+__global__ void __launch_bounds__(WAVE * WPB_A) k_group_gate_up(GroupArgs a) { group_gate_up<C, R, CAP>(a); }
+
+// The one-token form with a register budget of 5 waves per SIMD, so that a
+// 9-unit group (1152 blocks of 4 waves) is resident in one round on 256 CUs.
+#ifndef DQG_GU1_WAVES
+#define DQG_GU1_WAVES 5
+#endif
+template <int C, int R>
+__global__ void __launch_bounds__(WAVE * WPB_A) __attribute__((amdgpu_waves_per_eu(DQG_GU1_WAVES)))
+k_group_gate_up1(GroupArgs a) { group_gate_up<C, R, 1>(a); }
 
 // down rows row0.. of expert e applied to a batch of slots' h -> d (LDS)
 template <int C, int R, int SM>
@@ -872,7 +919,10 @@ hipError_t group_a_cap(const GroupArgs &a, hipStream_t st) {
     const int rows_per_block = RA * WPB_A;
     dim3 grid((a.I + rows_per_block - 1) / rows_per_block, units);
     const size_t lds = (size_t)CAP * a.H * sizeof(float);
-    launch("group_gate_up", (k_group_gate_up<C, RA, CAP>), grid, dim3(WAVE * WPB_A), lds, st, a);
+    if constexpr (CAP == 1 && C != C_I3)
+        launch("group_gate_up", (k_group_gate_up1<C, RA>), grid, dim3(WAVE * WPB_A), lds, st, a);
+    else
+        launch("group_gate_up", (k_group_gate_up<C, RA, CAP>), grid, dim3(WAVE * WPB_A), lds, st, a);
     return hipGetLastError();
 }
 
