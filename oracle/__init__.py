@@ -5,8 +5,8 @@ Only the tests, ``__graft_entry__.smoke()`` and the benchmark's
 path: it shares no code with it and neither imports the other.  Inputs come
 from the ``synth`` generators; the arithmetic is in ``oracle.c``.
 """
-from .oracle import (OracleLib, load, dequant, code_values, gemv, gate_up, expert_group,
+from .oracle import (OracleLib, load, dequant, code_values, gemv, gate_up, expert_group, route,
                      e2m1, silu, set_threads, get_threads)
 
-__all__ = ["OracleLib", "load", "dequant", "code_values", "gemv", "gate_up", "expert_group",
+__all__ = ["OracleLib", "load", "dequant", "code_values", "gemv", "gate_up", "expert_group", "route",
            "e2m1", "silu", "set_threads", "get_threads"]

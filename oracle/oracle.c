@@ -26,6 +26,8 @@
  *       the tier's list of properties (each expert's output joins its row in
  *       routing order) and the GLM-5.2 paragraph (routed experts in rank
  *       order, then the shared expert).
+ *  [A]  "opus colibri scout": the router row (strata's router does the
+ *       softmax and the top-k in one dispatch).
  *  [OCP] The OCP Microscaling (MX) Formats specification v1.0, FP4 E2M1:
  *       1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit, subnormal
  *       when the exponent field is 0.
@@ -304,6 +306,78 @@ void orc_expert_group(const orc_matrix *gates, const orc_matrix *ups, const orc_
 /* ------------------------------------------------------------------ */
 /* Threads.                                                             */
 /* ------------------------------------------------------------------ */
+
+/* ------------------------------------------------------------------ */
+/* Router: logits -> scores -> top-k -> (ids, weights).                 */
+/* ------------------------------------------------------------------ */
+
+/*
+ * One token's routing, from [V]'s engine tables (the host row of several
+ * engines: the router's softmax, then top-k; MiMo's: sigmoid scores, a
+ * correction bias that only picks, the top-k weights renormalised) and
+ * the router row of [A] (softmax and top-k in one dispatch).
+ *
+ *   mode 0: p[e] = exp(l[e]) / sum_j exp(l[j])   (max subtracted first)
+ *   mode 1: p[e] = 1 / (1 + exp(-l[e]))
+ *   the pick key is l[e] without a bias (both scores keep the logits'
+ *   order), or p[e] + bias[e] with one;
+ *   ids: the k experts of largest key, largest first, equal keys by the
+ *   lower index;
+ *   w[r] = p[ids[r]], divided by their sum when renorm, then times w_scale.
+ *
+ * Readings: selection by the logit order without a bias (the order the
+ * scores have in exact arithmetic); ties go to the lower index; the bias
+ * never enters a weight.  Everything in double precision; the key used
+ * for picking with a bias is the double p + bias.
+ */
+void orc_route(const float *logits, long S, long E, long k, int mode, int renorm,
+               const float *bias, double w_scale, int32_t *ids, double *w, double *key_out)
+{
+    for (long t = 0; t < S; ++t) {
+        const float *l = logits + t * E;
+        double p[E > 0 ? E : 1], key[E > 0 ? E : 1];
+        if (mode == 0) {
+            double mx = l[0];
+            for (long e = 1; e < E; ++e)
+                if (l[e] > mx)
+                    mx = l[e];
+            double z = 0.0;
+            for (long e = 0; e < E; ++e)
+                z += exp((double)l[e] - mx);
+            for (long e = 0; e < E; ++e)
+                p[e] = exp((double)l[e] - mx) / z;
+        } else {
+            for (long e = 0; e < E; ++e)
+                p[e] = 1.0 / (1.0 + exp(-(double)l[e]));
+        }
+        for (long e = 0; e < E; ++e)
+            key[e] = bias ? p[e] + (double)bias[e] : (double)l[e];
+        if (key_out)
+            for (long e = 0; e < E; ++e)
+                key_out[t * E + e] = key[e];
+        /* selection: k passes, each taking the largest key not yet taken */
+        char taken[E > 0 ? E : 1];
+        for (long e = 0; e < E; ++e)
+            taken[e] = 0;
+        double sum = 0.0;
+        for (long r = 0; r < k; ++r) {
+            long best = -1;
+            for (long e = 0; e < E; ++e)
+                if (!taken[e] && (best < 0 || key[e] > key[best]))
+                    best = e;
+            taken[best] = 1;
+            ids[t * k + r] = (int32_t)best;
+            w[t * k + r] = p[best];
+            sum += p[best];
+        }
+        for (long r = 0; r < k; ++r) {
+            double v = w[t * k + r];
+            if (renorm)
+                v = v / sum;
+            w[t * k + r] = v * w_scale;
+        }
+    }
+}
 
 void orc_set_threads(int n)
 {

@@ -74,6 +74,8 @@ class OracleLib:
         lib.orc_gate_up.argtypes = [C.POINTER(_Mat), C.POINTER(_Mat), _P, _L, _P, _P, _P, _P, _P, _P]
         lib.orc_expert_group.restype = None
         lib.orc_expert_group.argtypes = [_P, _P, _P, _L, _L, _L, _P, _P, _L, _P, _P, _P, _P, _P, _P, _P]
+        lib.orc_route.restype = None
+        lib.orc_route.argtypes = [_P, _L, _L, _L, C.c_int, C.c_int, _P, C.c_double, _P, _P, _P]
         lib.orc_set_threads.restype = None
         lib.orc_set_threads.argtypes = [C.c_int]
         lib.orc_get_threads.restype = C.c_int
@@ -133,6 +135,25 @@ class OracleLib:
         self.lib.orc_gate_up(C.byref(_mat(G)), C.byref(_mat(U)), _ptr(x), S,
                              *[_ptr(out[n]) for n in ("h", "nh", "g", "u", "ag", "au")])
         return out
+
+    def route(self, logits, k: int, mode: int = 0, renorm: bool = False, bias=None,
+              w_scale: float = 1.0) -> dict:
+        """Router: ids [S][k] int32, w [S][k] float64 and the pick keys [S][E]
+        (the logits without a bias, p + bias with one).  mode 0 softmax, 1 sigmoid."""
+        lg = np.ascontiguousarray(logits, dtype=np.float32)
+        S, E = lg.shape
+        if not 1 <= k <= E:
+            raise ValueError("k must be in [1, E]")
+        b = None if bias is None else np.ascontiguousarray(bias, dtype=np.float32)
+        if b is not None and b.shape != (E,):
+            raise ValueError("bias must be [E]")
+        ids = np.empty((S, k), np.int32)
+        w = np.empty((S, k), np.float64)
+        key = np.empty((S, E), np.float64)
+        self.lib.orc_route(lg.ctypes.data, S, E, k, int(mode), int(bool(renorm)),
+                           None if b is None else b.ctypes.data, float(w_scale),
+                           ids.ctypes.data, w.ctypes.data, key.ctypes.data)
+        return {"ids": ids, "w": w, "key": key}
 
     def expert_group(self, experts: Sequence, ids, w, shared: Optional[int], x) -> tuple:
         """y[S][H] and its normaliser for a token batch.
@@ -217,3 +238,7 @@ def gate_up(G, U, x):
 
 def expert_group(experts, ids, w, shared, x):
     return load().expert_group(experts, ids, w, shared, x)
+
+
+def route(logits, k, mode=0, renorm=False, bias=None, w_scale=1.0):
+    return load().route(logits, k, mode, renorm, bias, w_scale)

@@ -500,4 +500,112 @@ def pin_group_normaliser(lib):
     assert np.all(a >= np.abs(y)) and np.all(a > 0)
 
 
+# ---------------------------------------------------------------------------
+# router
+# ---------------------------------------------------------------------------
+
+def golden_routes():
+    """The hand-worked router cases of tests/golden/route_examples.txt."""
+    cases, cur = [], None
+    for r in _rows("route_examples.txt"):
+        if r[0] == "case":
+            f = dict(zip(r[2::2], r[3::2]))
+            cur = {"name": r[1], "mode": int(f["mode"]), "k": int(f["k"]), "renorm": bool(int(f["renorm"])),
+                   "scale": float(f["scale"])}
+            cases.append(cur)
+        elif r[0] == "logits":
+            cur["logits"] = np.array([[float(v) for v in r[1:]]], np.float32)
+        elif r[0] == "bias":
+            cur["bias"] = None if r[1] == "none" else np.array([float(v) for v in r[1:]], np.float32)
+        elif r[0] == "ids":
+            cur["ids"] = [int(v) for v in r[1:]]
+        elif r[0] == "w":
+            cur["w"] = [float(v) for v in r[1:]]
+    return cases
+
+
+def pin_route_golden(lib):
+    for c in golden_routes():
+        r = lib.route(c["logits"], c["k"], c["mode"], c["renorm"], c["bias"], c["scale"])
+        assert r["ids"][0].tolist() == c["ids"], (c["name"], r["ids"])
+        assert np.allclose(r["w"][0], c["w"], rtol=1e-6, atol=0), (c["name"], r["w"])
+
+
+def _logits(S, E, seed, spread=2.0):
+    return (synth.rng_for(seed, S, E).standard_normal((S, E)) * spread).astype(np.float32)
+
+
+def pin_route_softmax_is_library_softmax(lib):
+    """k = E without renormalising: the weights, read back by id, are scipy's softmax."""
+    from scipy.special import softmax
+    lg = _logits(5, 37, 7001)
+    r = lib.route(lg, 37, 0)
+    for t in range(5):
+        ref = softmax(lg[t].astype(np.float64))
+        got = np.empty(37)
+        got[r["ids"][t]] = r["w"][t]
+        assert np.allclose(got, ref, rtol=1e-13, atol=0)
+        assert sorted(r["ids"][t].tolist()) == list(range(37))
+
+
+def pin_route_sigmoid_is_library_expit(lib):
+    from scipy.special import expit
+    lg = _logits(4, 19, 7002, spread=6.0)
+    r = lib.route(lg, 19, 1)
+    for t in range(4):
+        got = np.empty(19)
+        got[r["ids"][t]] = r["w"][t]
+        assert np.allclose(got, expit(lg[t].astype(np.float64)), rtol=1e-14, atol=0)
+
+
+def pin_route_topk_brute_force(lib):
+    """Selection against a sort by (-key, index), with many equal logits."""
+    rng = synth.rng_for(7003)
+    for mode in (0, 1):
+        for E, k in ((6, 1), (9, 4), (33, 8), (64, 10), (70, 70)):
+            lg = rng.integers(-3, 4, size=(6, E)).astype(np.float32) * np.float32(0.5)
+            r = lib.route(lg, k, mode)
+            for t in range(6):
+                want = sorted(range(E), key=lambda e: (-float(lg[t, e]), e))[:k]
+                assert r["ids"][t].tolist() == want, (mode, E, k, t)
+
+
+def pin_route_bias_picks_only(lib):
+    """A bias changes which experts are picked, never their weights."""
+    from scipy.special import expit
+    lg = _logits(3, 16, 7004)
+    bias = np.zeros(16, np.float32)
+    bias[5] = 10.0   # expert 5 is always picked first
+    bias[11] = 9.0   # then expert 11
+    for mode in (0, 1):
+        r = lib.route(lg, 4, mode, False, bias)
+        for t in range(3):
+            assert r["ids"][t][:2].tolist() == [5, 11]
+            if mode == 1:
+                assert np.allclose(r["w"][t][:2], expit(lg[t, [5, 11]].astype(np.float64)), rtol=1e-14)
+            key = r["key"][t]
+            picked = set(r["ids"][t].tolist())
+            worst = min(key[e] for e in picked)
+            assert all(key[e] <= worst for e in range(16) if e not in picked)
+
+
+def pin_route_renorm_and_scale(lib):
+    lg = _logits(6, 40, 7005)
+    for mode in (0, 1):
+        r = lib.route(lg, 6, mode, True, None, 2.5)
+        assert np.allclose(r["w"].sum(axis=1), 2.5, rtol=1e-14)
+        plain = lib.route(lg, 6, mode, False, None, 1.0)
+        ratio = r["w"] / plain["w"]
+        assert np.allclose(ratio, ratio[:, :1], rtol=1e-13)   # one factor per token
+
+
+def pin_route_tokens_independent(lib):
+    lg = _logits(7, 24, 7006)
+    r = lib.route(lg, 5, 0, True)
+    for t in range(7):
+        one = lib.route(lg[t:t + 1], 5, 0, True)
+        assert one["ids"][0].tolist() == r["ids"][t].tolist()
+        assert np.array_equal(one["w"][0], r["w"][t])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

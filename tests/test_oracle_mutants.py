@@ -52,6 +52,14 @@ MUTANTS = {
     "router_weight_dropped": ("yt[o] += wr * dy_work[o];", "yt[o] += dy_work[o];"),
     "shared_expert_dropped": ("                yt[o] += dy_work[o];", "                yt[o] += 0.0 * dy_work[o];"),
     "down_uses_gate_rows": ("mlp_one(&gates[e], &ups[e], &downs[e],", "mlp_one(&gates[e], &ups[e], &downs[(e + 1) % n_experts],"),
+    "route_ties_to_higher_index": ("(best < 0 || key[e] > key[best])", "(best < 0 || key[e] >= key[best])"),
+    "route_max_not_subtracted": ("z += exp((double)l[e] - mx);", "z += exp((double)l[e]);"),
+    "route_sigmoid_sign": ("p[e] = 1.0 / (1.0 + exp(-(double)l[e]));", "p[e] = 1.0 / (1.0 + exp((double)l[e]));"),
+    "route_bias_in_weight": ("w[t * k + r] = p[best];", "w[t * k + r] = bias ? key[best] : p[best];"),
+    "route_bias_ignored": ("key[e] = bias ? p[e] + (double)bias[e] : (double)l[e];", "key[e] = (double)l[e];"),
+    "route_renorm_ignored": ("            if (renorm)\n                v = v / sum;", "            (void)renorm;"),
+    "route_scale_dropped": ("w[t * k + r] = v * w_scale;", "w[t * k + r] = v;"),
+    "route_weight_of_wrong_expert": ("w[t * k + r] = p[best];", "w[t * k + r] = p[(best + 1) % E];"),
     "token_x_not_advanced": ("mlp_one(&gates[e], &ups[e], &downs[e], x + t * gates[e].K,",
                              "mlp_one(&gates[e], &ups[e], &downs[e], x,"),
 }
