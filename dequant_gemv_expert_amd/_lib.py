@@ -20,6 +20,7 @@ STATUS = {0: "DQG_OK", -1: "DQG_EINVAL", -2: "DQG_EFORMAT", -3: "DQG_ESHAPE", -4
           -5: "DQG_ELAUNCH", -6: "DQG_ENOMEM", -7: "DQG_EROUTE"}
 
 DQG_I8_ROW, DQG_I4_ROW, DQG_I4_GS, DQG_I3_G64, DQG_MXFP4 = 1, 2, 4, 5, 7
+DQG_ROUTE_SOFTMAX, DQG_ROUTE_SIGMOID = 0, 1
 
 
 class DqgError(RuntimeError):
@@ -44,7 +45,7 @@ class dqg_ticket(C.Structure):
 class dqg_counters(C.Structure):
     _fields_ = [("calls_matmul", C.c_uint64), ("calls_gate_up", C.c_uint64),
                 ("calls_dequant", C.c_uint64), ("calls_expert_group", C.c_uint64),
-                ("launches", C.c_uint64), ("bytes", C.c_uint64)]
+                ("launches", C.c_uint64), ("bytes", C.c_uint64), ("calls_route", C.c_uint64)]
 
 
 class dqg_prof_record(C.Structure):
@@ -64,6 +65,7 @@ SIGNATURES = {
     "dqg_expert_group_issue": (C.c_int, [_P, _I32, _I32, _P, _P, _I32, _P, _P, _P, _SZ, _P,
                                          C.POINTER(dqg_ticket)]),
     "dqg_expert_group_take": (C.c_int, [C.POINTER(dqg_ticket)]),
+    "dqg_route": (C.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _P, C.c_float, _P, _P, _P]),
     "dqg_prof_begin": (C.c_int, [_I32]),
     "dqg_prof_end": (C.c_int, [C.POINTER(dqg_prof_record), _I32, C.POINTER(_I32)]),
     "dqg_last_error": (C.c_char_p, []),
@@ -247,6 +249,21 @@ def dqg_expert_group_issue(table: ExpertTable, ids: torch.Tensor, w: torch.Tenso
 
 def dqg_expert_group_take(ticket: dqg_ticket) -> None:
     _check(load().dqg_expert_group_take(C.byref(ticket)))
+
+
+def dqg_route(logits: torch.Tensor, k: int, mode: int = DQG_ROUTE_SOFTMAX, renorm: bool = False,
+              bias: Optional[torch.Tensor] = None, w_scale: float = 1.0,
+              ids: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None, stream=None):
+    """Router on the device: returns (ids int32 [S][k], w f32 [S][k])."""
+    S, E = logits.shape
+    if ids is None:
+        ids = torch.empty((S, k), dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty((S, k), dtype=torch.float32, device=logits.device)
+    _check(load().dqg_route(_dev(logits, "logits", torch.float32), S, E, int(k), int(mode), int(bool(renorm)),
+                            _dev(bias, "bias", torch.float32), float(w_scale),
+                            _dev(ids, "ids", torch.int32), _dev(w, "w", torch.float32), _stream(stream)))
+    return ids, w
 
 
 def dqg_last_error() -> str:

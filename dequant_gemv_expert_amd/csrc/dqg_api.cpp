@@ -8,6 +8,7 @@
 #include <atomic>
 #include <mutex>
 #include <vector>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -28,7 +29,7 @@ namespace {
 thread_local char g_err[512] = "";
 
 std::atomic<uint64_t> g_calls_matmul{0}, g_calls_gate_up{0}, g_calls_dequant{0},
-    g_calls_group{0}, g_launches{0}, g_bytes{0};
+    g_calls_group{0}, g_calls_route{0}, g_launches{0}, g_bytes{0};
 std::atomic<long> g_launch_attempts{0};
 
 int fail(int code, const char *fmt, ...) {
@@ -324,6 +325,28 @@ int dqg_dequant(const dqg_matrix *W, float *out, void *stream) {
     return DQG_OK;
 }
 
+int dqg_route(const float *logits, int32_t S, int32_t E, int32_t k, int32_t mode, int32_t renorm,
+              const float *bias, float w_scale, int32_t *ids, float *w, void *stream) {
+    ++g_calls_route;
+    if (S < 1) return fail(DQG_EINVAL, "route: S=%d, need S >= 1", S);
+    if (E < 1 || E > ROUTE_MAX_E) return fail(DQG_EINVAL, "route: E=%d outside [1, %d]", E, ROUTE_MAX_E);
+    if (k < 1 || k > E || k > 64) return fail(DQG_EINVAL, "route: k=%d outside [1, min(E, 64)]", k);
+    if (mode != DQG_ROUTE_SOFTMAX && mode != DQG_ROUTE_SIGMOID)
+        return fail(DQG_EINVAL, "route: mode=%d is neither DQG_ROUTE_SOFTMAX nor DQG_ROUTE_SIGMOID", mode);
+    if (renorm != 0 && renorm != 1) return fail(DQG_EINVAL, "route: renorm=%d, need 0 or 1", renorm);
+    if (!std::isfinite(w_scale)) return fail(DQG_EINVAL, "route: w_scale is not finite");
+    if (!logits || !aligned(logits, 4)) return fail(DQG_EINVAL, "route: logits must be a 4-byte aligned device pointer");
+    if (bias && !aligned(bias, 4)) return fail(DQG_EINVAL, "route: bias must be NULL or a 4-byte aligned device pointer");
+    if (!ids || !aligned(ids, 4)) return fail(DQG_EINVAL, "route: ids must be a 4-byte aligned device pointer");
+    if (!w || !aligned(w, 4)) return fail(DQG_EINVAL, "route: w must be a 4-byte aligned device pointer");
+    if (inject_fault()) return fail(DQG_ELAUNCH, "route: injected launch failure (DQG_FAULT)");
+    RouteArgs a{logits, S, E, k, mode, renorm, bias, w_scale, ids, w};
+    int rc;
+    if ((rc = launched(launch_route(a, static_cast<hipStream_t>(stream)), "route"))) return rc;
+    ++g_launches;
+    return DQG_OK;
+}
+
 int dqg_expert_table_create(const dqg_expert *experts, int32_t n, dqg_expert_table **out) {
     if (!out) return fail(DQG_EINVAL, "expert_table_create: out is NULL");
     *out = nullptr;
@@ -449,12 +472,13 @@ void dqg_stats(dqg_counters *out) {
     out->calls_gate_up = g_calls_gate_up;
     out->calls_dequant = g_calls_dequant;
     out->calls_expert_group = g_calls_group;
+    out->calls_route = g_calls_route;
     out->launches = g_launches;
     out->bytes = g_bytes;
 }
 
 void dqg_stats_reset(void) {
-    g_calls_matmul = g_calls_gate_up = g_calls_dequant = g_calls_group = 0;
+    g_calls_matmul = g_calls_gate_up = g_calls_dequant = g_calls_group = g_calls_route = 0;
     g_launches = g_bytes = 0;
 }
 

@@ -50,6 +50,19 @@ struct GroupArgs {
     int32_t H, I;
 };
 
+// Launch parameters of the router.
+constexpr int ROUTE_MAX_E = 1024;   // experts per token the router kernel holds
+struct RouteArgs {
+    const float *logits;   // [S][E]
+    int32_t S, E, k;
+    int32_t mode;          // 0 softmax, 1 sigmoid
+    int32_t renorm;        // 1: picked weights divided by their sum
+    const float *bias;     // [E] pick bias or null
+    float w_scale;
+    int32_t *ids;          // [S][k]
+    float *w;              // [S][k]
+};
+
 // Optional event timing of launches (dqg_api.cpp): when timing is on,
 // prof_slot hands out the start/stop events the next launch of `kernel`
 // records (hipExtLaunchKernelGGL attaches them to the dispatch itself);
@@ -62,6 +75,7 @@ hipError_t launch_matmul(int codec, const MatDev &m, const float *x, int S, floa
 hipError_t launch_gate_up(int codec, const MatDev &g, const MatDev &u, const float *x, int S,
                           float *h, hipStream_t st);
 hipError_t launch_dequant(int codec, const MatDev &m, float *out, hipStream_t st);
+hipError_t launch_route(const RouteArgs &a, hipStream_t st);
 hipError_t launch_group(int codec_gu, int codec_down, const GroupArgs &a, hipStream_t st,
                         int *launches);
 

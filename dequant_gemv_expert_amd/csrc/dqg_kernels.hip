@@ -858,6 +858,105 @@ __global__ void __launch_bounds__(WAVE * down_max_waves<CAP>()) k_group_down(Gro
 }
 
 // ---------------------------------------------------------------------------
+// Router: logits -> scores -> top-k -> (ids, w), one wave per token.  The
+// scores are softmax (max subtracted) or sigmoid; the pick key is the logit
+// itself (both scores keep the logits' order) or, with a bias, score +
+// bias.  A pick is a wave-wide maximum of (ordered key, inverted index), so
+// equal keys go to the lower index; the picked expert's score is its
+// weight, renormalised over the k picks on request and scaled.
+// ---------------------------------------------------------------------------
+// Order-preserving map of a float's bits to an unsigned integer.
+__device__ __forceinline__ uint32_t float_order(float f) {
+    const uint32_t b = __float_as_uint(f);
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 1; m < WAVE; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
+    return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+    for (int m = 1; m < WAVE; m <<= 1) {
+        const uint64_t o = __shfl_xor(v, m);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+constexpr int ROUTE_WAVES = 4;   // tokens per block
+
+template <int NJ>   // experts per lane: E <= 64 * NJ
+__global__ void __launch_bounds__(WAVE * ROUTE_WAVES) k_route(RouteArgs a) {
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int t = blockIdx.x * ROUTE_WAVES + wave_id();
+    if (t >= a.S) return;   // the whole wave: t is uniform
+    const float *l = a.logits + (size_t)t * a.E;
+    float lv[NJ], p[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int e = lane + WAVE * j;
+        lv[j] = e < a.E ? l[e] : -INFINITY;
+    }
+    if (a.mode == 0) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) mx = fmaxf(mx, lv[j]);
+        mx = wave_max(mx);
+        float z = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            p[j] = lane + WAVE * j < a.E ? expf(lv[j] - mx) : 0.f;
+            z += p[j];
+        }
+        z = wave_sum(z);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) p[j] = p[j] / z;
+    } else {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) p[j] = lane + WAVE * j < a.E ? 1.f / (1.f + expf(-lv[j])) : 0.f;
+    }
+    // key: ordered pick value above, 0xFFFFFFFF - e below; 0 = not pickable
+    uint64_t key[NJ];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+        const int e = lane + WAVE * j;
+        if (e < a.E) {
+            const float kf = a.bias ? p[j] + a.bias[e] : lv[j];
+            key[j] = ((uint64_t)float_order(kf) << 32) | (0xFFFFFFFFu - (uint32_t)e);
+        } else {
+            key[j] = 0;
+        }
+    }
+    float mine = 0.f, sum = 0.f;
+    int my_id = 0;
+    for (int r = 0; r < a.k; ++r) {
+        uint64_t best = 0;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) best = key[j] > best ? key[j] : best;
+        best = wave_max_u64(best);
+        const int e = (int)(0xFFFFFFFFu - (uint32_t)best);   // uniform
+        const int owner = e & (WAVE - 1), jj = e / WAVE;
+        float pv = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            if (j == jj) pv = p[j];
+            if (j == jj && lane == owner) key[j] = 0;   // taken
+        }
+        pv = __shfl(pv, owner);
+        sum += pv;
+        if (lane == r) { mine = pv; my_id = e; }
+    }
+    if (lane < a.k) {
+        const float v = a.renorm ? mine / sum : mine;
+        a.ids[(size_t)t * a.k + lane] = my_id;
+        a.w[(size_t)t * a.k + lane] = v * a.w_scale;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
 constexpr int WPB = 4;   // waves per block for the row kernels
@@ -975,6 +1074,17 @@ hipError_t launch_gate_up(int codec, const MatDev &g, const MatDev &u, const flo
     case C_FP4: return gate_up_c<C_FP4>(g, u, x, S, h, st);
     }
     return hipErrorInvalidValue;
+}
+
+hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
+    const dim3 grid((a.S + ROUTE_WAVES - 1) / ROUTE_WAVES), block(WAVE * ROUTE_WAVES);
+    if (a.E <= 64) launch("route", k_route<1>, grid, block, 0, st, a);
+    else if (a.E <= 128) launch("route", k_route<2>, grid, block, 0, st, a);
+    else if (a.E <= 256) launch("route", k_route<4>, grid, block, 0, st, a);
+    else if (a.E <= 512) launch("route", k_route<8>, grid, block, 0, st, a);
+    else if (a.E <= ROUTE_MAX_E) launch("route", k_route<16>, grid, block, 0, st, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
 }
 
 hipError_t launch_dequant(int codec, const MatDev &m, float *out, hipStream_t st) {

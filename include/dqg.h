@@ -126,6 +126,7 @@ typedef struct {
     uint64_t calls_expert_group;
     uint64_t launches;
     uint64_t bytes;   /* weight codes + scales + x + y of matmul, gate_up, dequant */
+    uint64_t calls_route;
 } dqg_counters;
 
 /*
@@ -205,13 +206,42 @@ int dqg_expert_group_issue(const dqg_expert_table *table, int32_t S, int32_t k,
  * the event; a ticket is taken once. */
 int dqg_expert_group_take(dqg_ticket *ticket);
 
+/* Router scores (dqg_route's mode). */
+typedef enum { DQG_ROUTE_SOFTMAX = 0, DQG_ROUTE_SIGMOID = 1 } dqg_route_mode;
+
+/*
+ * The router that feeds dqg_expert_group, on the device: for each token t,
+ * scores p from its logits, the k experts of largest pick key, and their
+ * weights.  ("colibri -- Vulkan backend (docs/vulkan.md)": the engine
+ * tables, whose host rows run the router's softmax and top-k, and MiMo's
+ * row: sigmoid scores, a correction bias that picks, the picked weights
+ * renormalised; "opus colibri scout": the router row, softmax and top-k in
+ * one dispatch.)
+ *   mode DQG_ROUTE_SOFTMAX: p[e] = exp(l[e] - max) / sum_j exp(l[j] - max);
+ *   mode DQG_ROUTE_SIGMOID: p[e] = 1 / (1 + exp(-l[e]));
+ *   pick key: l[e] when bias is NULL (both scores keep the logits' order),
+ *   else p[e] + bias[e]; the bias never enters a weight;
+ *   ids[t][r], r < k: the picked experts, largest key first, equal keys by
+ *   the lower index;
+ *   w[t][r] = p[ids[t][r]], divided by the sum of the k picks when renorm,
+ *   then times w_scale.
+ *   logits: f32 [S][E] device; bias: f32 [E] device or NULL; ids: int32
+ *   [S][k] device; w: f32 [S][k] device, the layout dqg_expert_group reads.
+ *   1 <= E <= 1024, 1 <= k <= min(E, 64), renorm 0 or 1, w_scale finite.
+ *   Logits are expected finite; a NaN logit gives unspecified picks.
+ * Checks its arguments before any launch (DQG_EINVAL).  One launch, no
+ * host sync; ids and w are ordered with later work on the stream.
+ */
+int dqg_route(const float *logits, int32_t S, int32_t E, int32_t k, int32_t mode, int32_t renorm,
+              const float *bias, float w_scale, int32_t *ids, float *w, void *stream);
+
 /* Per-kernel device time, measured with HIP events that the library
  * records on the launch stream around each kernel it enqueues.
  * dqg_prof_begin(capacity) creates `capacity` event pairs (host-blocking,
  * call it outside timed regions); the next `capacity` launches are timed.
  * dqg_prof_end waits for the recorded events, fills up to `max` records
  * (one per kernel name, in first-launch order), stores their count in *n
- * and releases the events.  Kernel names: "matmul", "gate_up", "dequant",
+ * and releases the events.  Kernel names: "matmul", "gate_up", "dequant", "route",
  * "group_gate_up", "group_down". */
 typedef struct {
     char kernel[32];

@@ -162,6 +162,19 @@ def routing(S: int, n_experts: int, k: int, *key: int):
     return ids, w
 
 
+def router_logits(S: int, n_experts: int, *key: int, spread: float = 2.0) -> np.ndarray:
+    """Router logits [S][E] f32: spread * N(0, 1), a stand-in for a router
+    projection's output (the workloads' real routers are not available)."""
+    rng = rng_for(*key)
+    return (rng.standard_normal((S, n_experts)) * spread).astype(np.float32)
+
+
+def router_bias(n_experts: int, *key: int, spread: float = 0.05) -> np.ndarray:
+    """A picking bias [E] f32, uniform in [-spread, spread]."""
+    rng = rng_for(*key)
+    return rng.uniform(-spread, spread, n_experts).astype(np.float32)
+
+
 @dataclasses.dataclass
 class Expert:
     gate: QMatrix   # [I x H]

@@ -84,6 +84,36 @@ def test_expert_group_validation(lib):
     assert lib.dqg_expert_group_take(C.byref(t)) == -1
 
 
+FAKE_L, FAKE_IDS, FAKE_W = 0x60000, 0x70000, 0x80000
+
+
+@pytest.mark.parametrize("S,E,k,mode,renorm,bias,scale,logits,ids,w", [
+    (0, 64, 8, 0, 0, None, 1.0, FAKE_L, FAKE_IDS, FAKE_W),          # no tokens
+    (1, 0, 1, 0, 0, None, 1.0, FAKE_L, FAKE_IDS, FAKE_W),           # no experts
+    (1, 1025, 8, 0, 0, None, 1.0, FAKE_L, FAKE_IDS, FAKE_W),        # more experts than one wave holds
+    (1, 64, 0, 0, 0, None, 1.0, FAKE_L, FAKE_IDS, FAKE_W),          # k = 0
+    (1, 6, 7, 0, 0, None, 1.0, FAKE_L, FAKE_IDS, FAKE_W),           # k > E
+    (1, 256, 65, 0, 0, None, 1.0, FAKE_L, FAKE_IDS, FAKE_W),        # k > 64
+    (1, 64, 8, 2, 0, None, 1.0, FAKE_L, FAKE_IDS, FAKE_W),          # unknown mode
+    (1, 64, 8, 0, 2, None, 1.0, FAKE_L, FAKE_IDS, FAKE_W),          # renorm not 0/1
+    (1, 64, 8, 0, 0, None, float("inf"), FAKE_L, FAKE_IDS, FAKE_W), # scale not finite
+    (1, 64, 8, 0, 0, None, float("nan"), FAKE_L, FAKE_IDS, FAKE_W),
+    (1, 64, 8, 0, 0, None, 1.0, 0, FAKE_IDS, FAKE_W),               # null logits
+    (1, 64, 8, 0, 0, None, 1.0, FAKE_L + 2, FAKE_IDS, FAKE_W),      # misaligned
+    (1, 64, 8, 0, 0, 0x90002, 1.0, FAKE_L, FAKE_IDS, FAKE_W),
+    (1, 64, 8, 0, 0, None, 1.0, FAKE_L, 0, FAKE_W),
+    (1, 64, 8, 0, 0, None, 1.0, FAKE_L, FAKE_IDS, FAKE_W + 1),
+])
+def test_route_validation(lib, S, E, k, mode, renorm, bias, scale, logits, ids, w):
+    lib.dqg_stats_reset()
+    rc = lib.dqg_route(logits, S, E, k, mode, renorm, bias, scale, ids, w, None)
+    assert rc == -1, (rc, lib.dqg_last_error())
+    assert lib.dqg_last_error()
+    c = L.dqg_counters()
+    lib.dqg_stats(C.byref(c))
+    assert c.calls_route == 1 and c.launches == 0
+
+
 def test_table_validation(lib):
     e = L.dqg_expert(_mat(O=32, K=64), _mat(O=32, K=64), _mat(O=64, K=64))   # down must be [64 x 32]
     out = C.c_void_p()
