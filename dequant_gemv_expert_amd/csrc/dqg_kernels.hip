@@ -858,6 +858,224 @@ __global__ void __launch_bounds__(WAVE * down_max_waves<CAP>()) k_group_down(Gro
 }
 
 // ---------------------------------------------------------------------------
+// Prefill GEMM on the matrix cores, for 16 or more tokens (the pages move a
+// batch of 16 or more rows to a tiled GEMM): Y[s][o] = W[o] . x[s], and
+// gate_up's h = silu(G x) * (U x).
+//
+// v_mfma_f32_16x16x32_f16 computes D (16 rows x 16 tokens, f32) from
+// A (16 rows x 32 inputs, f16) and B (32 inputs x 16 tokens, f16).  Lane
+// layout: A lane l holds row l%16, inputs 8(l/16)..+8 of the window; B lane
+// l holds token l%16, the same inputs; D lane l holds rows 4(l/16)..+4 of
+// token l%16.  A is the decoded f16 pattern of the codes (exact: the matrix
+// cores keep f16 subnormals); B is x' = x * 2^-e split as f16 hi + lo, with
+// e per token and k-step so that x' fits f16, which leaves x' - hi - lo
+// below 2^-22 |x'|.  A 32-input window never crosses a scale group, so each
+// window's D is offset-corrected and scaled on the vector unit:
+//   acc += scale * VMUL * 2^e * (D - OFFS * sum(x' over the window)).
+// A block is 4 waves; a wave holds 2 row tiles (32 rows of W, or 16 rows of
+// G and the same 16 of U) for NC token tiles of 16.  x' for 64 tokens x 128
+// inputs is staged in LDS per k-step, in the order the decode emits.
+// ---------------------------------------------------------------------------
+typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
+
+// Codes of 8 consecutive inputs of one row (a quarter window) and their
+// decode into the 4 f16 pairs of an MFMA A operand; PERM[p] is the input
+// (0..7) that half p of the operand multiplies.
+template <int C>
+struct GemmCodec;
+
+template <>
+struct GemmCodec<C_I4> {
+    static constexpr int PERM[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+    using Raw = uint32_t;
+    __device__ static Raw load(gbytes row, uint32_t k) { return *(const GLOBAL uint32_t *)(row + k / 2); }
+    __device__ static void decode(Raw w, uint32_t (&pr)[4]) {
+        Codec<C_I4>::decode({{w, 0u, 0u, 0u}}, 0, pr);
+    }
+};
+
+template <>
+struct GemmCodec<C_FP4> {
+    static constexpr int PERM[8] = {0, 1, 2, 3, 4, 5, 6, 7};
+    using Raw = uint32_t;
+    __device__ static Raw load(gbytes row, uint32_t k) { return *(const GLOBAL uint32_t *)(row + k / 2); }
+    __device__ static void decode(Raw w, uint32_t (&pr)[4]) {
+        Codec<C_FP4>::decode({{w, 0u, 0u, 0u}}, 0, pr);
+    }
+};
+
+template <>
+struct GemmCodec<C_I8> {
+    static constexpr int PERM[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+    using Raw = u32x2;
+    __device__ static Raw load(gbytes row, uint32_t k) { return *(const GLOBAL u32x2 *)(row + k); }
+    __device__ static void decode(Raw w, uint32_t (&pr)[4]) {
+        const typename Codec<C_I8>::Chunk ch{{w.x, w.y, 0u, 0u}};
+        uint32_t a[2], b[2];
+        Codec<C_I8>::decode(ch, 0, a);
+        Codec<C_I8>::decode(ch, 1, b);
+        pr[0] = a[0]; pr[1] = a[1]; pr[2] = b[0]; pr[3] = b[1];
+    }
+};
+
+constexpr int GK = 128;            // inputs per k-step: 4 windows of 32
+constexpr int GWIN = GK / 32;
+constexpr int GTOK = 64;           // tokens staged per block (4 tiles of 16)
+constexpr int GXS = GK + 8;        // f16 per token row in LDS (padded against bank conflicts)
+constexpr int GROWS = 128;         // row slots per block: 4 waves x 2 tiles x 16
+
+struct GemmLds {
+    _Float16 xh[GTOK][GXS];
+    _Float16 xl[GTOK][GXS];
+    float xo[GTOK][GWIN];    // OFFS * sum of x' over each window
+    float xe[GTOK];          // 2^e of the token for this k-step
+    float sc[GWIN][GROWS];   // scale * VMUL per window and row slot
+};
+
+// Row of slot (wave w, tile t, lane row r) and the matrix it comes from.
+template <bool GU>
+__device__ __forceinline__ int gemm_row(int block_row, int w, int t, int r) {
+    return GU ? block_row + 16 * w + r : block_row + 32 * w + 16 * t + r;
+}
+
+template <int C, bool GU, int NC>
+__global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float *__restrict__ x, int S,
+                                              float *__restrict__ y) {
+    using Gc = GemmCodec<C>;
+    using Cd = Codec<C>;
+    __shared__ GemmLds L;
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = wave_id();
+    const int O = m0.O, K = m0.K;
+    const int block_row = blockIdx.x * (GU ? GROWS / 2 : GROWS);
+    const int s0 = blockIdx.y * (16 * NC);
+    const int lr = lane & 15, lq = lane >> 4;   // A/B: row or token within a tile; quarter of the window
+    // this lane's A rows (clamped; rows past O are computed and dropped)
+    gbytes arow[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const MatDev &m = (GU && t == 1) ? m1 : m0;
+        const int row = min(gemm_row<GU>(block_row, w, t, lr), O - 1);
+        arow[t] = (gbytes)(m.q + (size_t)row * m.qstride);
+    }
+    float acc[2][NC][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[t][c][i] = 0.f;
+
+    for (int k0 = 0; k0 < K; k0 += GK) {
+        const int nwin = min(GWIN, (K - k0) / 32);   // K is a multiple of 32
+        // codes of this step's windows (issued before the staging below)
+        typename Gc::Raw raw[2][GWIN];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < GWIN; ++j)
+                if (j < nwin) raw[t][j] = Gc::load(arow[t], (uint32_t)(k0 + 32 * j + 8 * lq));
+        __syncthreads();   // the previous step's readers of L are done
+        // stage x': thread = (token tt, window qq), 32 inputs each
+        {
+            const int tt = tid >> 2, qq = tid & 3, s = s0 + tt, kb = k0 + 32 * qq;
+            f32x4 v[8];
+            const bool live = tt < 16 * NC && s < S && qq < nwin;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                v[i] = live ? *(const GLOBAL f32x4 *)(gf(x) + (size_t)s * K + kb + 4 * i) : f32x4{0.f, 0.f, 0.f, 0.f};
+            float mx = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+            mx = fmaxf(mx, __shfl_xor(mx, 1));
+            mx = fmaxf(mx, __shfl_xor(mx, 2));
+            int ex = 0;
+            if (mx > 0.f) { frexpf(mx, &ex); ex -= 15; }   // mx * 2^-ex < 2^15
+            float xs = 0.f;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                h16x8 hi, lo;
+#pragma unroll
+                for (int p = 0; p < 8; ++p) {
+                    const int i = 8 * g + Gc::PERM[p];
+                    const float xv = ldexpf(v[i >> 2][i & 3], -ex);
+                    const _Float16 h = (_Float16)xv;
+                    hi[p] = h;
+                    lo[p] = (_Float16)(xv - (float)h);
+                    xs += xv;
+                }
+                if (tt < GTOK) {
+                    *(LDS h16x8 *)&L.xh[tt][32 * qq + 8 * g] = hi;
+                    *(LDS h16x8 *)&L.xl[tt][32 * qq + 8 * g] = lo;
+                }
+            }
+            if (tt < GTOK) {
+                L.xo[tt][qq] = Cd::OFFS * xs;
+                if (qq == 0) L.xe[tt] = ldexpf(1.f, ex);
+            }
+        }
+        // scales * VMUL per (window, row slot)
+        for (int i = tid; i < GWIN * GROWS; i += 256) {
+            const int j = i / GROWS, slot = i - j * GROWS;
+            const int sw = slot >> 5, st = (slot >> 4) & 1, sr = slot & 15;
+            const MatDev &m = (GU && st == 1) ? m1 : m0;
+            const int row = min(gemm_row<GU>(block_row, sw, st, sr), O - 1);
+            const int k = k0 + 32 * j;
+            float sv = 0.f;
+            if (j < nwin) sv = m.s[(size_t)row * m.sstride + ((uint32_t)(k / Cd::CW) >> m.shift)] * Cd::VMUL;
+            L.sc[j][slot] = sv;
+        }
+        __syncthreads();
+        for (int j = 0; j < nwin; ++j) {
+            h16x8 a[2];
+            f32x4 sc4[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                uint32_t pr[4];
+                Gc::decode(raw[t][j], pr);
+                a[t] = __builtin_bit_cast(h16x8, u32x4{pr[0], pr[1], pr[2], pr[3]});
+                sc4[t] = *(LDS f32x4 *)&L.sc[j][32 * w + 16 * t + 4 * lq];
+            }
+#pragma unroll
+            for (int c = 0; c < NC; ++c) {
+                const int tok = 16 * c + lr;
+                const h16x8 bh = *(LDS h16x8 *)&L.xh[tok][32 * j + 8 * lq];
+                const h16x8 bl = *(LDS h16x8 *)&L.xl[tok][32 * j + 8 * lq];
+                // D rows belong to token (16c + lane%16) as well: same tok for the offset and 2^e
+                const float xo = L.xo[tok][j], xe = L.xe[tok];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    f32x4 d = {0.f, 0.f, 0.f, 0.f};
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bh, d, 0, 0, 0);
+                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bl, d, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[t][c][i] = fmaf(sc4[t][i] * xe, d[i] - xo, acc[t][c][i]);
+                }
+            }
+        }
+    }
+    // D lane layout: rows 4*lq + i of each tile, token 16c + lr
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int s = s0 + 16 * c + lr;
+        if (s >= S) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (GU) {
+                const int row = gemm_row<GU>(block_row, w, 0, 4 * lq + i);
+                if (row < O) y[(size_t)s * O + row] = silu(acc[0][c][i]) * acc[1][c][i];
+            } else {
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int row = gemm_row<GU>(block_row, w, t, 4 * lq + i);
+                    if (row < O) y[(size_t)s * O + row] = acc[t][c][i];
+                }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Router: logits -> scores -> top-k -> (ids, w), one wave per token.  The
 // scores are softmax (max subtracted) or sigmoid; the pick key is the logit
 // itself (both scores keep the logits' order) or, with a bias, score +
@@ -979,8 +1197,37 @@ hipError_t go_matmul(const MatDev &m, const float *x, int S, float *y, hipStream
     return hipGetLastError();
 }
 
+// The matrix-core GEMM from this many tokens on, for the formats whose
+// 8-input quarter windows are whole bytes.  The pages switch at 16 rows; on
+// MI355X the per-row route stays faster below 32 tokens for matmul and 64
+// for gate_up (6144 x 6144 and 2 x 2048 x 6144 int4-g32, measured), where
+// the GEMM's grid has too few blocks.
+constexpr int GEMM_MIN_S = 32, GEMM_MIN_S_GU = 64;
+
+template <int C>
+constexpr bool gemm_codec() { return C == C_I8 || C == C_I4 || C == C_FP4; }
+
+template <int C, bool GU, int NC>
+hipError_t go_gemm_nc(const MatDev &m0, const MatDev &m1, const float *x, int S, float *y, hipStream_t st,
+                      const char *name) {
+    const int rows_per_block = GU ? GROWS / 2 : GROWS;
+    dim3 grid((m0.O + rows_per_block - 1) / rows_per_block, (S + 16 * NC - 1) / (16 * NC));
+    launch(name, (k_gemm<C, GU, NC>), grid, dim3(256), 0, st, m0, m1, x, S, y);
+    return hipGetLastError();
+}
+
+template <int C, bool GU>
+hipError_t go_gemm(const MatDev &m0, const MatDev &m1, const float *x, int S, float *y, hipStream_t st) {
+    const char *name = GU ? "gemm_gate_up" : "gemm";
+    if (S <= 16) return go_gemm_nc<C, GU, 1>(m0, m1, x, S, y, st, name);
+    if (S <= 32) return go_gemm_nc<C, GU, 2>(m0, m1, x, S, y, st, name);
+    return go_gemm_nc<C, GU, 4>(m0, m1, x, S, y, st, name);
+}
+
 template <int C>
 hipError_t matmul_c(const MatDev &m, const float *x, int S, float *y, hipStream_t st) {
+    if constexpr (gemm_codec<C>())
+        if (S >= GEMM_MIN_S && m.K % 32 == 0) return go_gemm<C, false>(m, m, x, S, y, st);
     if (S >= 8) return go_matmul<C, 2, 8>(m, x, S, y, st);
     if (S >= 4) return go_matmul<C, 4, 4>(m, x, S, y, st);
     if (S >= 2) return go_matmul<C, 8, 2>(m, x, S, y, st);
@@ -997,6 +1244,8 @@ hipError_t go_gate_up(const MatDev &g, const MatDev &u, const float *x, int S, f
 
 template <int C>
 hipError_t gate_up_c(const MatDev &g, const MatDev &u, const float *x, int S, float *h, hipStream_t st) {
+    if constexpr (gemm_codec<C>())
+        if (S >= GEMM_MIN_S_GU && g.K % 32 == 0) return go_gemm<C, true>(g, u, x, S, h, st);
     if (S >= 8) return go_gate_up<C, 1, 8>(g, u, x, S, h, st);
     if (S >= 4) return go_gate_up<C, 2, 4>(g, u, x, S, h, st);
     if (S >= 2) return go_gate_up<C, 4, 2>(g, u, x, S, h, st);
