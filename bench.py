@@ -82,7 +82,8 @@ def main():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default="int4g32_expert_group_256top8_shared")
-    ap.add_argument("--tokens", type=int, default=None, help="token batch (default: the workload's first)")
+    ap.add_argument("--tokens", type=int, default=None,
+                    help="token batch (default: the workload's first; any S for the dense GEMV workloads)")
     ap.add_argument("--pool", type=int, default=1024, help="distinct routings drawn")
     ap.add_argument("--shared-copies", type=int, default=12)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -116,8 +117,10 @@ def main():
     from dequant_gemv_expert_amd import _lib as L
 
     c = synth.WORKLOADS[args.workload]
+    if c["kind"] == "gemv":
+        return bench_gemv(args, c)
     if c["kind"] != "group":
-        raise SystemExit("bench.py times the routed expert group workloads")
+        raise SystemExit("bench.py times the expert-group and dense GEMV workloads")
     S = args.tokens or c["S"][0]
     E, k, H, I, fmt, gs, seed = c["E"], c["k"], c["H"], c["I"], c["fmt"], c["gs"], c["seed"]
     n_shared = args.shared_copies if c["shared"] else 0
@@ -292,6 +295,105 @@ def main():
     }
     print(json.dumps(out), flush=True)
     table.close()
+
+
+MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense f16 matrix-core peak
+GEMM_MIN_TOKENS = 16               # dqg_matmul's matrix-core route starts here (int8, int4, MXFP4)
+
+
+def bench_gemv(args, c):
+    """A dense quantised matrix (dqg_matmul) at --tokens S: one step is one call.
+
+    Distinct device copies of the matrix (about 2 GB in all) rotate so that
+    the Infinity Cache cannot serve a step's weights.  For S below the GEMM
+    cut-over the call streams the weights (HBM-bound, GB/s); from it on it
+    runs on the matrix cores (TFLOP/s of useful products, against the f16
+    peak).
+    """
+    import numpy as np
+    import torch
+    import synth
+    import dequant_gemv_expert_amd as dq
+
+    S = args.tokens or c["S"][0]
+    fmt, O, K, gs, seed = c["fmt"], c["O"], c["K"], c["gs"], c["seed"]
+    torch.cuda.set_device(0)
+    dev_name = torch.cuda.get_device_name(0)
+    hm = synth.matrix(fmt, O, K, gs, seed, 0)
+    w_bytes = hm.q.nbytes + hm.scales.nbytes + (0 if hm.q2 is None else hm.q2.nbytes)
+    copies = max(2, min(256, (2 << 30) // w_bytes))
+    mats = [dq.Matrix.upload(hm) for _ in range(copies)]
+    x = torch.from_numpy(synth.activations(S, K, seed, 9, S)).cuda()
+    y = torch.empty((S, O), dtype=torch.float32, device="cuda")
+    gemm = S >= GEMM_MIN_TOKENS and fmt in (1, 2, 4, 7) and K % 32 == 0
+    log(f"[bench] {dev_name}: {copies} copies of {args.workload} ({w_bytes / 1e6:.2f} MB each), "
+        f"S = {S}, {'matrix-core GEMM' if gemm else 'per-row GEMV'} route")
+    for i in range(args.warmup):
+        dq.dqg_matmul(mats[i % copies], x, y)
+    torch.cuda.synchronize()
+    K_steps = args.steps
+    dq.dqg_prof_begin(K_steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K_steps):
+        dq.dqg_matmul(mats[(args.warmup + i) % copies], x, y)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t0
+    prof = dq.dqg_prof_end()
+    kname = "gemm" if gemm else "matmul"
+    n_k, ms_k = prof.get(kname, (0, 0.0))
+    avg_s = ms_k * 1e-3 / max(n_k, 1)
+    step_bytes = w_bytes + S * K * 4 + S * O * 4
+    flops = 2.0 * S * O * K
+    value = step_bytes * K_steps / t_wall / 1e9
+    if gemm:
+        achieved = flops / avg_s / 1e12 if avg_s > 0 else None
+        roof = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2) if achieved else None,
+                "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4) if achieved else None, "traffic": None,
+                "avg_us": round(avg_s * 1e6, 2), "flops_per_launch": flops}
+    else:
+        achieved = step_bytes / avg_s / 1e9 if avg_s > 0 else None
+        roof = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1) if achieved else None,
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
+                "traffic": None, "avg_us": round(avg_s * 1e6, 2), "bytes_per_launch": step_bytes}
+    log(f"[bench] {K_steps} steps: {t_wall / K_steps * 1e6:.1f} us/step wall; {kname} kernel "
+        f"{avg_s * 1e6:.1f} us avg; {flops / avg_s / 1e12 if avg_s else 0:.1f} TFLOP/s, "
+        f"{step_bytes / avg_s / 1e9 if avg_s else 0:.0f} GB/s")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        rows = max(1, min(O, int(O * 0.05)))
+        sub = synth.QMatrix(hm.fmt, rows, hm.K, hm.gs, hm.q[:rows], None if hm.q2 is None else hm.q2[:rows],
+                            hm.scales[:rows])
+        xs = x.cpu().numpy()
+        spent, calls = 0.0, 0
+        while spent < args.cpu_seconds and calls < 1000:
+            t = time.perf_counter()
+            oracle.gemv(sub, xs)
+            spent += time.perf_counter() - t
+            calls += 1
+        per_call = spent / calls * O / rows   # the whole matrix, scaled from the row sample
+        cpu = {"value": round((step_bytes / per_call / 1e9) if not gemm else (flops / per_call / 1e12), 4),
+               "unit": "GB/s" if not gemm else "TFLOP/s", "cores": oracle.get_threads(), "kind": "oracle",
+               "sample": f"{calls} oracle GEMVs of the first {rows} of {O} rows at S = {S}, {spent:.1f} s, "
+                         f"scaled to the whole matrix"}
+        log(f"[bench] cpu oracle: {cpu['value']} {cpu['unit']} on {cpu['cores']} threads")
+
+    out = {
+        "metric": METRIC if not gemm else "quant GEMM TFLOP/s (prefill, useful products)",
+        "value": round(value, 2) if not gemm else round(flops * K_steps / t_wall / 1e12, 3),
+        "unit": "GB/s" if not gemm else "TFLOP/s",
+        "n_gpus": 1, "steps": K_steps, "warmup": args.warmup,
+        "ms_per_step": round(t_wall / K_steps * 1e3, 5), "us_per_call": round(t_wall / K_steps * 1e6, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": S, "O": O, "K": K, "format": f"fmt {fmt}, gs {gs}",
+                   "copies": copies, "route": "gemm" if gemm else "gemv", "device": dev_name},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

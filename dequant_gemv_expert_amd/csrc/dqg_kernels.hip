@@ -918,18 +918,22 @@ struct GemmCodec<C_I8> {
     }
 };
 
-constexpr int GK = 128;            // inputs per k-step: 4 windows of 32
-constexpr int GWIN = GK / 32;
-constexpr int GTOK = 64;           // tokens staged per block (4 tiles of 16)
-constexpr int GXS = GK + 8;        // f16 per token row in LDS (padded against bank conflicts)
+// A k-step is GK(NC) inputs: 512 for one token tile, 256 for two, 128 for
+// four, so that the staged x' (16 NC tokens x GK, hi and lo) stays near
+// 34 KB and batches of few tokens take few, long steps (each step exposes one
+// memory latency).
+template <int NC>
+constexpr int gemm_k() { return 512 / NC; }
 constexpr int GROWS = 128;         // row slots per block: 4 waves x 2 tiles x 16
 
+template <int NC>
 struct GemmLds {
-    _Float16 xh[GTOK][GXS];
-    _Float16 xl[GTOK][GXS];
-    float xo[GTOK][GWIN];    // OFFS * sum of x' over each window
-    float xe[GTOK];          // 2^e of the token for this k-step
-    float sc[GWIN][GROWS];   // scale * VMUL per window and row slot
+    static constexpr int GK = gemm_k<NC>(), GWIN = GK / 32, GT = 16 * NC, XS = GK + 8;   // XS padded
+    _Float16 xh[GT][XS];
+    _Float16 xl[GT][XS];
+    float xo[GT][GWIN];    // OFFS * sum of x' over each window
+    float xe[GT];          // 2^e of the token for this k-step
+    float sc[GWIN][GROWS]; // scale * VMUL per window and row slot
 };
 
 // Row of slot (wave w, tile t, lane row r) and the matrix it comes from.
@@ -943,7 +947,11 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
                                               float *__restrict__ y) {
     using Gc = GemmCodec<C>;
     using Cd = Codec<C>;
-    __shared__ GemmLds L;
+    using Lt = GemmLds<NC>;
+    constexpr int GK = Lt::GK, GWIN = Lt::GWIN;
+    constexpr int TPT = 256 / Lt::GT;   // staging threads per token, one window each
+    static_assert(TPT * 32 == GK, "one staging thread per token and window");
+    __shared__ Lt L;
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = wave_id();
     const int O = m0.O, K = m0.K;
     const int block_row = blockIdx.x * (GU ? GROWS / 2 : GROWS);
@@ -965,30 +973,56 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[t][c][i] = 0.f;
 
-    for (int k0 = 0; k0 < K; k0 += GK) {
+    // Software pipeline over k-steps: the codes, x and scales of step k0 + GK
+    // are requested before step k0 is computed, so their latency hides
+    // behind the matrix-core work.
+    const int tt = tid / TPT, qq = tid % TPT;   // staging: token tt, window qq (32 inputs)
+    constexpr int SCN = GWIN * GROWS / 256;     // scales staged per thread
+    typename Gc::Raw raw[2][GWIN], raw_n[2][GWIN];
+    f32x4 xv_n[8];
+    float sc_n[SCN];
+    const auto fetch = [&](int k0) {
         const int nwin = min(GWIN, (K - k0) / 32);   // K is a multiple of 32
-        // codes of this step's windows (issued before the staging below)
-        typename Gc::Raw raw[2][GWIN];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int j = 0; j < GWIN; ++j)
-                if (j < nwin) raw[t][j] = Gc::load(arow[t], (uint32_t)(k0 + 32 * j + 8 * lq));
-        __syncthreads();   // the previous step's readers of L are done
-        // stage x': thread = (token tt, window qq), 32 inputs each
-        {
-            const int tt = tid >> 2, qq = tid & 3, s = s0 + tt, kb = k0 + 32 * qq;
-            f32x4 v[8];
-            const bool live = tt < 16 * NC && s < S && qq < nwin;
+                if (j < nwin) raw_n[t][j] = Gc::load(arow[t], (uint32_t)(k0 + 32 * j + 8 * lq));
+        const int s = s0 + tt, kb = k0 + 32 * qq;
+        const bool live = s < S && qq < nwin;
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                v[i] = live ? *(const GLOBAL f32x4 *)(gf(x) + (size_t)s * K + kb + 4 * i) : f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < 8; ++i)
+            xv_n[i] = live ? *(const GLOBAL f32x4 *)(gf(x) + (size_t)s * K + kb + 4 * i) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int h = 0; h < SCN; ++h) {
+            const int i = tid + 256 * h;   // GWIN * GROWS entries
+            const int j = i / GROWS, slot = i - j * GROWS;
+            const int sw = slot >> 5, st = (slot >> 4) & 1, sr = slot & 15;
+            const MatDev &m = (GU && st == 1) ? m1 : m0;
+            const int row = min(gemm_row<GU>(block_row, sw, st, sr), O - 1);
+            const int k = k0 + 32 * j;
+            sc_n[h] = j < nwin ? m.s[(size_t)row * m.sstride + ((uint32_t)(k / Cd::CW) >> m.shift)] * Cd::VMUL : 0.f;
+        }
+    };
+    fetch(0);
+    for (int k0 = 0; k0 < K; k0 += GK) {
+        const int nwin = min(GWIN, (K - k0) / 32);
+        f32x4 v[8];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int j = 0; j < GWIN; ++j) raw[t][j] = raw_n[t][j];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = xv_n[i];
+        __syncthreads();   // the previous step's readers of L are done
+        // stage x' of token tt, window qq
+        {
             float mx = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
-            mx = fmaxf(mx, __shfl_xor(mx, 1));
-            mx = fmaxf(mx, __shfl_xor(mx, 2));
+#pragma unroll
+            for (int o = 1; o < TPT; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));   // the token's TPT threads
             int ex = 0;
             if (mx > 0.f) { frexpf(mx, &ex); ex -= 15; }   // mx * 2^-ex < 2^15
             float xs = 0.f;
@@ -1004,28 +1038,19 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
                     lo[p] = (_Float16)(xv - (float)h);
                     xs += xv;
                 }
-                if (tt < GTOK) {
-                    *(LDS h16x8 *)&L.xh[tt][32 * qq + 8 * g] = hi;
-                    *(LDS h16x8 *)&L.xl[tt][32 * qq + 8 * g] = lo;
-                }
+                *(LDS h16x8 *)&L.xh[tt][32 * qq + 8 * g] = hi;
+                *(LDS h16x8 *)&L.xl[tt][32 * qq + 8 * g] = lo;
             }
-            if (tt < GTOK) {
-                L.xo[tt][qq] = Cd::OFFS * xs;
-                if (qq == 0) L.xe[tt] = ldexpf(1.f, ex);
-            }
+            L.xo[tt][qq] = Cd::OFFS * xs;
+            if (qq == 0) L.xe[tt] = ldexpf(1.f, ex);
         }
-        // scales * VMUL per (window, row slot)
-        for (int i = tid; i < GWIN * GROWS; i += 256) {
-            const int j = i / GROWS, slot = i - j * GROWS;
-            const int sw = slot >> 5, st = (slot >> 4) & 1, sr = slot & 15;
-            const MatDev &m = (GU && st == 1) ? m1 : m0;
-            const int row = min(gemm_row<GU>(block_row, sw, st, sr), O - 1);
-            const int k = k0 + 32 * j;
-            float sv = 0.f;
-            if (j < nwin) sv = m.s[(size_t)row * m.sstride + ((uint32_t)(k / Cd::CW) >> m.shift)] * Cd::VMUL;
-            L.sc[j][slot] = sv;
+#pragma unroll
+        for (int h = 0; h < SCN; ++h) {
+            const int i = tid + 256 * h, j = i / GROWS;
+            L.sc[j][i - j * GROWS] = sc_n[h];
         }
         __syncthreads();
+        if (k0 + GK < K) fetch(k0 + GK);   // next step's requests go out now
         for (int j = 0; j < nwin; ++j) {
             h16x8 a[2];
             f32x4 sc4[2];
@@ -1041,7 +1066,7 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
                 const int tok = 16 * c + lr;
                 const h16x8 bh = *(LDS h16x8 *)&L.xh[tok][32 * j + 8 * lq];
                 const h16x8 bl = *(LDS h16x8 *)&L.xl[tok][32 * j + 8 * lq];
-                // D rows belong to token (16c + lane%16) as well: same tok for the offset and 2^e
+                // the D lanes of token 16c + lane%16 take its offset and 2^e
                 const float xo = L.xo[tok][j], xe = L.xe[tok];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
@@ -1198,11 +1223,10 @@ hipError_t go_matmul(const MatDev &m, const float *x, int S, float *y, hipStream
 }
 
 // The matrix-core GEMM from this many tokens on, for the formats whose
-// 8-input quarter windows are whole bytes.  The pages switch at 16 rows; on
-// MI355X the per-row route stays faster below 32 tokens for matmul and 64
-// for gate_up (6144 x 6144 and 2 x 2048 x 6144 int4-g32, measured), where
-// the GEMM's grid has too few blocks.
-constexpr int GEMM_MIN_S = 32, GEMM_MIN_S_GU = 64;
+// 8-input quarter windows are whole bytes: from 16 for matmul (the pages'
+// cut-over) and from 32 for gate_up, below which the per-row route measured
+// faster (2 x 2048 x 6144 int4-g32 at 16 tokens: 96 against 119 us).
+constexpr int GEMM_MIN_S = 16, GEMM_MIN_S_GU = 32;
 
 template <int C>
 constexpr bool gemm_codec() { return C == C_I8 || C == C_I4 || C == C_FP4; }
@@ -1210,6 +1234,7 @@ constexpr bool gemm_codec() { return C == C_I8 || C == C_I4 || C == C_FP4; }
 template <int C, bool GU, int NC>
 hipError_t go_gemm_nc(const MatDev &m0, const MatDev &m1, const float *x, int S, float *y, hipStream_t st,
                       const char *name) {
+    static_assert(C != C_I8 || NC >= 2, "int8 steps hold at most 256 inputs");
     const int rows_per_block = GU ? GROWS / 2 : GROWS;
     dim3 grid((m0.O + rows_per_block - 1) / rows_per_block, (S + 16 * NC - 1) / (16 * NC));
     launch(name, (k_gemm<C, GU, NC>), grid, dim3(256), 0, st, m0, m1, x, S, y);
@@ -1218,9 +1243,13 @@ hipError_t go_gemm_nc(const MatDev &m0, const MatDev &m1, const float *x, int S,
 
 template <int C, bool GU>
 hipError_t go_gemm(const MatDev &m0, const MatDev &m1, const float *x, int S, float *y, hipStream_t st) {
+    // token tiles per block: fewer for smaller batches, so that the grid has
+    // enough blocks (at least 4 token blocks per row block up to 256 tokens)
     const char *name = GU ? "gemm_gate_up" : "gemm";
-    if (S <= 16) return go_gemm_nc<C, GU, 1>(m0, m1, x, S, y, st, name);
-    if (S <= 32) return go_gemm_nc<C, GU, 2>(m0, m1, x, S, y, st, name);
+    // int8 holds twice the code registers per step: at most 256 inputs a step
+    if constexpr (C != C_I8)
+        if (S <= 64) return go_gemm_nc<C, GU, 1>(m0, m1, x, S, y, st, name);
+    if (S <= 128) return go_gemm_nc<C, GU, 2>(m0, m1, x, S, y, st, name);
     return go_gemm_nc<C, GU, 4>(m0, m1, x, S, y, st, name);
 }
 

@@ -1,6 +1,6 @@
 """Parity of the matrix-core GEMM route with the CPU oracle.
 
-dqg_matmul (from 32 tokens) and dqg_gate_up (from 64) take the route for
+dqg_matmul (from 16 tokens) and dqg_gate_up (from 32) take the route for
 int8, int4 and MXFP4 when K is a multiple of 32; the sizes below straddle
 the cut-overs, so both routes are checked at 16..130 tokens.  Bar: as for
 the GEMV route, every output within 1e-5 of its row's normaliser
