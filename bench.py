@@ -328,15 +328,27 @@ def bench_gemv(args, c):
     gemm = S >= GEMM_MIN_TOKENS and fmt in (1, 2, 4, 7) and K % 32 == 0
     log(f"[bench] {dev_name}: {copies} copies of {args.workload} ({w_bytes / 1e6:.2f} MB each), "
         f"S = {S}, {'matrix-core GEMM' if gemm else 'per-row GEMV'} route")
+    # ctypes arguments prepared up front, so the timed loop is the C calls
+    import ctypes
+    from dequant_gemv_expert_amd import _lib as L
+    fn = L.load().dqg_matmul
+    stream = torch.cuda.current_stream().cuda_stream
+    plan = [(ctypes.byref(mt.struct), x.data_ptr(), S, y.data_ptr(), stream) for mt in mats]
+
+    def call(i):
+        rc = fn(*plan[i % copies])
+        if rc:
+            raise RuntimeError(dq.dqg_last_error())
+
     for i in range(args.warmup):
-        dq.dqg_matmul(mats[i % copies], x, y)
+        call(i)
     torch.cuda.synchronize()
     K_steps = args.steps
     dq.dqg_prof_begin(K_steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K_steps):
-        dq.dqg_matmul(mats[(args.warmup + i) % copies], x, y)
+        call(args.warmup + i)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t0
     prof = dq.dqg_prof_end()

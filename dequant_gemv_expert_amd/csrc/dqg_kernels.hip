@@ -416,42 +416,56 @@ __device__ __forceinline__ void dot_rows(const GRow (&rows)[NR], int nch, int sh
     }
 }
 
-// step_compute for one token with x in LDS: x is read per decode unit (UW
-// values) as the unit is used, so only UW values of x are live at a time
-// instead of the chunk's CW; the register budget this frees lets more waves
-// share a SIMD.
-template <int C, int NR>
-__device__ __forceinline__ void step_compute_lds(const Step<C, NR, 1> &st, lfloats x, uint32_t cu,
-                                                 float (&acc)[NR][1]) {
+// step_compute with x in LDS: x is read per decode unit (UW values per
+// token) as the unit is used, so only SM * UW values of x are live at a
+// time instead of SM * CW; the operations and their order are those of
+// step_compute, so the results have the same bits.  x + s * xstride is
+// token s's row of the staged x.
+template <int C, int NR, int SM>
+__device__ __forceinline__ void step_compute_lds(const Step<C, NR, SM> &st, lfloats x, uint32_t xstride,
+                                                 uint32_t cu, float (&acc)[NR][SM]) {
     using Cd = Codec<C>;
-    float p[NR], xs = 0.f;
+    float p[NR][SM], xs[SM];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) p[r] = 0.f;
+    for (int s = 0; s < SM; ++s) {
+        xs[s] = 0.f;
+#pragma unroll
+        for (int r = 0; r < NR; ++r) p[r][s] = 0.f;
+    }
 #pragma unroll
     for (int u = 0; u < Cd::UNITS; ++u) {
-        float xv[Cd::UW];
+        float xv[SM][Cd::UW];
 #pragma unroll
-        for (int i = 0; i < Cd::UW / 4; ++i) {
-            const f32x4 t = *(const LDS f32x4 *)(x + cu * Cd::CW + u * Cd::UW + 4 * i);
-            xv[4 * i] = t.x; xv[4 * i + 1] = t.y; xv[4 * i + 2] = t.z; xv[4 * i + 3] = t.w;
-        }
+        for (int s = 0; s < SM; ++s)
+#pragma unroll
+            for (int i = 0; i < Cd::UW / 4; ++i) {
+                const f32x4 t = *(const LDS f32x4 *)(x + s * xstride + cu * Cd::CW + u * Cd::UW + 4 * i);
+                xv[s][4 * i] = t.x; xv[s][4 * i + 1] = t.y; xv[s][4 * i + 2] = t.z; xv[s][4 * i + 3] = t.w;
+            }
         if (Cd::OFFS != 0.f) {
 #pragma unroll
-            for (int i = 0; i < Cd::UW; ++i) xs += xv[i];
+            for (int s = 0; s < SM; ++s)
+#pragma unroll
+                for (int i = 0; i < Cd::UW; ++i) xs[s] += xv[s][i];
         }
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
             uint32_t pr[Cd::UW / 2];
             Cd::decode(st.ch[r], u, pr);
 #pragma unroll
-            for (int q = 0; q < Cd::UW / 2; ++q) {
-                p[r] = fma_lo(pr[q], xv[Cd::IDX[2 * q]], p[r]);
-                p[r] = fma_hi(pr[q], xv[Cd::IDX[2 * q + 1]], p[r]);
-            }
+            for (int s = 0; s < SM; ++s)
+#pragma unroll
+                for (int q = 0; q < Cd::UW / 2; ++q) {
+                    p[r][s] = fma_lo(pr[q], xv[s][Cd::IDX[2 * q]], p[r][s]);
+                    p[r][s] = fma_hi(pr[q], xv[s][Cd::IDX[2 * q + 1]], p[r][s]);
+                }
         }
     }
 #pragma unroll
-    for (int r = 0; r < NR; ++r) acc[r][0] = fmaf(st.sc[r] * Cd::VMUL, fmaf(-Cd::OFFS, xs, p[r]), acc[r][0]);
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int s = 0; s < SM; ++s)
+            acc[r][s] = fmaf(st.sc[r] * Cd::VMUL, fmaf(-Cd::OFFS, xs[s], p[r][s]), acc[r][s]);
 }
 
 // dot_rows for one token with x in LDS, when the caller has already issued
@@ -467,7 +481,7 @@ __device__ __forceinline__ void dot_rows_lds1(Step<C, NR, 1> &st, bool have, con
         const uint32_t cu = opaque((uint32_t)c);
         if (!(have && c == lane)) step_load_w(st, rows, shift, cu);
         __builtin_amdgcn_sched_barrier(0);
-        step_compute_lds(st, x, cu, acc);
+        step_compute_lds(st, x, 0u, cu, acc);
     }
 }
 
@@ -505,6 +519,71 @@ __global__ void __launch_bounds__(256) k_matmul(MatDev m, const float *__restric
         for (int s = 0; s < SM; ++s) xp[s] = {gf(x + (size_t)min(s0 + s, S - 1) * m.K)};
         float acc[R][SM];
         dot_rows<C, R, SM>(rows, nch, m.shift, xp, acc);
+        float out = 0.f;
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int s = 0; s < SM; ++s) {
+                const float t = wave_sum(acc[r][s]);
+                if (lane == r * SM + s) out = t;
+            }
+        const int r = lane / SM, s = lane % SM;
+        if (lane < R * SM && row0 + r < m.O && s0 + s < S) y[(size_t)(s0 + s) * m.O + row0 + r] = out;
+    }
+}
+
+// dqg_matmul with x staged in LDS, K-chunk by K-chunk: the block's waves
+// share one copy of x instead of each reading it from L2.  A K-chunk is a
+// multiple of 64 code chunks, so every lane still takes chunks lane,
+// lane + 64, ... in order: a token's bits are those of k_matmul at any S.
+// Every wave stays to the end (block barriers); rows past O are clamped and
+// their outputs dropped.
+template <int C, int R, int SM>
+__global__ void __launch_bounds__(256) k_matmul_lds(MatDev m, const float *__restrict__ x, int S,
+                                                    float *__restrict__ y, int KC) {
+    extern __shared__ float xl_raw[];
+    lfloats_w xs = (lfloats_w)xl_raw;
+    using Cd = Codec<C>;
+    const int wave = blockIdx.x * (blockDim.x / WAVE) + wave_id();
+    const int row0 = wave * R;
+    const int lane = threadIdx.x & (WAVE - 1);
+    GRow rows[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) rows[r] = row_ptrs(m, min(row0 + r, m.O - 1));
+    for (int s0 = 0; s0 < S; s0 += SM) {
+        float acc[R][SM];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int s = 0; s < SM; ++s) acc[r][s] = 0.f;
+        for (int kc0 = 0; kc0 < m.K; kc0 += KC) {
+            const int kn = min(KC, m.K - kc0), n4 = kn / 4;
+            __syncthreads();   // the previous chunk's readers are done
+            for (int i0 = threadIdx.x; i0 < SM * n4; i0 += 8 * (int)blockDim.x) {
+                f32x4 v[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int i = i0 + u * (int)blockDim.x, sl = i / n4, k4 = i - sl * n4;
+                    v[u] = (i < SM * n4 && s0 + sl < S)
+                               ? *(const GLOBAL f32x4 *)(gf(x) + (size_t)(s0 + sl) * m.K + kc0 + 4 * k4)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int i = i0 + u * (int)blockDim.x, sl = i / n4, k4 = i - sl * n4;
+                    if (i < SM * n4) *(LDS f32x4 *)(xs + (size_t)sl * KC + 4 * k4) = v[u];
+                }
+            }
+            __syncthreads();
+            const int c0 = kc0 / Cd::CW, nc = kn / Cd::CW;
+            for (int c = lane; c < nc; c += WAVE) {
+                const uint32_t cu = opaque((uint32_t)c);
+                Step<C, R, SM> st;
+                step_load_w(st, rows, m.shift, cu + (uint32_t)c0);
+                __builtin_amdgcn_sched_barrier(0);
+                step_compute_lds(st, (lfloats)xs, (uint32_t)KC, cu, acc);
+            }
+        }
         float out = 0.f;
 #pragma unroll
         for (int r = 0; r < R; ++r)
@@ -1214,11 +1293,42 @@ void launch(const char *name, K kernel, dim3 grid, dim3 block, size_t lds, hipSt
         hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
 }
 
+#ifndef DQG_MM_R1
+#define DQG_MM_R1 4
+#endif
+#ifndef DQG_MM_LDS
+#define DQG_MM_LDS 1
+#endif
+#ifndef DQG_MM_R4
+#define DQG_MM_R4 4
+#endif
+#ifndef DQG_MM_R8
+#define DQG_MM_R8 4
+#endif
+#ifndef DQG_MM_R2
+#define DQG_MM_R2 4
+#endif
+// Inputs of x per K-chunk: the largest multiple of 64 code chunks that keeps
+// SM tokens within 64 KB of LDS, or the whole of K.  (Batches for which not
+// even 64 code chunks fit read x from L2 with k_matmul.)
+constexpr int MM_LDS_BYTES = 64 * 1024;
+template <int C, int SM>
+int matmul_kc(int K) {
+    const int unit = WAVE * Codec<C>::CW;            // inputs per 64 code chunks
+    const int fit = (MM_LDS_BYTES / 4 / SM) / unit * unit;
+    return K <= fit ? K : fit;
+}
+
 template <int C, int R, int SM>
 hipError_t go_matmul(const MatDev &m, const float *x, int S, float *y, hipStream_t st) {
     const int rows_per_block = R * WPB;
     dim3 grid((m.O + rows_per_block - 1) / rows_per_block);
-    launch("matmul", (k_matmul<C, R, SM>), grid, dim3(WAVE * WPB), 0, st, m, x, S, y);
+    if constexpr (DQG_MM_LDS && SM * WAVE * Codec<C>::CW * 4 <= MM_LDS_BYTES) {
+        const int KC = matmul_kc<C, SM>(m.K);
+        launch("matmul", (k_matmul_lds<C, R, SM>), grid, dim3(WAVE * WPB), (size_t)SM * KC * 4, st, m, x, S, y, KC);
+    } else {
+        launch("matmul", (k_matmul<C, R, SM>), grid, dim3(WAVE * WPB), 0, st, m, x, S, y);
+    }
     return hipGetLastError();
 }
 
@@ -1257,10 +1367,10 @@ template <int C>
 hipError_t matmul_c(const MatDev &m, const float *x, int S, float *y, hipStream_t st) {
     if constexpr (gemm_codec<C>())
         if (S >= GEMM_MIN_S && m.K % 32 == 0) return go_gemm<C, false>(m, m, x, S, y, st);
-    if (S >= 8) return go_matmul<C, 2, 8>(m, x, S, y, st);
-    if (S >= 4) return go_matmul<C, 4, 4>(m, x, S, y, st);
-    if (S >= 2) return go_matmul<C, 8, 2>(m, x, S, y, st);
-    return go_matmul<C, 8, 1>(m, x, S, y, st);
+    if (S >= 8) return go_matmul<C, DQG_MM_R8, 8>(m, x, S, y, st);
+    if (S >= 4) return go_matmul<C, DQG_MM_R4, 4>(m, x, S, y, st);
+    if (S >= 2) return go_matmul<C, DQG_MM_R2, 2>(m, x, S, y, st);
+    return go_matmul<C, DQG_MM_R1, 1>(m, x, S, y, st);
 }
 
 template <int C, int R, int SM>
