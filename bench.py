@@ -381,7 +381,7 @@ def bench_gemv(args, c):
                             hm.scales[:rows])
         xs = x.cpu().numpy()
         spent, calls = 0.0, 0
-        while spent < args.cpu_seconds and calls < 1000:
+        while spent < args.cpu_seconds and calls < 1_000_000:
             t = time.perf_counter()
             oracle.gemv(sub, xs)
             spent += time.perf_counter() - t
