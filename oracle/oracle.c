@@ -213,9 +213,18 @@ static double silu_slope(double z)
  *   nh = |silu'(g)| * absn_g * |u| + |silu(g)| * absn_u.
  * Any output pointer may be NULL except h.
  */
-void orc_gate_up(const orc_matrix *G, const orc_matrix *U, const float *x, long S,
-                 double *h, double *nh, double *g_out, double *u_out,
-                 double *ag_out, double *au_out)
+/*
+ * gate_up with the clamped SwiGLU of [V]'s GLM paragraph (swiglu_limit L):
+ *   g' = min(g, L), u' = min(max(u, -L), L), h = silu(g') * u'.
+ * The pages give only what a limit of 0 does (every routed expert's output
+ * is zero); this clamp is the reading that does that.  L = +inf is the
+ * plain SwiGLU: both clamps are then the identity.  The normaliser carries
+ * the clamped values; the clamps are 1-Lipschitz, so the first-order reach
+ * of the errors in g and u is still |silu'(g')| A_g |u'| + |silu(g')| A_u.
+ */
+void orc_gate_up_clamped(const orc_matrix *G, const orc_matrix *U, const float *x, long S, double limit,
+                         double *h, double *nh, double *g_out, double *u_out,
+                         double *ag_out, double *au_out)
 {
     long I = G->O, idx;
 #pragma omp parallel for schedule(static)
@@ -224,9 +233,11 @@ void orc_gate_up(const orc_matrix *G, const orc_matrix *U, const float *x, long 
         double g, u, ag, au;
         row_dot(G, i, x + s * G->K, NULL, &g, &ag);
         row_dot(U, i, x + s * U->K, NULL, &u, &au);
-        h[idx] = orc_silu(g) * u;
+        double gc = g > limit ? limit : g;   /* NaN stays NaN */
+        double uc = u > limit ? limit : (u < -limit ? -limit : u);
+        h[idx] = orc_silu(gc) * uc;
         if (nh)
-            nh[idx] = fabs(silu_slope(g)) * ag * fabs(u) + fabs(orc_silu(g)) * au;
+            nh[idx] = fabs(silu_slope(gc)) * ag * fabs(uc) + fabs(orc_silu(gc)) * au;
         if (g_out) g_out[idx] = g;
         if (u_out) u_out[idx] = u;
         if (ag_out) ag_out[idx] = ag;
@@ -234,22 +245,18 @@ void orc_gate_up(const orc_matrix *G, const orc_matrix *U, const float *x, long 
     }
 }
 
-/* ------------------------------------------------------------------ */
-/* Expert group.                                                        */
-/*   y[t] = sum_{r=0..k-1} w[t][r] * MLP_{ids[t][r]}(x[t])   (rank order) */
-/*        + MLP_shared(x[t])                       (if shared >= 0)       */
-/*   MLP_e(x) = down_e * (silu(gate_e x) * (up_e x)).                     */
-/* absn[t][o] = sum over the terms of |weight| * sum_k |down[o][k]| *     */
-/*   (|h[k]| + nh[k]): the down row's own normaliser plus the first-order */
-/*   reach of the errors h may carry.                                    */
-/* ids outside [0, n_experts) make the token's row NaN.                  */
-/* ------------------------------------------------------------------ */
+void orc_gate_up(const orc_matrix *G, const orc_matrix *U, const float *x, long S,
+                 double *h, double *nh, double *g_out, double *u_out,
+                 double *ag_out, double *au_out)
+{
+    orc_gate_up_clamped(G, U, x, S, INFINITY, h, nh, g_out, u_out, ag_out, au_out);
+}
 
 static void mlp_one(const orc_matrix *gate, const orc_matrix *up, const orc_matrix *down,
-                    const float *x, double *h, double *nh, double *dy, double *dabs)
+                    const float *x, double limit, double *h, double *nh, double *dy, double *dabs)
 {
     long I = gate->O, H = down->O;
-    orc_gate_up(gate, up, x, 1, h, nh, NULL, NULL, NULL, NULL);
+    orc_gate_up_clamped(gate, up, x, 1, limit, h, nh, NULL, NULL, NULL, NULL);
     long o;
 #pragma omp parallel for schedule(static)
     for (o = 0; o < H; o++) {
@@ -264,11 +271,11 @@ static void mlp_one(const orc_matrix *gate, const orc_matrix *up, const orc_matr
     }
 }
 
-void orc_expert_group(const orc_matrix *gates, const orc_matrix *ups, const orc_matrix *downs,
-                      long n_experts, long S, long k, const int32_t *ids, const float *w,
-                      long shared, const float *x, double *y, double *absn,
-                      double *h_work /* [I] */, double *nh_work /* [I] */,
-                      double *dy_work /* [H] */, double *dabs_work /* [H] */)
+void orc_expert_group_clamped(const orc_matrix *gates, const orc_matrix *ups, const orc_matrix *downs,
+                              long n_experts, long S, long k, const int32_t *ids, const float *w,
+                              long shared, const float *x, double limit, double *y, double *absn,
+                              double *h_work /* [I] */, double *nh_work /* [I] */,
+                              double *dy_work /* [H] */, double *dabs_work /* [H] */)
 {
     long H = downs[0].O;
     for (long t = 0; t < S; t++) {
@@ -285,7 +292,7 @@ void orc_expert_group(const orc_matrix *gates, const orc_matrix *ups, const orc_
                 continue;
             }
             double wr = (double)w[t * k + r];
-            mlp_one(&gates[e], &ups[e], &downs[e], x + t * gates[e].K, h_work, nh_work,
+            mlp_one(&gates[e], &ups[e], &downs[e], x + t * gates[e].K, limit, h_work, nh_work,
                     dy_work, dabs_work);
             for (long o = 0; o < H; o++) {
                 yt[o] += wr * dy_work[o];
@@ -294,7 +301,7 @@ void orc_expert_group(const orc_matrix *gates, const orc_matrix *ups, const orc_
         }
         if (shared >= 0) {
             mlp_one(&gates[shared], &ups[shared], &downs[shared], x + t * gates[shared].K,
-                    h_work, nh_work, dy_work, dabs_work);
+                    limit, h_work, nh_work, dy_work, dabs_work);
             for (long o = 0; o < H; o++) {
                 yt[o] += dy_work[o];
                 at[o] += dabs_work[o];
@@ -306,6 +313,15 @@ void orc_expert_group(const orc_matrix *gates, const orc_matrix *ups, const orc_
 /* ------------------------------------------------------------------ */
 /* Threads.                                                             */
 /* ------------------------------------------------------------------ */
+
+void orc_expert_group(const orc_matrix *gates, const orc_matrix *ups, const orc_matrix *downs,
+                      long n_experts, long S, long k, const int32_t *ids, const float *w,
+                      long shared, const float *x, double *y, double *absn,
+                      double *h_work, double *nh_work, double *dy_work, double *dabs_work)
+{
+    orc_expert_group_clamped(gates, ups, downs, n_experts, S, k, ids, w, shared, x, INFINITY, y, absn,
+                             h_work, nh_work, dy_work, dabs_work);
+}
 
 /* ------------------------------------------------------------------ */
 /* Router: logits -> scores -> top-k -> (ids, weights).                 */

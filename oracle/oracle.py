@@ -7,6 +7,7 @@ except ``dequant`` (float32, the materialised weights).
 from __future__ import annotations
 
 import ctypes as C
+import math
 import os
 from typing import Optional, Sequence
 
@@ -74,6 +75,12 @@ class OracleLib:
         lib.orc_gate_up.argtypes = [C.POINTER(_Mat), C.POINTER(_Mat), _P, _L, _P, _P, _P, _P, _P, _P]
         lib.orc_expert_group.restype = None
         lib.orc_expert_group.argtypes = [_P, _P, _P, _L, _L, _L, _P, _P, _L, _P, _P, _P, _P, _P, _P, _P]
+        lib.orc_gate_up_clamped.restype = None
+        lib.orc_gate_up_clamped.argtypes = [C.POINTER(_Mat), C.POINTER(_Mat), _P, _L, C.c_double,
+                                            _P, _P, _P, _P, _P, _P]
+        lib.orc_expert_group_clamped.restype = None
+        lib.orc_expert_group_clamped.argtypes = [_P, _P, _P, _L, _L, _L, _P, _P, _L, _P, C.c_double,
+                                                 _P, _P, _P, _P, _P, _P]
         lib.orc_route.restype = None
         lib.orc_route.argtypes = [_P, _L, _L, _L, C.c_int, C.c_int, _P, C.c_double, _P, _P, _P]
         lib.orc_set_threads.restype = None
@@ -126,14 +133,18 @@ class OracleLib:
             self.lib.orc_gemv(C.byref(_mat(m)), _ptr(xx), S, _ptr(y), _ptr(a))
         return y, a
 
-    def gate_up(self, G, U, x) -> dict:
+    def gate_up(self, G, U, x, limit: float = math.inf) -> dict:
+        """h = silu(min(g, L)) * clamp(u, -L, L) with L = ``limit`` (inf: plain SwiGLU)."""
         x = _f32(np.atleast_2d(x))
         S, I = x.shape[0], G.O
         if G.K != x.shape[1] or U.K != x.shape[1] or U.O != I:
             raise ValueError("gate/up/x shapes disagree")
         out = {n: np.empty((S, I), dtype=np.float64) for n in ("h", "nh", "g", "u", "ag", "au")}
-        self.lib.orc_gate_up(C.byref(_mat(G)), C.byref(_mat(U)), _ptr(x), S,
-                             *[_ptr(out[n]) for n in ("h", "nh", "g", "u", "ag", "au")])
+        ptrs = [_ptr(out[n]) for n in ("h", "nh", "g", "u", "ag", "au")]
+        if math.isinf(limit) and limit > 0:
+            self.lib.orc_gate_up(C.byref(_mat(G)), C.byref(_mat(U)), _ptr(x), S, *ptrs)
+        else:
+            self.lib.orc_gate_up_clamped(C.byref(_mat(G)), C.byref(_mat(U)), _ptr(x), S, float(limit), *ptrs)
         return out
 
     def route(self, logits, k: int, mode: int = 0, renorm: bool = False, bias=None,
@@ -155,7 +166,8 @@ class OracleLib:
                            ids.ctypes.data, w.ctypes.data, key.ctypes.data)
         return {"ids": ids, "w": w, "key": key}
 
-    def expert_group(self, experts: Sequence, ids, w, shared: Optional[int], x) -> tuple:
+    def expert_group(self, experts: Sequence, ids, w, shared: Optional[int], x,
+                     limit: float = math.inf) -> tuple:
         """y[S][H] and its normaliser for a token batch.
 
         ``experts`` is a sequence of objects with gate/up/down matrices,
@@ -184,10 +196,13 @@ class OracleLib:
         nw = np.empty(I, dtype=np.float64)
         dw = np.empty(H, dtype=np.float64)
         aw = np.empty(H, dtype=np.float64)
-        self.lib.orc_expert_group(C.cast(gates, C.c_void_p), C.cast(ups, C.c_void_p),
-                                  C.cast(downs, C.c_void_p), n, S, k, _ptr(cids), _ptr(w),
-                                  cshared, _ptr(x), _ptr(y), _ptr(a), _ptr(hw), _ptr(nw),
-                                  _ptr(dw), _ptr(aw))
+        args = (C.cast(gates, C.c_void_p), C.cast(ups, C.c_void_p), C.cast(downs, C.c_void_p), n, S, k,
+                _ptr(cids), _ptr(w), cshared, _ptr(x))
+        work = (_ptr(y), _ptr(a), _ptr(hw), _ptr(nw), _ptr(dw), _ptr(aw))
+        if math.isinf(limit) and limit > 0:
+            self.lib.orc_expert_group(*args, *work)
+        else:
+            self.lib.orc_expert_group_clamped(*args, float(limit), *work)
         return y, a
 
 
@@ -232,12 +247,12 @@ def gemv(m, x):
     return load().gemv(m, x)
 
 
-def gate_up(G, U, x):
-    return load().gate_up(G, U, x)
+def gate_up(G, U, x, limit=math.inf):
+    return load().gate_up(G, U, x, limit)
 
 
-def expert_group(experts, ids, w, shared, x):
-    return load().expert_group(experts, ids, w, shared, x)
+def expert_group(experts, ids, w, shared, x, limit=math.inf):
+    return load().expert_group(experts, ids, w, shared, x, limit)
 
 
 def route(logits, k, mode=0, renorm=False, bias=None, w_scale=1.0):

@@ -501,6 +501,90 @@ def pin_group_normaliser(lib):
 
 
 # ---------------------------------------------------------------------------
+# clamped SwiGLU (swiglu_limit)
+# ---------------------------------------------------------------------------
+
+def _gu_pair(seed=7100, I=96, H=256):
+    G = synth.matrix(4, I, H, 32, seed, 0)
+    U = synth.matrix(4, I, H, 32, seed, 1)
+    x = synth.activations(3, H, seed, 2)
+    return G, U, x
+
+
+def pin_clamp_huge_limit_is_plain(lib):
+    """A limit above every |g| and |u| changes nothing, bit for bit."""
+    G, U, x = _gu_pair()
+    plain = lib.gate_up(G, U, x)
+    for L in (1e3, 1e300):
+        r = lib.gate_up(G, U, x, L)
+        assert np.array_equal(r["h"], plain["h"]), L
+        assert np.array_equal(r["nh"], plain["nh"]), L
+
+
+def pin_clamp_regions(lib):
+    """Against the plain SwiGLU (pinned above), region by region:
+    g < L and |u| <= L: unchanged; g < L and |u| > L: scaled by L/|u|;
+    g >= L: h / clamp(u) is one value for every output (silu(L))."""
+    G, U, x = _gu_pair(7101)
+    plain = lib.gate_up(G, U, x)
+    g, u = plain["g"], plain["u"]
+    L = float(np.median(np.abs(u)))
+    r = lib.gate_up(G, U, x, L)
+    h, hp = r["h"], plain["h"]
+    free = (g < L) & (np.abs(u) <= L)
+    assert free.any() and np.array_equal(h[free], hp[free])
+    cut = (g < L) & (np.abs(u) > L)
+    assert cut.any() and np.allclose(h[cut], hp[cut] * L / np.abs(u[cut]), rtol=1e-14, atol=0)
+    sat = (g >= L) & (np.abs(u) > 1e-6)
+    assert sat.sum() > 3
+    ratio = h[sat] / np.clip(u[sat], -L, L)
+    assert np.allclose(ratio, ratio[0], rtol=1e-14, atol=0)
+    assert ratio[0] > 0
+
+
+def pin_clamp_is_odd_in_up(lib):
+    """Negating the up weights negates h exactly, clamped or not."""
+    G, U, x = _gu_pair(7102)
+    Un = synth.QMatrix(U.fmt, U.O, U.K, U.gs, U.q, U.q2, (-U.scales).astype(np.float32))
+    for L in (math.inf, 0.3, 0.01):
+        a = lib.gate_up(G, U, x, L)["h"]
+        b = lib.gate_up(G, Un, x, L)["h"]
+        assert np.array_equal(a, -b), L
+
+
+def pin_clamp_tiny_limit_zeroes_outputs(lib):
+    """The pages: a limit of 0 zeroes every expert's output; as L -> 0+ so does h and y."""
+    G, U, x = _gu_pair(7103)
+    r = lib.gate_up(G, U, x, 1e-150)
+    assert np.all(np.abs(r["h"]) <= 1e-150)
+    ex = _tiny_experts(4)
+    ids = np.array([[0, 2], [3, 1]], np.int32)
+    w = np.array([[0.7, 0.3], [0.5, 0.5]], np.float32)
+    xg = synth.activations(2, 64, 7104)
+    y, _ = lib.expert_group(ex, ids, w, 1, xg, 1e-150)
+    assert np.all(np.abs(y) < 1e-140)
+    y_plain, _ = lib.expert_group(ex, ids, w, 1, xg)
+    assert np.abs(y_plain).max() > 1e-3
+
+
+def pin_clamp_group_uses_limit(lib):
+    """The group applies the limit in every expert, shared included: each token's y equals the
+    weighted sum of the clamped single-expert MLPs."""
+    ex = _tiny_experts(3)
+    xg = synth.activations(1, 64, 7105)
+    L = 0.05
+    ys = []
+    for e in range(3):
+        y1, _ = lib.expert_group(ex, np.array([[e]], np.int32), np.array([[1.0]], np.float32), None, xg, L)
+        ys.append(y1[0])
+    y, _ = lib.expert_group(ex, np.array([[0, 1]], np.int32), np.array([[0.25, 0.75]], np.float32), 2, xg, L)
+    want = np.float64(np.float32(0.25)) * ys[0] + np.float64(np.float32(0.75)) * ys[1] + ys[2]
+    assert np.allclose(y[0], want, rtol=1e-12, atol=1e-15)
+    y_plain, _ = lib.expert_group(ex, np.array([[0, 1]], np.int32), np.array([[0.25, 0.75]], np.float32), 2, xg)
+    assert not np.allclose(y[0], y_plain[0])
+
+
+# ---------------------------------------------------------------------------
 # router
 # ---------------------------------------------------------------------------
 

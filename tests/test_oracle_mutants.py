@@ -48,7 +48,15 @@ MUTANTS = {
                                "row_dot(m, o, x + s * m->K, NULL, &y[o * S + s]"),
     "silu_sign": ("return z / (1.0 + exp(-z));", "return z / (1.0 + exp(z));"),
     "silu_missing_z": ("return z / (1.0 + exp(-z));", "return 1.0 / (1.0 + exp(-z));"),
-    "gate_up_swapped": ("h[idx] = orc_silu(g) * u;", "h[idx] = orc_silu(u) * g;"),
+    "gate_up_swapped": ("h[idx] = orc_silu(gc) * uc;", "h[idx] = orc_silu(uc) * gc;"),
+    "clamp_gate_from_below": ("double gc = g > limit ? limit : g;", "double gc = g < limit ? limit : g;"),
+    "clamp_up_one_sided": ("double uc = u > limit ? limit : (u < -limit ? -limit : u);",
+                           "double uc = u > limit ? limit : u;"),
+    "clamp_gate_ignored": ("double gc = g > limit ? limit : g;", "double gc = g;"),
+    "clamp_group_ignores_limit": ("mlp_one(&gates[e], &ups[e], &downs[e], x + t * gates[e].K, limit,",
+                                  "mlp_one(&gates[e], &ups[e], &downs[e], x + t * gates[e].K, INFINITY,"),
+    "clamp_shared_ignores_limit": ("                    limit, h_work, nh_work, dy_work, dabs_work);",
+                                   "                    INFINITY, h_work, nh_work, dy_work, dabs_work);"),
     "router_weight_dropped": ("yt[o] += wr * dy_work[o];", "yt[o] += dy_work[o];"),
     "shared_expert_dropped": ("                yt[o] += dy_work[o];", "                yt[o] += 0.0 * dy_work[o];"),
     "down_uses_gate_rows": ("mlp_one(&gates[e], &ups[e], &downs[e],", "mlp_one(&gates[e], &ups[e], &downs[(e + 1) % n_experts],"),
