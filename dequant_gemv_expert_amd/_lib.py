@@ -57,9 +57,11 @@ _P, _I32, _SZ = C.c_void_p, C.c_int32, C.c_size_t
 SIGNATURES = {
     "dqg_matmul": (C.c_int, [C.POINTER(dqg_matrix), _P, _I32, _P, _P]),
     "dqg_gate_up": (C.c_int, [C.POINTER(dqg_matrix), C.POINTER(dqg_matrix), _P, _I32, _P, _P]),
+    "dqg_gate_up_clamped": (C.c_int, [C.POINTER(dqg_matrix), C.POINTER(dqg_matrix), _P, _I32, C.c_float, _P, _P]),
     "dqg_dequant": (C.c_int, [C.POINTER(dqg_matrix), _P, _P]),
     "dqg_expert_table_create": (C.c_int, [C.POINTER(dqg_expert), _I32, C.POINTER(C.c_void_p)]),
     "dqg_expert_table_destroy": (None, [_P]),
+    "dqg_expert_table_set_swiglu_limit": (C.c_int, [_P, C.c_float]),
     "dqg_expert_group_scratch_bytes": (_SZ, [_P, _I32, _I32]),
     "dqg_expert_group": (C.c_int, [_P, _I32, _I32, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "dqg_expert_group_issue": (C.c_int, [_P, _I32, _I32, _P, _P, _I32, _P, _P, _P, _SZ, _P,
@@ -164,6 +166,16 @@ def dqg_gate_up(G: Matrix, U: Matrix, x: torch.Tensor, h: Optional[torch.Tensor]
     return h
 
 
+def dqg_gate_up_clamped(G: Matrix, U: Matrix, x: torch.Tensor, limit: float, h: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    S = x.shape[0]
+    if h is None:
+        h = torch.empty((S, G.O), dtype=torch.float32, device=x.device)
+    _check(load().dqg_gate_up_clamped(C.byref(G.struct), C.byref(U.struct), _dev(x, "x", torch.float32), S,
+                                      float(limit), _dev(h, "h", torch.float32), _stream(stream)))
+    return h
+
+
 def dqg_dequant(W: Matrix, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     if out is None:
         out = torch.empty((W.O, W.K), dtype=torch.float32, device=W.q.device)
@@ -207,6 +219,10 @@ class ExpertTable:
             self.close()
         except Exception:
             pass
+
+    def set_swiglu_limit(self, limit: float) -> None:
+        """dqg_expert_table_set_swiglu_limit (math.inf: the plain SwiGLU)."""
+        _check(load().dqg_expert_table_set_swiglu_limit(self.handle, float(limit)))
 
     def scratch_bytes(self, S: int, k: int) -> int:
         return load().dqg_expert_group_scratch_bytes(self.handle, S, k)

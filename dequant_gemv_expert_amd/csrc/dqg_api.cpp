@@ -22,6 +22,7 @@ struct dqg_expert_table {
     int device;
     int codec_gu, codec_down;
     int32_t H, I;
+    float swiglu_limit;   // +inf: plain SwiGLU
 };
 
 namespace {
@@ -193,6 +194,7 @@ int group_common(const dqg_expert_table *t, int32_t S, int32_t k, const int32_t 
     a.flag = reinterpret_cast<int32_t *>(base + FLAG_OFFSET);
     a.H = t->H;
     a.I = t->I;
+    a.limit = t->swiglu_limit;
     int nl = 0;
     const hipError_t e = launch_group(t->codec_gu, t->codec_down, a, static_cast<hipStream_t>(stream), &nl);
     g_launches += nl;
@@ -293,8 +295,17 @@ int dqg_matmul(const dqg_matrix *W, const float *x, int32_t S, float *y, void *s
     return DQG_OK;
 }
 
-int dqg_gate_up(const dqg_matrix *G, const dqg_matrix *U, const float *x, int32_t S, float *h,
-                void *stream) {
+namespace {
+
+// A SwiGLU limit: positive (clamped) or +inf (plain).  Zero and negative
+// limits are refused, as the backend's shader runs only above 0.
+int check_limit(float limit, const char *what) {
+    if (!(limit > 0.f)) return fail(DQG_EINVAL, "%s: swiglu limit %g must be > 0 (or +inf for none)", what, (double)limit);
+    return DQG_OK;
+}
+
+int gate_up_common(const dqg_matrix *G, const dqg_matrix *U, const float *x, int32_t S, float limit, float *h,
+                   void *stream) {
     ++g_calls_gate_up;
     MatDev g, u;
     int rc;
@@ -302,12 +313,33 @@ int dqg_gate_up(const dqg_matrix *G, const dqg_matrix *U, const float *x, int32_
     if (G->fmt != U->fmt || G->O != U->O || G->K != U->K || G->gs != U->gs)
         return fail(DQG_ESHAPE, "gate_up: G and U must share format, shape and group size");
     if (S < 1) return fail(DQG_EINVAL, "gate_up: S=%d must be >= 1", S);
+    if ((rc = check_limit(limit, "gate_up"))) return rc;
     if ((rc = check_vec(x, "gate_up: x")) || (rc = check_vec(h, "gate_up: h"))) return rc;
     if (inject_fault()) return fail(DQG_ELAUNCH, "gate_up: injected launch failure (DQG_FAULT)");
-    hipError_t e = launch_gate_up(codec_of(G->fmt), g, u, x, S, h, static_cast<hipStream_t>(stream));
+    hipError_t e = launch_gate_up(codec_of(G->fmt), g, u, x, S, h, limit, static_cast<hipStream_t>(stream));
     if ((rc = launched(e, "gate_up"))) return rc;
     ++g_launches;
     g_bytes += 2 * matrix_bytes(G) + (uint64_t)S * (G->K + G->O) * 4;
+    return DQG_OK;
+}
+
+}  // namespace
+
+int dqg_gate_up(const dqg_matrix *G, const dqg_matrix *U, const float *x, int32_t S, float *h,
+                void *stream) {
+    return gate_up_common(G, U, x, S, INFINITY, h, stream);
+}
+
+int dqg_gate_up_clamped(const dqg_matrix *G, const dqg_matrix *U, const float *x, int32_t S, float limit,
+                        float *h, void *stream) {
+    return gate_up_common(G, U, x, S, limit, h, stream);
+}
+
+int dqg_expert_table_set_swiglu_limit(dqg_expert_table *t, float limit) {
+    if (!t) return fail(DQG_EINVAL, "expert_table_set_swiglu_limit: table is NULL");
+    int rc;
+    if ((rc = check_limit(limit, "expert_table_set_swiglu_limit"))) return rc;
+    t->swiglu_limit = limit;
     return DQG_OK;
 }
 
@@ -386,6 +418,7 @@ int dqg_expert_table_create(const dqg_expert *experts, int32_t n, dqg_expert_tab
     t->codec_down = codec_of(e0.down.fmt);
     t->H = e0.gate.K;
     t->I = e0.gate.O;
+    t->swiglu_limit = INFINITY;
     hipError_t e = hipGetDevice(&t->device);
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&t->dev), (size_t)n * sizeof(ExpertDev));
     if (e == hipSuccess) e = hipMemcpy(t->dev, host, (size_t)n * sizeof(ExpertDev), hipMemcpyHostToDevice);

@@ -48,6 +48,7 @@ struct GroupArgs {
     int32_t *flag;       // cleared by the gate_up launch, set by the down launch
                          // when an id is out of range
     int32_t H, I;
+    float limit;         // swiglu_limit of the experts' SwiGLU, +inf for none
 };
 
 // Launch parameters of the router.
@@ -73,7 +74,7 @@ bool prof_slot(const char *kernel, hipEvent_t *start, hipEvent_t *stop);
 hipError_t launch_matmul(int codec, const MatDev &m, const float *x, int S, float *y,
                          hipStream_t st);
 hipError_t launch_gate_up(int codec, const MatDev &g, const MatDev &u, const float *x, int S,
-                          float *h, hipStream_t st);
+                          float *h, float limit, hipStream_t st);   // limit: swiglu_limit, +inf for none
 hipError_t launch_dequant(int codec, const MatDev &m, float *out, hipStream_t st);
 hipError_t launch_route(const RouteArgs &a, hipStream_t st);
 hipError_t launch_group(int codec_gu, int codec_down, const GroupArgs &a, hipStream_t st,

@@ -293,6 +293,14 @@ __device__ __forceinline__ int wave_id() {
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
 
+// SwiGLU with a limit L (swiglu_limit): silu(min(g, L)) * clamp(u, -L, L).
+// L = +inf leaves g and u unchanged, bit for bit; a NaN stays NaN.
+__device__ __forceinline__ float swiglu(float g, float u, float L) {
+    const float gc = g > L ? L : g;
+    const float uc = u > L ? L : (u < -L ? -L : u);
+    return silu(gc) * uc;
+}
+
 // ---------------------------------------------------------------------------
 // The row-set dot product.  acc[r][s] (per lane) = this lane's share of
 // sum_k W_r[k] * x_s[k]; reduce with wave_sum.  Per chunk and row:
@@ -602,7 +610,7 @@ __global__ void __launch_bounds__(256) k_matmul_lds(MatDev m, const float *__res
 // ---------------------------------------------------------------------------
 template <int C, int R, int SM>
 __global__ void __launch_bounds__(256) k_gate_up(MatDev g, MatDev u, const float *__restrict__ x,
-                                                 int S, float *__restrict__ h) {
+                                                 int S, float *__restrict__ h, float L) {
     const int I = g.O;
     const int wave = blockIdx.x * (blockDim.x / WAVE) + wave_id();
     const int row0 = wave * R;
@@ -631,7 +639,7 @@ __global__ void __launch_bounds__(256) k_gate_up(MatDev g, MatDev u, const float
                 if (lane == r * SM + s) { gv = tg; uv = tu; }
             }
         const int r = lane / SM, s = lane % SM;
-        if (lane < R * SM && row0 + r < I && s0 + s < S) h[(size_t)(s0 + s) * I + row0 + r] = silu(gv) * uv;
+        if (lane < R * SM && row0 + r < I && s0 + s < S) h[(size_t)(s0 + s) * I + row0 + r] = swiglu(gv, uv, L);
     }
 }
 
@@ -818,7 +826,7 @@ __device__ __forceinline__ void group_gu_batch(const GroupArgs &a, const ExpertD
 #pragma unroll
         for (int j = 1; j < SM; ++j)
             if (s == j) slot = b.slot[j];
-        a.h[(size_t)slot * a.I + row0 + r] = silu(gv) * uv;
+        a.h[(size_t)slot * a.I + row0 + r] = swiglu(gv, uv, a.limit);
     }
 }
 
@@ -1023,7 +1031,7 @@ __device__ __forceinline__ int gemm_row(int block_row, int w, int t, int r) {
 
 template <int C, bool GU, int NC>
 __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float *__restrict__ x, int S,
-                                              float *__restrict__ y) {
+                                              float *__restrict__ y, float limit) {
     using Gc = GemmCodec<C>;
     using Cd = Codec<C>;
     using Lt = GemmLds<NC>;
@@ -1167,7 +1175,7 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
         for (int i = 0; i < 4; ++i) {
             if (GU) {
                 const int row = gemm_row<GU>(block_row, w, 0, 4 * lq + i);
-                if (row < O) y[(size_t)s * O + row] = silu(acc[0][c][i]) * acc[1][c][i];
+                if (row < O) y[(size_t)s * O + row] = swiglu(acc[0][c][i], acc[1][c][i], limit);
             } else {
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
@@ -1342,31 +1350,31 @@ template <int C>
 constexpr bool gemm_codec() { return C == C_I8 || C == C_I4 || C == C_FP4; }
 
 template <int C, bool GU, int NC>
-hipError_t go_gemm_nc(const MatDev &m0, const MatDev &m1, const float *x, int S, float *y, hipStream_t st,
-                      const char *name) {
+hipError_t go_gemm_nc(const MatDev &m0, const MatDev &m1, const float *x, int S, float *y, float L,
+                      hipStream_t st, const char *name) {
     static_assert(C != C_I8 || NC >= 2, "int8 steps hold at most 256 inputs");
     const int rows_per_block = GU ? GROWS / 2 : GROWS;
     dim3 grid((m0.O + rows_per_block - 1) / rows_per_block, (S + 16 * NC - 1) / (16 * NC));
-    launch(name, (k_gemm<C, GU, NC>), grid, dim3(256), 0, st, m0, m1, x, S, y);
+    launch(name, (k_gemm<C, GU, NC>), grid, dim3(256), 0, st, m0, m1, x, S, y, L);
     return hipGetLastError();
 }
 
 template <int C, bool GU>
-hipError_t go_gemm(const MatDev &m0, const MatDev &m1, const float *x, int S, float *y, hipStream_t st) {
+hipError_t go_gemm(const MatDev &m0, const MatDev &m1, const float *x, int S, float *y, float L, hipStream_t st) {
     // token tiles per block: fewer for smaller batches, so that the grid has
     // enough blocks (at least 4 token blocks per row block up to 256 tokens)
     const char *name = GU ? "gemm_gate_up" : "gemm";
     // int8 holds twice the code registers per step: at most 256 inputs a step
     if constexpr (C != C_I8)
-        if (S <= 64) return go_gemm_nc<C, GU, 1>(m0, m1, x, S, y, st, name);
-    if (S <= 128) return go_gemm_nc<C, GU, 2>(m0, m1, x, S, y, st, name);
-    return go_gemm_nc<C, GU, 4>(m0, m1, x, S, y, st, name);
+        if (S <= 64) return go_gemm_nc<C, GU, 1>(m0, m1, x, S, y, L, st, name);
+    if (S <= 128) return go_gemm_nc<C, GU, 2>(m0, m1, x, S, y, L, st, name);
+    return go_gemm_nc<C, GU, 4>(m0, m1, x, S, y, L, st, name);
 }
 
 template <int C>
 hipError_t matmul_c(const MatDev &m, const float *x, int S, float *y, hipStream_t st) {
     if constexpr (gemm_codec<C>())
-        if (S >= GEMM_MIN_S && m.K % 32 == 0) return go_gemm<C, false>(m, m, x, S, y, st);
+        if (S >= GEMM_MIN_S && m.K % 32 == 0) return go_gemm<C, false>(m, m, x, S, y, INFINITY, st);
     if (S >= 8) return go_matmul<C, DQG_MM_R8, 8>(m, x, S, y, st);
     if (S >= 4) return go_matmul<C, DQG_MM_R4, 4>(m, x, S, y, st);
     if (S >= 2) return go_matmul<C, DQG_MM_R2, 2>(m, x, S, y, st);
@@ -1374,21 +1382,21 @@ hipError_t matmul_c(const MatDev &m, const float *x, int S, float *y, hipStream_
 }
 
 template <int C, int R, int SM>
-hipError_t go_gate_up(const MatDev &g, const MatDev &u, const float *x, int S, float *h, hipStream_t st) {
+hipError_t go_gate_up(const MatDev &g, const MatDev &u, const float *x, int S, float *h, float L, hipStream_t st) {
     const int rows_per_block = R * WPB;
     dim3 grid((g.O + rows_per_block - 1) / rows_per_block);
-    launch("gate_up", (k_gate_up<C, R, SM>), grid, dim3(WAVE * WPB), 0, st, g, u, x, S, h);
+    launch("gate_up", (k_gate_up<C, R, SM>), grid, dim3(WAVE * WPB), 0, st, g, u, x, S, h, L);
     return hipGetLastError();
 }
 
 template <int C>
-hipError_t gate_up_c(const MatDev &g, const MatDev &u, const float *x, int S, float *h, hipStream_t st) {
+hipError_t gate_up_c(const MatDev &g, const MatDev &u, const float *x, int S, float *h, float L, hipStream_t st) {
     if constexpr (gemm_codec<C>())
-        if (S >= GEMM_MIN_S_GU && g.K % 32 == 0) return go_gemm<C, true>(g, u, x, S, h, st);
-    if (S >= 8) return go_gate_up<C, 1, 8>(g, u, x, S, h, st);
-    if (S >= 4) return go_gate_up<C, 2, 4>(g, u, x, S, h, st);
-    if (S >= 2) return go_gate_up<C, 4, 2>(g, u, x, S, h, st);
-    return go_gate_up<C, 4, 1>(g, u, x, S, h, st);
+        if (S >= GEMM_MIN_S_GU && g.K % 32 == 0) return go_gemm<C, true>(g, u, x, S, h, L, st);
+    if (S >= 8) return go_gate_up<C, 1, 8>(g, u, x, S, h, L, st);
+    if (S >= 4) return go_gate_up<C, 2, 4>(g, u, x, S, h, L, st);
+    if (S >= 2) return go_gate_up<C, 4, 2>(g, u, x, S, h, L, st);
+    return go_gate_up<C, 4, 1>(g, u, x, S, h, L, st);
 }
 
 template <int C>
@@ -1454,12 +1462,12 @@ hipError_t launch_matmul(int codec, const MatDev &m, const float *x, int S, floa
 }
 
 hipError_t launch_gate_up(int codec, const MatDev &g, const MatDev &u, const float *x, int S,
-                          float *h, hipStream_t st) {
+                          float *h, float limit, hipStream_t st) {
     switch (codec) {
-    case C_I8: return gate_up_c<C_I8>(g, u, x, S, h, st);
-    case C_I4: return gate_up_c<C_I4>(g, u, x, S, h, st);
-    case C_I3: return gate_up_c<C_I3>(g, u, x, S, h, st);
-    case C_FP4: return gate_up_c<C_FP4>(g, u, x, S, h, st);
+    case C_I8: return gate_up_c<C_I8>(g, u, x, S, h, limit, st);
+    case C_I4: return gate_up_c<C_I4>(g, u, x, S, h, limit, st);
+    case C_I3: return gate_up_c<C_I3>(g, u, x, S, h, limit, st);
+    case C_FP4: return gate_up_c<C_FP4>(g, u, x, S, h, limit, st);
     }
     return hipErrorInvalidValue;
 }

@@ -147,6 +147,18 @@ int dqg_gate_up(const dqg_matrix *G, const dqg_matrix *U, const float *x, int32_
                 void *stream);
 
 /*
+ * dqg_gate_up with the clamped SwiGLU (swiglu_limit L):
+ *   h = silu(min(G.x, L)) * min(max(U.x, -L), L).
+ * ("colibri -- Vulkan backend (docs/vulkan.md)", the GLM paragraph: the
+ * experts' SwiGLU is clamped; a limit of 0 zeroes every expert's output and
+ * the backend's shader runs only above 0.)  L > 0, or +inf for the plain
+ * SwiGLU (the same bits as dqg_gate_up); other values give DQG_EINVAL.  A
+ * NaN in g or u stays NaN.  Everything else as dqg_gate_up.
+ */
+int dqg_gate_up_clamped(const dqg_matrix *G, const dqg_matrix *U, const float *x, int32_t S, float limit,
+                        float *h, void *stream);
+
+/*
  * out[o][k] = value(o, k) * scale(o, k), rounded once to f32.
  * Materialises the dequantised weights (for bit-exact checks of the decode
  * that the other calls do in registers).  out: f32 [O][K].
@@ -163,6 +175,12 @@ int dqg_dequant(const dqg_matrix *W, float *out, void *stream);
  */
 int dqg_expert_table_create(const dqg_expert *experts, int32_t n_experts, dqg_expert_table **out);
 void dqg_expert_table_destroy(dqg_expert_table *table);
+
+/* The limit of the table's experts' SwiGLU in dqg_expert_group (the clamped
+ * form of dqg_gate_up_clamped): L > 0, or +inf (the default at creation)
+ * for the plain SwiGLU; other values give DQG_EINVAL and leave it as it
+ * was.  Applies to calls issued after it returns. */
+int dqg_expert_table_set_swiglu_limit(dqg_expert_table *table, float limit);
 
 /* Scratch bytes dqg_expert_group needs for S tokens of top-k routing: a
  * header of DQG_SCRATCH_H_OFFSET bytes (the error flag at byte 0), then the

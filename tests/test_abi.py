@@ -114,6 +114,14 @@ def test_route_validation(lib, S, E, k, mode, renorm, bias, scale, logits, ids, 
     assert c.calls_route == 1 and c.launches == 0
 
 
+@pytest.mark.parametrize("limit", [0.0, -1.0, float("nan"), float("-inf")])
+def test_swiglu_limit_validation(lib, limit):
+    g, u = _mat(), _mat()
+    assert lib.dqg_gate_up_clamped(C.byref(g), C.byref(u), FAKE_X, 1, limit, FAKE_Y, None) == -1
+    assert "limit" in lib.dqg_last_error().decode()
+    assert lib.dqg_expert_table_set_swiglu_limit(None, 1.0) == -1
+
+
 def test_table_validation(lib):
     e = L.dqg_expert(_mat(O=32, K=64), _mat(O=32, K=64), _mat(O=64, K=64))   # down must be [64 x 32]
     out = C.c_void_p()
