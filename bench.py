@@ -88,6 +88,8 @@ def main():
     ap.add_argument("--shared-copies", type=int, default=12)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--swiglu-limit", type=float, default=None,
+                    help="clamp the experts' SwiGLU at this limit (expert-group workloads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (torch) 5 times, the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -144,6 +146,8 @@ def main():
                     down_bytes = matrix_bytes(h.down)
                     exp_bytes = gu_bytes + down_bytes
     table = dq.ExpertTable(experts)
+    if args.swiglu_limit is not None:
+        table.set_swiglu_limit(args.swiglu_limit)
     torch.cuda.synchronize()
     log(f"[bench] {dev_name}: {n_total} experts resident ({n_total * exp_bytes / 1e9:.2f} GB) "
         f"in {time.time() - t0:.1f}s")
@@ -251,7 +255,8 @@ def main():
             for e in set(ids[p].ravel().tolist()) | ({shared_of(i)} if n_shared else set()):
                 host_expert(e)   # drawn before the clock starts
             t = time.perf_counter()
-            oracle.expert_group(View(), ids[p], w[p], shared_of(i), x[p])
+            oracle.expert_group(View(), ids[p], w[p], shared_of(i), x[p],
+                                *([] if args.swiglu_limit is None else [args.swiglu_limit]))
             spent += time.perf_counter() - t
             calls += 1
             cbytes += step_bytes(i)
@@ -280,7 +285,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "tokens": S, "top_k": k, "experts": E,
                    "shared_expert": bool(n_sh), "H": H, "I": I, "format": f"fmt {fmt}, gs {gs}",
-                   "routing_pool": P, "shared_copies": n_shared, "device": dev_name},
+                   "routing_pool": P, "shared_copies": n_shared, "device": dev_name,
+                   **({} if args.swiglu_limit is None else {"swiglu_limit": args.swiglu_limit})},
         "roofline": {"kernel": dom, "bound": "hbm",
                      "achieved": round(achieved, 1) if achieved else None, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
