@@ -28,9 +28,20 @@
  *       order, then the shared expert).
  *  [A]  "opus colibri scout": the router row (strata's router does the
  *       softmax and the top-k in one dispatch).
+ *       The f16-rows paragraph of [V] (format 14: f16 values, no scales, the
+ *       low half of a word the even column, laid out like bf16's format 11)
+ *       and the expert-tier engine table of [V] (format 10 F32, 11 BF16, 12
+ *       FP8 in 128x128 blocks, 13 int8 with a scale per 64 inputs).
  *  [OCP] The OCP Microscaling (MX) Formats specification v1.0, FP4 E2M1:
  *       1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit, subnormal
  *       when the exponent field is 0.
+ *  [OFP8] The OCP 8-bit floating point specification (OFP8), E4M3: 1 sign
+ *       bit, 4 exponent bits with bias 7, 3 mantissa bits, subnormal when the
+ *       exponent field is 0, no infinities, S.1111.111 is NaN.
+ *  [IEEE] IEEE 754 binary16 (5 exponent bits, bias 15, 10 fraction bits) and
+ *       binary32; bfloat16 is the upper 16 bits of a binary32 (8 exponent
+ *       bits, bias 127, 7 fraction bits).  The all-ones exponent holds the
+ *       infinities (fraction 0) and NaNs.
  *
  * Readings taken where the pages are silent (each is a listed reading, not
  * a page fact):
@@ -47,6 +58,13 @@
  *    weight is that product rounded once to nearest-even.
  *  - router weights multiply each expert's down output; the shared expert
  *    is added last with weight 1.
+ *  - formats 10, 11 and 14 carry no scales (a weight is its stored value).
+ *  - format 12: E4M3 codes [O][K] and one f32 scale per block of 128 rows x
+ *    128 inputs, row-major [ceil(O/128)][K/128]; K is a multiple of 128.
+ *  - format 13: int8 codes [O][K] with f32 scales [O][K/gs], groups of gs
+ *    consecutive inputs as in format 4 (gs 64 in the pages' containers).
+ *  - 16-bit values are little-endian words in column order, which puts the
+ *    even column in the low half of each 32-bit word.
  */
 #include <math.h>
 #include <stdint.h>
@@ -54,11 +72,12 @@
 #include <omp.h>
 
 typedef struct {
-    int fmt;               /* 1 int8/row, 2 int4/row, 4 int4/gs, 5 int3-g64, 7 MXFP4 */
+    int fmt;               /* 1 int8/row, 2 int4/row, 4 int4/gs, 5 int3-g64, 7 MXFP4,
+                              10 f32, 11 bf16, 12 E4M3 128x128, 13 int8/gs, 14 f16 */
     long O, K, gs;         /* rows, inputs per row, inputs per scale */
     const void *q;         /* codes (fmt 5: the 2-bit plane) */
     const void *q2;        /* fmt 5: the 1-bit plane; otherwise unused */
-    const float *scales;   /* [O][K/gs] */
+    const float *scales;   /* [O][K/gs]; fmt 12 [ceil(O/128)][K/128]; unused by 10, 11, 14 */
 } orc_matrix;
 
 /* ------------------------------------------------------------------ */
@@ -85,6 +104,30 @@ double orc_e2m1(int code)
         mag = 0.5 * mant;                       /* 2^(1-1) * (mant / 2) */
     else
         mag = ldexp(1.0 + 0.5 * mant, expo - 1);   /* 2^(expo-1) * (1 + mant/2) */
+    return sign ? -mag : mag;
+}
+
+/* Value of a binary floating-point code from its fields [IEEE], [OFP8]:
+   1 sign bit over ebits exponent bits (bias 2^(ebits-1) - 1) over mbits
+   fraction bits; subnormal when the exponent field is 0.  ieee: the
+   all-ones exponent holds infinities and NaNs; otherwise (E4M3) only the
+   all-ones magnitude is NaN and every other code is finite. */
+double orc_minifloat(uint32_t code, int ebits, int mbits, int ieee)
+{
+    uint32_t frac = code & ((1u << mbits) - 1);
+    uint32_t expo = (code >> mbits) & ((1u << ebits) - 1);
+    int sign = (code >> (ebits + mbits)) & 1;
+    int bias = (1 << (ebits - 1)) - 1;
+    uint32_t emax = (1u << ebits) - 1;
+    double mag;
+    if (ieee && expo == emax)
+        mag = frac ? NAN : INFINITY;
+    else if (!ieee && expo == emax && frac == (1u << mbits) - 1)
+        mag = NAN;
+    else if (expo == 0)
+        mag = ldexp((double)frac, 1 - bias - mbits);               /* 2^(1-bias) * frac / 2^mbits */
+    else
+        mag = ldexp((double)((1u << mbits) + frac), (int)expo - bias - mbits);   /* 2^(e-bias) * (1.frac) */
     return sign ? -mag : mag;
 }
 
@@ -118,6 +161,26 @@ double orc_code_value(const orc_matrix *m, long o, long k)
         const uint8_t *row = (const uint8_t *)m->q + o * (m->K / 2);
         return orc_e2m1(nibble_at(row, k));
     }
+    case 10: {
+        const float *row = (const float *)m->q + o * m->K;
+        return (double)row[k];
+    }
+    case 11: {
+        const uint16_t *row = (const uint16_t *)m->q + o * m->K;
+        return orc_minifloat(row[k], 8, 7, 1);
+    }
+    case 12: {
+        const uint8_t *row = (const uint8_t *)m->q + o * m->K;
+        return orc_minifloat(row[k], 4, 3, 0);
+    }
+    case 13: {
+        const int8_t *row = (const int8_t *)m->q + o * m->K;
+        return (double)row[k];
+    }
+    case 14: {
+        const uint16_t *row = (const uint16_t *)m->q + o * m->K;
+        return orc_minifloat(row[k], 5, 10, 1);
+    }
     }
     return NAN;
 }
@@ -125,12 +188,19 @@ double orc_code_value(const orc_matrix *m, long o, long k)
 /* The scale that applies to weight (o, k). */
 double orc_scale(const orc_matrix *m, long o, long k)
 {
+    if (m->fmt == 10 || m->fmt == 11 || m->fmt == 14)
+        return 1.0;
+    if (m->fmt == 12) {
+        long blocks = m->K / 128;
+        return (double)m->scales[(o / 128) * blocks + k / 128];
+    }
     long groups = m->K / m->gs;
     return (double)m->scales[o * groups + k / m->gs];
 }
 
 /* Weight (o, k) as a real number: v * s.  Exact in double (v has at most
-   8 significant bits, s has 24). */
+   8 significant bits and s 24, or s is 1 and v is a stored f32 or
+   narrower float). */
 double orc_weight(const orc_matrix *m, long o, long k)
 {
     return orc_code_value(m, o, k) * orc_scale(m, o, k);

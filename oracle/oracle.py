@@ -29,22 +29,33 @@ def _ptr(a: Optional[np.ndarray]):
     return None if a is None else a.ctypes.data_as(C.c_void_p)
 
 
+NO_SCALES = (10, 11, 14)   # f32, bf16 and f16 rows carry no scales
+_QBYTES = {1: 1, 13: 1, 12: 1, 10: 4, 11: 2, 14: 2}   # bytes per input of the one-code-per-input formats
+
+
 def _check_matrix(m) -> None:
-    for name in ("q", "scales"):
-        a = getattr(m, name)
-        if not a.flags["C_CONTIGUOUS"]:
-            raise ValueError(f"{name} must be C-contiguous")
+    if not m.q.flags["C_CONTIGUOUS"]:
+        raise ValueError("q must be C-contiguous")
+    if m.fmt in _QBYTES and m.q.nbytes != m.O * m.K * _QBYTES[m.fmt]:
+        raise ValueError(f"fmt {m.fmt}: q holds {m.q.nbytes} bytes, expected {m.O * m.K * _QBYTES[m.fmt]}")
+    if m.fmt in NO_SCALES:
+        return
+    if not m.scales.flags["C_CONTIGUOUS"]:
+        raise ValueError("scales must be C-contiguous")
     if m.scales.dtype != np.float32:
         raise ValueError("scales must be float32")
     if m.K % m.gs:
         raise ValueError("K must be a multiple of gs")
+    if m.fmt == 12 and (m.gs != 128 or m.scales.size != -(-m.O // 128) * (m.K // 128)):
+        raise ValueError("fmt 12 has one scale per 128 x 128 block")
     if m.fmt == 5 and m.q2 is None:
         raise ValueError("fmt 5 needs its 1-bit plane")
 
 
 def _mat(m) -> _Mat:
     _check_matrix(m)
-    return _Mat(int(m.fmt), int(m.O), int(m.K), int(m.gs), _ptr(m.q), _ptr(m.q2), _ptr(m.scales))
+    scales = None if m.fmt in NO_SCALES else m.scales
+    return _Mat(int(m.fmt), int(m.O), int(m.K), int(m.gs), _ptr(m.q), _ptr(m.q2), _ptr(scales))
 
 
 def _f32(x) -> np.ndarray:
@@ -59,6 +70,8 @@ class OracleLib:
         lib = C.CDLL(path)
         lib.orc_e2m1.restype = C.c_double
         lib.orc_e2m1.argtypes = [C.c_int]
+        lib.orc_minifloat.restype = C.c_double
+        lib.orc_minifloat.argtypes = [C.c_uint32, C.c_int, C.c_int, C.c_int]
         lib.orc_code_value.restype = C.c_double
         lib.orc_code_value.argtypes = [C.POINTER(_Mat), _L, _L]
         lib.orc_weight.restype = C.c_double
@@ -92,6 +105,11 @@ class OracleLib:
     # -- scalar helpers ---------------------------------------------------
     def e2m1(self, code: int) -> float:
         return self.lib.orc_e2m1(int(code))
+
+    def minifloat(self, code: int, ebits: int, mbits: int, ieee: bool) -> float:
+        """A binary float code's value from its fields (E4M3: 4, 3, False;
+        f16: 5, 10, True; bf16: 8, 7, True)."""
+        return self.lib.orc_minifloat(int(code), int(ebits), int(mbits), int(bool(ieee)))
 
     def silu(self, z: float) -> float:
         return self.lib.orc_silu(float(z))
@@ -221,6 +239,10 @@ def load(path: Optional[str] = None) -> OracleLib:
 
 def e2m1(code):
     return load().e2m1(code)
+
+
+def minifloat(code, ebits, mbits, ieee):
+    return load().minifloat(code, ebits, mbits, ieee)
 
 
 def silu(z):

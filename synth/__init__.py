@@ -20,9 +20,22 @@ Vulkan backend (docs/vulkan.md)"):
          scales: f32 [O][K/64]
   fmt 7  MXFP4: e2m1 nibbles, f32 scale per 32 inputs (pre-expanded e8m0)
          q: uint8 [O][K/2]                  scales: f32 [O][K/32]
+  fmt 10 f32 rows, no scales
+         q: float32 [O][K]                  scales: None
+  fmt 11 bf16 rows, no scales
+         q: uint16 [O][K] (bf16 bits)       scales: None
+  fmt 12 FP8 E4M3, one f32 scale per block of 128 rows x 128 inputs
+         q: uint8 [O][K] (E4M3 bits)        scales: f32 [ceil(O/128)][K/128]
+  fmt 13 int8, one f32 scale per gs inputs (gs 64 by default)
+         q: int8 [O][K]                     scales: f32 [O][K/gs]
+  fmt 14 f16 rows, no scales
+         q: uint16 [O][K] (f16 bits)        scales: None
 
 Uniform random words give uniform codes in every field, so drawing words is
-the same as drawing codes; no bit of any code is computed here.
+the same as drawing codes; no bit of any code is computed here.  The float
+forms draw their fields (sign, exponent field in a weight-like range,
+uniform fraction) and place them in the word; E4M3 draws a sign and a
+non-NaN magnitude byte.
 """
 from __future__ import annotations
 
@@ -37,8 +50,16 @@ FMT_I4_ROW = 2
 FMT_I4_GS = 4
 FMT_I3_G64 = 5
 FMT_MXFP4 = 7
+FMT_F32 = 10
+FMT_BF16 = 11
+FMT_FP8_BLOCK = 12
+FMT_I8_GS = 13
+FMT_F16 = 14
 
-FORMATS = (FMT_I8_ROW, FMT_I4_ROW, FMT_I4_GS, FMT_I3_G64, FMT_MXFP4)
+FORMATS = (FMT_I8_ROW, FMT_I4_ROW, FMT_I4_GS, FMT_I3_G64, FMT_MXFP4,
+           FMT_F32, FMT_BF16, FMT_FP8_BLOCK, FMT_I8_GS, FMT_F16)
+NO_SCALE_FORMATS = (FMT_F32, FMT_BF16, FMT_F16)
+FP8_BLOCK = 128   # rows and inputs per E4M3 scale block
 
 BASE_SEED = 20261202
 
@@ -52,20 +73,25 @@ class QMatrix:
     gs: int
     q: np.ndarray
     q2: Optional[np.ndarray]
-    scales: np.ndarray
+    scales: Optional[np.ndarray]   # None for the formats without scales
 
     @property
     def nbytes(self) -> int:
-        n = self.q.nbytes + self.scales.nbytes
+        n = self.q.nbytes + (0 if self.scales is None else self.scales.nbytes)
         if self.q2 is not None:
             n += self.q2.nbytes
         return n
 
 
 def group_size(fmt: int, K: int, gs: Optional[int] = None) -> int:
-    """Inputs per scale for a format (the whole row for the per-row forms)."""
-    if fmt in (FMT_I8_ROW, FMT_I4_ROW):
+    """Inputs per scale for a format (the whole row for the per-row forms
+    and for the forms without scales)."""
+    if fmt in (FMT_I8_ROW, FMT_I4_ROW) or fmt in NO_SCALE_FORMATS:
         return K
+    if fmt == FMT_FP8_BLOCK:
+        return FP8_BLOCK
+    if fmt == FMT_I8_GS:
+        return 64 if gs is None else gs
     if fmt == FMT_I3_G64:
         return 64
     if fmt == FMT_MXFP4:
@@ -85,6 +111,14 @@ def storage_shapes(fmt: int, O: int, K: int, gs: int):
         return (O, K // 2), np.uint8, None, (O, K // gs)
     if fmt == FMT_I3_G64:
         return (O, K // 16), np.uint32, (O, K // 32), (O, K // 64)
+    if fmt == FMT_F32:
+        return (O, K), np.float32, None, None
+    if fmt in (FMT_BF16, FMT_F16):
+        return (O, K), np.uint16, None, None
+    if fmt == FMT_FP8_BLOCK:
+        return (O, K), np.uint8, None, (-(-O // FP8_BLOCK), K // FP8_BLOCK)
+    if fmt == FMT_I8_GS:
+        return (O, K), np.int8, None, (O, K // gs)
     raise ValueError(f"unknown format {fmt}")
 
 
@@ -100,14 +134,18 @@ def _scales(rng: np.random.Generator, fmt: int, shape, kind: str) -> np.ndarray:
         return np.ldexp(np.ones(shape, dtype=np.float32), e).astype(np.float32)
     if kind == "row_int8":
         lo, hi = 1e-3, 1e-2
+    elif kind == "fp8_block":   # E4M3's largest magnitude 448 maps to about 0.01 to 0.05
+        lo, hi = 2e-5, 1e-4
     else:
         lo, hi = 1e-3, 2e-2
     return rng.uniform(lo, hi, size=shape).astype(np.float32)
 
 
 def default_scale_kind(fmt: int) -> str:
-    if fmt == FMT_I8_ROW:
+    if fmt in (FMT_I8_ROW, FMT_I8_GS):
         return "row_int8"
+    if fmt == FMT_FP8_BLOCK:
+        return "fp8_block"
     if fmt == FMT_MXFP4:
         return "pow2"
     return "uniform"
@@ -117,17 +155,33 @@ def matrix(fmt: int, O: int, K: int, gs: Optional[int], *key: int,
            scale_kind: Optional[str] = None) -> QMatrix:
     """Draw one quantised matrix from the stream named by ``key``.
 
-    int8 codes are uniform in [-127, 127]; every other format's fields are
-    uniform over all their codes.  Scales: int8 rows U[1e-3, 1e-2], int4 and
-    int3 groups U[1e-3, 2e-2], MXFP4 powers of two 2^U{-10..-6}.
+    int8 codes are uniform in [-127, 127]; int4, int3 and MXFP4 fields are
+    uniform over all their codes.  f32 rows are N(0, 0.02); bf16 and f16
+    rows have a uniform sign, an exponent of 2^-12 .. 2^-3 and a uniform
+    fraction; E4M3 codes have a uniform sign and a uniform non-NaN
+    magnitude.  Scales: int8 rows and groups U[1e-3, 1e-2], int4 and int3
+    groups U[1e-3, 2e-2], MXFP4 powers of two 2^U{-10..-6}, E4M3 blocks
+    U[2e-5, 1e-4].
     """
     gs = group_size(fmt, K, gs)
     if K % gs:
         raise ValueError("K must be a multiple of the group size")
     qshape, qdtype, q2shape, sshape = storage_shapes(fmt, O, K, gs)
     rng = rng_for(*key)
-    if fmt == FMT_I8_ROW:
+    if fmt in (FMT_I8_ROW, FMT_I8_GS):
         q = rng.integers(-127, 128, size=qshape, dtype=np.int8)
+    elif fmt == FMT_F32:
+        q = (rng.standard_normal(size=qshape) * 0.02).astype(np.float32)
+    elif fmt in (FMT_BF16, FMT_F16):
+        mbits, bias = (7, 127) if fmt == FMT_BF16 else (10, 15)
+        sign = rng.integers(0, 2, size=qshape, dtype=np.uint16)
+        expo = rng.integers(bias - 12, bias - 2, size=qshape).astype(np.uint16)
+        frac = rng.integers(0, 1 << mbits, size=qshape, dtype=np.uint16)
+        q = (sign << np.uint16(15)) | (expo << np.uint16(mbits)) | frac
+    elif fmt == FMT_FP8_BLOCK:
+        sign = rng.integers(0, 2, size=qshape, dtype=np.uint8)
+        mag = rng.integers(0, 0x7F, size=qshape, dtype=np.uint8)   # 0x7F is NaN
+        q = (sign << np.uint8(7)) | mag
     elif qdtype == np.uint8:
         q = rng.integers(0, 256, size=qshape, dtype=np.uint8)
     else:
@@ -135,7 +189,7 @@ def matrix(fmt: int, O: int, K: int, gs: Optional[int], *key: int,
     q2 = None
     if q2shape is not None:
         q2 = rng.integers(0, 2**32, size=q2shape, dtype=np.uint32)
-    s = _scales(rng, fmt, sshape, scale_kind or default_scale_kind(fmt))
+    s = None if sshape is None else _scales(rng, fmt, sshape, scale_kind or default_scale_kind(fmt))
     return QMatrix(fmt, O, K, gs, q, q2, s)
 
 
@@ -187,7 +241,7 @@ def expert(fmt: int, H: int, I: int, gs: Optional[int], seed: int, index: int,
     """Expert ``index`` of a seeded set: gate, up [I x H] and down [H x I]."""
     dfmt = fmt if down_fmt is None else down_fmt
     dgs = gs if down_gs is None else down_gs
-    if dfmt in (FMT_I8_ROW, FMT_I4_ROW):
+    if dfmt in (FMT_I8_ROW, FMT_I4_ROW) or dfmt in NO_SCALE_FORMATS or dfmt == FMT_FP8_BLOCK:
         dgs = None
     return Expert(matrix(fmt, I, H, gs, seed, index, 0),
                   matrix(fmt, I, H, gs, seed, index, 1),

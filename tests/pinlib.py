@@ -61,14 +61,34 @@ def golden_int3():
     return low, high, values
 
 
+def golden_minifloats():
+    """{kind: [(code, value)]} from the hand-written float code table."""
+    out = {}
+    for kind, code, val in _rows("minifloat_values.txt"):
+        v = float.fromhex(val) if "0x" in val else float(val)
+        out.setdefault(kind, []).append((int(code, 16), v))
+    return out
+
+
 def _same_bits(a, b) -> bool:
+    if math.isnan(a) or math.isnan(b):
+        return math.isnan(a) and math.isnan(b)
     return np.float64(a).tobytes() == np.float64(b).tobytes()
+
+
+def _same_values(a, b) -> bool:
+    """Arrays equal element by element, NaN matching NaN and -0 only -0."""
+    a, b = np.asarray(a, np.float64), np.asarray(b, np.float64)
+    na, nb = np.isnan(a), np.isnan(b)
+    if not np.array_equal(na, nb):
+        return False
+    return a[~na].tobytes() == b[~nb].tobytes()
 
 
 def _qm(fmt, O, K, gs, q, scales, q2=None):
     return synth.QMatrix(fmt, O, K, gs, np.ascontiguousarray(q),
                          None if q2 is None else np.ascontiguousarray(q2),
-                         np.ascontiguousarray(scales, dtype=np.float32))
+                         None if scales is None else np.ascontiguousarray(scales, dtype=np.float32))
 
 
 # ---------------------------------------------------------------------------
@@ -143,6 +163,54 @@ def pin_exhaustive_codes(lib):
         assert np.array_equal(lib.code_values(m)[0], np.full(64, code - 4)), code
 
 
+_FLOAT_FMT = {"e4m3": (synth.FMT_FP8_BLOCK, np.uint8), "f16": (synth.FMT_F16, np.uint16),
+              "bf16": (synth.FMT_BF16, np.uint16)}
+
+
+def _float_row(kind, codes):
+    """One row of a float format holding ``codes`` (padded to a whole block)."""
+    fmt, dt = _FLOAT_FMT[kind]
+    K = max(128, -(-len(codes) // 128) * 128)
+    q = np.zeros((1, K), dt)
+    q[0, :len(codes)] = codes
+    scales = np.ones((1, K // 128), np.float32) if fmt == synth.FMT_FP8_BLOCK else None
+    return _qm(fmt, 1, K, 128 if fmt == synth.FMT_FP8_BLOCK else K, q, scales)
+
+
+def pin_minifloat_table(lib):
+    """E4M3, f16 and bf16 codes decode to the hand-written table, through the
+    field decoder and through a matrix row of each format."""
+    ieee = {"e4m3": (4, 3, False), "f16": (5, 10, True), "bf16": (8, 7, True)}
+    for kind, rows in golden_minifloats().items():
+        for code, val in rows:
+            got = lib.minifloat(code, *ieee[kind])
+            assert _same_bits(got, val), f"{kind} {code:#x}: {got!r} != {val!r}"
+        m = _float_row(kind, [c for c, _ in rows])
+        got = lib.code_values(m)[0, :len(rows)]
+        assert _same_values(got, [v for _, v in rows]), f"{kind} row: {got}"
+
+
+def pin_float_formats_exhaustive(lib):
+    """Every code of the float formats against a library decode: numpy's
+    binary16 for f16, numpy's binary32 of the code in the upper half for
+    bf16, torch's float8_e4m3fn for E4M3; f32 rows are their own values."""
+    import torch
+    f16 = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    assert _same_values(lib.code_values(_float_row("f16", f16))[0], f16.view(np.float16).astype(np.float64))
+    bf = np.arange(65536, dtype=np.uint32)
+    with np.errstate(invalid="ignore"):   # signalling NaNs widen quietly
+        want = (bf << np.uint32(16)).view(np.float32).astype(np.float64)
+    assert _same_values(lib.code_values(_float_row("bf16", bf.astype(np.uint16)))[0], want)
+    e = np.arange(256, dtype=np.uint8)
+    want = torch.from_numpy(e.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert _same_values(lib.code_values(_float_row("e4m3", e))[0, :256], want)
+    # f32: random words with the special values mixed in
+    w = synth.rng_for(12, 10).integers(0, 2**32, size=(2, 64), dtype=np.uint64).astype(np.uint32)
+    w[0, :6] = [0x00000000, 0x80000000, 0x7F800000, 0xFF800000, 0x00000001, 0x7F7FFFFF]
+    m = _qm(synth.FMT_F32, 2, 64, 64, w.view(np.float32), None)
+    assert _same_values(lib.code_values(m), w.view(np.float32).astype(np.float64))
+
+
 # ---------------------------------------------------------------------------
 # an independent NumPy decoder (vectorised), pinned to the same fixtures,
 # used to check the oracle's row and word indexing on large random matrices
@@ -150,8 +218,15 @@ def pin_exhaustive_codes(lib):
 
 def numpy_values(m) -> np.ndarray:
     O, K = m.O, m.K
-    if m.fmt == 1:
+    if m.fmt in (1, 13, 10):
         return m.q.astype(np.float64)
+    if m.fmt == 11:
+        return (m.q.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    if m.fmt == 14:
+        return m.q.view(np.float16).astype(np.float64)
+    if m.fmt == 12:
+        import torch
+        return torch.from_numpy(np.ascontiguousarray(m.q)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
     if m.fmt in (2, 4, 7):
         lo = (m.q & 0x0F).astype(np.int64)
         hi = (m.q >> 4).astype(np.int64)
@@ -170,6 +245,11 @@ def numpy_values(m) -> np.ndarray:
 
 
 def numpy_scales(m) -> np.ndarray:
+    if m.fmt in synth.NO_SCALE_FORMATS:
+        return np.ones((m.O, m.K))
+    if m.fmt == 12:   # 128 x 128 blocks: expand along both axes
+        b = np.repeat(m.scales.astype(np.float64), 128, axis=0)[:m.O]
+        return np.repeat(b, 128, axis=1)
     return np.repeat(m.scales.astype(np.float64), m.gs, axis=1)
 
 
@@ -192,6 +272,12 @@ def _random_matrices():
     yield synth.matrix(4, 3, 256, 64, 11, 4)
     yield synth.matrix(5, 4, 192, 64, 11, 5)
     yield synth.matrix(7, 5, 128, 32, 11, 6)
+    yield synth.matrix(10, 3, 64, None, 11, 10)
+    yield synth.matrix(11, 4, 96, None, 11, 11)
+    yield synth.matrix(12, 130, 256, None, 11, 12)   # two row blocks, the second ragged
+    yield synth.matrix(13, 5, 128, 32, 11, 13)
+    yield synth.matrix(13, 3, 256, 64, 11, 14)
+    yield synth.matrix(14, 4, 96, None, 11, 15)
 
 
 def pin_random_layouts(lib):
@@ -205,10 +291,13 @@ def pin_random_layouts(lib):
 def pin_dequant_rounding_and_scale_index(lib):
     """dequant[o][k] == RNE_f32(v * s[o][k // gs]), with every group's scale distinct."""
     for m in _random_matrices():
-        groups = m.K // m.gs
-        # distinct scales per (row, group): identifiable if mis-indexed
-        s = (1.0 + np.arange(m.O * groups, dtype=np.float64) / 64.0) * 1e-3
-        m.scales = s.reshape(m.O, groups).astype(np.float32)
+        if m.fmt in synth.NO_SCALE_FORMATS:
+            assert lib.dequant(m).tobytes() == numpy_values(m).astype(np.float32).tobytes(), m.fmt
+            continue
+        # distinct scales per (row, group) or block: identifiable if mis-indexed
+        shape = m.scales.shape
+        s = (1.0 + np.arange(shape[0] * shape[1], dtype=np.float64) / 64.0) * 1e-3
+        m.scales = s.reshape(shape).astype(np.float32)
         want = (numpy_values(m) * numpy_scales(m)).astype(np.float32)   # exact product, one rounding
         got = lib.dequant(m)
         assert got.tobytes() == want.tobytes(), f"fmt {m.fmt}: dequant bits differ"
@@ -249,6 +338,7 @@ def pin_fraction_brute_force(lib):
         O, K = min(m.O, 3), m.K
         x = synth.activations(2, K, 99, m.fmt)
         y, a = lib.gemv(m, x)
+        assert np.all(np.isfinite(y)) and np.all(np.isfinite(a)), m.fmt
         v = numpy_values(m)
         sc = numpy_scales(m)
         for s in range(2):
@@ -281,21 +371,53 @@ def pin_constant_codes_closed_form(lib):
     for c in range(8):
         cases.append((5, 64, np.full((3, K // 16), (c & 3) * 0x55555555, np.uint32),
                       np.full((3, K // 32), 0xFFFFFFFF if c & 4 else 0, np.uint32), c - 4))
+    for c in (-127, -3, 0, 64, 127):   # int8 with group scales
+        for gs in (32, 64):
+            cases.append((13, gs, np.full((3, K), c, np.int8), None, c))
+    for code, val in ((0x38, 1.0), (0xD4, -12.0), (0x7E, 448.0), (0x01, 2.0**-9)):   # E4M3
+        cases.append((12, 128, np.full((3, K), code, np.uint8), None, val))
+    for fmt, code, val in ((14, 0x3555, 0.333251953125), (14, 0x8001, -2.0**-24), (11, 0x4049, 3.140625),
+                           (11, 0xBE00, -0.125)):
+        cases.append((fmt, K, np.full((3, K), code, np.uint16), None, val))
+    cases.append((10, K, np.full((3, K), -0.375, np.float32), None, -0.375))
     for fmt, gs, q, q2, val in cases:
         G = K // gs
-        s = synth.rng_for(5, fmt, gs).uniform(1e-3, 2e-2, size=(3, G)).astype(np.float32)
+        if fmt in synth.NO_SCALE_FORMATS:
+            s, srow = None, lambda o: np.ones(G)
+        elif fmt == 12:   # one row block: every row takes block row 0
+            s = synth.rng_for(5, fmt, gs).uniform(1e-3, 2e-2, size=(1, G)).astype(np.float32)
+            srow = lambda o: s[0]
+        else:
+            s = synth.rng_for(5, fmt, gs).uniform(1e-3, 2e-2, size=(3, G)).astype(np.float32)
+            srow = lambda o: s[o]
         m = _qm(fmt, 3, K, gs, q, s, q2=q2)
         y, _ = lib.gemv(m, x[None, :])
         xs = _group_sums(x, gs)
         xa = _group_sums(np.abs(x), gs)
         for o in range(3):
-            want = val * math.fsum(float(s[o, g]) * xs[g] for g in range(G))
-            ref = abs(val) * math.fsum(float(s[o, g]) * xa[g] for g in range(G))
+            sr = srow(o)
+            want = val * math.fsum(float(sr[g]) * xs[g] for g in range(G))
+            ref = abs(val) * math.fsum(float(sr[g]) * xa[g] for g in range(G))
             assert abs(y[0, o] - want) <= 2 * K * 2.0**-52 * ref, (fmt, gs, val, o, y[0, o], want)
+
+
+def pin_fp8_block_scales_closed_form(lib):
+    """E4M3 blocks: all codes 1.0, scale of block (i, j) 2^-(4i + j), x = 1:
+    y[o] = 128 * sum_j 2^-(4 (o // 128) + j), exactly (three row blocks, the
+    last ragged, three column blocks)."""
+    O, K = 300, 384
+    q = np.full((O, K), 0x38, np.uint8)
+    s = np.array([[2.0 ** -(4 * i + j) for j in range(3)] for i in range(3)], np.float32)
+    y, _ = lib.gemv(_qm(12, O, K, 128, q, s), np.ones((1, K), np.float32))
+    for o in range(O):
+        want = 128.0 * sum(2.0 ** -(4 * (o // 128) + j) for j in range(3))
+        assert y[0, o] == want, (o, y[0, o], want)
 
 
 def pin_zero_scales(lib):
     for m in _random_matrices():
+        if m.fmt in synth.NO_SCALE_FORMATS:
+            continue
         m.scales = np.zeros_like(m.scales)
         y, a = lib.gemv(m, synth.activations(2, m.K, 3))
         assert np.all(y == 0) and np.all(a == 0), m.fmt

@@ -34,13 +34,15 @@ MUTANTS = {
                           "return (double)m->scales[k / m->gs];"),
     "e2m1_bias_wrong": ("mag = ldexp(1.0 + 0.5 * mant, expo - 1);", "mag = ldexp(1.0 + 0.5 * mant, expo);"),
     "e2m1_subnormal_wrong": ("mag = 0.5 * mant;", "mag = 1.0 * mant;"),
-    "e2m1_sign_ignored": ("return sign ? -mag : mag;", "return (void)sign, mag;"),
+    "e2m1_sign_ignored": ("    return sign ? -mag : mag;\n}\n\n/* Value of a binary",
+                          "    return (void)sign, mag;\n}\n\n/* Value of a binary"),
     "int3_planes_swapped": ("return low | (high << 2);", "return (low << 1) | high;"),
     "int3_offset_wrong": ("return (double)(int3_code(low_row, high_row, k) - 4);",
                           "return (double)(int3_code(low_row, high_row, k) - 3);"),
     "int3_low_bits_reversed": ("(low_row[k / 16] >> (2 * (k % 16)))", "(low_row[k / 16] >> (30 - 2 * (k % 16)))"),
     "int3_high_bits_reversed": ("(high_row[k / 32] >> (k % 32))", "(high_row[k / 32] >> (31 - k % 32))"),
-    "int8_unsigned": ("return (double)row[k];", "return (double)(uint8_t)row[k];"),
+    "int8_unsigned": ("    case 1: {\n        const int8_t *row = (const int8_t *)m->q + o * m->K;\n        return (double)row[k];",
+                      "    case 1: {\n        const int8_t *row = (const int8_t *)m->q + o * m->K;\n        return (double)(uint8_t)row[k];"),
     "dot_first_term_dropped": ("        sum += term;", "        sum += (k == 0) ? 0.0 : term;"),
     "dot_sign_flipped": ("        double term = orc_weight(m, o, k) * xk;", "        double term = -orc_weight(m, o, k) * xk;"),
     "normaliser_not_absolute": ("        mag += fabs(term);", "        mag += term;"),
@@ -68,6 +70,30 @@ MUTANTS = {
     "route_renorm_ignored": ("            if (renorm)\n                v = v / sum;", "            (void)renorm;"),
     "route_scale_dropped": ("w[t * k + r] = v * w_scale;", "w[t * k + r] = v;"),
     "route_weight_of_wrong_expert": ("w[t * k + r] = p[best];", "w[t * k + r] = p[(best + 1) % E];"),
+    "minifloat_bias_off_by_one": ("int bias = (1 << (ebits - 1)) - 1;", "int bias = (1 << (ebits - 1));"),
+    "minifloat_subnormal_scale": ("mag = ldexp((double)frac, 1 - bias - mbits);",
+                                  "mag = ldexp((double)frac, -bias - mbits);"),
+    "minifloat_implicit_one_dropped": ("mag = ldexp((double)((1u << mbits) + frac), (int)expo - bias - mbits);",
+                                       "mag = ldexp((double)frac, (int)expo - bias - mbits);"),
+    "minifloat_sign_ignored": ("    return sign ? -mag : mag;\n}\n\n/* int3", "    return (void)sign, mag;\n}\n\n/* int3"),
+    "e4m3_read_as_ieee": ("return orc_minifloat(row[k], 4, 3, 0);", "return orc_minifloat(row[k], 4, 3, 1);"),
+    "e4m3_read_as_e5m2": ("return orc_minifloat(row[k], 4, 3, 0);", "return orc_minifloat(row[k], 5, 2, 0);"),
+    "bf16_fields_shifted": ("return orc_minifloat(row[k], 8, 7, 1);", "return orc_minifloat(row[k], 7, 8, 1);"),
+    "f16_odd_column_low": ("        return orc_minifloat(row[k], 5, 10, 1);",
+                           "        return orc_minifloat(row[k ^ 1], 5, 10, 1);"),
+    "f16_read_as_bf16": ("return orc_minifloat(row[k], 5, 10, 1);", "return orc_minifloat(row[k], 8, 7, 1);"),
+    "f32_row_stride_halved": ("        const float *row = (const float *)m->q + o * m->K;",
+                              "        const float *row = (const float *)m->q + o * (m->K / 2);"),
+    "int8_gs_unsigned": ("    case 13: {\n        const int8_t *row = (const int8_t *)m->q + o * m->K;\n        return (double)row[k];",
+                         "    case 13: {\n        const int8_t *row = (const int8_t *)m->q + o * m->K;\n        return (double)(uint8_t)row[k];"),
+    "fp8_block_row_ignored": ("return (double)m->scales[(o / 128) * blocks + k / 128];",
+                              "return (double)m->scales[0 * (o / 128) * blocks + k / 128];"),
+    "fp8_block_axes_swapped": ("return (double)m->scales[(o / 128) * blocks + k / 128];",
+                               "return (double)m->scales[((k / 128) % ((m->O + 127) / 128)) * blocks + (o / 128) % blocks];"),
+    "fp8_block_column_ignored": ("return (double)m->scales[(o / 128) * blocks + k / 128];",
+                                 "return (double)m->scales[(o / 128) * blocks];"),
+    "no_scale_formats_take_f16_scale": ("if (m->fmt == 10 || m->fmt == 11 || m->fmt == 14)\n        return 1.0;",
+                                        "if (m->fmt == 10 || m->fmt == 11 || m->fmt == 14)\n        return m->fmt == 14 ? 0.5 : 1.0;"),
     "token_x_not_advanced": ("mlp_one(&gates[e], &ups[e], &downs[e], x + t * gates[e].K,",
                              "mlp_one(&gates[e], &ups[e], &downs[e], x,"),
 }
@@ -88,6 +114,7 @@ def test_mutant_is_caught(name, tmp_path):
             pin(lib)
         except AssertionError:
             failed.append(pin.__name__)
+            break   # one failing pin is enough
     assert failed, f"mutant {name} passed every pin"
 
 
