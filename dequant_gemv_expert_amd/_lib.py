@@ -11,6 +11,7 @@ import ctypes as C
 import os
 from typing import Optional, Sequence
 
+import numpy as np
 import torch
 
 from . import build as _build
@@ -20,6 +21,7 @@ STATUS = {0: "DQG_OK", -1: "DQG_EINVAL", -2: "DQG_EFORMAT", -3: "DQG_ESHAPE", -4
           -5: "DQG_ELAUNCH", -6: "DQG_ENOMEM", -7: "DQG_EROUTE"}
 
 DQG_I8_ROW, DQG_I4_ROW, DQG_I4_GS, DQG_I3_G64, DQG_MXFP4 = 1, 2, 4, 5, 7
+DQG_F32, DQG_BF16, DQG_FP8_BLOCK, DQG_I8_GS, DQG_F16 = 10, 11, 12, 13, 14
 DQG_ROUTE_SOFTMAX, DQG_ROUTE_SIGMOID = 0, 1
 
 
@@ -124,10 +126,11 @@ def _stream(stream) -> int:
 
 
 class Matrix:
-    """A resident quantised matrix: device tensors q, q2 (fmt 5), scales."""
+    """A resident quantised matrix: device tensors q, q2 (fmt 5), scales
+    (None for the formats without scales: 10 f32, 11 bf16, 14 f16)."""
 
     def __init__(self, fmt: int, O: int, K: int, gs: int, q: torch.Tensor,
-                 scales: torch.Tensor, q2: Optional[torch.Tensor] = None):
+                 scales: Optional[torch.Tensor], q2: Optional[torch.Tensor] = None):
         self.fmt, self.O, self.K, self.gs = int(fmt), int(O), int(K), int(gs)
         self.q, self.q2, self.scales = q, q2, scales
         self.struct = dqg_matrix(self.fmt, self.O, self.K, self.gs, _dev(q, "q"),
@@ -136,12 +139,17 @@ class Matrix:
     @classmethod
     def upload(cls, m, device="cuda") -> "Matrix":
         """Copy a host matrix (fields fmt, O, K, gs, q, q2, scales as numpy) to the GPU."""
-        to = lambda a: None if a is None else torch.from_numpy(a).to(device)
+        def to(a):
+            if a is None:
+                return None
+            if a.dtype == np.uint16:   # bf16 / f16 bits: same bytes, a dtype torch copies everywhere
+                a = a.view(np.int16)
+            return torch.from_numpy(np.ascontiguousarray(a)).to(device)
         return cls(m.fmt, m.O, m.K, m.gs, to(m.q), to(m.scales), to(m.q2))
 
     @property
     def nbytes(self) -> int:
-        n = self.q.numel() * self.q.element_size() + self.scales.numel() * 4
+        n = self.q.numel() * self.q.element_size() + (0 if self.scales is None else self.scales.numel() * 4)
         if self.q2 is not None:
             n += self.q2.numel() * self.q2.element_size()
         return n

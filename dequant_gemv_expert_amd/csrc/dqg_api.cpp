@@ -64,20 +64,47 @@ int ilog2(long v) {
 
 int codec_of(int fmt) {
     switch (fmt) {
-    case DQG_I8_ROW: return C_I8;
+    case DQG_I8_ROW:
+    case DQG_I8_GS: return C_I8;
     case DQG_I4_ROW:
     case DQG_I4_GS: return C_I4;
     case DQG_I3_G64: return C_I3;
     case DQG_MXFP4: return C_FP4;
+    case DQG_F32: return C_F32;
+    case DQG_BF16: return C_BF16;
+    case DQG_FP8_BLOCK: return C_FP8;
+    case DQG_F16: return C_F16;
     }
     return 0;
 }
 
+bool has_scales(int fmt) { return fmt != DQG_F32 && fmt != DQG_BF16 && fmt != DQG_F16; }
+
+// Inputs of one 16-byte code chunk (a whole group of 64 for int3).
 int chunk_inputs(int fmt) {
     switch (fmt) {
-    case DQG_I8_ROW: return 16;
+    case DQG_I8_ROW:
+    case DQG_I8_GS:
+    case DQG_FP8_BLOCK: return 16;
     case DQG_I3_G64: return 64;
+    case DQG_F32: return 4;
+    case DQG_BF16:
+    case DQG_F16: return 8;
     default: return 32;
+    }
+}
+
+// Bytes of codes per input, times 8.
+int code_bits(int fmt) {
+    switch (fmt) {
+    case DQG_I8_ROW:
+    case DQG_I8_GS:
+    case DQG_FP8_BLOCK: return 8;
+    case DQG_I3_G64: return 3;
+    case DQG_F32: return 32;
+    case DQG_BF16:
+    case DQG_F16: return 16;
+    default: return 4;
     }
 }
 
@@ -96,9 +123,21 @@ int check_matrix(const dqg_matrix *W, const char *what, MatDev *out) {
         if (W->gs != W->K) return fail(DQG_EFORMAT, "%s: format %d has one scale per row (gs must be K=%d, got %d)", what, fmt, W->K, W->gs);
         break;
     case DQG_I4_GS:
+    case DQG_I8_GS:
         if (!pow2(W->gs) || W->gs < 32)
             return fail(DQG_EFORMAT, "%s: gs=%d must be a power of two >= 32", what, W->gs);
         if (W->K % W->gs) return fail(DQG_ESHAPE, "%s: K=%d is not a multiple of gs=%d", what, W->K, W->gs);
+        break;
+    case DQG_FP8_BLOCK:
+        if (W->gs != 128) return fail(DQG_EFORMAT, "%s: format 12 has 128 x 128 blocks (gs must be 128, got %d)", what, W->gs);
+        if (W->K % 128) return fail(DQG_ESHAPE, "%s: K=%d is not a multiple of 128 for format 12", what, W->K);
+        break;
+    case DQG_F32:
+    case DQG_BF16:
+    case DQG_F16:
+        if (W->gs != 0 && W->gs != W->K)
+            return fail(DQG_EFORMAT, "%s: format %d has no scales (gs must be 0 or K=%d, got %d)", what, fmt, W->K, W->gs);
+        if (W->scales) return fail(DQG_EINVAL, "%s: format %d has no scales (scales must be NULL)", what, fmt);
         break;
     case DQG_I3_G64:
         if (W->gs != 64) return fail(DQG_EFORMAT, "%s: format 5 has gs 64 (got %d)", what, W->gs);
@@ -108,7 +147,8 @@ int check_matrix(const dqg_matrix *W, const char *what, MatDev *out) {
         break;
     }
     if (!W->q || !aligned(W->q, 16)) return fail(DQG_EINVAL, "%s: q must be a 16-byte aligned device pointer", what);
-    if (!W->scales || !aligned(W->scales, 4)) return fail(DQG_EINVAL, "%s: scales must be a 4-byte aligned device pointer", what);
+    if (has_scales(fmt) && (!W->scales || !aligned(W->scales, 4)))
+        return fail(DQG_EINVAL, "%s: scales must be a 4-byte aligned device pointer", what);
     if (fmt == DQG_I3_G64 && (!W->q2 || !aligned(W->q2, 16)))
         return fail(DQG_EINVAL, "%s: format 5 needs a 16-byte aligned q2 (the 1-bit plane)", what);
     MatDev m{};
@@ -117,13 +157,25 @@ int check_matrix(const dqg_matrix *W, const char *what, MatDev *out) {
     m.s = W->scales;
     m.O = W->O;
     m.K = W->K;
-    switch (fmt) {
-    case DQG_I8_ROW: m.qstride = W->K; break;
-    case DQG_I3_G64: m.qstride = W->K / 4; m.q2stride = W->K / 8; break;
-    default: m.qstride = W->K / 2; break;
+    if (fmt == DQG_I3_G64) {
+        m.qstride = W->K / 4;
+        m.q2stride = W->K / 8;
+    } else {
+        m.qstride = (int32_t)((int64_t)W->K * code_bits(fmt) / 8);
     }
-    m.sstride = W->K / W->gs;
-    m.shift = (W->gs == W->K && (fmt == DQG_I8_ROW || fmt == DQG_I4_ROW)) ? 31 : ilog2(W->gs / cw);
+    m.srow = 0;
+    if (!has_scales(fmt)) {
+        m.s = nullptr;
+        m.sstride = 0;
+        m.shift = 31;
+    } else if (fmt == DQG_I8_ROW || fmt == DQG_I4_ROW) {
+        m.sstride = 1;
+        m.shift = 31;
+    } else {
+        m.sstride = W->K / W->gs;
+        m.shift = ilog2(W->gs / cw);
+        if (fmt == DQG_FP8_BLOCK) m.srow = 7;   // 128 rows share a row of block scales
+    }
     *out = m;
     return DQG_OK;
 }
@@ -139,13 +191,13 @@ int launched(hipError_t e, const char *what) {
 }
 
 uint64_t matrix_bytes(const dqg_matrix *W) {
-    uint64_t codes = (uint64_t)W->O * W->K;
-    switch (W->fmt) {
-    case DQG_I8_ROW: break;
-    case DQG_I3_G64: codes = codes * 3 / 8; break;
-    default: codes /= 2; break;
-    }
-    return codes + (uint64_t)W->O * (W->K / W->gs) * 4;
+    const uint64_t codes = (uint64_t)W->O * W->K * code_bits(W->fmt) / 8;
+    uint64_t scales = 0;
+    if (W->fmt == DQG_FP8_BLOCK)
+        scales = (uint64_t)((W->O + 127) / 128) * (W->K / 128);
+    else if (has_scales(W->fmt))
+        scales = (uint64_t)W->O * (W->K / W->gs);
+    return codes + scales * 4;
 }
 
 constexpr int32_t MAX_S = 256, MAX_K = 64, MAX_SLOTS = 2048;

@@ -22,8 +22,9 @@ struct MatDev {
     int32_t O, K;
     int32_t qstride;    // bytes of codes per row
     int32_t q2stride;   // bytes of the high plane per row (fmt 5)
-    int32_t sstride;    // scales per row
+    int32_t sstride;    // scales per row of scales
     int32_t shift;      // chunk index >> shift = scale index (31 for one scale a row)
+    int32_t srow;       // row >> srow = row of scales (7 for 128-row blocks, else 0)
 };
 
 // One expert's matrices in the device table.
@@ -31,8 +32,9 @@ struct ExpertDev {
     MatDev gate, up, down;
 };
 
-// Codec family a format decodes with (fmt 2 and 4 share the int4 codec).
-enum Codec : int { C_I8 = 1, C_I4 = 4, C_I3 = 5, C_FP4 = 7 };
+// Codec family a format decodes with (fmt 2 and 4 share the int4 codec,
+// fmt 1 and 13 the int8 one).
+enum Codec : int { C_I8 = 1, C_I4 = 4, C_I3 = 5, C_FP4 = 7, C_F32 = 10, C_BF16 = 11, C_FP8 = 12, C_F16 = 14 };
 
 // Launch parameters of the grouped expert call.
 struct GroupArgs {

@@ -30,6 +30,7 @@
 #include <hip/hip_ext.h>
 
 #include <mutex>
+#include <type_traits>
 
 namespace dqg {
 namespace {
@@ -154,6 +155,11 @@ __device__ __forceinline__ float fma_hi(uint32_t pair, float x, float acc) {
 //    formats put the implicit one and the exponent bias in the same places.
 // So weight = (pattern - OFF * 2^-24) * VMUL with VMUL a power of two that
 // folds into the scale; f16 and f32 denormals are kept (IEEE mode).
+//
+// WIDE codecs (f32, bf16 and E4M3 rows) decode to f32 values instead,
+// decode_f(ch, u, v): v[i] multiplies x[unit base + i], with plain f32 FMAs.
+// SCALED is false for the formats without scales (f32, bf16, f16 rows):
+// their scale is the constant 1 and no scale is read.
 // ---------------------------------------------------------------------------
 template <int C>
 struct Codec;
@@ -163,6 +169,7 @@ struct Codec;
 template <>
 struct Codec<C_I8> {
     static constexpr int CW = 16, UNITS = 4, UW = 4;
+    static constexpr bool WIDE = false, SCALED = true;
     static constexpr float VMUL = 16777216.f, OFFS = 128.f / 16777216.f;
     static constexpr int IDX[UW] = {0, 2, 1, 3};
     struct Chunk { uint32_t w[4]; };
@@ -182,6 +189,7 @@ struct Codec<C_I8> {
 template <>
 struct Codec<C_I4> {
     static constexpr int CW = 32, UNITS = 4, UW = 8;
+    static constexpr bool WIDE = false, SCALED = true;
     static constexpr float VMUL = 16777216.f, OFFS = 8.f / 16777216.f;
     static constexpr int IDX[UW] = {0, 4, 1, 5, 2, 6, 3, 7};
     struct Chunk { uint32_t w[4]; };
@@ -205,6 +213,7 @@ struct Codec<C_I4> {
 template <>
 struct Codec<C_FP4> {
     static constexpr int CW = 32, UNITS = 4, UW = 8;
+    static constexpr bool WIDE = false, SCALED = true;
     static constexpr float VMUL = 16384.f, OFFS = 0.f;
     static constexpr int IDX[UW] = {0, 1, 2, 3, 4, 5, 6, 7};
     struct Chunk { uint32_t w[4]; };
@@ -233,6 +242,7 @@ struct Codec<C_FP4> {
 template <>
 struct Codec<C_I3> {
     static constexpr int CW = 64, UNITS = 2, UW = 32;
+    static constexpr bool WIDE = false, SCALED = true;
     static constexpr float VMUL = 16777216.f, OFFS = 4.f / 16777216.f;
     // pair 2m: inputs m, 8+m; pair 2m+1: inputs 16+m, 24+m
     static constexpr int IDX[UW] = {0, 8, 16, 24, 1, 9, 17, 25, 2, 10, 18, 26, 3, 11, 19, 27,
@@ -258,6 +268,83 @@ struct Codec<C_I3> {
             pr[2 * m] = __builtin_amdgcn_perm(0u, q, 0x0C010C00u);
             pr[2 * m + 1] = __builtin_amdgcn_perm(0u, q, 0x0C030C02u);
         }
+    }
+};
+
+// f16 rows: the words are already f16 pairs, the even input in the low half.
+template <>
+struct Codec<C_F16> {
+    static constexpr int CW = 8, UNITS = 2, UW = 4;
+    static constexpr bool WIDE = false, SCALED = false;
+    static constexpr float VMUL = 1.f, OFFS = 0.f;
+    static constexpr int IDX[UW] = {0, 1, 2, 3};
+    struct Chunk { uint32_t w[4]; };
+    __device__ static Chunk load(const GRow &r, uint32_t c) {
+        uint4 v = ld16(r.q, c * 16u);
+        return {{v.x, v.y, v.z, v.w}};
+    }
+    __device__ static void decode(const Chunk &ch, int u, uint32_t (&pr)[UW / 2]) {
+        pr[0] = ch.w[2 * u];
+        pr[1] = ch.w[2 * u + 1];
+    }
+};
+
+// f32 rows: four values a chunk, read as they are.
+template <>
+struct Codec<C_F32> {
+    static constexpr int CW = 4, UNITS = 1, UW = 4;
+    static constexpr bool WIDE = true, SCALED = false;
+    static constexpr float VMUL = 1.f, OFFS = 0.f;
+    struct Chunk { uint32_t w[4]; };
+    __device__ static Chunk load(const GRow &r, uint32_t c) {
+        uint4 v = ld16(r.q, c * 16u);
+        return {{v.x, v.y, v.z, v.w}};
+    }
+    __device__ static void decode_f(const Chunk &ch, int, float (&v)[UW]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = __uint_as_float(ch.w[i]);
+    }
+};
+
+// bf16 rows: a bf16 is the upper half of an f32, so each half of a word
+// becomes an f32 by one shift or one mask (even input in the low half).
+template <>
+struct Codec<C_BF16> {
+    static constexpr int CW = 8, UNITS = 2, UW = 4;
+    static constexpr bool WIDE = true, SCALED = false;
+    static constexpr float VMUL = 1.f, OFFS = 0.f;
+    struct Chunk { uint32_t w[4]; };
+    __device__ static Chunk load(const GRow &r, uint32_t c) {
+        uint4 v = ld16(r.q, c * 16u);
+        return {{v.x, v.y, v.z, v.w}};
+    }
+    __device__ static void decode_f(const Chunk &ch, int u, float (&v)[UW]) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t w = ch.w[2 * u + j];
+            v[2 * j] = __uint_as_float(w << 16);
+            v[2 * j + 1] = __uint_as_float(w & 0xFFFF0000u);
+        }
+    }
+};
+
+// E4M3 (OCP FP8) with one f32 scale per 128 x 128 block: v_cvt_pk_f32_fp8
+// turns two codes into two f32 values, exactly (NaN codes stay NaN).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+template <>
+struct Codec<C_FP8> {
+    static constexpr int CW = 16, UNITS = 4, UW = 4;
+    static constexpr bool WIDE = true, SCALED = true;
+    static constexpr float VMUL = 1.f, OFFS = 0.f;
+    struct Chunk { uint32_t w[4]; };
+    __device__ static Chunk load(const GRow &r, uint32_t c) {
+        uint4 v = ld16(r.q, c * 16u);
+        return {{v.x, v.y, v.z, v.w}};
+    }
+    __device__ static void decode_f(const Chunk &ch, int u, float (&v)[UW]) {
+        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(ch.w[u], false);   // bytes 0, 1
+        const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(ch.w[u], true);    // bytes 2, 3
+        v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
     }
 };
 
@@ -291,7 +378,14 @@ __device__ __forceinline__ int wave_id() {
     return __builtin_amdgcn_readfirstlane((int)(threadIdx.x / WAVE));
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + expf(-z)); }
+// silu(z) = z * sigmoid(z), the sigmoid taken from e = exp(-|z|), which lies
+// in [0, 1]: no intermediate overflows, so for z < -88.7 (where exp(-z)
+// would) the result is still z e^z / (1 + e^z) down to f32's subnormals.
+__device__ __forceinline__ float silu(float z) {
+    const float e = expf(-fabsf(z));
+    const float r = 1.0f / (1.0f + e);
+    return z >= 0.f ? z * r : (z * e) * r;
+}
 
 // SwiGLU with a limit L (swiglu_limit): silu(min(g, L)) * clamp(u, -L, L).
 // L = +inf leaves g and u unchanged, bit for bit; a NaN stays NaN.
@@ -330,7 +424,7 @@ __device__ __forceinline__ void step_load_w(Step<C, NR, SM> &st, const GRow (&ro
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
         st.ch[r] = Cd::load(rows[r], cu);
-        st.sc[r] = ldf(rows[r].s, si);
+        st.sc[r] = Cd::SCALED ? ldf(rows[r].s, si) : 1.f;
     }
 }
 
@@ -372,15 +466,24 @@ __device__ __forceinline__ void step_compute(const Step<C, NR, SM> &st, float (&
     for (int u = 0; u < Cd::UNITS; ++u) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            uint32_t pr[Cd::UW / 2];
-            Cd::decode(st.ch[r], u, pr);
+            if constexpr (Cd::WIDE) {
+                float v[Cd::UW];
+                Cd::decode_f(st.ch[r], u, v);
 #pragma unroll
-            for (int s = 0; s < SM; ++s)
+                for (int s = 0; s < SM; ++s)
 #pragma unroll
-                for (int q = 0; q < Cd::UW / 2; ++q) {
-                    p[r][s] = fma_lo(pr[q], st.xv[s][u * Cd::UW + Cd::IDX[2 * q]], p[r][s]);
-                    p[r][s] = fma_hi(pr[q], st.xv[s][u * Cd::UW + Cd::IDX[2 * q + 1]], p[r][s]);
-                }
+                    for (int i = 0; i < Cd::UW; ++i) p[r][s] = fmaf(v[i], st.xv[s][u * Cd::UW + i], p[r][s]);
+            } else {
+                uint32_t pr[Cd::UW / 2];
+                Cd::decode(st.ch[r], u, pr);
+#pragma unroll
+                for (int s = 0; s < SM; ++s)
+#pragma unroll
+                    for (int q = 0; q < Cd::UW / 2; ++q) {
+                        p[r][s] = fma_lo(pr[q], st.xv[s][u * Cd::UW + Cd::IDX[2 * q]], p[r][s]);
+                        p[r][s] = fma_hi(pr[q], st.xv[s][u * Cd::UW + Cd::IDX[2 * q + 1]], p[r][s]);
+                    }
+            }
         }
     }
 #pragma unroll
@@ -458,15 +561,24 @@ __device__ __forceinline__ void step_compute_lds(const Step<C, NR, SM> &st, lflo
         }
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            uint32_t pr[Cd::UW / 2];
-            Cd::decode(st.ch[r], u, pr);
+            if constexpr (Cd::WIDE) {
+                float v[Cd::UW];
+                Cd::decode_f(st.ch[r], u, v);
 #pragma unroll
-            for (int s = 0; s < SM; ++s)
+                for (int s = 0; s < SM; ++s)
 #pragma unroll
-                for (int q = 0; q < Cd::UW / 2; ++q) {
-                    p[r][s] = fma_lo(pr[q], xv[s][Cd::IDX[2 * q]], p[r][s]);
-                    p[r][s] = fma_hi(pr[q], xv[s][Cd::IDX[2 * q + 1]], p[r][s]);
-                }
+                    for (int i = 0; i < Cd::UW; ++i) p[r][s] = fmaf(v[i], xv[s][i], p[r][s]);
+            } else {
+                uint32_t pr[Cd::UW / 2];
+                Cd::decode(st.ch[r], u, pr);
+#pragma unroll
+                for (int s = 0; s < SM; ++s)
+#pragma unroll
+                    for (int q = 0; q < Cd::UW / 2; ++q) {
+                        p[r][s] = fma_lo(pr[q], xv[s][Cd::IDX[2 * q]], p[r][s]);
+                        p[r][s] = fma_hi(pr[q], xv[s][Cd::IDX[2 * q + 1]], p[r][s]);
+                    }
+            }
         }
     }
 #pragma unroll
@@ -498,13 +610,13 @@ __device__ __forceinline__ void dot_rows_lds1(Step<C, NR, 1> &st, bool have, con
 // read with vector loads.
 __device__ __forceinline__ GRow row_ptrs(const MatDev &m, int row) {
     return {gb(m.q + (size_t)row * m.qstride), gb(m.q2 + (size_t)row * m.q2stride),
-            gf(m.s + (size_t)row * m.sstride)};
+            gf(m.s + (size_t)(row >> m.srow) * m.sstride)};
 }
 
 // Pointers of a row that may differ from lane to lane (the dequant kernel).
 __device__ __forceinline__ GRow lane_row_ptrs(const MatDev &m, int row) {
     return {(gbytes)(m.q + (size_t)row * m.qstride), (gbytes)(m.q2 + (size_t)row * m.q2stride),
-            (gfloats)(m.s + (size_t)row * m.sstride)};
+            (gfloats)(m.s + (size_t)(row >> m.srow) * m.sstride)};
 }
 
 // ---------------------------------------------------------------------------
@@ -656,18 +768,26 @@ __global__ void __launch_bounds__(256) k_dequant(MatDev m, float *__restrict__ o
     const int row = (int)(idx / nch), c = (int)(idx % nch);
     const GRow rp = lane_row_ptrs(m, row);
     const typename Cd::Chunk ch = Cd::load(rp, (uint32_t)c);
-    const float sc = ldf(rp.s, (uint32_t)c >> m.shift);
+    const float sc = Cd::SCALED ? ldf(rp.s, (uint32_t)c >> m.shift) : 1.f;
     float *o = out + (size_t)row * m.K + (size_t)c * Cd::CW;
 #pragma unroll
     for (int u = 0; u < Cd::UNITS; ++u) {
-        uint32_t pr[Cd::UW / 2];
-        Cd::decode(ch, u, pr);
         float v[Cd::UW];
+        if constexpr (Cd::WIDE) {
+            Cd::decode_f(ch, u, v);
+            if constexpr (Cd::SCALED) {
 #pragma unroll
-        for (int q = 0; q < Cd::UW / 2; ++q) {
-            const half2_t h = __builtin_bit_cast(half2_t, pr[q]);
-            v[Cd::IDX[2 * q]] = (((float)h.x - Cd::OFFS) * Cd::VMUL) * sc;
-            v[Cd::IDX[2 * q + 1]] = (((float)h.y - Cd::OFFS) * Cd::VMUL) * sc;
+                for (int i = 0; i < Cd::UW; ++i) v[i] *= sc;
+            }
+        } else {
+            uint32_t pr[Cd::UW / 2];
+            Cd::decode(ch, u, pr);
+#pragma unroll
+            for (int q = 0; q < Cd::UW / 2; ++q) {
+                const half2_t h = __builtin_bit_cast(half2_t, pr[q]);
+                v[Cd::IDX[2 * q]] = (((float)h.x - Cd::OFFS) * Cd::VMUL) * sc;
+                v[Cd::IDX[2 * q + 1]] = (((float)h.y - Cd::OFFS) * Cd::VMUL) * sc;
+            }
         }
 #pragma unroll
         for (int i = 0; i < Cd::UW; i += 4)
@@ -1005,6 +1125,35 @@ struct GemmCodec<C_I8> {
     }
 };
 
+// E4M3 -> f32 -> f16 pairs: every E4M3 value is an f16, so both steps are exact.
+template <>
+struct GemmCodec<C_FP8> {
+    static constexpr int PERM[8] = {0, 1, 2, 3, 4, 5, 6, 7};
+    using Raw = u32x2;
+    __device__ static Raw load(gbytes row, uint32_t k) { return *(const GLOBAL u32x2 *)(row + k); }
+    __device__ static void decode(Raw w, uint32_t (&pr)[4]) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t v = j ? w.y : w.x;
+            const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(v, false);
+            const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(v, true);
+            pr[2 * j] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a.x, a.y));
+            pr[2 * j + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(b.x, b.y));
+        }
+    }
+};
+
+// f16 rows: the 16 bytes of 8 inputs are the operand as they stand.
+template <>
+struct GemmCodec<C_F16> {
+    static constexpr int PERM[8] = {0, 1, 2, 3, 4, 5, 6, 7};
+    using Raw = u32x4;
+    __device__ static Raw load(gbytes row, uint32_t k) { return *(const GLOBAL u32x4 *)(row + 2 * k); }
+    __device__ static void decode(Raw w, uint32_t (&pr)[4]) {
+        pr[0] = w.x; pr[1] = w.y; pr[2] = w.z; pr[3] = w.w;
+    }
+};
+
 // A k-step is GK(NC) inputs: 512 for one token tile, 256 for two, 128 for
 // four, so that the staged x' (16 NC tokens x GK, hi and lo) stays near
 // 34 KB and batches of few tokens take few, long steps (each step exposes one
@@ -1088,7 +1237,11 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
             const MatDev &m = (GU && st == 1) ? m1 : m0;
             const int row = min(gemm_row<GU>(block_row, sw, st, sr), O - 1);
             const int k = k0 + 32 * j;
-            sc_n[h] = j < nwin ? m.s[(size_t)row * m.sstride + ((uint32_t)(k / Cd::CW) >> m.shift)] * Cd::VMUL : 0.f;
+            if constexpr (Cd::SCALED)
+                sc_n[h] = j < nwin ? m.s[(size_t)(row >> m.srow) * m.sstride + ((uint32_t)(k / Cd::CW) >> m.shift)] * Cd::VMUL
+                                   : 0.f;
+            else
+                sc_n[h] = Cd::VMUL;
         }
     };
     fetch(0);
@@ -1347,12 +1500,18 @@ hipError_t go_matmul(const MatDev &m, const float *x, int S, float *y, hipStream
 constexpr int GEMM_MIN_S = 16, GEMM_MIN_S_GU = 32;
 
 template <int C>
-constexpr bool gemm_codec() { return C == C_I8 || C == C_I4 || C == C_FP4; }
+constexpr bool gemm_codec() { return C == C_I8 || C == C_I4 || C == C_FP4 || C == C_FP8 || C == C_F16; }
+
+// Code registers per step: GWIN windows x 2 row tiles x Raw, at most 32 VGPRs
+// (and as many for the next step's requests), so the formats with more code
+// bytes per input take shorter steps: NC >= Raw words.
+template <int C>
+constexpr int gemm_min_nc() { return (int)(sizeof(typename GemmCodec<C>::Raw) / 4); }
 
 template <int C, bool GU, int NC>
 hipError_t go_gemm_nc(const MatDev &m0, const MatDev &m1, const float *x, int S, float *y, float L,
                       hipStream_t st, const char *name) {
-    static_assert(C != C_I8 || NC >= 2, "int8 steps hold at most 256 inputs");
+    static_assert(NC >= gemm_min_nc<C>(), "a step's codes must fit 32 registers");
     const int rows_per_block = GU ? GROWS / 2 : GROWS;
     dim3 grid((m0.O + rows_per_block - 1) / rows_per_block, (S + 16 * NC - 1) / (16 * NC));
     launch(name, (k_gemm<C, GU, NC>), grid, dim3(256), 0, st, m0, m1, x, S, y, L);
@@ -1364,10 +1523,11 @@ hipError_t go_gemm(const MatDev &m0, const MatDev &m1, const float *x, int S, fl
     // token tiles per block: fewer for smaller batches, so that the grid has
     // enough blocks (at least 4 token blocks per row block up to 256 tokens)
     const char *name = GU ? "gemm_gate_up" : "gemm";
-    // int8 holds twice the code registers per step: at most 256 inputs a step
-    if constexpr (C != C_I8)
+    // int8 and E4M3 hold twice int4's code registers per step, f16 four times
+    if constexpr (gemm_min_nc<C>() <= 1)
         if (S <= 64) return go_gemm_nc<C, GU, 1>(m0, m1, x, S, y, L, st, name);
-    if (S <= 128) return go_gemm_nc<C, GU, 2>(m0, m1, x, S, y, L, st, name);
+    if constexpr (gemm_min_nc<C>() <= 2)
+        if (S <= 128) return go_gemm_nc<C, GU, 2>(m0, m1, x, S, y, L, st, name);
     return go_gemm_nc<C, GU, 4>(m0, m1, x, S, y, L, st, name);
 }
 
@@ -1449,27 +1609,31 @@ hipError_t group_b(const GroupArgs &a, hipStream_t st) {
     else return a.S == 1 ? group_b_cap<C, 1>(a, st) : a.S == 2 ? group_b_cap<C, 2>(a, st) : group_b_cap<C, 4>(a, st);
 }
 
-}  // namespace
-
-hipError_t launch_matmul(int codec, const MatDev &m, const float *x, int S, float *y, hipStream_t st) {
+// Calls f(std::integral_constant<int, C>) for the codec of a run-time id.
+template <typename F>
+hipError_t with_codec(int codec, F &&f) {
     switch (codec) {
-    case C_I8: return matmul_c<C_I8>(m, x, S, y, st);
-    case C_I4: return matmul_c<C_I4>(m, x, S, y, st);
-    case C_I3: return matmul_c<C_I3>(m, x, S, y, st);
-    case C_FP4: return matmul_c<C_FP4>(m, x, S, y, st);
+    case C_I8: return f(std::integral_constant<int, C_I8>{});
+    case C_I4: return f(std::integral_constant<int, C_I4>{});
+    case C_I3: return f(std::integral_constant<int, C_I3>{});
+    case C_FP4: return f(std::integral_constant<int, C_FP4>{});
+    case C_F32: return f(std::integral_constant<int, C_F32>{});
+    case C_BF16: return f(std::integral_constant<int, C_BF16>{});
+    case C_FP8: return f(std::integral_constant<int, C_FP8>{});
+    case C_F16: return f(std::integral_constant<int, C_F16>{});
     }
     return hipErrorInvalidValue;
 }
 
+}  // namespace
+
+hipError_t launch_matmul(int codec, const MatDev &m, const float *x, int S, float *y, hipStream_t st) {
+    return with_codec(codec, [&](auto c) { return matmul_c<decltype(c)::value>(m, x, S, y, st); });
+}
+
 hipError_t launch_gate_up(int codec, const MatDev &g, const MatDev &u, const float *x, int S,
                           float *h, float limit, hipStream_t st) {
-    switch (codec) {
-    case C_I8: return gate_up_c<C_I8>(g, u, x, S, h, limit, st);
-    case C_I4: return gate_up_c<C_I4>(g, u, x, S, h, limit, st);
-    case C_I3: return gate_up_c<C_I3>(g, u, x, S, h, limit, st);
-    case C_FP4: return gate_up_c<C_FP4>(g, u, x, S, h, limit, st);
-    }
-    return hipErrorInvalidValue;
+    return with_codec(codec, [&](auto c) { return gate_up_c<decltype(c)::value>(g, u, x, S, h, limit, st); });
 }
 
 hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
@@ -1484,32 +1648,14 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
 }
 
 hipError_t launch_dequant(int codec, const MatDev &m, float *out, hipStream_t st) {
-    switch (codec) {
-    case C_I8: return dequant_c<C_I8>(m, out, st);
-    case C_I4: return dequant_c<C_I4>(m, out, st);
-    case C_I3: return dequant_c<C_I3>(m, out, st);
-    case C_FP4: return dequant_c<C_FP4>(m, out, st);
-    }
-    return hipErrorInvalidValue;
+    return with_codec(codec, [&](auto c) { return dequant_c<decltype(c)::value>(m, out, st); });
 }
 
 hipError_t launch_group(int codec_gu, int codec_down, const GroupArgs &a, hipStream_t st, int *launches) {
-    hipError_t e = hipErrorInvalidValue;
-    switch (codec_gu) {
-    case C_I8: e = group_a<C_I8>(a, st); break;
-    case C_I4: e = group_a<C_I4>(a, st); break;
-    case C_I3: e = group_a<C_I3>(a, st); break;
-    case C_FP4: e = group_a<C_FP4>(a, st); break;
-    }
+    hipError_t e = with_codec(codec_gu, [&](auto c) { return group_a<decltype(c)::value>(a, st); });
     if (e != hipSuccess) return e;
     ++*launches;
-    e = hipErrorInvalidValue;
-    switch (codec_down) {
-    case C_I8: e = group_b<C_I8>(a, st); break;
-    case C_I4: e = group_b<C_I4>(a, st); break;
-    case C_I3: e = group_b<C_I3>(a, st); break;
-    case C_FP4: e = group_b<C_FP4>(a, st); break;
-    }
+    e = with_codec(codec_down, [&](auto c) { return group_b<decltype(c)::value>(a, st); });
     if (e == hipSuccess) ++*launches;
     return e;
 }

@@ -21,6 +21,15 @@
  *   DQG_I3_G64  (5)  int3 in two bit planes, value = code - 4, one f32 scale per 64
  *   DQG_MXFP4   (7)  e2m1 nibbles, bit 3 the sign, one f32 scale per 32
  *                    (the e8m0 scale pre-expanded to f32 by the host)
+ *   DQG_F32     (10) f32 rows, no scales
+ *   DQG_BF16    (11) bf16 rows, no scales
+ *   DQG_FP8_BLOCK (12) OCP FP8 E4M3 (no infinities, S.1111.111 NaN), one
+ *                    f32 scale per block of 128 rows x 128 inputs
+ *   DQG_I8_GS   (13) int8, two's complement, one f32 scale per gs inputs
+ *   DQG_F16     (14) f16 rows, no scales
+ * (formats 10 to 14: the same engine table, the qwen36 and qwen38 rows, and
+ * the f16-rows paragraph of that page: no scales, the even column in the
+ * low half of a word, as for bf16.)
  *
  * Storage of one matrix W with O rows of K inputs (all row-major):
  *   fmt 1:        q = int8 [O][K]                          scales = f32 [O]
@@ -32,8 +41,16 @@
  *                 q2 = uint32 [O][K/32]: 1 bit per input, input k at bit
  *                      (k mod 32) of word k/32;
  *                 code = low | high << 2               scales = f32 [O][K/64]
- * (The pages do not fix nibble order or plane bit order; these are the
- * readings this library and its tests use.)
+ *   fmt 10:       q = f32 [O][K]                           scales = NULL
+ *   fmt 11, 14:   q = uint16 [O][K] (bf16 or f16 bits, little-endian, so
+ *                 the even input is the low half of each 32-bit word)
+ *                                                          scales = NULL
+ *   fmt 12:       q = uint8 [O][K] (E4M3 bits)
+ *                                          scales = f32 [ceil(O/128)][K/128]
+ *                 (weight (o, k) takes scale [o/128][k/128])
+ *   fmt 13:       q = int8 [O][K]                          scales = f32 [O][K/gs]
+ * (The pages do not fix nibble order, plane bit order or the layout of the
+ * FP8 block scales; these are the readings this library and its tests use.)
  *
  * A weight is value * scale.  y[s][o] = sum_k W[o][k] * x[s][k] in f32.
  * Results match a double-precision evaluation of that sum to within 1e-5
@@ -81,13 +98,20 @@ enum {
     DQG_I4_ROW = 2,
     DQG_I4_GS = 4,
     DQG_I3_G64 = 5,
-    DQG_MXFP4 = 7
+    DQG_MXFP4 = 7,
+    DQG_F32 = 10,
+    DQG_BF16 = 11,
+    DQG_FP8_BLOCK = 12,
+    DQG_I8_GS = 13,
+    DQG_F16 = 14
 };
 
 /* One resident quantised matrix (device pointers, caller-owned).
  * gs: inputs per scale; K for fmt 1 and 2, a power of two >= 32 dividing K
- * for fmt 4, 64 for fmt 5, 32 for fmt 7.  K must be a multiple of 16
- * (fmt 1), 32 (fmt 2, 4, 7) or 64 (fmt 5).  q2 is used by fmt 5 only. */
+ * for fmt 4 and 13, 64 for fmt 5, 32 for fmt 7, 128 for fmt 12, 0 or K for
+ * the formats without scales (10, 11, 14), whose scales must be NULL.
+ * K must be a multiple of 16 (fmt 1), 32 (fmt 2, 4, 7), 64 (fmt 5), 128
+ * (fmt 12), 4 (fmt 10) or 8 (fmt 11, 14).  q2 is used by fmt 5 only. */
 typedef struct {
     int32_t fmt;
     int32_t O;

@@ -60,6 +60,22 @@ FAKE_X, FAKE_Y = 0x30000, 0x40000   # never dereferenced: each call below fails 
     (_mat(q=0x10008), -1),
     (_mat(s=0x20002), -1),
     (_mat(fmt=5, gs=64, q2=0), -1),
+    # formats without scales: gs 0 or K, scales NULL
+    (_mat(fmt=10, K=256, gs=32, s=0), -2),
+    (_mat(fmt=11, K=256, gs=256), -1),            # a scales pointer given
+    (_mat(fmt=14, K=100, gs=0, s=0), -3),         # K not a multiple of 8
+    (_mat(fmt=10, K=6, gs=0, s=0), -3),           # K not a multiple of 4
+    # E4M3 blocks: gs 128, K a multiple of 128, scales required
+    (_mat(fmt=12, K=256, gs=64), -2),
+    (_mat(fmt=12, K=192, gs=128), -3),
+    (_mat(fmt=12, K=256, gs=128, s=0), -1),
+    # int8 with group scales
+    (_mat(fmt=13, K=256, gs=16), -2),
+    (_mat(fmt=13, K=256, gs=48), -2),
+    (_mat(fmt=13, K=96, gs=64), -3),
+    (_mat(fmt=13, K=256, gs=64, s=0), -1),
+    (_mat(fmt=9), -2),
+    (_mat(fmt=15), -2),
 ])
 def test_matrix_validation(lib, mat, code):
     rc = lib.dqg_matmul(C.byref(mat), FAKE_X, 1, FAKE_Y, None)

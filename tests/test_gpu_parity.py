@@ -14,7 +14,7 @@ import torch
 import oracle
 import pinlib
 import synth
-from gpu_helpers import (HostExperts, TOL, assert_close, dev_f32, dev_i32, host, log,
+from gpu_helpers import (HostExperts, TOL, assert_close, check_group, dev_f32, dev_i32, host, log,
                          upload_experts)
 
 pytestmark = pytest.mark.gpu
@@ -167,31 +167,6 @@ def _small_group(n, fmt=4, gs=32, H=256, I=128, seed=4000, **kw):
     return hs, table
 
 
-def _check_group(hs, table, ids, w, shared, x, what):
-    S, k = ids.shape
-    scratch = table.scratch(S, k)
-    ticket, y, _ = dq.dqg_expert_group_issue(table, dev_i32(ids), dev_f32(w), shared, dev_f32(x),
-                                             scratch=scratch)
-    dq.dqg_expert_group_take(ticket)   # raises on an out-of-range id or a wait past its bound
-    y = host(y)
-    yr, a = oracle.expert_group(hs, ids, w, shared, x)
-    worst = assert_close(y, yr, a, what)
-    # stage check: h of every valid slot in scratch
-    I = table.I
-    off = 1024   # DQG_SCRATCH_H_OFFSET
-    hdev = host(scratch[off: off + (S * k + S) * I * 4].view(torch.float32)).reshape(S * k + S, I)
-    for t in range(S):
-        for r in range(k):
-            e = int(ids[t, r])
-            if 0 <= e < len(hs):
-                o = oracle.gate_up(hs[e].gate, hs[e].up, x[t:t + 1])
-                assert_close(hdev[t * k + r][None], o["h"], o["nh"], f"{what} h[{t},{r}]")
-        if shared is not None and shared >= 0:
-            o = oracle.gate_up(hs[shared].gate, hs[shared].up, x[t:t + 1])
-            assert_close(hdev[S * k + t][None], o["h"], o["nh"], f"{what} h[shared {t}]")
-    return y, worst
-
-
 @pytest.mark.parametrize("S", [1, 2, 3, 4, 5, 8])
 @pytest.mark.parametrize("shared", [True, False])
 def test_group_small(S, shared):
@@ -199,7 +174,7 @@ def test_group_small(S, shared):
     hs, table = _small_group(E + 1)
     ids, w = synth.routing(S, E, k, 4100 + S)
     x = synth.activations(S, 256, 4200 + S)
-    _check_group(hs, table, ids, w, E if shared else None, x, f"group S={S} shared={shared}")
+    check_group(hs, table, ids, w, E if shared else None, x, f"group S={S} shared={shared}")
 
 
 @pytest.mark.parametrize("fmts", [(7, 32, 4, 32), (4, 64, 1, None), (1, None, 7, 32), (5, 64, 4, 32)])
@@ -208,7 +183,7 @@ def test_group_mixed_formats(fmts):
     hs, table = _small_group(7, fmt=fmt, gs=gs, down_fmt=dfmt, down_gs=dgs, seed=4300)
     ids, w = synth.routing(3, 6, 3, 4301)
     x = synth.activations(3, 256, 4302)
-    _check_group(hs, table, ids, w, 6, x, f"group mixed {fmts}")
+    check_group(hs, table, ids, w, 6, x, f"group mixed {fmts}")
 
 
 def test_group_many_slots():
@@ -216,7 +191,7 @@ def test_group_many_slots():
     hs, table = _small_group(20)
     ids, w = synth.routing(20, 19, 8, 4400)
     x = synth.activations(20, 256, 4401)
-    _check_group(hs, table, ids, w, 19, x, "group S=20 k=8")
+    check_group(hs, table, ids, w, 19, x, "group S=20 k=8")
 
 
 def test_group_repeated_id_in_a_token():
@@ -224,7 +199,7 @@ def test_group_repeated_id_in_a_token():
     ids = np.array([[3, 3, 5, 7], [5, 1, 3, 3]], np.int32)
     w = np.array([[0.4, 0.3, 0.2, 0.1], [0.25, 0.25, 0.25, 0.25]], np.float32)
     x = synth.activations(2, 256, 4500)
-    _check_group(hs, table, ids, w, 0, x, "group repeated ids")
+    check_group(hs, table, ids, w, 0, x, "group repeated ids")
 
 
 def test_group_batch_invariant():
