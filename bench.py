@@ -70,7 +70,7 @@ def profiled_traffic(kernel: str):
 
 
 def matrix_bytes(m) -> int:
-    n = m.q.nbytes + m.scales.nbytes
+    n = m.q.nbytes + (0 if m.scales is None else m.scales.nbytes)
     if m.q2 is not None:
         n += m.q2.nbytes
     return n
@@ -304,7 +304,8 @@ def main():
 
 
 MFMA_F16_PEAK_TFLOPS = 2500.0   # MI355X dense f16 matrix-core peak
-GEMM_MIN_TOKENS = 16               # dqg_matmul's matrix-core route starts here (int8, int4, MXFP4)
+GEMM_MIN_TOKENS = 16               # dqg_matmul's matrix-core route starts here
+GEMM_FORMATS = (1, 2, 4, 7, 12, 13, 14)   # the formats that decode exactly to f16 take it
 
 
 def bench_gemv(args, c):
@@ -326,12 +327,12 @@ def bench_gemv(args, c):
     torch.cuda.set_device(0)
     dev_name = torch.cuda.get_device_name(0)
     hm = synth.matrix(fmt, O, K, gs, seed, 0)
-    w_bytes = hm.q.nbytes + hm.scales.nbytes + (0 if hm.q2 is None else hm.q2.nbytes)
+    w_bytes = matrix_bytes(hm)
     copies = max(2, min(256, (2 << 30) // w_bytes))
     mats = [dq.Matrix.upload(hm) for _ in range(copies)]
     x = torch.from_numpy(synth.activations(S, K, seed, 9, S)).cuda()
     y = torch.empty((S, O), dtype=torch.float32, device="cuda")
-    gemm = S >= GEMM_MIN_TOKENS and fmt in (1, 2, 4, 7) and K % 32 == 0
+    gemm = S >= GEMM_MIN_TOKENS and fmt in GEMM_FORMATS and K % 32 == 0
     log(f"[bench] {dev_name}: {copies} copies of {args.workload} ({w_bytes / 1e6:.2f} MB each), "
         f"S = {S}, {'matrix-core GEMM' if gemm else 'per-row GEMV'} route")
     # ctypes arguments prepared up front, so the timed loop is the C calls
@@ -383,8 +384,9 @@ def bench_gemv(args, c):
     if not args.no_cpu_baseline:
         import oracle
         rows = max(1, min(O, int(O * 0.05)))
+        srows = -(-rows // synth.FP8_BLOCK) if fmt == synth.FMT_FP8_BLOCK else rows   # whole scale blocks
         sub = synth.QMatrix(hm.fmt, rows, hm.K, hm.gs, hm.q[:rows], None if hm.q2 is None else hm.q2[:rows],
-                            hm.scales[:rows])
+                            None if hm.scales is None else hm.scales[:srows])
         xs = x.cpu().numpy()
         spent, calls = 0.0, 0
         while spent < args.cpu_seconds and calls < 1_000_000:

@@ -266,4 +266,14 @@ WORKLOADS = {
     "mxfp4_expert_group_384top8_s8": dict(kind="group", fmt=FMT_MXFP4, H=7168, I=2048, gs=32, E=384, k=8,
                                           shared=False, S=(8,), seed=BASE_SEED + 4),
     "int3g64_gemv_6144x16384": dict(kind="gemv", fmt=FMT_I3_G64, O=6144, K=16384, gs=64, S=(1,), seed=BASE_SEED + 5),
+    # the other device formats on the dense 6144 x 6144 shape
+    "f32_gemv_6144x6144": dict(kind="gemv", fmt=FMT_F32, O=6144, K=6144, gs=None, S=(1, 4), seed=BASE_SEED + 6),
+    "bf16_gemv_6144x6144": dict(kind="gemv", fmt=FMT_BF16, O=6144, K=6144, gs=None, S=(1, 4), seed=BASE_SEED + 7),
+    "fp8b128_gemv_6144x6144": dict(kind="gemv", fmt=FMT_FP8_BLOCK, O=6144, K=6144, gs=None, S=(1, 4),
+                                   seed=BASE_SEED + 8),
+    "int8gs64_gemv_6144x6144": dict(kind="gemv", fmt=FMT_I8_GS, O=6144, K=6144, gs=64, S=(1, 4), seed=BASE_SEED + 9),
+    "f16_gemv_6144x6144": dict(kind="gemv", fmt=FMT_F16, O=6144, K=6144, gs=None, S=(1, 4), seed=BASE_SEED + 10),
+    # E4M3 experts in 128 x 128 blocks on the expert-group shape
+    "fp8b128_expert_group_256top8_shared": dict(kind="group", fmt=FMT_FP8_BLOCK, H=6144, I=2048, gs=None, E=256,
+                                                k=8, shared=True, S=(1, 2, 4), seed=BASE_SEED + 11),
 }

@@ -229,3 +229,24 @@ def test_full_size_6144(fmt, S):
     y = host(dq.dqg_matmul(up(m), dev_f32(x)))
     yr, a = oracle.gemv(m, x)
     log(f"  worst normalised error {assert_close(y, yr, a, f'fmt {fmt} 6144 S={S}'):.2e}")
+
+
+def test_full_size_fp8_group_256top8_shared():
+    """The E4M3 expert group on the 6144 x 2048 shape, 257 experts, 2 tokens."""
+    import gc
+    from gpu_helpers import HostExperts, dev_i32, upload_experts
+    c = synth.WORKLOADS["fp8b128_expert_group_256top8_shared"]
+    S = 2
+    ids, w = synth.routing(S, c["E"], c["k"], c["seed"], S)
+    keep = set(ids.ravel().tolist()) | {c["E"]}
+    log(f"  drawing {c['E'] + 1} E4M3 experts ({len(keep)} kept on the host)")
+    dev, hosts = upload_experts(c["fmt"], c["H"], c["I"], c["gs"], c["seed"], c["E"] + 1, keep=keep)
+    table = dq.ExpertTable(dev)
+    x = synth.activations(S, c["H"], c["seed"], 300)
+    y = host(dq.dqg_expert_group(table, dev_i32(ids), dev_f32(w), c["E"], dev_f32(x)))
+    yr, a = oracle.expert_group(HostExperts(c["E"] + 1, hosts), ids, w, c["E"], x)
+    log(f"  worst normalised error {assert_close(y, yr, a, 'fp8 group S=2'):.2e}")
+    table.close()
+    del dev, table
+    gc.collect()
+    torch.cuda.empty_cache()
