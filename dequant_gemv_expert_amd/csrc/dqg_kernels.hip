@@ -69,10 +69,12 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 #ifndef DQG_NT
-#define DQG_NT 0
+#define DQG_NT 1
 #endif
-// Weight codes are read once per call: DQG_NT=1 marks those loads
-// non-temporal so that they do not displace x and h in the caches.
+// Weight codes are read once per call, so their loads are non-temporal:
+// they do not displace x, h and the descriptors in the caches (measured on
+// MI355X: the int4-g32 group's gate/up launch 29.3 -> 28.2 us at 1 token;
+// a plain read of the same bytes 24.0 -> 22.3 us).
 __device__ __forceinline__ uint4 ld16(gbytes base, uint32_t off) {
     const GLOBAL u32x4 *p = (const GLOBAL u32x4 *)(base + off);
     const u32x4 v = DQG_NT ? __builtin_nontemporal_load(p) : *p;
@@ -96,14 +98,34 @@ __device__ __forceinline__ float ldf(gfloats base, uint32_t idx) {
 typedef LDS float *lfloats_w;
 typedef const LDS float *lfloats;
 
+// Layout of x in LDS.  A wave's lanes read x one code chunk apart (CW
+// inputs: 128 bytes for int4 and MXFP4, 256 for int3), which at those
+// strides puts every lane of a 16-byte read on the same LDS banks.  In LDS
+// each chunk's slice of x is therefore followed by 4 floats of padding:
+// lane strides of 144 and 272 bytes reach every bank (measured on MI355X:
+// 127 -> 35 cycles per wave-wide 16-byte read at a 128-byte stride, 257 at
+// 256 bytes).  Chunks of 16 inputs (a 64-byte stride, 2-way conflicts)
+// stay unpadded: the padding's address arithmetic cost the one-token int8
+// launch its register budget.  Chunks of 8 or fewer are conflict-free.
+template <int CW>
+__host__ __device__ constexpr int x_pad() { return CW >= 32 ? 4 : 0; }
+// LDS floats of n inputs of x (n a multiple of CW), and the LDS index of input k
+template <int CW>
+__host__ __device__ constexpr int x_lds_len(int n) { return n + x_pad<CW>() * (n / CW); }
+template <int CW>
+__device__ __forceinline__ uint32_t x_lds_at(uint32_t k) { return k + x_pad<CW>() * (k / CW); }
+
 struct XGlobal {
     gfloats p;
-    __device__ __forceinline__ float4 load4(uint32_t idx) const { return ldf4(p, idx); }
+    // 4 inputs at offset off (a multiple of 4) of chunk cu
+    template <int CW>
+    __device__ __forceinline__ float4 load4(uint32_t cu, uint32_t off) const { return ldf4(p, cu * CW + off); }
 };
 struct XLds {
-    lfloats p;
-    __device__ __forceinline__ float4 load4(uint32_t idx) const {
-        const f32x4 v = *(const LDS f32x4 *)(p + idx);
+    lfloats p;   // the token's row, laid out by x_lds_at
+    template <int CW>
+    __device__ __forceinline__ float4 load4(uint32_t cu, uint32_t off) const {
+        const f32x4 v = *(const LDS f32x4 *)(p + x_lds_at<CW>(cu * CW) + off);
         return make_float4(v.x, v.y, v.z, v.w);
     }
 };
@@ -436,7 +458,7 @@ __device__ __forceinline__ void step_load_x(Step<C, NR, SM> &st, const XP (&xp)[
     for (int s = 0; s < SM; ++s)
 #pragma unroll
         for (int i = 0; i < Cd::CW / 4; ++i) {
-            const float4 t = xp[s].load4(cu * Cd::CW + 4 * i);
+            const float4 t = xp[s].template load4<Cd::CW>(cu, 4 * i);
             st.xv[s][4 * i] = t.x; st.xv[s][4 * i + 1] = t.y; st.xv[s][4 * i + 2] = t.z; st.xv[s][4 * i + 3] = t.w;
         }
 }
@@ -550,7 +572,7 @@ __device__ __forceinline__ void step_compute_lds(const Step<C, NR, SM> &st, lflo
         for (int s = 0; s < SM; ++s)
 #pragma unroll
             for (int i = 0; i < Cd::UW / 4; ++i) {
-                const f32x4 t = *(const LDS f32x4 *)(x + s * xstride + cu * Cd::CW + u * Cd::UW + 4 * i);
+                const f32x4 t = *(const LDS f32x4 *)(x + s * xstride + x_lds_at<Cd::CW>(cu * Cd::CW) + u * Cd::UW + 4 * i);
                 xv[s][4 * i] = t.x; xv[s][4 * i + 1] = t.y; xv[s][4 * i + 2] = t.z; xv[s][4 * i + 3] = t.w;
             }
         if (Cd::OFFS != 0.f) {
@@ -691,7 +713,7 @@ __global__ void __launch_bounds__(256) k_matmul_lds(MatDev m, const float *__res
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
                     const int i = i0 + u * (int)blockDim.x, sl = i / n4, k4 = i - sl * n4;
-                    if (i < SM * n4) *(LDS f32x4 *)(xs + (size_t)sl * KC + 4 * k4) = v[u];
+                    if (i < SM * n4) *(LDS f32x4 *)(xs + (size_t)sl * x_lds_len<Cd::CW>(KC) + x_lds_at<Cd::CW>(4 * k4)) = v[u];
                 }
             }
             __syncthreads();
@@ -701,7 +723,7 @@ __global__ void __launch_bounds__(256) k_matmul_lds(MatDev m, const float *__res
                 Step<C, R, SM> st;
                 step_load_w(st, rows, m.shift, cu + (uint32_t)c0);
                 __builtin_amdgcn_sched_barrier(0);
-                step_compute_lds(st, (lfloats)xs, (uint32_t)KC, cu, acc);
+                step_compute_lds(st, (lfloats)xs, (uint32_t)x_lds_len<Cd::CW>(KC), cu, acc);
             }
         }
         float out = 0.f;
@@ -870,29 +892,47 @@ __device__ __forceinline__ void for_slots(const GroupArgs &a, int q, int e, F &&
 // Each thread issues up to 8 loads (4 for batches of several tokens, whose
 // kernels hold more registers) before its first LDS write, so the copy
 // costs one round trip per batch of loads, not one per load.
-template <int SM>
+template <int SM, int CW>
 __device__ __forceinline__ void stage_x(const GroupArgs &a, const SlotBatch &b, lfloats_w xs) {
     constexpr int U = SM == 1 ? 8 : 4;
+    constexpr uint32_t NT = WAVE * WPB_A;   // the gate/up launch's block size
     __syncthreads();   // the previous batch's readers are done
-    const int n4 = a.H / 4, total = SM * n4;
-    for (int i0 = threadIdx.x; i0 < total; i0 += U * blockDim.x) {
-        f32x4 v[U];
+    const uint32_t n4 = a.H / 4;
+    if constexpr (SM == 1) {
+        const GLOBAL f32x4 *src = (const GLOBAL f32x4 *)(gf(a.x) + (size_t)b.token[0] * a.H);
+        for (uint32_t i0 = threadIdx.x; i0 < n4; i0 += U * NT) {
+            f32x4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int i = i0 + u * (int)blockDim.x;
-            if (i < total) {
-                const int s = i / n4, k4 = i - s * n4;
-                int t = b.token[0];
+            for (int u = 0; u < U; ++u)
+                if (i0 + u * NT < n4) v[u] = src[i0 + u * NT];
 #pragma unroll
-                for (int j = 1; j < SM; ++j)
-                    if (s == j) t = b.token[j];
-                v[u] = *(const GLOBAL f32x4 *)(gf(a.x) + (size_t)t * a.H + 4 * k4);
-            }
+            for (int u = 0; u < U; ++u)
+                if (i0 + u * NT < n4) *(LDS f32x4 *)(xs + x_lds_at<CW>(4 * (i0 + u * NT))) = v[u];
         }
+    } else {
+        const int total = SM * (int)n4;
+        for (int i0 = threadIdx.x; i0 < total; i0 += U * (int)NT) {
+            f32x4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int i = i0 + u * (int)blockDim.x;
-            if (i < total) *(LDS f32x4 *)(xs + 4 * (size_t)i) = v[u];
+            for (int u = 0; u < U; ++u) {
+                const int i = i0 + u * (int)NT;
+                if (i < total) {
+                    const int s = i / (int)n4, k4 = i - s * (int)n4;
+                    int t = b.token[0];
+#pragma unroll
+                    for (int j = 1; j < SM; ++j)
+                        if (s == j) t = b.token[j];
+                    v[u] = *(const GLOBAL f32x4 *)(gf(a.x) + (size_t)t * a.H + 4 * k4);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int i = i0 + u * (int)NT;
+                if (i < total) {
+                    const int s = i / (int)n4, k4 = i - s * (int)n4;
+                    *(LDS f32x4 *)(xs + (size_t)s * x_lds_len<CW>(a.H) + x_lds_at<CW>(4 * k4)) = v[u];
+                }
+            }
         }
     }
     __syncthreads();
@@ -913,7 +953,7 @@ __device__ __forceinline__ void group_gu_batch(const GroupArgs &a, const ExpertD
     };
     XLds xp[SM];
 #pragma unroll
-    for (int s = 0; s < SM; ++s) xp[s] = {xs + (size_t)s * a.H};
+    for (int s = 0; s < SM; ++s) xp[s] = {xs + (size_t)s * x_lds_len<Codec<C>::CW>(a.H)};
     float acc[2 * R][SM];
     GRow rows[2 * R];
     if constexpr (SM == 1) {
@@ -924,10 +964,10 @@ __device__ __forceinline__ void group_gu_batch(const GroupArgs &a, const ExpertD
         Step<C, 2 * R, SM> st;
         const bool have = lane < nch;
         if (have) step_load_w(st, rows, ex.gate.shift, opaque((uint32_t)lane));
-        stage_x<SM>(a, b, xs);
+        stage_x<SM, Codec<C>::CW>(a, b, xs);
         dot_rows_lds1<C, 2 * R>(st, have, rows, nch, ex.gate.shift, xs, acc);
     } else {
-        stage_x<SM>(a, b, xs);
+        stage_x<SM, Codec<C>::CW>(a, b, xs);
         row_set(rows);
         dot_rows<C, 2 * R, SM, DQG_PIPE, XLds>(rows, nch, ex.gate.shift, xp, acc);
     }
@@ -1486,7 +1526,8 @@ hipError_t go_matmul(const MatDev &m, const float *x, int S, float *y, hipStream
     dim3 grid((m.O + rows_per_block - 1) / rows_per_block);
     if constexpr (DQG_MM_LDS && SM * WAVE * Codec<C>::CW * 4 <= MM_LDS_BYTES) {
         const int KC = matmul_kc<C, SM>(m.K);
-        launch("matmul", (k_matmul_lds<C, R, SM>), grid, dim3(WAVE * WPB), (size_t)SM * KC * 4, st, m, x, S, y, KC);
+        launch("matmul", (k_matmul_lds<C, R, SM>), grid, dim3(WAVE * WPB), (size_t)SM * x_lds_len<Codec<C>::CW>(KC) * 4, st,
+               m, x, S, y, KC);
     } else {
         launch("matmul", (k_matmul<C, R, SM>), grid, dim3(WAVE * WPB), 0, st, m, x, S, y);
     }
@@ -1572,8 +1613,8 @@ template <int C, int CAP>
 hipError_t group_a_cap(const GroupArgs &a, hipStream_t st) {
     const int units = a.S * a.k + (a.shared >= 0 ? 1 : 0);
     const int rows_per_block = RA * WPB_A;
+    const size_t lds = (size_t)CAP * x_lds_len<Codec<C>::CW>(a.H) * sizeof(float);
     dim3 grid((a.I + rows_per_block - 1) / rows_per_block, units);
-    const size_t lds = (size_t)CAP * a.H * sizeof(float);
     if constexpr (CAP == 1 && C != C_I3)
         launch("group_gate_up", (k_group_gate_up1<C, RA>), grid, dim3(WAVE * WPB_A), lds, st, a);
     else
