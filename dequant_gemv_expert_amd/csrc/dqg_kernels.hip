@@ -1534,11 +1534,27 @@ hipError_t go_matmul(const MatDev &m, const float *x, int S, float *y, hipStream
     return hipGetLastError();
 }
 
-// The matrix-core GEMM from this many tokens on, for the formats whose
-// 8-input quarter windows are whole bytes: from 16 for matmul (the pages'
-// cut-over) and from 32 for gate_up, below which the per-row route measured
-// faster (2 x 2048 x 6144 int4-g32 at 16 tokens: 96 against 119 us).
-constexpr int GEMM_MIN_S = 16, GEMM_MIN_S_GU = 32;
+// The matrix-core GEMM from this many tokens on: where it measured faster
+// than the per-row route on MI355X.  The GEMM has a floor of 120-200 us on a
+// 6144 x 6144 matrix up to 64 tokens (few waves for the chip), the per-row
+// route grows by about 4 us a token: dense matmul breaks even at 32 tokens
+// for int4 and MXFP4 (124 against 124 us), 48 for int8 and E4M3 (at 32:
+// 133 and 111 us per row, 172 and 157 us GEMM; at 64 the GEMM wins) and 96
+// for f16 rows (at 64: 251 per row, 262 GEMM; at 128: 503 against 260);
+// gate_up from 32 tokens (2 x 2048 x 6144 int4-g32 at 16 tokens: 96 per
+// row against 119 us GEMM).
+#ifndef DQG_GEMM_MIN_S_GU
+#define DQG_GEMM_MIN_S_GU 32
+#endif
+constexpr int GEMM_MIN_S_GU = DQG_GEMM_MIN_S_GU;
+template <int C>
+constexpr int gemm_min_s() {
+#ifdef DQG_GEMM_MIN_S
+    return DQG_GEMM_MIN_S;
+#else
+    return C == C_F16 ? 96 : (C == C_I8 || C == C_FP8) ? 48 : 32;
+#endif
+}
 
 template <int C>
 constexpr bool gemm_codec() { return C == C_I8 || C == C_I4 || C == C_FP4 || C == C_FP8 || C == C_F16; }
@@ -1575,7 +1591,7 @@ hipError_t go_gemm(const MatDev &m0, const MatDev &m1, const float *x, int S, fl
 template <int C>
 hipError_t matmul_c(const MatDev &m, const float *x, int S, float *y, hipStream_t st) {
     if constexpr (gemm_codec<C>())
-        if (S >= GEMM_MIN_S && m.K % 32 == 0) return go_gemm<C, false>(m, m, x, S, y, INFINITY, st);
+        if (S >= gemm_min_s<C>() && m.K % 32 == 0) return go_gemm<C, false>(m, m, x, S, y, INFINITY, st);
     if (S >= 8) return go_matmul<C, DQG_MM_R8, 8>(m, x, S, y, st);
     if (S >= 4) return go_matmul<C, DQG_MM_R4, 4>(m, x, S, y, st);
     if (S >= 2) return go_matmul<C, DQG_MM_R2, 2>(m, x, S, y, st);

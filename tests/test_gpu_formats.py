@@ -6,9 +6,9 @@ Bars as for the other formats: dequantised weights bit for bit (NaN codes
 compare as NaN, whatever their payload), and every output within 1e-5 of its
 row's normaliser sum_k |w*x|.  The shapes have ragged rows (and ragged
 128-row scale blocks), K that is not a multiple of a wave's 64 chunks, and
-batches on both sides of the matrix-core cut-over (16 tokens for matmul, 32
-for gate_up; formats 12, 13 and 14 take that route, 10 and 11 stay on the
-per-row one).
+batches on both sides of the matrix-core cut-overs (matmul from 48 tokens
+for formats 12 and 13 and 96 for 14, gate_up from 32; formats 10 and 11
+stay on the per-row route).
 """
 import numpy as np
 import pytest
@@ -126,10 +126,11 @@ GEMM = [(12, 130, 1024, None), (12, 256, 4096, None), (13, 77, 2048, 64), (13, 1
         (14, 77, 1024, None), (14, 300, 2080, None)]
 
 
-@pytest.mark.parametrize("S", [16, 64, 100, 130, 200])
+@pytest.mark.parametrize("S", [16, 47, 48, 64, 95, 96, 130, 200])
 @pytest.mark.parametrize("spec", GEMM, ids=lambda s: f"fmt{s[0]}_{s[1]}x{s[2]}")
 def test_gemm_route_matches_oracle(spec, S):
-    """The matrix-core route (token tiles of 32 and 64 per block)."""
+    """Both sides of each format's cut-over, the matrix-core route with token
+    tiles of 32 and 64 per block."""
     fmt, O, K, gs = spec
     m = synth.matrix(fmt, O, K, gs, 6400, fmt, O, K)
     x = synth.activations(S, K, 6401, S, K)

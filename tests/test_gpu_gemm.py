@@ -1,8 +1,8 @@
 """Parity of the matrix-core GEMM route with the CPU oracle.
 
-dqg_matmul (from 16 tokens) and dqg_gate_up (from 32) take the route for
-int8, int4 and MXFP4 when K is a multiple of 32; the sizes below straddle
-the cut-overs, so both routes are checked at 16..130 tokens.  Bar: as for
+dqg_matmul (from 32 tokens for int4 and MXFP4, 48 for int8) and
+dqg_gate_up (from 32) take the route when K is a multiple of 32; the sizes
+below straddle the cut-overs, so both routes are checked at 16..130 tokens.  Bar: as for
 the GEMV route, every output within 1e-5 of its row's normaliser
 sum_k |w*x|.  The route's own error
 terms are far below it: x is split as f16 hi + lo (x - hi - lo < 2^-22 |x|),
@@ -45,7 +45,7 @@ SHAPES = [  # (fmt, O, K, gs): ragged rows, K not a multiple of the 128-input st
 ]
 
 
-@pytest.mark.parametrize("S", [16, 17, 31, 33, 64, 100])
+@pytest.mark.parametrize("S", [16, 31, 32, 33, 47, 48, 64, 100])
 @pytest.mark.parametrize("spec", SHAPES, ids=lambda s: f"fmt{s[0]}_{s[1]}x{s[2]}")
 def test_gemm_matmul_matches_oracle(spec, S):
     fmt, O, K, gs = spec
