@@ -52,4 +52,13 @@ def is_stale(lib: str = LIB) -> bool:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    # python -m dequant_gemv_expert_amd.build [--out PATH] [-DNAME=VALUE ...]:
+    # the library, or a copy built with compile-time settings overridden
+    # (tile shapes, route cut-overs) for a measurement
+    args = sys.argv[1:]
+    out = LIB
+    if args[:1] == ["--out"]:
+        out, args = args[1], args[2:]
+    if any(not a.startswith("-D") for a in args):
+        raise SystemExit("usage: python -m dequant_gemv_expert_amd.build [--out PATH] [-DNAME=VALUE ...]")
+    print(build(out, extra=args, verbose=True))
