@@ -88,6 +88,8 @@ def main():
     ap.add_argument("--shared-copies", type=int, default=12)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--gate-up", action="store_true",
+                    help="dense workloads: time dqg_gate_up on two matrices of the workload's shape")
     ap.add_argument("--swiglu-limit", type=float, default=None,
                     help="clamp the experts' SwiGLU at this limit (expert-group workloads)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -97,7 +99,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the path is measured "
-              "on one GPU's share; see DESIGN.md for how it would shard)", file=sys.stderr)
+              "on one GPU's share)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -314,7 +316,8 @@ def bench_gemv(args, c):
     route: the per-row route streams the weights (HBM-bound, GB/s); the
     matrix-core GEMM (from a format's cut-over on) is reported in TFLOP/s of
     useful products against the f16 peak.  The route is read off the timed
-    launches.
+    launches.  With --gate-up a step is one dqg_gate_up call on a gate and an
+    up matrix of the workload's shape.
     """
     import numpy as np
     import torch
@@ -325,19 +328,27 @@ def bench_gemv(args, c):
     fmt, O, K, gs, seed = c["fmt"], c["O"], c["K"], c["gs"], c["seed"]
     torch.cuda.set_device(0)
     dev_name = torch.cuda.get_device_name(0)
+    gu = args.gate_up
     hm = synth.matrix(fmt, O, K, gs, seed, 0)
-    w_bytes = matrix_bytes(hm)
+    hu = synth.matrix(fmt, O, K, gs, seed, 1) if gu else None
+    w_bytes = matrix_bytes(hm) * (2 if gu else 1)
     copies = max(2, min(256, (2 << 30) // w_bytes))
-    mats = [dq.Matrix.upload(hm) for _ in range(copies)]
+    mats = [(dq.Matrix.upload(hm), dq.Matrix.upload(hu) if gu else None) for _ in range(copies)]
     x = torch.from_numpy(synth.activations(S, K, seed, 9, S)).cuda()
     y = torch.empty((S, O), dtype=torch.float32, device="cuda")
-    log(f"[bench] {dev_name}: {copies} copies of {args.workload} ({w_bytes / 1e6:.2f} MB each), S = {S}")
+    log(f"[bench] {dev_name}: {copies} copies of {args.workload}{' (gate and up)' if gu else ''} "
+        f"({w_bytes / 1e6:.2f} MB each), S = {S}")
     # ctypes arguments prepared up front, so the timed loop is the C calls
     import ctypes
     from dequant_gemv_expert_amd import _lib as L
-    fn = L.load().dqg_matmul
     stream = torch.cuda.current_stream().cuda_stream
-    plan = [(ctypes.byref(mt.struct), x.data_ptr(), S, y.data_ptr(), stream) for mt in mats]
+    if gu:
+        fn = L.load().dqg_gate_up
+        plan = [(ctypes.byref(g.struct), ctypes.byref(u.struct), x.data_ptr(), S, y.data_ptr(), stream)
+                for g, u in mats]
+    else:
+        fn = L.load().dqg_matmul
+        plan = [(ctypes.byref(g.struct), x.data_ptr(), S, y.data_ptr(), stream) for g, _ in mats]
 
     def call(i):
         rc = fn(*plan[i % copies])
@@ -348,7 +359,7 @@ def bench_gemv(args, c):
         call(i)
     torch.cuda.synchronize()
     K_steps = args.steps
-    dq.dqg_prof_begin(K_steps)
+    dq.dqg_prof_begin(2 * K_steps)   # split-K calls launch two kernels
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K_steps):
@@ -357,12 +368,16 @@ def bench_gemv(args, c):
     t_wall = time.perf_counter() - t0
     prof = dq.dqg_prof_end()
     # the route the library took (the kernel whose launches were timed)
-    kname = max(("gemm", "matmul"), key=lambda k: prof.get(k, (0, 0.0))[0])
-    gemm = kname == "gemm"
+    routes = ("gemm_gate_up", "gate_up") if gu else ("gemm", "matmul")
+    kname = max(routes, key=lambda k: prof.get(k, (0, 0.0))[0])
+    gemm = kname == routes[0]
     n_k, ms_k = prof.get(kname, (0, 0.0))
+    if gemm and prof.get("gemm_reduce", (0, 0.0))[0]:   # split-K: the partials' sum is part of the call
+        ms_k += prof["gemm_reduce"][1]
+        kname += "+gemm_reduce"
     avg_s = ms_k * 1e-3 / max(n_k, 1)
     step_bytes = w_bytes + S * K * 4 + S * O * 4
-    flops = 2.0 * S * O * K
+    flops = 2.0 * S * O * K * (2 if gu else 1)
     value = step_bytes * K_steps / t_wall / 1e9
     if gemm:
         achieved = flops / avg_s / 1e12 if avg_s > 0 else None
@@ -384,30 +399,39 @@ def bench_gemv(args, c):
         import oracle
         rows = max(1, min(O, int(O * 0.05)))
         srows = -(-rows // synth.FP8_BLOCK) if fmt == synth.FMT_FP8_BLOCK else rows   # whole scale blocks
-        sub = synth.QMatrix(hm.fmt, rows, hm.K, hm.gs, hm.q[:rows], None if hm.q2 is None else hm.q2[:rows],
-                            None if hm.scales is None else hm.scales[:srows])
+
+        def head(m):   # the first rows of a matrix
+            return synth.QMatrix(m.fmt, rows, m.K, m.gs, m.q[:rows], None if m.q2 is None else m.q2[:rows],
+                                 None if m.scales is None else m.scales[:srows])
+        sub = head(hm)
+        subu = head(hu) if gu else None
         xs = x.cpu().numpy()
         spent, calls = 0.0, 0
         while spent < args.cpu_seconds and calls < 1_000_000:
             t = time.perf_counter()
-            oracle.gemv(sub, xs)
+            if gu:
+                oracle.gate_up(sub, subu, xs)
+            else:
+                oracle.gemv(sub, xs)
             spent += time.perf_counter() - t
             calls += 1
         per_call = spent / calls * O / rows   # the whole matrix, scaled from the row sample
         cpu = {"value": round((step_bytes / per_call / 1e9) if not gemm else (flops / per_call / 1e12), 4),
                "unit": "GB/s" if not gemm else "TFLOP/s", "cores": oracle.get_threads(), "kind": "oracle",
-               "sample": f"{calls} oracle GEMVs of the first {rows} of {O} rows at S = {S}, {spent:.1f} s, "
-                         f"scaled to the whole matrix"}
+               "sample": f"{calls} oracle {'gate_up calls' if gu else 'GEMVs'} of the first {rows} of {O} rows "
+                         f"at S = {S}, {spent:.1f} s, scaled to the whole matrix"}
         log(f"[bench] cpu oracle: {cpu['value']} {cpu['unit']} on {cpu['cores']} threads")
 
     out = {
-        "metric": METRIC if not gemm else "quant GEMM TFLOP/s (prefill, useful products)",
+        "metric": (METRIC if not gemm else "quant GEMM TFLOP/s (prefill, useful products)")
+                  + (" [gate_up]" if gu else ""),
         "value": round(value, 2) if not gemm else round(flops * K_steps / t_wall / 1e12, 3),
         "unit": "GB/s" if not gemm else "TFLOP/s",
         "n_gpus": 1, "steps": K_steps, "warmup": args.warmup,
         "ms_per_step": round(t_wall / K_steps * 1e3, 5), "us_per_call": round(t_wall / K_steps * 1e6, 2),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
-        "config": {"workload": args.workload, "tokens": S, "O": O, "K": K, "format": f"fmt {fmt}, gs {gs}",
+        "config": {"workload": args.workload + (" gate_up" if gu else ""), "tokens": S, "O": O, "K": K,
+                   "format": f"fmt {fmt}, gs {gs}",
                    "copies": copies, "route": "gemm" if gemm else "gemv", "device": dev_name},
         "roofline": roof,
         "cpu_baseline": cpu,

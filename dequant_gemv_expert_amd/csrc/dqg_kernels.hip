@@ -1201,6 +1201,12 @@ struct GemmCodec<C_F16> {
 template <int NC>
 constexpr int gemm_k() { return 512 / NC; }
 constexpr int GROWS = 128;         // row slots per block: 4 waves x 2 tiles x 16
+// The sum over K is taken per chunk of GEMM_KC inputs (a whole number of
+// k-steps for every NC), and the chunk sums are added in chunk order from
+// 0.  A block either walks all chunks itself or, when the grid would be too
+// small to fill the chip, computes one chunk into a workspace that
+// k_gemm_reduce adds up in the same order: the bits are the same either way.
+constexpr int GEMM_KC = 512;
 
 template <int NC>
 struct GemmLds {
@@ -1208,7 +1214,7 @@ struct GemmLds {
     _Float16 xh[GT][XS];
     _Float16 xl[GT][XS];
     float xo[GT][GWIN];    // OFFS * sum of x' over each window
-    float xe[GT];          // 2^e of the token for this k-step
+    float xe[GT][GWIN];    // 2^e of the token for each window
     float sc[GWIN][GROWS]; // scale * VMUL per window and row slot
 };
 
@@ -1218,9 +1224,13 @@ __device__ __forceinline__ int gemm_row(int block_row, int w, int t, int r) {
     return GU ? block_row + 16 * w + r : block_row + 32 * w + 16 * t + r;
 }
 
+// ws == nullptr: the block sums all of K and writes y (GU: swiglu(g, u)).
+// Otherwise the block sums chunk blockIdx.z only and writes the raw sums to
+// ws[(z * MATS + mat) * S + s][row] (MATS = 2 for GU, gate then up, else 1;
+// rows 0 .. gridDim.x * rows per block - 1 all have a slot, row stride op).
 template <int C, bool GU, int NC>
 __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float *__restrict__ x, int S,
-                                              float *__restrict__ y, float limit) {
+                                              float *__restrict__ y, float limit, float *__restrict__ ws, int op) {
     using Gc = GemmCodec<C>;
     using Cd = Codec<C>;
     using Lt = GemmLds<NC>;
@@ -1232,6 +1242,7 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
     const int O = m0.O, K = m0.K;
     const int block_row = blockIdx.x * (GU ? GROWS / 2 : GROWS);
     const int s0 = blockIdx.y * (16 * NC);
+    const int kbeg = ws ? blockIdx.z * GEMM_KC : 0, kend = ws ? min(K, kbeg + GEMM_KC) : K;
     const int lr = lane & 15, lq = lane >> 4;   // A/B: row or token within a tile; quarter of the window
     // this lane's A rows (clamped; rows past O are computed and dropped)
     gbytes arow[2];
@@ -1241,13 +1252,13 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
         const int row = min(gemm_row<GU>(block_row, w, t, lr), O - 1);
         arow[t] = (gbytes)(m.q + (size_t)row * m.qstride);
     }
-    float acc[2][NC][4];
+    float acc[2][NC][4], tot[2][NC][4];   // this chunk's sums; the chunk sums so far
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int c = 0; c < NC; ++c)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[t][c][i] = 0.f;
+            for (int i = 0; i < 4; ++i) acc[t][c][i] = tot[t][c][i] = 0.f;
 
     // Software pipeline over k-steps: the codes, x and scales of step k0 + GK
     // are requested before step k0 is computed, so their latency hides
@@ -1258,7 +1269,7 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
     f32x4 xv_n[8];
     float sc_n[SCN];
     const auto fetch = [&](int k0) {
-        const int nwin = min(GWIN, (K - k0) / 32);   // K is a multiple of 32
+        const int nwin = min(GWIN, (kend - k0) / 32);   // K is a multiple of 32
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -1284,9 +1295,9 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
                 sc_n[h] = Cd::VMUL;
         }
     };
-    fetch(0);
-    for (int k0 = 0; k0 < K; k0 += GK) {
-        const int nwin = min(GWIN, (K - k0) / 32);
+    fetch(kbeg);
+    for (int k0 = kbeg; k0 < kend; k0 += GK) {
+        const int nwin = min(GWIN, (kend - k0) / 32);
         f32x4 v[8];
 #pragma unroll
         for (int t = 0; t < 2; ++t)
@@ -1295,14 +1306,12 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = xv_n[i];
         __syncthreads();   // the previous step's readers of L are done
-        // stage x' of token tt, window qq
+        // stage x' of token tt, window qq, scaled by a power of two of its own
         {
             float mx = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
-#pragma unroll
-            for (int o = 1; o < TPT; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o));   // the token's TPT threads
             int ex = 0;
             if (mx > 0.f) { frexpf(mx, &ex); ex -= 15; }   // mx * 2^-ex < 2^15
             float xs = 0.f;
@@ -1322,7 +1331,7 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
                 *(LDS h16x8 *)&L.xl[tt][32 * qq + 8 * g] = lo;
             }
             L.xo[tt][qq] = Cd::OFFS * xs;
-            if (qq == 0) L.xe[tt] = ldexpf(1.f, ex);
+            L.xe[tt][qq] = ldexpf(1.f, ex);
         }
 #pragma unroll
         for (int h = 0; h < SCN; ++h) {
@@ -1330,7 +1339,7 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
             L.sc[j][i - j * GROWS] = sc_n[h];
         }
         __syncthreads();
-        if (k0 + GK < K) fetch(k0 + GK);   // next step's requests go out now
+        if (k0 + GK < kend) fetch(k0 + GK);   // next step's requests go out now
         for (int j = 0; j < nwin; ++j) {
             h16x8 a[2];
             f32x4 sc4[2];
@@ -1347,7 +1356,7 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
                 const h16x8 bh = *(LDS h16x8 *)&L.xh[tok][32 * j + 8 * lq];
                 const h16x8 bl = *(LDS h16x8 *)&L.xl[tok][32 * j + 8 * lq];
                 // the D lanes of token 16c + lane%16 take its offset and 2^e
-                const float xo = L.xo[tok][j], xe = L.xe[tok];
+                const float xo = L.xo[tok][j], xe = L.xe[tok][j];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     f32x4 d = {0.f, 0.f, 0.f, 0.f};
@@ -1358,26 +1367,63 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
                 }
             }
         }
+        if ((k0 + GK) % GEMM_KC == 0 || k0 + GK >= kend) {   // a chunk ends with this step
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int c = 0; c < NC; ++c)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        tot[t][c][i] += acc[t][c][i];
+                        acc[t][c][i] = 0.f;
+                    }
+        }
     }
     // D lane layout: rows 4*lq + i of each tile, token 16c + lr
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int s = s0 + 16 * c + lr;
         if (s >= S) continue;
+        if (ws) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int row = gemm_row<GU>(block_row, w, GU ? 0 : t, 4 * lq), mat = GU ? t : 0;
+                float *p = ws + ((size_t)(blockIdx.z * (GU ? 2 : 1) + mat) * S + s) * op + row;
+                *(f32x4 *)p = f32x4{tot[t][c][0], tot[t][c][1], tot[t][c][2], tot[t][c][3]};
+            }
+            continue;
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             if (GU) {
                 const int row = gemm_row<GU>(block_row, w, 0, 4 * lq + i);
-                if (row < O) y[(size_t)s * O + row] = swiglu(acc[0][c][i], acc[1][c][i], limit);
+                if (row < O) y[(size_t)s * O + row] = swiglu(tot[0][c][i], tot[1][c][i], limit);
             } else {
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     const int row = gemm_row<GU>(block_row, w, t, 4 * lq + i);
-                    if (row < O) y[(size_t)s * O + row] = acc[t][c][i];
+                    if (row < O) y[(size_t)s * O + row] = tot[t][c][i];
                 }
             }
         }
     }
+}
+
+// Sums the chunk partials of k_gemm in chunk order, one output per thread.
+template <bool GU>
+__global__ void __launch_bounds__(256) k_gemm_reduce(const float *__restrict__ ws, int nch, int S, int O, int op,
+                                                     float *__restrict__ y, float limit) {
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)S * O) return;
+    const int s = (int)(i / O), o = (int)(i - (size_t)s * O);
+    const size_t plane = (size_t)S * op;   // one (chunk, matrix) slice
+    const float *p = ws + (size_t)s * op + o;
+    float g = 0.f, u = 0.f;
+    for (int z = 0; z < nch; ++z) {
+        g += p[(size_t)(GU ? 2 * z : z) * plane];
+        if (GU) u += p[(size_t)(2 * z + 1) * plane];
+    }
+    y[i] = GU ? swiglu(g, u, limit) : g;
 }
 
 // ---------------------------------------------------------------------------
@@ -1535,24 +1581,27 @@ hipError_t go_matmul(const MatDev &m, const float *x, int S, float *y, hipStream
 }
 
 // The matrix-core GEMM from this many tokens on: where it measured faster
-// than the per-row route on MI355X.  The GEMM has a floor of 120-200 us on a
-// 6144 x 6144 matrix up to 64 tokens (few waves for the chip), the per-row
-// route grows by about 4 us a token: dense matmul breaks even at 32 tokens
-// for int4 and MXFP4 (124 against 124 us), 48 for int8 and E4M3 (at 32:
-// 133 and 111 us per row, 172 and 157 us GEMM; at 64 the GEMM wins) and 96
-// for f16 rows (at 64: 251 per row, 262 GEMM; at 128: 503 against 260);
-// gate_up from 32 tokens (2 x 2048 x 6144 int4-g32 at 16 tokens: 96 per
-// row against 119 us GEMM).
-#ifndef DQG_GEMM_MIN_S_GU
-#define DQG_GEMM_MIN_S_GU 32
-#endif
-constexpr int GEMM_MIN_S_GU = DQG_GEMM_MIN_S_GU;
+// than the per-row route on MI355X.  The per-row route takes its tokens 8 at
+// a time, so 9 to 16 tokens cost it two passes over the weights; the GEMM
+// with split-K costs about the same from 8 to 16 tokens.  On 6144 x 6144,
+// 8 tokens: per row 30-35 us, GEMM 34-52 us; 10 tokens: per row 54-66 us,
+// GEMM 34-52 us, in every GEMM format.  gate_up (2 x 2048 x 6144) at 8
+// tokens: int4 54 us per row against 29 GEMM, E4M3 30 against 28, int8 35
+// against 33, f16 26 against 35.
 template <int C>
 constexpr int gemm_min_s() {
 #ifdef DQG_GEMM_MIN_S
     return DQG_GEMM_MIN_S;
 #else
-    return C == C_F16 ? 96 : (C == C_I8 || C == C_FP8) ? 48 : 32;
+    return 9;
+#endif
+}
+template <int C>
+constexpr int gemm_min_s_gu() {
+#ifdef DQG_GEMM_MIN_S_GU
+    return DQG_GEMM_MIN_S_GU;
+#else
+    return C == C_F16 ? 9 : 8;
 #endif
 }
 
@@ -1565,14 +1614,72 @@ constexpr bool gemm_codec() { return C == C_I8 || C == C_I4 || C == C_FP4 || C =
 template <int C>
 constexpr int gemm_min_nc() { return (int)(sizeof(typename GemmCodec<C>::Raw) / 4); }
 
+// A grid of fewer blocks than this takes one block per K chunk (split-K).
+#ifndef DQG_GEMM_SPLIT_BELOW
+#define DQG_GEMM_SPLIT_BELOW 1024
+#endif
+
+// The split-K partials live in one buffer per device that the library keeps
+// and grows on demand, up to WS_MAX bytes (larger needs take the unsplit
+// kernel).  Every use waits on its stream for the event recorded after the
+// previous use, whichever stream that was, so calls on different streams
+// take turns with the buffer; a grow first waits on the host for that event.
+// A stream under graph capture takes the unsplit kernel, so that no graph
+// refers to the buffer.
+constexpr size_t WS_MAX = size_t(1) << 30;
+struct Workspace {
+    std::mutex mu;
+    float *buf = nullptr;
+    size_t bytes = 0;
+    hipEvent_t done = nullptr;   // recorded after the last use
+    bool used = false;
+};
+Workspace g_ws[64];
+
 template <int C, bool GU, int NC>
 hipError_t go_gemm_nc(const MatDev &m0, const MatDev &m1, const float *x, int S, float *y, float L,
                       hipStream_t st, const char *name) {
     static_assert(NC >= gemm_min_nc<C>(), "a step's codes must fit 32 registers");
     const int rows_per_block = GU ? GROWS / 2 : GROWS;
-    dim3 grid((m0.O + rows_per_block - 1) / rows_per_block, (S + 16 * NC - 1) / (16 * NC));
-    launch(name, (k_gemm<C, GU, NC>), grid, dim3(256), 0, st, m0, m1, x, S, y, L);
-    return hipGetLastError();
+    const int O = m0.O, nch = (m0.K + GEMM_KC - 1) / GEMM_KC;
+    dim3 grid((O + rows_per_block - 1) / rows_per_block, (S + 16 * NC - 1) / (16 * NC));
+    if (nch == 1 || (size_t)grid.x * grid.y >= DQG_GEMM_SPLIT_BELOW) {
+        launch(name, (k_gemm<C, GU, NC>), grid, dim3(256), 0, st, m0, m1, x, S, y, L, (float *)nullptr, 0);
+        return hipGetLastError();
+    }
+    const int op = grid.x * rows_per_block;
+    const size_t bytes = (size_t)nch * (GU ? 2 : 1) * S * op * sizeof(float);
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t e = hipStreamIsCapturing(st, &cs);
+    if (e != hipSuccess) return e;
+    int dev = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if (bytes > WS_MAX || cs != hipStreamCaptureStatusNone || dev < 0 || dev >= 64) {
+        launch(name, (k_gemm<C, GU, NC>), grid, dim3(256), 0, st, m0, m1, x, S, y, L, (float *)nullptr, 0);
+        return hipGetLastError();
+    }
+    Workspace &W = g_ws[dev];
+    std::lock_guard<std::mutex> lock(W.mu);
+    if (!W.done && (e = hipEventCreateWithFlags(&W.done, hipEventDisableTiming)) != hipSuccess) return e;
+    if (W.bytes < bytes) {
+        if (W.used && (e = hipEventSynchronize(W.done)) != hipSuccess) return e;
+        if (W.buf) (void)hipFree(W.buf);
+        W.buf = nullptr;
+        W.bytes = 0;
+        if ((e = hipMalloc((void **)&W.buf, bytes)) != hipSuccess) return e;
+        W.bytes = bytes;
+    }
+    if (W.used && (e = hipStreamWaitEvent(st, W.done, 0)) != hipSuccess) return e;
+    grid.z = nch;
+    launch(name, (k_gemm<C, GU, NC>), grid, dim3(256), 0, st, m0, m1, x, S, y, L, W.buf, op);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const size_t n = (size_t)S * O;
+    launch("gemm_reduce", (k_gemm_reduce<GU>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, W.buf, nch, S, O,
+           op, y, L);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if ((e = hipEventRecord(W.done, st)) != hipSuccess) return e;
+    W.used = true;
+    return hipSuccess;
 }
 
 template <int C, bool GU>
@@ -1609,7 +1716,7 @@ hipError_t go_gate_up(const MatDev &g, const MatDev &u, const float *x, int S, f
 template <int C>
 hipError_t gate_up_c(const MatDev &g, const MatDev &u, const float *x, int S, float *h, float L, hipStream_t st) {
     if constexpr (gemm_codec<C>())
-        if (S >= GEMM_MIN_S_GU && g.K % 32 == 0) return go_gemm<C, true>(g, u, x, S, h, L, st);
+        if (S >= gemm_min_s_gu<C>() && g.K % 32 == 0) return go_gemm<C, true>(g, u, x, S, h, L, st);
     if (S >= 8) return go_gate_up<C, 1, 8>(g, u, x, S, h, L, st);
     if (S >= 4) return go_gate_up<C, 2, 4>(g, u, x, S, h, L, st);
     if (S >= 2) return go_gate_up<C, 4, 2>(g, u, x, S, h, L, st);

@@ -157,7 +157,15 @@ typedef struct {
  * y[s][o] = sum_k W[o][k] * x[s][k] for s < S.
  * Quantised GEMV (the guide's API-contract section, coli_vk_matmul; the
  * shader-level section for the decode).  x: f32 [S][K]; y: f32 [S][O].
- * S >= 1; every token's row has the same bits whatever S is.
+ * S >= 1.  Two routes, each giving a token's row the same bits whatever S
+ * is: up to 8 tokens the per-row route; from 9 tokens, for formats 1, 4, 7,
+ * 12, 13 and 14 with K a multiple of 32, the matrix-core GEMM (the bits of
+ * the two routes differ within the error bound).  When the GEMM's grid is
+ * too small for the chip it splits K and keeps the partial sums in a device
+ * buffer that the library allocates on first need (hipMalloc, one per
+ * device, grown to at most 1 GiB, held until the process ends); calls on
+ * different streams take turns with it, in the order they were made.  A
+ * stream under graph capture uses no such buffer.
  */
 int dqg_matmul(const dqg_matrix *W, const float *x, int32_t S, float *y, void *stream);
 
@@ -165,7 +173,8 @@ int dqg_matmul(const dqg_matrix *W, const float *x, int32_t S, float *y, void *s
  * h[s][i] = silu(G[i] . x[s]) * (U[i] . x[s]), silu(z) = z / (1 + e^-z).
  * The SwiGLU half of an expert MLP in one launch with x read once (the
  * guide's API-contract section, coli_vk_gate_up).  G and U: [I x H] of one
- * format; x: f32 [S][H]; h: f32 [S][I].
+ * format; x: f32 [S][H]; h: f32 [S][I].  Routes and the partials buffer as
+ * for dqg_matmul, with the GEMM from 8 tokens (9 for format 14).
  */
 int dqg_gate_up(const dqg_matrix *G, const dqg_matrix *U, const float *x, int32_t S, float *h,
                 void *stream);
@@ -283,8 +292,9 @@ int dqg_route(const float *logits, int32_t S, int32_t E, int32_t k, int32_t mode
  * call it outside timed regions); the next `capacity` launches are timed.
  * dqg_prof_end waits for the recorded events, fills up to `max` records
  * (one per kernel name, in first-launch order), stores their count in *n
- * and releases the events.  Kernel names: "matmul", "gate_up", "dequant", "route",
- * "group_gate_up", "group_down". */
+ * and releases the events.  Kernel names: "matmul", "gate_up", "gemm",
+ * "gemm_gate_up", "gemm_reduce", "dequant", "route", "group_gate_up",
+ * "group_down". */
 typedef struct {
     char kernel[32];
     int64_t launches;
