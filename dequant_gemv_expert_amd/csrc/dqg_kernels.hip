@@ -674,28 +674,35 @@ __global__ void __launch_bounds__(256) k_matmul(MatDev m, const float *__restric
     }
 }
 
-// dqg_matmul with x staged in LDS, K-chunk by K-chunk: the block's waves
-// share one copy of x instead of each reading it from L2.  A K-chunk is a
-// multiple of 64 code chunks, so every lane still takes chunks lane,
-// lane + 64, ... in order: a token's bits are those of k_matmul at any S.
-// Every wave stays to the end (block barriers); rows past O are clamped and
-// their outputs dropped.
-template <int C, int R, int SM>
-__global__ void __launch_bounds__(256) k_matmul_lds(MatDev m, const float *__restrict__ x, int S,
-                                                    float *__restrict__ y, int KC) {
+// dqg_matmul (GU false: y[s][o] = W[o] . x[s], W = m0) and dqg_gate_up
+// (GU true: y[s][i] = swiglu(G[i] . x[s], U[i] . x[s]), G = m0, U = m1)
+// with x staged in LDS, K-chunk by K-chunk: the block's waves share one copy
+// of x instead of each reading it from L2.  A K-chunk is a multiple of 64
+// code chunks, so every lane still takes chunks lane, lane + 64, ... in
+// order: a token's bits are those of k_matmul / k_gate_up at any S.  Every
+// wave stays to the end (block barriers); rows past O are clamped and their
+// outputs dropped.
+template <int C, int R, int SM, bool GU>
+__global__ void __launch_bounds__(256) k_rows_lds(MatDev m0, MatDev m1, const float *__restrict__ x, int S,
+                                                  float *__restrict__ y, int KC, float L) {
     extern __shared__ float xl_raw[];
     lfloats_w xs = (lfloats_w)xl_raw;
     using Cd = Codec<C>;
+    constexpr int NR = GU ? 2 * R : R;   // GU: gate rows, then the same rows of up
+    const MatDev &m = m0;
     const int wave = blockIdx.x * (blockDim.x / WAVE) + wave_id();
     const int row0 = wave * R;
     const int lane = threadIdx.x & (WAVE - 1);
-    GRow rows[R];
+    GRow rows[NR];
 #pragma unroll
-    for (int r = 0; r < R; ++r) rows[r] = row_ptrs(m, min(row0 + r, m.O - 1));
+    for (int r = 0; r < R; ++r) {
+        rows[r] = row_ptrs(m0, min(row0 + r, m.O - 1));
+        if (GU) rows[R + r] = row_ptrs(m1, min(row0 + r, m.O - 1));
+    }
     for (int s0 = 0; s0 < S; s0 += SM) {
-        float acc[R][SM];
+        float acc[NR][SM];
 #pragma unroll
-        for (int r = 0; r < R; ++r)
+        for (int r = 0; r < NR; ++r)
 #pragma unroll
             for (int s = 0; s < SM; ++s) acc[r][s] = 0.f;
         for (int kc0 = 0; kc0 < m.K; kc0 += KC) {
@@ -720,22 +727,24 @@ __global__ void __launch_bounds__(256) k_matmul_lds(MatDev m, const float *__res
             const int c0 = kc0 / Cd::CW, nc = kn / Cd::CW;
             for (int c = lane; c < nc; c += WAVE) {
                 const uint32_t cu = opaque((uint32_t)c);
-                Step<C, R, SM> st;
+                Step<C, NR, SM> st;
                 step_load_w(st, rows, m.shift, cu + (uint32_t)c0);
                 __builtin_amdgcn_sched_barrier(0);
                 step_compute_lds(st, (lfloats)xs, (uint32_t)x_lds_len<Cd::CW>(KC), cu, acc);
             }
         }
-        float out = 0.f;
+        float out = 0.f, outu = 0.f;
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
             for (int s = 0; s < SM; ++s) {
                 const float t = wave_sum(acc[r][s]);
-                if (lane == r * SM + s) out = t;
+                const float tu = GU ? wave_sum(acc[R + r][s]) : 0.f;
+                if (lane == r * SM + s) { out = t; outu = tu; }
             }
         const int r = lane / SM, s = lane % SM;
-        if (lane < R * SM && row0 + r < m.O && s0 + s < S) y[(size_t)(s0 + s) * m.O + row0 + r] = out;
+        if (lane < R * SM && row0 + r < m.O && s0 + s < S)
+            y[(size_t)(s0 + s) * m.O + row0 + r] = GU ? swiglu(out, outu, L) : out;
     }
 }
 
@@ -1546,6 +1555,9 @@ void launch(const char *name, K kernel, dim3 grid, dim3 block, size_t lds, hipSt
 #ifndef DQG_MM_LDS
 #define DQG_MM_LDS 1
 #endif
+#ifndef DQG_GU_LDS
+#define DQG_GU_LDS 1
+#endif
 #ifndef DQG_MM_R4
 #define DQG_MM_R4 4
 #endif
@@ -1572,8 +1584,8 @@ hipError_t go_matmul(const MatDev &m, const float *x, int S, float *y, hipStream
     dim3 grid((m.O + rows_per_block - 1) / rows_per_block);
     if constexpr (DQG_MM_LDS && SM * WAVE * Codec<C>::CW * 4 <= MM_LDS_BYTES) {
         const int KC = matmul_kc<C, SM>(m.K);
-        launch("matmul", (k_matmul_lds<C, R, SM>), grid, dim3(WAVE * WPB), (size_t)SM * x_lds_len<Codec<C>::CW>(KC) * 4, st,
-               m, x, S, y, KC);
+        launch("matmul", (k_rows_lds<C, R, SM, false>), grid, dim3(WAVE * WPB),
+               (size_t)SM * x_lds_len<Codec<C>::CW>(KC) * 4, st, m, m, x, S, y, KC, INFINITY);
     } else {
         launch("matmul", (k_matmul<C, R, SM>), grid, dim3(WAVE * WPB), 0, st, m, x, S, y);
     }
@@ -1699,7 +1711,9 @@ template <int C>
 hipError_t matmul_c(const MatDev &m, const float *x, int S, float *y, hipStream_t st) {
     if constexpr (gemm_codec<C>())
         if (S >= gemm_min_s<C>() && m.K % 32 == 0) return go_gemm<C, false>(m, m, x, S, y, INFINITY, st);
-    if (S >= 8) return go_matmul<C, DQG_MM_R8, 8>(m, x, S, y, st);
+    // int3's 64-input chunks: 8 tokens at a time would spill, 4 fit with x in LDS
+    if constexpr (C != C_I3)
+        if (S >= 8) return go_matmul<C, DQG_MM_R8, 8>(m, x, S, y, st);
     if (S >= 4) return go_matmul<C, DQG_MM_R4, 4>(m, x, S, y, st);
     if (S >= 2) return go_matmul<C, DQG_MM_R2, 2>(m, x, S, y, st);
     return go_matmul<C, DQG_MM_R1, 1>(m, x, S, y, st);
@@ -1709,7 +1723,13 @@ template <int C, int R, int SM>
 hipError_t go_gate_up(const MatDev &g, const MatDev &u, const float *x, int S, float *h, float L, hipStream_t st) {
     const int rows_per_block = R * WPB;
     dim3 grid((g.O + rows_per_block - 1) / rows_per_block);
-    launch("gate_up", (k_gate_up<C, R, SM>), grid, dim3(WAVE * WPB), 0, st, g, u, x, S, h, L);
+    if constexpr (DQG_GU_LDS && SM * WAVE * Codec<C>::CW * 4 <= MM_LDS_BYTES) {
+        const int KC = matmul_kc<C, SM>(g.K);
+        launch("gate_up", (k_rows_lds<C, R, SM, true>), grid, dim3(WAVE * WPB),
+               (size_t)SM * x_lds_len<Codec<C>::CW>(KC) * 4, st, g, u, x, S, h, KC, L);
+    } else {
+        launch("gate_up", (k_gate_up<C, R, SM>), grid, dim3(WAVE * WPB), 0, st, g, u, x, S, h, L);
+    }
     return hipGetLastError();
 }
 
@@ -1717,7 +1737,9 @@ template <int C>
 hipError_t gate_up_c(const MatDev &g, const MatDev &u, const float *x, int S, float *h, float L, hipStream_t st) {
     if constexpr (gemm_codec<C>())
         if (S >= gemm_min_s_gu<C>() && g.K % 32 == 0) return go_gemm<C, true>(g, u, x, S, h, L, st);
-    if (S >= 8) return go_gate_up<C, 1, 8>(g, u, x, S, h, L, st);
+    // int3's 64-input chunks: 8 tokens at a time would spill, 4 fit with x in LDS
+    if constexpr (C != C_I3)
+        if (S >= 8) return go_gate_up<C, 2, 8>(g, u, x, S, h, L, st);
     if (S >= 4) return go_gate_up<C, 2, 4>(g, u, x, S, h, L, st);
     if (S >= 2) return go_gate_up<C, 4, 2>(g, u, x, S, h, L, st);
     return go_gate_up<C, 4, 1>(g, u, x, S, h, L, st);
