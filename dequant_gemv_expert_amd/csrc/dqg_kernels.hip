@@ -1114,23 +1114,24 @@ __global__ void __launch_bounds__(WAVE * down_max_waves<CAP>()) k_group_down(Gro
 }
 
 // ---------------------------------------------------------------------------
-// Prefill GEMM on the matrix cores, for 16 or more tokens (the pages move a
-// batch of 16 or more rows to a tiled GEMM): Y[s][o] = W[o] . x[s], and
-// gate_up's h = silu(G x) * (U x).
+// Prefill GEMM on the matrix cores, for batches of several tokens (the
+// pages move a batch of 16 or more rows to a tiled GEMM): Y[s][o] =
+// W[o] . x[s], and gate_up's h = silu(G x) * (U x).
 //
 // v_mfma_f32_16x16x32_f16 computes D (16 rows x 16 tokens, f32) from
 // A (16 rows x 32 inputs, f16) and B (32 inputs x 16 tokens, f16).  Lane
 // layout: A lane l holds row l%16, inputs 8(l/16)..+8 of the window; B lane
 // l holds token l%16, the same inputs; D lane l holds rows 4(l/16)..+4 of
-// token l%16.  A is the decoded f16 pattern of the codes (exact: the matrix
-// cores keep f16 subnormals); B is x' = x * 2^-e split as f16 hi + lo, with
-// e per token and k-step so that x' fits f16, which leaves x' - hi - lo
-// below 2^-22 |x'|.  A 32-input window never crosses a scale group, so each
-// window's D is offset-corrected and scaled on the vector unit:
-//   acc += scale * VMUL * 2^e * (D - OFFS * sum(x' over the window)).
+// token l%16.  A is the code's value as an f16: the decoded pattern, less
+// the code offset for the offset formats (both exact: the values are
+// integer multiples of 2^-24, and the matrix cores keep f16 subnormals).
+// B is x' = x * 2^-e split as f16 hi + lo, with e per token and 32-input
+// window so that x' fits f16, which leaves x' - hi - lo below 2^-22 |x'|.
+// A window never crosses a scale group, so each window's D is scaled on the
+// vector unit:  acc += (scale * VMUL * 2^e) * D.
 // A block is 4 waves; a wave holds 2 row tiles (32 rows of W, or 16 rows of
-// G and the same 16 of U) for NC token tiles of 16.  x' for 64 tokens x 128
-// inputs is staged in LDS per k-step, in the order the decode emits.
+// G and the same 16 of U) for NC token tiles of 16.  x' for 16 NC tokens x
+// GK inputs is staged in LDS per k-step, in the order the decode emits.
 // ---------------------------------------------------------------------------
 typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 
@@ -1217,12 +1218,15 @@ constexpr int GROWS = 128;         // row slots per block: 4 waves x 2 tiles x 1
 // k_gemm_reduce adds up in the same order: the bits are the same either way.
 constexpr int GEMM_KC = 512;
 
+// 16-byte aligned so that the operand reads and the staging writes are
+// single ds_read_b128 / ds_write_b128 (with 4-byte alignment the compiler
+// splits each into dword pairs, twice the LDS instructions, and dword
+// accesses at the operand's row stride collide in the banks).
 template <int NC>
-struct GemmLds {
+struct alignas(16) GemmLds {
     static constexpr int GK = gemm_k<NC>(), GWIN = GK / 32, GT = 16 * NC, XS = GK + 8;   // XS padded
     _Float16 xh[GT][XS];
     _Float16 xl[GT][XS];
-    float xo[GT][GWIN];    // OFFS * sum of x' over each window
     float xe[GT][GWIN];    // 2^e of the token for each window
     float sc[GWIN][GROWS]; // scale * VMUL per window and row slot
 };
@@ -1323,7 +1327,6 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
                 mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
             int ex = 0;
             if (mx > 0.f) { frexpf(mx, &ex); ex -= 15; }   // mx * 2^-ex < 2^15
-            float xs = 0.f;
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 h16x8 hi, lo;
@@ -1334,12 +1337,10 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
                     const _Float16 h = (_Float16)xv;
                     hi[p] = h;
                     lo[p] = (_Float16)(xv - (float)h);
-                    xs += xv;
                 }
                 *(LDS h16x8 *)&L.xh[tt][32 * qq + 8 * g] = hi;
                 *(LDS h16x8 *)&L.xl[tt][32 * qq + 8 * g] = lo;
             }
-            L.xo[tt][qq] = Cd::OFFS * xs;
             L.xe[tt][qq] = ldexpf(1.f, ex);
         }
 #pragma unroll
@@ -1349,13 +1350,33 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
         }
         __syncthreads();
         if (k0 + GK < kend) fetch(k0 + GK);   // next step's requests go out now
-        for (int j = 0; j < nwin; ++j) {
+        // the 2^e of every window of this step, for the tokens of this lane's D columns
+        float xe[NC][GWIN];
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int q = 0; q < GWIN / 4; ++q) {
+                const f32x4 e4 = *(LDS f32x4 *)&L.xe[16 * c + lr][4 * q];
+                xe[c][4 * q] = e4.x; xe[c][4 * q + 1] = e4.y; xe[c][4 * q + 2] = e4.z; xe[c][4 * q + 3] = e4.w;
+            }
+#pragma unroll
+        for (int j = 0; j < GWIN; ++j) {
+            if (j >= nwin) break;
             h16x8 a[2];
             f32x4 sc4[2];
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 uint32_t pr[4];
                 Gc::decode(raw[t][j], pr);
+                if constexpr (Cd::OFFS != 0.f) {
+                    // offset codes to signed values: exact, the f16 patterns
+                    // are integer multiples of 2^-24 far below f16's precision
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const half2_t o = half2_t{(_Float16)(-Cd::OFFS), (_Float16)(-Cd::OFFS)};
+                        pr[q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, pr[q]) + o);
+                    }
+                }
                 a[t] = __builtin_bit_cast(h16x8, u32x4{pr[0], pr[1], pr[2], pr[3]});
                 sc4[t] = *(LDS f32x4 *)&L.sc[j][32 * w + 16 * t + 4 * lq];
             }
@@ -1364,15 +1385,14 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
                 const int tok = 16 * c + lr;
                 const h16x8 bh = *(LDS h16x8 *)&L.xh[tok][32 * j + 8 * lq];
                 const h16x8 bl = *(LDS h16x8 *)&L.xl[tok][32 * j + 8 * lq];
-                // the D lanes of token 16c + lane%16 take its offset and 2^e
-                const float xo = L.xo[tok][j], xe = L.xe[tok][j];
 #pragma unroll
                 for (int t = 0; t < 2; ++t) {
                     f32x4 d = {0.f, 0.f, 0.f, 0.f};
                     d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bh, d, 0, 0, 0);
                     d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], bl, d, 0, 0, 0);
+                    // the D lanes of token 16c + lane%16 take its window's 2^e
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc[t][c][i] = fmaf(sc4[t][i] * xe, d[i] - xo, acc[t][c][i]);
+                    for (int i = 0; i < 4; ++i) acc[t][c][i] = fmaf(sc4[t][i] * xe[c][j], d[i], acc[t][c][i]);
                 }
             }
         }
