@@ -1231,6 +1231,30 @@ struct alignas(16) GemmLds {
     float sc[GWIN][GROWS]; // scale * VMUL per window and row slot
 };
 
+// One 32-input window of a token as the B operand: x' = x * 2^-e with e
+// chosen so that max |x'| < 2^15, split as f16 hi + lo, quarter g (8
+// inputs) in the decode's order PERM.  Returns 2^e.
+template <int C>
+__device__ __forceinline__ float split_window(const f32x4 (&v)[8], h16x8 (&hi)[4], h16x8 (&lo)[4]) {
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
+    int ex = 0;
+    if (mx > 0.f) { frexpf(mx, &ex); ex -= 15; }   // mx * 2^-ex < 2^15
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+            const int i = 8 * g + GemmCodec<C>::PERM[p];
+            const float xv = ldexpf(v[i >> 2][i & 3], -ex);
+            const _Float16 h = (_Float16)xv;
+            hi[g][p] = h;
+            lo[g][p] = (_Float16)(xv - (float)h);
+        }
+    return ldexpf(1.f, ex);
+}
+
 // Row of slot (wave w, tile t, lane row r) and the matrix it comes from.
 template <bool GU>
 __device__ __forceinline__ int gemm_row(int block_row, int w, int t, int r) {
@@ -1241,16 +1265,21 @@ __device__ __forceinline__ int gemm_row(int block_row, int w, int t, int r) {
 // Otherwise the block sums chunk blockIdx.z only and writes the raw sums to
 // ws[(z * MATS + mat) * S + s][row] (MATS = 2 for GU, gate then up, else 1;
 // rows 0 .. gridDim.x * rows per block - 1 all have a slot, row stride op).
+// With 2 or 4 token tiles the LDS tile is double-buffered (one barrier per
+// k-step; two blocks still fit a CU); with one it is single (its tile is
+// larger).
 template <int C, bool GU, int NC>
-__global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float *__restrict__ x, int S,
-                                              float *__restrict__ y, float limit, float *__restrict__ ws, int op) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2)))
+k_gemm(MatDev m0, MatDev m1, const float *__restrict__ x, int S, float *__restrict__ y, float limit,
+       float *__restrict__ ws, int op) {
     using Gc = GemmCodec<C>;
     using Cd = Codec<C>;
     using Lt = GemmLds<NC>;
     constexpr int GK = Lt::GK, GWIN = Lt::GWIN;
     constexpr int TPT = 256 / Lt::GT;   // staging threads per token, one window each
     static_assert(TPT * 32 == GK, "one staging thread per token and window");
-    __shared__ Lt L;
+    constexpr bool DB = NC > 1;
+    __shared__ Lt Ls[DB ? 2 : 1];
     const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = wave_id();
     const int O = m0.O, K = m0.K;
     const int block_row = blockIdx.x * (GU ? GROWS / 2 : GROWS);
@@ -1309,7 +1338,9 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
         }
     };
     fetch(kbeg);
+    int buf = 0;
     for (int k0 = kbeg; k0 < kend; k0 += GK) {
+        Lt &L = Ls[buf];
         const int nwin = min(GWIN, (kend - k0) / 32);
         f32x4 v[8];
 #pragma unroll
@@ -1318,30 +1349,20 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
             for (int j = 0; j < GWIN; ++j) raw[t][j] = raw_n[t][j];
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = xv_n[i];
-        __syncthreads();   // the previous step's readers of L are done
+        // Single buffer: the previous step's readers of L must be done.
+        // Double: L was last read two steps ago, before the barrier below
+        // of the previous step, which every wave has passed.
+        if (!DB) __syncthreads();
         // stage x' of token tt, window qq, scaled by a power of two of its own
         {
-            float mx = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                mx = fmaxf(mx, fmaxf(fmaxf(fabsf(v[i].x), fabsf(v[i].y)), fmaxf(fabsf(v[i].z), fabsf(v[i].w))));
-            int ex = 0;
-            if (mx > 0.f) { frexpf(mx, &ex); ex -= 15; }   // mx * 2^-ex < 2^15
+            h16x8 hi[4], lo[4];
+            const float e2 = split_window<C>(v, hi, lo);
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                h16x8 hi, lo;
-#pragma unroll
-                for (int p = 0; p < 8; ++p) {
-                    const int i = 8 * g + Gc::PERM[p];
-                    const float xv = ldexpf(v[i >> 2][i & 3], -ex);
-                    const _Float16 h = (_Float16)xv;
-                    hi[p] = h;
-                    lo[p] = (_Float16)(xv - (float)h);
-                }
-                *(LDS h16x8 *)&L.xh[tt][32 * qq + 8 * g] = hi;
-                *(LDS h16x8 *)&L.xl[tt][32 * qq + 8 * g] = lo;
+                *(LDS h16x8 *)&L.xh[tt][32 * qq + 8 * g] = hi[g];
+                *(LDS h16x8 *)&L.xl[tt][32 * qq + 8 * g] = lo[g];
             }
-            L.xe[tt][qq] = ldexpf(1.f, ex);
+            L.xe[tt][qq] = e2;
         }
 #pragma unroll
         for (int h = 0; h < SCN; ++h) {
@@ -1407,6 +1428,7 @@ __global__ void __launch_bounds__(256) k_gemm(MatDev m0, MatDev m1, const float 
                         acc[t][c][i] = 0.f;
                     }
         }
+        if (DB) buf ^= 1;
     }
     // D lane layout: rows 4*lq + i of each tile, token 16c + lr
 #pragma unroll
@@ -1675,10 +1697,11 @@ hipError_t go_gemm_nc(const MatDev &m0, const MatDev &m1, const float *x, int S,
     const int rows_per_block = GU ? GROWS / 2 : GROWS;
     const int O = m0.O, nch = (m0.K + GEMM_KC - 1) / GEMM_KC;
     dim3 grid((O + rows_per_block - 1) / rows_per_block, (S + 16 * NC - 1) / (16 * NC));
-    if (nch == 1 || (size_t)grid.x * grid.y >= DQG_GEMM_SPLIT_BELOW) {
+    const auto plain = [&]() {   // each block walks all of K
         launch(name, (k_gemm<C, GU, NC>), grid, dim3(256), 0, st, m0, m1, x, S, y, L, (float *)nullptr, 0);
         return hipGetLastError();
-    }
+    };
+    if (nch == 1 || (size_t)grid.x * grid.y >= DQG_GEMM_SPLIT_BELOW) return plain();
     const int op = grid.x * rows_per_block;
     const size_t bytes = (size_t)nch * (GU ? 2 : 1) * S * op * sizeof(float);
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -1686,10 +1709,7 @@ hipError_t go_gemm_nc(const MatDev &m0, const MatDev &m1, const float *x, int S,
     if (e != hipSuccess) return e;
     int dev = 0;
     if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
-    if (bytes > WS_MAX || cs != hipStreamCaptureStatusNone || dev < 0 || dev >= 64) {
-        launch(name, (k_gemm<C, GU, NC>), grid, dim3(256), 0, st, m0, m1, x, S, y, L, (float *)nullptr, 0);
-        return hipGetLastError();
-    }
+    if (bytes > WS_MAX || cs != hipStreamCaptureStatusNone || dev < 0 || dev >= 64) return plain();
     Workspace &W = g_ws[dev];
     std::lock_guard<std::mutex> lock(W.mu);
     if (!W.done && (e = hipEventCreateWithFlags(&W.done, hipEventDisableTiming)) != hipSuccess) return e;
