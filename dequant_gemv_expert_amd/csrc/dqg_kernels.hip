@@ -107,13 +107,18 @@ typedef const LDS float *lfloats;
 // 256 bytes).  Chunks of 16 inputs (a 64-byte stride, 2-way conflicts)
 // stay unpadded: the padding's address arithmetic cost the one-token int8
 // launch its register budget.  Chunks of 8 or fewer are conflict-free.
-template <int CW>
-__host__ __device__ constexpr int x_pad() { return CW >= 32 ? 4 : 0; }
+// The expert group's gate/up launch stages x unpadded (P false): there the
+// 12% more LDS per block costs a resident block per CU with 2 tokens (3 x
+// 48 KB fit 160 KB, 3 x 54 KB do not; measured 54 against 62 us at 2
+// tokens), and at 1 token it measured the same either way.
+template <int CW, bool P = true>
+__host__ __device__ constexpr int x_pad() { return P && CW >= 32 ? 4 : 0; }
 // LDS floats of n inputs of x (n a multiple of CW), and the LDS index of input k
-template <int CW>
-__host__ __device__ constexpr int x_lds_len(int n) { return n + x_pad<CW>() * (n / CW); }
-template <int CW>
-__device__ __forceinline__ uint32_t x_lds_at(uint32_t k) { return k + x_pad<CW>() * (k / CW); }
+template <int CW, bool P = true>
+__host__ __device__ constexpr int x_lds_len(int n) { return n + x_pad<CW, P>() * (n / CW); }
+template <int CW, bool P = true>
+__device__ __forceinline__ uint32_t x_lds_at(uint32_t k) { return k + x_pad<CW, P>() * (k / CW); }
+constexpr bool GROUP_XPAD = false;
 
 struct XGlobal {
     gfloats p;
@@ -121,11 +126,12 @@ struct XGlobal {
     template <int CW>
     __device__ __forceinline__ float4 load4(uint32_t cu, uint32_t off) const { return ldf4(p, cu * CW + off); }
 };
-struct XLds {
-    lfloats p;   // the token's row, laid out by x_lds_at
+template <bool P>
+struct XLdsT {
+    lfloats p;   // the token's row, laid out by x_lds_at<CW, P>
     template <int CW>
     __device__ __forceinline__ float4 load4(uint32_t cu, uint32_t off) const {
-        const f32x4 v = *(const LDS f32x4 *)(p + x_lds_at<CW>(cu * CW) + off);
+        const f32x4 v = *(const LDS f32x4 *)(p + x_lds_at<CW, P>(cu * CW) + off);
         return make_float4(v.x, v.y, v.z, v.w);
     }
 };
@@ -554,7 +560,7 @@ __device__ __forceinline__ void dot_rows(const GRow (&rows)[NR], int nch, int sh
 // time instead of SM * CW; the operations and their order are those of
 // step_compute, so the results have the same bits.  x + s * xstride is
 // token s's row of the staged x.
-template <int C, int NR, int SM>
+template <int C, int NR, int SM, bool P = true>
 __device__ __forceinline__ void step_compute_lds(const Step<C, NR, SM> &st, lfloats x, uint32_t xstride,
                                                  uint32_t cu, float (&acc)[NR][SM]) {
     using Cd = Codec<C>;
@@ -572,7 +578,7 @@ __device__ __forceinline__ void step_compute_lds(const Step<C, NR, SM> &st, lflo
         for (int s = 0; s < SM; ++s)
 #pragma unroll
             for (int i = 0; i < Cd::UW / 4; ++i) {
-                const f32x4 t = *(const LDS f32x4 *)(x + s * xstride + x_lds_at<Cd::CW>(cu * Cd::CW) + u * Cd::UW + 4 * i);
+                const f32x4 t = *(const LDS f32x4 *)(x + s * xstride + x_lds_at<Cd::CW, P>(cu * Cd::CW) + u * Cd::UW + 4 * i);
                 xv[s][4 * i] = t.x; xv[s][4 * i + 1] = t.y; xv[s][4 * i + 2] = t.z; xv[s][4 * i + 3] = t.w;
             }
         if (Cd::OFFS != 0.f) {
@@ -623,7 +629,7 @@ __device__ __forceinline__ void dot_rows_lds1(Step<C, NR, 1> &st, bool have, con
         const uint32_t cu = opaque((uint32_t)c);
         if (!(have && c == lane)) step_load_w(st, rows, shift, cu);
         __builtin_amdgcn_sched_barrier(0);
-        step_compute_lds(st, x, 0u, cu, acc);
+        step_compute_lds<C, NR, 1, GROUP_XPAD>(st, x, 0u, cu, acc);
     }
 }
 
@@ -916,7 +922,7 @@ __device__ __forceinline__ void stage_x(const GroupArgs &a, const SlotBatch &b, 
                 if (i0 + u * NT < n4) v[u] = src[i0 + u * NT];
 #pragma unroll
             for (int u = 0; u < U; ++u)
-                if (i0 + u * NT < n4) *(LDS f32x4 *)(xs + x_lds_at<CW>(4 * (i0 + u * NT))) = v[u];
+                if (i0 + u * NT < n4) *(LDS f32x4 *)(xs + x_lds_at<CW, GROUP_XPAD>(4 * (i0 + u * NT))) = v[u];
         }
     } else {
         const int total = SM * (int)n4;
@@ -939,7 +945,7 @@ __device__ __forceinline__ void stage_x(const GroupArgs &a, const SlotBatch &b, 
                 const int i = i0 + u * (int)NT;
                 if (i < total) {
                     const int s = i / (int)n4, k4 = i - s * (int)n4;
-                    *(LDS f32x4 *)(xs + (size_t)s * x_lds_len<CW>(a.H) + x_lds_at<CW>(4 * k4)) = v[u];
+                    *(LDS f32x4 *)(xs + (size_t)s * x_lds_len<CW, GROUP_XPAD>(a.H) + x_lds_at<CW, GROUP_XPAD>(4 * k4)) = v[u];
                 }
             }
         }
@@ -960,9 +966,9 @@ __device__ __forceinline__ void group_gu_batch(const GroupArgs &a, const ExpertD
             rows[R + r] = row_ptrs(ex.up, min(row0 + r, a.I - 1));
         }
     };
-    XLds xp[SM];
+    XLdsT<GROUP_XPAD> xp[SM];
 #pragma unroll
-    for (int s = 0; s < SM; ++s) xp[s] = {xs + (size_t)s * x_lds_len<Codec<C>::CW>(a.H)};
+    for (int s = 0; s < SM; ++s) xp[s] = {xs + (size_t)s * x_lds_len<Codec<C>::CW, GROUP_XPAD>(a.H)};
     float acc[2 * R][SM];
     GRow rows[2 * R];
     if constexpr (SM == 1) {
@@ -978,7 +984,7 @@ __device__ __forceinline__ void group_gu_batch(const GroupArgs &a, const ExpertD
     } else {
         stage_x<SM, Codec<C>::CW>(a, b, xs);
         row_set(rows);
-        dot_rows<C, 2 * R, SM, DQG_PIPE, XLds>(rows, nch, ex.gate.shift, xp, acc);
+        dot_rows<C, 2 * R, SM, DQG_PIPE, XLdsT<GROUP_XPAD>>(rows, nch, ex.gate.shift, xp, acc);
     }
     float gv = 0.f, uv = 0.f;
 #pragma unroll
@@ -1798,7 +1804,7 @@ template <int C, int CAP>
 hipError_t group_a_cap(const GroupArgs &a, hipStream_t st) {
     const int units = a.S * a.k + (a.shared >= 0 ? 1 : 0);
     const int rows_per_block = RA * WPB_A;
-    const size_t lds = (size_t)CAP * x_lds_len<Codec<C>::CW>(a.H) * sizeof(float);
+    const size_t lds = (size_t)CAP * x_lds_len<Codec<C>::CW, GROUP_XPAD>(a.H) * sizeof(float);
     dim3 grid((a.I + rows_per_block - 1) / rows_per_block, units);
     if constexpr (CAP == 1 && C != C_I3)
         launch("group_gate_up", (k_group_gate_up1<C, RA>), grid, dim3(WAVE * WPB_A), lds, st, a);
