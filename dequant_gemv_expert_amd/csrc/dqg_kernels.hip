@@ -1643,11 +1643,11 @@ hipError_t go_matmul(const MatDev &m, const float *x, int S, float *y, hipStream
 // The matrix-core GEMM from this many tokens on: where it measured faster
 // than the per-row route on MI355X.  The per-row route takes its tokens 8 at
 // a time, so 9 to 16 tokens cost it two passes over the weights; the GEMM
-// with split-K costs about the same from 8 to 16 tokens.  On 6144 x 6144,
-// 8 tokens: per row 30-35 us, GEMM 34-52 us; 10 tokens: per row 54-66 us,
-// GEMM 34-52 us, in every GEMM format.  gate_up (2 x 2048 x 6144) at 8
-// tokens: int4 54 us per row against 29 GEMM, E4M3 30 against 28, int8 35
-// against 33, f16 26 against 35.
+// with split-K costs about the same from 8 to 16 tokens.  Kernel times on
+// 6144 x 6144: matmul at 8 tokens per row 29-36 us, GEMM 28-37 us (even);
+// at 9 tokens per row 54-66 us, GEMM 27-37 us.  gate_up (two such
+// matrices) at 8 tokens: int4 53 us per row against 48 GEMM, E4M3 49
+// against 41, f16 58 against 51, int8 57 against 61.
 template <int C>
 constexpr int gemm_min_s() {
 #ifdef DQG_GEMM_MIN_S
@@ -1661,7 +1661,7 @@ constexpr int gemm_min_s_gu() {
 #ifdef DQG_GEMM_MIN_S_GU
     return DQG_GEMM_MIN_S_GU;
 #else
-    return C == C_F16 ? 9 : 8;
+    return C == C_I8 ? 9 : 8;
 #endif
 }
 

@@ -174,7 +174,7 @@ int dqg_matmul(const dqg_matrix *W, const float *x, int32_t S, float *y, void *s
  * The SwiGLU half of an expert MLP in one launch with x read once (the
  * guide's API-contract section, coli_vk_gate_up).  G and U: [I x H] of one
  * format; x: f32 [S][H]; h: f32 [S][I].  Routes and the partials buffer as
- * for dqg_matmul, with the GEMM from 8 tokens (9 for format 14).
+ * for dqg_matmul, with the GEMM from 8 tokens (9 for formats 1 and 13).
  */
 int dqg_gate_up(const dqg_matrix *G, const dqg_matrix *U, const float *x, int32_t S, float *h,
                 void *stream);

@@ -7,7 +7,7 @@ compare as NaN, whatever their payload), and every output within 1e-5 of its
 row's normaliser sum_k |w*x|.  The shapes have ragged rows (and ragged
 128-row scale blocks), K that is not a multiple of a wave's 64 chunks, and
 batches on both sides of the matrix-core cut-overs (matmul from 9 tokens,
-gate_up from 8, 9 for format 14; formats 10 and 11 stay on the per-row
+gate_up from 8, 9 for formats 1 and 13; formats 10 and 11 stay on the per-row
 route).
 """
 import numpy as np

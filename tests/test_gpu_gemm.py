@@ -1,6 +1,6 @@
 """Parity of the matrix-core GEMM route with the CPU oracle.
 
-dqg_matmul (from 9 tokens) and dqg_gate_up (from 8, 9 for f16 rows) take
+dqg_matmul (from 9 tokens) and dqg_gate_up (from 8, 9 for int8 codes) take
 the route when K is a multiple of 32; the batches below straddle the
 cut-overs and the token-tile sizes.  Bar: as for the GEMV route, every
 output within 1e-5 of its row's normaliser sum_k |w*x|.  The route's own
