@@ -616,12 +616,67 @@ __device__ __forceinline__ void step_compute_lds(const Step<C, NR, SM> &st, lflo
             acc[r][s] = fmaf(st.sc[r] * Cd::VMUL, fmaf(-Cd::OFFS, xs[s], p[r][s]), acc[r][s]);
 }
 
+// step_compute_lds for one token, rows in pairs: all units of a pair before
+// the next pair, so that a pair's arithmetic waits only for its own rows'
+// loads (a step's loads go out in row order) and arithmetic overlaps the
+// arrival of the later rows.  x is read again per pair; the chunk's sum of x
+// (for the code offset) comes from LDS, summed at staging in the order
+// step_compute and step_compute_lds sum it, so the bits are theirs.
+template <int C, int NR, bool P>
+__device__ __forceinline__ void step_compute_lds_pairs(const Step<C, NR, 1> &st, lfloats x, float xsum, uint32_t cu,
+                                                       float (&acc)[NR][1]) {
+    using Cd = Codec<C>;
+    static_assert(NR % 2 == 0, "rows in pairs");
+#pragma unroll
+    for (int r0 = 0; r0 < NR; r0 += 2) {
+        float p[2] = {0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < Cd::UNITS; ++u) {
+            float xv[Cd::UW];
+#pragma unroll
+            for (int i = 0; i < Cd::UW / 4; ++i) {
+                const f32x4 t = *(const LDS f32x4 *)(x + x_lds_at<Cd::CW, P>(cu * Cd::CW) + u * Cd::UW + 4 * i);
+                xv[4 * i] = t.x; xv[4 * i + 1] = t.y; xv[4 * i + 2] = t.z; xv[4 * i + 3] = t.w;
+            }
+#pragma unroll
+            for (int rr = 0; rr < 2; ++rr) {
+                if constexpr (Cd::WIDE) {
+                    float v[Cd::UW];
+                    Cd::decode_f(st.ch[r0 + rr], u, v);
+#pragma unroll
+                    for (int i = 0; i < Cd::UW; ++i) p[rr] = fmaf(v[i], xv[i], p[rr]);
+                } else {
+                    uint32_t pr[Cd::UW / 2];
+                    Cd::decode(st.ch[r0 + rr], u, pr);
+#pragma unroll
+                    for (int q = 0; q < Cd::UW / 2; ++q) {
+                        p[rr] = fma_lo(pr[q], xv[Cd::IDX[2 * q]], p[rr]);
+                        p[rr] = fma_hi(pr[q], xv[Cd::IDX[2 * q + 1]], p[rr]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+            acc[r0 + rr][0] = fmaf(st.sc[r0 + rr] * Cd::VMUL, fmaf(-Cd::OFFS, xsum, p[rr]), acc[r0 + rr][0]);
+    }
+}
+
+#ifndef DQG_GU1_PAIRS
+#define DQG_GU1_PAIRS 1
+#endif
+// Whether the one-token group path takes its rows in pairs (and so stages
+// the chunk sums of x): codes with an offset, rows in pairs.
+template <int C, int NR>
+constexpr bool gu1_pairs() { return DQG_GU1_PAIRS && NR % 2 == 0; }
+
 // dot_rows for one token with x in LDS, when the caller has already issued
 // the codes and scales of this lane's first chunk into st (have: this lane
 // has a first chunk), e.g. before staging x, so that both latencies overlap.
+// xsum: the chunk sums of x (used with gu1_pairs).
 template <int C, int NR>
 __device__ __forceinline__ void dot_rows_lds1(Step<C, NR, 1> &st, bool have, const GRow (&rows)[NR], int nch,
-                                              int shift, lfloats x, float (&acc)[NR][1]) {
+                                              int shift, lfloats x, lfloats xsum, float (&acc)[NR][1]) {
     const int lane = threadIdx.x & (WAVE - 1);
 #pragma unroll
     for (int r = 0; r < NR; ++r) acc[r][0] = 0.f;
@@ -629,7 +684,10 @@ __device__ __forceinline__ void dot_rows_lds1(Step<C, NR, 1> &st, bool have, con
         const uint32_t cu = opaque((uint32_t)c);
         if (!(have && c == lane)) step_load_w(st, rows, shift, cu);
         __builtin_amdgcn_sched_barrier(0);
-        step_compute_lds<C, NR, 1, GROUP_XPAD>(st, x, 0u, cu, acc);
+        if constexpr (gu1_pairs<C, NR>())
+            step_compute_lds_pairs<C, NR, GROUP_XPAD>(st, x, Codec<C>::OFFS != 0.f ? xsum[cu] : 0.f, cu, acc);
+        else
+            step_compute_lds<C, NR, 1, GROUP_XPAD>(st, x, 0u, cu, acc);
     }
 }
 
@@ -908,7 +966,7 @@ __device__ __forceinline__ void for_slots(const GroupArgs &a, int q, int e, F &&
 // kernels hold more registers) before its first LDS write, so the copy
 // costs one round trip per batch of loads, not one per load.
 template <int SM, int CW>
-__device__ __forceinline__ void stage_x(const GroupArgs &a, const SlotBatch &b, lfloats_w xs) {
+__device__ __forceinline__ void stage_x(const GroupArgs &a, const SlotBatch &b, lfloats_w xs, bool sums = false) {
     constexpr int U = SM == 1 ? 8 : 4;
     constexpr uint32_t NT = WAVE * WPB_A;   // the gate/up launch's block size
     __syncthreads();   // the previous batch's readers are done
@@ -951,6 +1009,23 @@ __device__ __forceinline__ void stage_x(const GroupArgs &a, const SlotBatch &b, 
         }
     }
     __syncthreads();
+    if (SM == 1 && sums) {
+        // the sum of each chunk of x, in input order, after the row
+        lfloats_w xsum = xs + x_lds_len<CW, GROUP_XPAD>(a.H);
+        for (int t = threadIdx.x; t < a.H / CW; t += (int)NT) {
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < CW / 4; ++i) {
+                const f32x4 v = *(const LDS f32x4 *)(xs + x_lds_at<CW, GROUP_XPAD>((uint32_t)(t * CW + 4 * i)));
+                acc += v.x;
+                acc += v.y;
+                acc += v.z;
+                acc += v.w;
+            }
+            xsum[t] = acc;
+        }
+        __syncthreads();
+    }
 }
 
 // gate_up of R rows (row0..) of expert e for a batch of SM slots, x from LDS.
@@ -979,8 +1054,10 @@ __device__ __forceinline__ void group_gu_batch(const GroupArgs &a, const ExpertD
         Step<C, 2 * R, SM> st;
         const bool have = lane < nch;
         if (have) step_load_w(st, rows, ex.gate.shift, opaque((uint32_t)lane));
-        stage_x<SM, Codec<C>::CW>(a, b, xs);
-        dot_rows_lds1<C, 2 * R>(st, have, rows, nch, ex.gate.shift, xs, acc);
+        constexpr bool sums = gu1_pairs<C, 2 * R>() && Codec<C>::OFFS != 0.f;
+        stage_x<SM, Codec<C>::CW>(a, b, xs, sums);
+        dot_rows_lds1<C, 2 * R>(st, have, rows, nch, ex.gate.shift, xs, xs + x_lds_len<Codec<C>::CW, GROUP_XPAD>(a.H),
+                                acc);
     } else {
         stage_x<SM, Codec<C>::CW>(a, b, xs);
         row_set(rows);
@@ -1804,7 +1881,9 @@ template <int C, int CAP>
 hipError_t group_a_cap(const GroupArgs &a, hipStream_t st) {
     const int units = a.S * a.k + (a.shared >= 0 ? 1 : 0);
     const int rows_per_block = RA * WPB_A;
-    const size_t lds = (size_t)CAP * x_lds_len<Codec<C>::CW, GROUP_XPAD>(a.H) * sizeof(float);
+    // CAP rows of x; a one-token batch keeps the chunk sums of x after its row
+    const size_t lds = ((size_t)CAP * x_lds_len<Codec<C>::CW, GROUP_XPAD>(a.H) +
+                        (CAP == 1 ? (size_t)a.H / Codec<C>::CW : 0)) * sizeof(float);
     dim3 grid((a.I + rows_per_block - 1) / rows_per_block, units);
     if constexpr (CAP == 1 && C != C_I3)
         launch("group_gate_up", (k_group_gate_up1<C, RA>), grid, dim3(WAVE * WPB_A), lds, st, a);
