@@ -15,10 +15,11 @@ weights from the previous steps.
 
 Prints one JSON line: the metric is weight-stream GB/s (algorithmic bytes:
 codes + scales of each distinct expert the step needs, once, plus x and
-y) over wall time; `roofline` is the dominant kernel (the one-launch group
-kernel; the gate/up launch when a call takes the two-launch form) timed
-with HIP events on its stream; `cpu_baseline` is the CPU oracle on a
-bounded sample of the same steps.
+y) over wall time; `roofline` is the dominant kernel (the gate/up launch)
+timed with HIP events on its stream, on the launches of every
+--prof-every-th call of the timed loop (events cost the wall clock about
+8 us a call; every call runs, 1 in 8 is timed by default);
+`cpu_baseline` is the CPU oracle on a bounded sample of the same steps.
 """
 import argparse
 import json
@@ -88,6 +89,9 @@ def main():
     ap.add_argument("--shared-copies", type=int, default=12)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prof-every", type=int, default=8,
+                    help="HIP events on the launches of every N-th call of the timed loop (1: every call); "
+                         "each timed call adds the events' cost to the wall clock")
     ap.add_argument("--gate-up", action="store_true",
                     help="dense workloads: time dqg_gate_up on two matrices of the workload's shape")
     ap.add_argument("--swiglu-limit", type=float, default=None,
@@ -197,9 +201,11 @@ def main():
             raise RuntimeError(dq.dqg_last_error())
     torch.cuda.synchronize()
 
-    # -- timed region (HIP events around each kernel, on its stream) --------
+    # -- timed region (HIP events around the kernels of every --prof-every-th
+    #    call, on their stream) ---------------------------------------------
     K = args.steps
-    dq.dqg_prof_begin(2 * K)
+    every = max(1, args.prof_every)
+    dq.dqg_prof_begin_sampled(2 * (K // every + 1), every)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.warmup, args.warmup + K):
@@ -211,20 +217,17 @@ def main():
     prof = dq.dqg_prof_end()
 
     total_bytes = sum(step_bytes(i) for i in range(args.warmup, args.warmup + K))
-    gu_total = sum(step_bytes_gate_up(i) for i in range(args.warmup, args.warmup + K))
+    timed = range(args.warmup, args.warmup + K, every)   # the calls whose launches carry events
     ms_per_step = t_wall * 1e3 / K
     value = total_bytes / t_wall / 1e9
-    # the dominant kernel: the one-launch group kernel, or the gate/up launch
-    # when the call took the two-launch form
-    if "group_fused" in prof:
-        dom, dom_total = "group_fused", total_bytes
-    else:
-        dom, dom_total = "group_gate_up", gu_total
+    # the dominant kernel: the gate/up launch, its bytes summed over the timed calls
+    dom, dom_total = "group_gate_up", sum(step_bytes_gate_up(i) for i in timed)
     n_dom, ms_dom = prof.get(dom, (0, 0.0))
+    if n_dom != len(timed):
+        raise RuntimeError(f"{n_dom} gate/up launches timed, {len(timed)} expected")
     achieved = dom_total / (ms_dom * 1e-3) / 1e9 if ms_dom > 0 else None
     n_b, ms_b = prof.get("group_down", (0, 0.0))
-    down_total = sum((union[i % P] + n_sh) * down_bytes + h_bytes + S * H * 4
-                     for i in range(args.warmup, args.warmup + K))
+    down_total = sum((union[i % P] + n_sh) * down_bytes + h_bytes + S * H * 4 for i in timed)
     log(f"[bench] {K} steps: {ms_per_step * 1e3:.1f} us/step wall, {value:.0f} GB/s; "
         f"{dom} kernel {ms_dom / max(n_dom, 1) * 1e3:.1f} us avg ({achieved or 0:.0f} GB/s)"
         + (f", down kernel {ms_b / max(n_b, 1) * 1e3:.1f} us avg "
@@ -295,10 +298,11 @@ def main():
                      "traffic": profiled_traffic(dom) if (S == 1 and args.workload ==
                                 "int4g32_expert_group_256top8_shared") else None,
                      "avg_us": round(ms_dom / max(n_dom, 1) * 1e3, 2),
-                     "bytes_per_launch": round(dom_total / K)},
+                     "bytes_per_launch": round(dom_total / max(n_dom, 1)),
+                     "timed_launches": n_dom, "timed_every": every},
         "roofline_down": ({"kernel": "group_down", "avg_us": round(ms_b / max(n_b, 1) * 1e3, 2),
                            "achieved": round(down_total / (ms_b * 1e-3) / 1e9, 1),
-                           "bytes_per_launch": round(down_total / K)} if ms_b else None),
+                           "bytes_per_launch": round(down_total / max(n_b, 1))} if ms_b else None),
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -359,7 +363,8 @@ def bench_gemv(args, c):
         call(i)
     torch.cuda.synchronize()
     K_steps = args.steps
-    dq.dqg_prof_begin(2 * K_steps)   # split-K calls launch two kernels
+    every = max(1, args.prof_every)
+    dq.dqg_prof_begin_sampled(2 * (K_steps // every + 1), every)   # split-K calls launch two kernels
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K_steps):
@@ -384,12 +389,14 @@ def bench_gemv(args, c):
         roof = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2) if achieved else None,
                 "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4) if achieved else None, "traffic": None,
-                "avg_us": round(avg_s * 1e6, 2), "flops_per_launch": flops}
+                "avg_us": round(avg_s * 1e6, 2), "flops_per_launch": flops, "timed_launches": n_k,
+                "timed_every": every}
     else:
         achieved = step_bytes / avg_s / 1e9 if avg_s > 0 else None
         roof = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1) if achieved else None,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
-                "traffic": None, "avg_us": round(avg_s * 1e6, 2), "bytes_per_launch": step_bytes}
+                "traffic": None, "avg_us": round(avg_s * 1e6, 2), "bytes_per_launch": step_bytes,
+                "timed_launches": n_k, "timed_every": every}
     log(f"[bench] {K_steps} steps: {t_wall / K_steps * 1e6:.1f} us/step wall; {kname} kernel "
         f"{avg_s * 1e6:.1f} us avg; {flops / avg_s / 1e12 if avg_s else 0:.1f} TFLOP/s, "
         f"{step_bytes / avg_s / 1e9 if avg_s else 0:.0f} GB/s")

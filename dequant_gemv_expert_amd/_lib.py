@@ -71,6 +71,7 @@ SIGNATURES = {
     "dqg_expert_group_take": (C.c_int, [C.POINTER(dqg_ticket)]),
     "dqg_route": (C.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _P, C.c_float, _P, _P, _P]),
     "dqg_prof_begin": (C.c_int, [_I32]),
+    "dqg_prof_begin_sampled": (C.c_int, [_I32, _I32]),
     "dqg_prof_end": (C.c_int, [C.POINTER(dqg_prof_record), _I32, C.POINTER(_I32)]),
     "dqg_last_error": (C.c_char_p, []),
     "dqg_stats": (None, [C.POINTER(dqg_counters)]),
@@ -307,6 +308,11 @@ def dqg_stats_reset() -> None:
 def dqg_prof_begin(capacity: int) -> None:
     """Time the next ``capacity`` launches with HIP events on their streams."""
     _check(load().dqg_prof_begin(int(capacity)))
+
+
+def dqg_prof_begin_sampled(capacity: int, every: int) -> None:
+    """Time the launches of every `every`-th call, up to `capacity` launches (host-blocking setup)."""
+    _check(load().dqg_prof_begin_sampled(int(capacity), int(every)))
 
 
 def dqg_prof_end() -> dict:

@@ -200,6 +200,8 @@ uint64_t matrix_bytes(const dqg_matrix *W) {
     return codes + scales * 4;
 }
 
+void prof_call();   // event timing: counts an API call (below)
+
 constexpr int32_t MAX_S = 256, MAX_K = 64, MAX_SLOTS = 2048;
 
 // Scratch: a fixed header (the error flag at byte 0; the rest is reserved),
@@ -216,6 +218,7 @@ int group_common(const dqg_expert_table *t, int32_t S, int32_t k, const int32_t 
                  const float *w, int32_t shared, const float *x, float *y, void *scratch,
                  size_t scratch_bytes, void *stream, int32_t **flag_out) {
     ++g_calls_group;
+    prof_call();
     if (!t) return fail(DQG_EINVAL, "expert_group: table is NULL");
     if (S < 1 || S > MAX_S) return fail(DQG_EINVAL, "expert_group: S=%d outside [1, %d]", S, MAX_S);
     if (k < 1 || k > MAX_K) return fail(DQG_EINVAL, "expert_group: k=%d outside [1, %d]", k, MAX_K);
@@ -262,8 +265,18 @@ struct Prof {
     std::vector<hipEvent_t> ev;       // 2 per launch
     std::vector<const char *> name;   // per launch
     int used = 0;
+    int every = 1;                    // time the launches of every every-th call
+    std::atomic<long> calls{0};       // calls since dqg_prof_begin
 };
 Prof g_prof;
+// Whether the calling thread's current API call has its launches timed.
+thread_local bool t_prof_sampled = true;
+
+// Called once at the start of every entry point that launches kernels.
+void prof_call() {
+    if (!g_prof.on.load(std::memory_order_relaxed)) return;
+    t_prof_sampled = g_prof.calls.fetch_add(1, std::memory_order_relaxed) % g_prof.every == 0;
+}
 
 void prof_release() {
     for (hipEvent_t e : g_prof.ev) (void)hipEventDestroy(e);
@@ -275,7 +288,7 @@ void prof_release() {
 }  // namespace
 
 bool dqg::prof_slot(const char *kernel, hipEvent_t *start, hipEvent_t *stop) {
-    if (!g_prof.on.load(std::memory_order_relaxed)) return false;
+    if (!g_prof.on.load(std::memory_order_relaxed) || !t_prof_sampled) return false;
     std::lock_guard<std::mutex> lock(g_prof.mu);
     if (g_prof.used >= (int)g_prof.name.size()) return false;
     *start = g_prof.ev[2 * g_prof.used];
@@ -287,10 +300,15 @@ bool dqg::prof_slot(const char *kernel, hipEvent_t *start, hipEvent_t *stop) {
 
 extern "C" {
 
-int dqg_prof_begin(int32_t capacity) {
+int dqg_prof_begin(int32_t capacity) { return dqg_prof_begin_sampled(capacity, 1); }
+
+int dqg_prof_begin_sampled(int32_t capacity, int32_t every) {
     if (capacity < 1) return fail(DQG_EINVAL, "prof_begin: capacity=%d must be >= 1", capacity);
+    if (every < 1) return fail(DQG_EINVAL, "prof_begin: every=%d must be >= 1", every);
     std::lock_guard<std::mutex> lock(g_prof.mu);
     prof_release();
+    g_prof.every = every;
+    g_prof.calls = 0;
     g_prof.ev.resize(2 * (size_t)capacity, nullptr);
     g_prof.name.assign(capacity, nullptr);
     for (auto &e : g_prof.ev) {
@@ -334,6 +352,7 @@ int dqg_prof_end(dqg_prof_record *out, int32_t max, int32_t *n) {
 
 int dqg_matmul(const dqg_matrix *W, const float *x, int32_t S, float *y, void *stream) {
     ++g_calls_matmul;
+    prof_call();
     MatDev m;
     int rc;
     if ((rc = check_matrix(W, "matmul: W", &m))) return rc;
@@ -359,6 +378,7 @@ int check_limit(float limit, const char *what) {
 int gate_up_common(const dqg_matrix *G, const dqg_matrix *U, const float *x, int32_t S, float limit, float *h,
                    void *stream) {
     ++g_calls_gate_up;
+    prof_call();
     MatDev g, u;
     int rc;
     if ((rc = check_matrix(G, "gate_up: G", &g)) || (rc = check_matrix(U, "gate_up: U", &u))) return rc;
@@ -397,6 +417,7 @@ int dqg_expert_table_set_swiglu_limit(dqg_expert_table *t, float limit) {
 
 int dqg_dequant(const dqg_matrix *W, float *out, void *stream) {
     ++g_calls_dequant;
+    prof_call();
     MatDev m;
     int rc;
     if ((rc = check_matrix(W, "dequant: W", &m))) return rc;
@@ -412,6 +433,7 @@ int dqg_dequant(const dqg_matrix *W, float *out, void *stream) {
 int dqg_route(const float *logits, int32_t S, int32_t E, int32_t k, int32_t mode, int32_t renorm,
               const float *bias, float w_scale, int32_t *ids, float *w, void *stream) {
     ++g_calls_route;
+    prof_call();
     if (S < 1) return fail(DQG_EINVAL, "route: S=%d, need S >= 1", S);
     if (E < 1 || E > ROUTE_MAX_E) return fail(DQG_EINVAL, "route: E=%d outside [1, %d]", E, ROUTE_MAX_E);
     if (k < 1 || k > E || k > 64) return fail(DQG_EINVAL, "route: k=%d outside [1, min(E, 64)]", k);

@@ -302,6 +302,11 @@ typedef struct {
 } dqg_prof_record;
 
 int dqg_prof_begin(int32_t capacity);
+/* dqg_prof_begin that times only the launches of every `every`-th API call
+ * (calls counted from this begin, the first one timed): a timed loop pays
+ * for the events of 1 call in `every` while the averages still come from
+ * its own dispatches.  every >= 1; 1 is dqg_prof_begin. */
+int dqg_prof_begin_sampled(int32_t capacity, int32_t every);
 int dqg_prof_end(dqg_prof_record *out, int32_t max, int32_t *n);
 
 /* Text of the calling thread's last error (never NULL). */
