@@ -16,9 +16,10 @@ weights from the previous steps.
 Prints one JSON line: the metric is weight-stream GB/s (algorithmic bytes:
 codes + scales of each distinct expert the step needs, once, plus x and
 y) over wall time; `roofline` is the dominant kernel (the gate/up launch)
-timed with HIP events on its stream, on the launches of every
---prof-every-th call of the timed loop (events cost the wall clock about
-8 us a call; every call runs, 1 in 8 is timed by default);
+timed with HIP events on its stream.  The steps run twice back to back:
+first with the wall clock only (value, ms_per_step), then with events on
+every launch (roofline; ms_per_step_with_events), because the events
+themselves add about 8 us a call to the wall clock;
 `cpu_baseline` is the CPU oracle on a bounded sample of the same steps.
 """
 import argparse
@@ -89,9 +90,6 @@ def main():
     ap.add_argument("--shared-copies", type=int, default=12)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--prof-every", type=int, default=8,
-                    help="HIP events on the launches of every N-th call of the timed loop (1: every call); "
-                         "each timed call adds the events' cost to the wall clock")
     ap.add_argument("--gate-up", action="store_true",
                     help="dense workloads: time dqg_gate_up on two matrices of the workload's shape")
     ap.add_argument("--swiglu-limit", type=float, default=None,
@@ -201,23 +199,29 @@ def main():
             raise RuntimeError(dq.dqg_last_error())
     torch.cuda.synchronize()
 
-    # -- timed region (HIP events around the kernels of every --prof-every-th
-    #    call, on their stream) ---------------------------------------------
+    # -- timed region 1: the steps back to back, wall clock only ------------
     K = args.steps
-    every = max(1, args.prof_every)
-    dq.dqg_prof_begin_sampled(2 * (K // every + 1), every)
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for i in range(args.warmup, args.warmup + K):
-        rc = fn(*plan[i])
-        if rc:
-            raise RuntimeError(dq.dqg_last_error())
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_start
+
+    def run_steps():
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for i in range(args.warmup, args.warmup + K):
+            rc = fn(*plan[i])
+            if rc:
+                raise RuntimeError(dq.dqg_last_error())
+        torch.cuda.synchronize()
+        return time.perf_counter() - t
+
+    t_wall = run_steps()
+    # -- timed region 2: the same steps with HIP events around every launch,
+    #    on the launch's stream (the events add about 8 us a call to the wall
+    #    clock, which is why value comes from region 1) ---------------------
+    dq.dqg_prof_begin(2 * K)
+    t_wall_events = run_steps()
     prof = dq.dqg_prof_end()
 
     total_bytes = sum(step_bytes(i) for i in range(args.warmup, args.warmup + K))
-    timed = range(args.warmup, args.warmup + K, every)   # the calls whose launches carry events
+    timed = range(args.warmup, args.warmup + K)   # region 2 times every call's launches
     ms_per_step = t_wall * 1e3 / K
     value = total_bytes / t_wall / 1e9
     # the dominant kernel: the gate/up launch, its bytes summed over the timed calls
@@ -282,6 +286,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
         "us_per_call": round(ms_per_step * 1e3, 2),
+        "ms_per_step_with_events": round(t_wall_events * 1e3 / K, 5),
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -299,7 +304,7 @@ def main():
                                 "int4g32_expert_group_256top8_shared") else None,
                      "avg_us": round(ms_dom / max(n_dom, 1) * 1e3, 2),
                      "bytes_per_launch": round(dom_total / max(n_dom, 1)),
-                     "timed_launches": n_dom, "timed_every": every},
+                     "timed_launches": n_dom},
         "roofline_down": ({"kernel": "group_down", "avg_us": round(ms_b / max(n_b, 1) * 1e3, 2),
                            "achieved": round(down_total / (ms_b * 1e-3) / 1e9, 1),
                            "bytes_per_launch": round(down_total / max(n_b, 1))} if ms_b else None),
@@ -363,14 +368,18 @@ def bench_gemv(args, c):
         call(i)
     torch.cuda.synchronize()
     K_steps = args.steps
-    every = max(1, args.prof_every)
-    dq.dqg_prof_begin_sampled(2 * (K_steps // every + 1), every)   # split-K calls launch two kernels
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(K_steps):
-        call(args.warmup + i)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t0
+
+    def run_steps():
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for i in range(K_steps):
+            call(args.warmup + i)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t
+
+    t_wall = run_steps()                     # region 1: wall clock only
+    dq.dqg_prof_begin(2 * K_steps)           # region 2: events on every launch (split-K: two a call)
+    t_wall_events = run_steps()
     prof = dq.dqg_prof_end()
     # the route the library took (the kernel whose launches were timed)
     routes = ("gemm_gate_up", "gate_up") if gu else ("gemm", "matmul")
@@ -389,14 +398,13 @@ def bench_gemv(args, c):
         roof = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2) if achieved else None,
                 "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4) if achieved else None, "traffic": None,
-                "avg_us": round(avg_s * 1e6, 2), "flops_per_launch": flops, "timed_launches": n_k,
-                "timed_every": every}
+                "avg_us": round(avg_s * 1e6, 2), "flops_per_launch": flops, "timed_launches": n_k}
     else:
         achieved = step_bytes / avg_s / 1e9 if avg_s > 0 else None
         roof = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1) if achieved else None,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
                 "traffic": None, "avg_us": round(avg_s * 1e6, 2), "bytes_per_launch": step_bytes,
-                "timed_launches": n_k, "timed_every": every}
+                "timed_launches": n_k}
     log(f"[bench] {K_steps} steps: {t_wall / K_steps * 1e6:.1f} us/step wall; {kname} kernel "
         f"{avg_s * 1e6:.1f} us avg; {flops / avg_s / 1e12 if avg_s else 0:.1f} TFLOP/s, "
         f"{step_bytes / avg_s / 1e9 if avg_s else 0:.0f} GB/s")
@@ -436,6 +444,7 @@ def bench_gemv(args, c):
         "unit": "GB/s" if not gemm else "TFLOP/s",
         "n_gpus": 1, "steps": K_steps, "warmup": args.warmup,
         "ms_per_step": round(t_wall / K_steps * 1e3, 5), "us_per_call": round(t_wall / K_steps * 1e6, 2),
+        "ms_per_step_with_events": round(t_wall_events / K_steps * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": args.workload + (" gate_up" if gu else ""), "tokens": S, "O": O, "K": K,
                    "format": f"fmt {fmt}, gs {gs}",

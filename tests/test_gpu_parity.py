@@ -346,3 +346,25 @@ def test_workload_mxfp4_group_384top8_s8():
     del dev, table
     gc.collect()
     torch.cuda.empty_cache()
+
+
+def test_event_timing_all_and_sampled():
+    """dqg_prof_begin times every launch; dqg_prof_begin_sampled(capacity, 3)
+    the launches of calls 0, 3, 6, ... counted from the begin."""
+    m = _small(0, SMALL[0])
+    W = up(m)
+    x = dev_f32(synth.activations(2, m.K, 2200))
+    dq.dqg_prof_begin(16)
+    for _ in range(7):
+        dq.dqg_matmul(W, x)
+    prof = dq.dqg_prof_end()
+    assert prof["matmul"][0] == 7 and prof["matmul"][1] > 0
+    dq.dqg_prof_begin_sampled(16, 3)
+    for _ in range(7):
+        dq.dqg_matmul(W, x)
+    prof = dq.dqg_prof_end()
+    assert prof["matmul"][0] == 3 and prof["matmul"][1] > 0
+    dq.dqg_prof_begin_sampled(2, 1)   # capacity caps the timed launches
+    for _ in range(5):
+        dq.dqg_matmul(W, x)
+    assert dq.dqg_prof_end()["matmul"][0] == 2
