@@ -706,46 +706,16 @@ __device__ __forceinline__ GRow lane_row_ptrs(const MatDev &m, int row) {
 }
 
 // ---------------------------------------------------------------------------
-// dqg_matmul: y[s][o] = W[o] . x[s]
+// dqg_matmul and dqg_gate_up, per-row route (up to 8 tokens a pass)
 // ---------------------------------------------------------------------------
-template <int C, int R, int SM>
-__global__ void __launch_bounds__(256) k_matmul(MatDev m, const float *__restrict__ x, int S,
-                                                float *__restrict__ y) {
-    const int wave = blockIdx.x * (blockDim.x / WAVE) + wave_id();
-    const int row0 = wave * R;
-    if (row0 >= m.O) return;
-    const int lane = threadIdx.x & (WAVE - 1);
-    GRow rows[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) rows[r] = row_ptrs(m, min(row0 + r, m.O - 1));
-    const int nch = m.K / Codec<C>::CW;
-    for (int s0 = 0; s0 < S; s0 += SM) {
-        XGlobal xp[SM];
-#pragma unroll
-        for (int s = 0; s < SM; ++s) xp[s] = {gf(x + (size_t)min(s0 + s, S - 1) * m.K)};
-        float acc[R][SM];
-        dot_rows<C, R, SM>(rows, nch, m.shift, xp, acc);
-        float out = 0.f;
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int s = 0; s < SM; ++s) {
-                const float t = wave_sum(acc[r][s]);
-                if (lane == r * SM + s) out = t;
-            }
-        const int r = lane / SM, s = lane % SM;
-        if (lane < R * SM && row0 + r < m.O && s0 + s < S) y[(size_t)(s0 + s) * m.O + row0 + r] = out;
-    }
-}
-
 // dqg_matmul (GU false: y[s][o] = W[o] . x[s], W = m0) and dqg_gate_up
 // (GU true: y[s][i] = swiglu(G[i] . x[s], U[i] . x[s]), G = m0, U = m1)
 // with x staged in LDS, K-chunk by K-chunk: the block's waves share one copy
 // of x instead of each reading it from L2.  A K-chunk is a multiple of 64
-// code chunks, so every lane still takes chunks lane, lane + 64, ... in
-// order: a token's bits are those of k_matmul / k_gate_up at any S.  Every
-// wave stays to the end (block barriers); rows past O are clamped and their
-// outputs dropped.
+// code chunks, so every lane takes chunks lane, lane + 64, ... in order
+// whatever the K-chunk and the batch: a token's bits do not depend on S.
+// Every wave stays to the end (block barriers); rows past O are clamped and
+// their outputs dropped.
 template <int C, int R, int SM, bool GU>
 __global__ void __launch_bounds__(256) k_rows_lds(MatDev m0, MatDev m1, const float *__restrict__ x, int S,
                                                   float *__restrict__ y, int KC, float L) {
@@ -809,44 +779,6 @@ __global__ void __launch_bounds__(256) k_rows_lds(MatDev m0, MatDev m1, const fl
         const int r = lane / SM, s = lane % SM;
         if (lane < R * SM && row0 + r < m.O && s0 + s < S)
             y[(size_t)(s0 + s) * m.O + row0 + r] = GU ? swiglu(out, outu, L) : out;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// dqg_gate_up: h[s][i] = silu(G[i] . x[s]) * (U[i] . x[s])
-// ---------------------------------------------------------------------------
-template <int C, int R, int SM>
-__global__ void __launch_bounds__(256) k_gate_up(MatDev g, MatDev u, const float *__restrict__ x,
-                                                 int S, float *__restrict__ h, float L) {
-    const int I = g.O;
-    const int wave = blockIdx.x * (blockDim.x / WAVE) + wave_id();
-    const int row0 = wave * R;
-    if (row0 >= I) return;
-    const int lane = threadIdx.x & (WAVE - 1);
-    GRow rows[2 * R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        rows[r] = row_ptrs(g, min(row0 + r, I - 1));
-        rows[R + r] = row_ptrs(u, min(row0 + r, I - 1));
-    }
-    const int nch = g.K / Codec<C>::CW;
-    for (int s0 = 0; s0 < S; s0 += SM) {
-        XGlobal xp[SM];
-#pragma unroll
-        for (int s = 0; s < SM; ++s) xp[s] = {gf(x + (size_t)min(s0 + s, S - 1) * g.K)};
-        float acc[2 * R][SM];
-        dot_rows<C, 2 * R, SM>(rows, nch, g.shift, xp, acc);
-        float gv = 0.f, uv = 0.f;
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-#pragma unroll
-            for (int s = 0; s < SM; ++s) {
-                const float tg = wave_sum(acc[r][s]);
-                const float tu = wave_sum(acc[R + r][s]);
-                if (lane == r * SM + s) { gv = tg; uv = tu; }
-            }
-        const int r = lane / SM, s = lane % SM;
-        if (lane < R * SM && row0 + r < I && s0 + s < S) h[(size_t)(s0 + s) * I + row0 + r] = swiglu(gv, uv, L);
     }
 }
 
@@ -1465,7 +1397,7 @@ k_gemm(MatDev m0, MatDev m1, const float *__restrict__ x, int S, float *__restri
             }
 #pragma unroll
         for (int j = 0; j < GWIN; ++j) {
-            if (j >= nwin) break;
+            if (j >= nwin) continue;   // the chunk's last step may hold fewer windows
             h16x8 a[2];
             f32x4 sc4[2];
 #pragma unroll
@@ -1677,12 +1609,6 @@ void launch(const char *name, K kernel, dim3 grid, dim3 block, size_t lds, hipSt
 #ifndef DQG_MM_R1
 #define DQG_MM_R1 4
 #endif
-#ifndef DQG_MM_LDS
-#define DQG_MM_LDS 1
-#endif
-#ifndef DQG_GU_LDS
-#define DQG_GU_LDS 1
-#endif
 #ifndef DQG_MM_R4
 #define DQG_MM_R4 4
 #endif
@@ -1693,8 +1619,9 @@ void launch(const char *name, K kernel, dim3 grid, dim3 block, size_t lds, hipSt
 #define DQG_MM_R2 4
 #endif
 // Inputs of x per K-chunk: the largest multiple of 64 code chunks that keeps
-// SM tokens within 64 KB of LDS, or the whole of K.  (Batches for which not
-// even 64 code chunks fit read x from L2 with k_matmul.)
+// SM tokens within 64 KB of LDS, or the whole of K.  (Every format's batch
+// size keeps at least 64 code chunks within it: int3's 64-input chunks take
+// at most 4 tokens a pass.)
 constexpr int MM_LDS_BYTES = 64 * 1024;
 template <int C, int SM>
 int matmul_kc(int K) {
@@ -1707,13 +1634,10 @@ template <int C, int R, int SM>
 hipError_t go_matmul(const MatDev &m, const float *x, int S, float *y, hipStream_t st) {
     const int rows_per_block = R * WPB;
     dim3 grid((m.O + rows_per_block - 1) / rows_per_block);
-    if constexpr (DQG_MM_LDS && SM * WAVE * Codec<C>::CW * 4 <= MM_LDS_BYTES) {
-        const int KC = matmul_kc<C, SM>(m.K);
-        launch("matmul", (k_rows_lds<C, R, SM, false>), grid, dim3(WAVE * WPB),
-               (size_t)SM * x_lds_len<Codec<C>::CW>(KC) * 4, st, m, m, x, S, y, KC, INFINITY);
-    } else {
-        launch("matmul", (k_matmul<C, R, SM>), grid, dim3(WAVE * WPB), 0, st, m, x, S, y);
-    }
+    static_assert(SM * WAVE * Codec<C>::CW * 4 <= MM_LDS_BYTES, "64 code chunks of x per token fit the LDS budget");
+    const int KC = matmul_kc<C, SM>(m.K);
+    launch("matmul", (k_rows_lds<C, R, SM, false>), grid, dim3(WAVE * WPB),
+           (size_t)SM * x_lds_len<Codec<C>::CW>(KC) * 4, st, m, m, x, S, y, KC, INFINITY);
     return hipGetLastError();
 }
 
@@ -1846,13 +1770,10 @@ template <int C, int R, int SM>
 hipError_t go_gate_up(const MatDev &g, const MatDev &u, const float *x, int S, float *h, float L, hipStream_t st) {
     const int rows_per_block = R * WPB;
     dim3 grid((g.O + rows_per_block - 1) / rows_per_block);
-    if constexpr (DQG_GU_LDS && SM * WAVE * Codec<C>::CW * 4 <= MM_LDS_BYTES) {
-        const int KC = matmul_kc<C, SM>(g.K);
-        launch("gate_up", (k_rows_lds<C, R, SM, true>), grid, dim3(WAVE * WPB),
-               (size_t)SM * x_lds_len<Codec<C>::CW>(KC) * 4, st, g, u, x, S, h, KC, L);
-    } else {
-        launch("gate_up", (k_gate_up<C, R, SM>), grid, dim3(WAVE * WPB), 0, st, g, u, x, S, h, L);
-    }
+    static_assert(SM * WAVE * Codec<C>::CW * 4 <= MM_LDS_BYTES, "64 code chunks of x per token fit the LDS budget");
+    const int KC = matmul_kc<C, SM>(g.K);
+    launch("gate_up", (k_rows_lds<C, R, SM, true>), grid, dim3(WAVE * WPB),
+           (size_t)SM * x_lds_len<Codec<C>::CW>(KC) * 4, st, g, u, x, S, h, KC, L);
     return hipGetLastError();
 }
 
