@@ -35,6 +35,52 @@ METRIC = "quant GEMV weight-stream GB/s (% of HBM peak); µs per top-8 expert ML
 HBM_PEAK_GBS = 8000.0
 
 
+def launch_stats(launches):
+    """{kernel: (count, total ms, median, p10, p90 in us)} from [(kernel, ms)]."""
+    import numpy as np
+    by = {}
+    for name, ms in launches:
+        by.setdefault(name, []).append(ms)
+    out = {}
+    for name, v in by.items():
+        a = np.asarray(v) * 1e3
+        out[name] = (len(v), float(np.sum(v)), round(float(np.median(a)), 2), round(float(np.percentile(a, 10)), 2),
+                     round(float(np.percentile(a, 90)), 2))
+    return out
+
+
+def gpu_clocks():
+    """The GPU's current clock levels as rocm-smi reports them (a child process), or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
+        d = json.loads(r.stdout)
+        card = next(iter(d.values()))
+        return {k: v for k, v in card.items() if "clock" in k.lower()}
+    except Exception:   # the clock state is context; its absence is not an error
+        return None
+
+
+def oracle_one_core(run_once, seconds, prepare=None):
+    """(calls, seconds) of run_once(j) on one host thread, restoring the thread
+    count; prepare(j), if given, runs before each call outside the clock."""
+    import oracle
+    n = oracle.get_threads()
+    oracle.set_threads(1)
+    try:
+        spent, calls = 0.0, 0
+        while spent < seconds:
+            if prepare:
+                prepare(calls)
+            t = time.perf_counter()
+            run_once(calls)
+            spent += time.perf_counter() - t
+            calls += 1
+        return calls, spent
+    finally:
+        oracle.set_threads(n)
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -216,9 +262,11 @@ def main():
     # -- timed region 2: the same steps with HIP events around every launch,
     #    on the launch's stream (the events add about 8 us a call to the wall
     #    clock, which is why value comes from region 1) ---------------------
+    clocks = gpu_clocks()
     dq.dqg_prof_begin(2 * K)
     t_wall_events = run_steps()
-    prof = dq.dqg_prof_end()
+    pstats = launch_stats(dq.dqg_prof_end_launches(2 * K))
+    prof = {name: v[:2] for name, v in pstats.items()}
 
     total_bytes = sum(step_bytes(i) for i in range(args.warmup, args.warmup + K))
     timed = range(args.warmup, args.warmup + K)   # region 2 times every call's launches
@@ -275,7 +323,23 @@ def main():
                "sample": f"{calls} expert-group calls ({S} token(s), top-{k} of {E}"
                          f"{' + shared' if n_sh else ''}) from the same routing pool, {spent:.1f} s",
                "us_per_call": round(spent / calls * 1e6, 1)}
-        log(f"[bench] cpu oracle: {cpu['value']} GB/s on {threads} threads ({calls} calls)")
+
+        def draw(j):   # the call's experts, drawn before the clock starts
+            i = args.warmup + (j % calls)
+            if len(cache) > 64:
+                cache.clear()
+            for e in set(ids[i % P].ravel().tolist()) | ({shared_of(i)} if n_shared else set()):
+                host_expert(e)
+
+        def one_call(j):   # the same calls again, on one host thread
+            i = args.warmup + (j % calls)
+            oracle.expert_group(View(), ids[i % P], w[i % P], shared_of(i), x[i % P],
+                                *([] if args.swiglu_limit is None else [args.swiglu_limit]))
+
+        c1, s1 = oracle_one_core(one_call, max(1.0, args.cpu_seconds / 3), draw)
+        cpu["value_1core"] = round(sum(step_bytes(args.warmup + (j % calls)) for j in range(c1)) / s1 / 1e9, 3)
+        log(f"[bench] cpu oracle: {cpu['value']} GB/s on {threads} threads ({calls} calls), "
+            f"{cpu['value_1core']} GB/s on 1")
 
     out = {
         "metric": METRIC,
@@ -304,10 +368,14 @@ def main():
                                 "int4g32_expert_group_256top8_shared") else None,
                      "avg_us": round(ms_dom / max(n_dom, 1) * 1e3, 2),
                      "bytes_per_launch": round(dom_total / max(n_dom, 1)),
-                     "timed_launches": n_dom},
+                     "timed_launches": n_dom, "median_us": pstats[dom][2], "p10_us": pstats[dom][3],
+                     "p90_us": pstats[dom][4]},
         "roofline_down": ({"kernel": "group_down", "avg_us": round(ms_b / max(n_b, 1) * 1e3, 2),
                            "achieved": round(down_total / (ms_b * 1e-3) / 1e9, 1),
-                           "bytes_per_launch": round(down_total / max(n_b, 1))} if ms_b else None),
+                           "bytes_per_launch": round(down_total / max(n_b, 1)),
+                           "median_us": pstats["group_down"][2], "p10_us": pstats["group_down"][3],
+                           "p90_us": pstats["group_down"][4]} if ms_b else None),
+        "gpu_clocks": clocks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -378,9 +446,21 @@ def bench_gemv(args, c):
         return time.perf_counter() - t
 
     t_wall = run_steps()                     # region 1: wall clock only
+    clocks = gpu_clocks()
     dq.dqg_prof_begin(2 * K_steps)           # region 2: events on every launch (split-K: two a call)
     t_wall_events = run_steps()
-    prof = dq.dqg_prof_end()
+    launches = dq.dqg_prof_end_launches(2 * K_steps)
+    prof = {name: v[:2] for name, v in launch_stats(launches).items()}
+    # kernel time per call: a call's launch, plus its split-K reduce when it has one
+    call_us = []
+    for name, ms in launches:
+        if name == "gemm_reduce" and call_us:
+            call_us[-1] += ms * 1e3
+        else:
+            call_us.append(ms * 1e3)
+    pc = np.asarray(call_us)
+    pct = {"median_us": round(float(np.median(pc)), 2), "p10_us": round(float(np.percentile(pc, 10)), 2),
+           "p90_us": round(float(np.percentile(pc, 90)), 2)}
     # the route the library took (the kernel whose launches were timed)
     routes = ("gemm_gate_up", "gate_up") if gu else ("gemm", "matmul")
     kname = max(routes, key=lambda k: prof.get(k, (0, 0.0))[0])
@@ -398,13 +478,13 @@ def bench_gemv(args, c):
         roof = {"kernel": kname, "bound": "mfma", "achieved": round(achieved, 2) if achieved else None,
                 "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / MFMA_F16_PEAK_TFLOPS, 4) if achieved else None, "traffic": None,
-                "avg_us": round(avg_s * 1e6, 2), "flops_per_launch": flops, "timed_launches": n_k}
+                "avg_us": round(avg_s * 1e6, 2), "flops_per_launch": flops, "timed_launches": n_k, **pct}
     else:
         achieved = step_bytes / avg_s / 1e9 if avg_s > 0 else None
         roof = {"kernel": kname, "bound": "hbm", "achieved": round(achieved, 1) if achieved else None,
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
                 "traffic": None, "avg_us": round(avg_s * 1e6, 2), "bytes_per_launch": step_bytes,
-                "timed_launches": n_k}
+                "timed_launches": n_k, **pct}
     log(f"[bench] {K_steps} steps: {t_wall / K_steps * 1e6:.1f} us/step wall; {kname} kernel "
         f"{avg_s * 1e6:.1f} us avg; {flops / avg_s / 1e12 if avg_s else 0:.1f} TFLOP/s, "
         f"{step_bytes / avg_s / 1e9 if avg_s else 0:.0f} GB/s")
@@ -431,11 +511,24 @@ def bench_gemv(args, c):
             spent += time.perf_counter() - t
             calls += 1
         per_call = spent / calls * O / rows   # the whole matrix, scaled from the row sample
-        cpu = {"value": round((step_bytes / per_call / 1e9) if not gemm else (flops / per_call / 1e12), 4),
+
+        def rate(t_call):
+            return round((step_bytes / t_call / 1e9) if not gemm else (flops / t_call / 1e12), 4)
+
+        cpu = {"value": rate(per_call),
                "unit": "GB/s" if not gemm else "TFLOP/s", "cores": oracle.get_threads(), "kind": "oracle",
                "sample": f"{calls} oracle {'gate_up calls' if gu else 'GEMVs'} of the first {rows} of {O} rows "
                          f"at S = {S}, {spent:.1f} s, scaled to the whole matrix"}
-        log(f"[bench] cpu oracle: {cpu['value']} {cpu['unit']} on {cpu['cores']} threads")
+
+        def one_call(j):   # the same sample on one host thread
+            if gu:
+                oracle.gate_up(sub, subu, xs)
+            else:
+                oracle.gemv(sub, xs)
+
+        c1, s1 = oracle_one_core(one_call, max(1.0, args.cpu_seconds / 3))
+        cpu["value_1core"] = rate(s1 / c1 * O / rows)
+        log(f"[bench] cpu oracle: {cpu['value']} {cpu['unit']} on {cpu['cores']} threads, {cpu['value_1core']} on 1")
 
     out = {
         "metric": (METRIC if not gemm else "quant GEMM TFLOP/s (prefill, useful products)")
@@ -450,6 +543,7 @@ def bench_gemv(args, c):
                    "format": f"fmt {fmt}, gs {gs}",
                    "copies": copies, "route": "gemm" if gemm else "gemv", "device": dev_name},
         "roofline": roof,
+        "gpu_clocks": clocks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

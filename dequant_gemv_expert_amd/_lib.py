@@ -50,6 +50,10 @@ class dqg_counters(C.Structure):
                 ("launches", C.c_uint64), ("bytes", C.c_uint64), ("calls_route", C.c_uint64)]
 
 
+class dqg_prof_launch(C.Structure):
+    _fields_ = [("kernel", C.c_char * 32), ("ms", C.c_double)]
+
+
 class dqg_prof_record(C.Structure):
     _fields_ = [("kernel", C.c_char * 32), ("launches", C.c_int64), ("total_ms", C.c_double)]
 
@@ -72,6 +76,7 @@ SIGNATURES = {
     "dqg_route": (C.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _P, C.c_float, _P, _P, _P]),
     "dqg_prof_begin": (C.c_int, [_I32]),
     "dqg_prof_begin_sampled": (C.c_int, [_I32, _I32]),
+    "dqg_prof_end_launches": (C.c_int, [C.POINTER(dqg_prof_launch), _I32, C.POINTER(_I32)]),
     "dqg_prof_end": (C.c_int, [C.POINTER(dqg_prof_record), _I32, C.POINTER(_I32)]),
     "dqg_last_error": (C.c_char_p, []),
     "dqg_stats": (None, [C.POINTER(dqg_counters)]),
@@ -313,6 +318,14 @@ def dqg_prof_begin(capacity: int) -> None:
 def dqg_prof_begin_sampled(capacity: int, every: int) -> None:
     """Time the launches of every `every`-th call, up to `capacity` launches (host-blocking setup)."""
     _check(load().dqg_prof_begin_sampled(int(capacity), int(every)))
+
+
+def dqg_prof_end_launches(capacity: int) -> list:
+    """[(kernel name, device ms)] of the timed launches in launch order (up to ``capacity``)."""
+    recs = (dqg_prof_launch * max(1, int(capacity)))()
+    n = C.c_int32()
+    _check(load().dqg_prof_end_launches(recs, len(recs), C.byref(n)))
+    return [(recs[i].kernel.decode(), recs[i].ms) for i in range(n.value)]
 
 
 def dqg_prof_end() -> dict:

@@ -350,6 +350,29 @@ int dqg_prof_end(dqg_prof_record *out, int32_t max, int32_t *n) {
     return rc;
 }
 
+int dqg_prof_end_launches(dqg_prof_launch *out, int32_t max, int32_t *n) {
+    std::lock_guard<std::mutex> lock(g_prof.mu);
+    g_prof.on = false;
+    int count = 0, rc = DQG_OK;
+    for (int i = 0; i < g_prof.used; ++i) {
+        float ms = 0.f;
+        hipError_t e = hipEventSynchronize(g_prof.ev[2 * i + 1]);
+        if (e == hipSuccess) e = hipEventElapsedTime(&ms, g_prof.ev[2 * i], g_prof.ev[2 * i + 1]);
+        if (e != hipSuccess) {
+            rc = fail(DQG_EDEVICE, "prof_end_launches: %s", hipGetErrorString(e));
+            break;
+        }
+        if (!out || count >= max) continue;
+        std::memset(&out[count], 0, sizeof out[count]);
+        std::snprintf(out[count].kernel, sizeof out[count].kernel, "%s", g_prof.name[i]);
+        out[count].ms = ms;
+        ++count;
+    }
+    if (n) *n = count;
+    prof_release();
+    return rc;
+}
+
 int dqg_matmul(const dqg_matrix *W, const float *x, int32_t S, float *y, void *stream) {
     ++g_calls_matmul;
     prof_call();

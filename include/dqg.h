@@ -303,11 +303,22 @@ typedef struct {
 
 int dqg_prof_begin(int32_t capacity);
 /* dqg_prof_begin that times only the launches of every `every`-th API call
- * (calls counted from this begin, the first one timed): a timed loop pays
- * for the events of 1 call in `every` while the averages still come from
- * its own dispatches.  every >= 1; 1 is dqg_prof_begin. */
+ * (calls counted from this begin, the first one timed), so that a loop pays
+ * for the events of 1 call in `every`.  every >= 1; 1 is dqg_prof_begin.
+ * On MI355X the launches of a back-to-back loop overlap, and a launch
+ * timed among untimed ones reads longer than one timed in a loop where
+ * every launch carries events (the events separate the launches). */
 int dqg_prof_begin_sampled(int32_t capacity, int32_t every);
 int dqg_prof_end(dqg_prof_record *out, int32_t max, int32_t *n);
+
+/* dqg_prof_end launch by launch: fills up to `max` entries in launch order
+ * with each timed launch's kernel name and duration, stores their count in
+ * *n and releases the events (for percentiles). */
+typedef struct {
+    char kernel[32];
+    double ms;
+} dqg_prof_launch;
+int dqg_prof_end_launches(dqg_prof_launch *out, int32_t max, int32_t *n);
 
 /* Text of the calling thread's last error (never NULL). */
 const char *dqg_last_error(void);

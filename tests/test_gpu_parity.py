@@ -368,3 +368,9 @@ def test_event_timing_all_and_sampled():
     for _ in range(5):
         dq.dqg_matmul(W, x)
     assert dq.dqg_prof_end()["matmul"][0] == 2
+    dq.dqg_prof_begin(8)              # launch by launch, in launch order
+    for _ in range(3):
+        dq.dqg_matmul(W, x)
+    dq.dqg_dequant(W, torch.empty((m.O, m.K), dtype=torch.float32, device="cuda"))
+    each = dq.dqg_prof_end_launches(8)
+    assert [k for k, _ in each] == ["matmul"] * 3 + ["dequant"] and all(ms > 0 for _, ms in each)
