@@ -159,6 +159,7 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
 }
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 // acc + f16(pair half) * x: the f16 -> f32 widening folds into v_fma_mix_f32.
 __device__ __forceinline__ float fma_lo(uint32_t pair, float x, float acc) {
@@ -230,7 +231,9 @@ struct Codec<C_I4> {
         pr[0] = w & 0x000F000Fu;
         pr[1] = (w >> 4) & 0x000F000Fu;
         pr[2] = (w >> 8) & 0x000F000Fu;
-        pr[3] = (w >> 12) & 0x000F000Fu;
+        // each 16-bit half shifted by 12 keeps only its top nibble: one
+        // packed 16-bit shift and no mask
+        pr[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, w) >> (unsigned short)12);
     }
 };
 
