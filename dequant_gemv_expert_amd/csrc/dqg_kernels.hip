@@ -1132,9 +1132,10 @@ __global__ void __launch_bounds__(WAVE * down_max_waves<CAP>()) k_group_down(Gro
 }
 
 // ---------------------------------------------------------------------------
-// Prefill GEMM on the matrix cores, for batches of several tokens (the
-// pages move a batch of 16 or more rows to a tiled GEMM): Y[s][o] =
-// W[o] . x[s], and gate_up's h = silu(G x) * (U x).
+// Prefill GEMM on the matrix cores, for batches of several tokens
+// ("colibri -- Vulkan backend (docs/vulkan.md)", tier properties: a batch of
+// 16 or more rows per expert goes to a tiled GEMM): Y[s][o] = W[o] . x[s],
+// and gate_up's h = silu(G x) * (U x).
 //
 // v_mfma_f32_16x16x32_f16 computes D (16 rows x 16 tokens, f32) from
 // A (16 rows x 32 inputs, f16) and B (32 inputs x 16 tokens, f16).  Lane
