@@ -69,6 +69,7 @@
 #include <math.h>
 #include <stdint.h>
 #include <stddef.h>
+#include <stdlib.h>
 #include <omp.h>
 
 typedef struct {
@@ -391,6 +392,186 @@ void orc_expert_group(const orc_matrix *gates, const orc_matrix *ups, const orc_
 {
     orc_expert_group_clamped(gates, ups, downs, n_experts, S, k, ids, w, shared, x, INFINITY, y, absn,
                              h_work, nh_work, dy_work, dabs_work);
+}
+
+/* ------------------------------------------------------------------ */
+/* DeepSeek V4's rounding activation.                                   */
+/* ------------------------------------------------------------------ */
+
+/*
+ * [V], the paragraph on DeepSeek V4's CPU expert and the tier's third
+ * activation: gate and up are rounded to bf16 before the clamped SwiGLU;
+ * the activation times the route weight is rounded to bf16; down's input
+ * is rounded to E4M3 with one power-of-two scale per 128 values (the
+ * smallest power of two that takes the block's largest magnitude below
+ * 448); down's output is rounded to bf16; the rows of one token are added
+ * with no further weight, in ascending expert id, then rank.
+ *
+ * Readings: every rounding is to nearest, ties to even; a block is 128
+ * consecutive values of one slot's activation (I a multiple of 128); a block
+ * whose values are all zero takes scale 1; the shared expert's weight is 1
+ * and its row is added after the routed ones; the sum of a token's rows is
+ * an f32 sum from 0 in that order (the engine's rows are f32).  x is taken
+ * as given: the pages round it on the host before the call.
+ */
+
+/* v rounded to nearest-even in a binary format with mbits fraction bits and
+ * smallest normal exponent emin, subnormals sharing the quantum 2^(emin -
+ * mbits).  No largest exponent: callers stay inside the format's range.
+ * bf16: (7, -126) [IEEE]; E4M3: (3, -6) [OFP8]. */
+double orc_round_fmt(double v, int mbits, int emin)
+{
+    if (v == 0.0 || isnan(v) || isinf(v))
+        return v;
+    int e;
+    frexp(fabs(v), &e);            /* |v| = f 2^e with f in [1/2, 1): the leading bit is 2^(e-1) */
+    int lead = e - 1 < emin ? emin : e - 1;
+    double quantum = ldexp(1.0, lead - mbits);
+    return nearbyint(v / quantum) * quantum;   /* v / quantum is exact; the default mode is to nearest-even */
+}
+
+/* The smallest power of two s with m / s < 448; 1 when m is 0. */
+double orc_v4_block_scale(double m)
+{
+    if (!(m > 0.0))
+        return 1.0;
+    double s = 1.0;
+    while (m / s >= 448.0)
+        s *= 2.0;
+    while (m / (s / 2.0) < 448.0)
+        s /= 2.0;
+    return s;
+}
+
+/* One token's rows added in ascending (expert id, rank), then the shared
+ * row: y[o] = f32 sum from 0.  rows: [k + has_shared][H], rank order, the
+ * shared row last. */
+void orc_v4_combine(const double *rows, const int32_t *ids, long k, int has_shared, long H, float *y)
+{
+    for (long o = 0; o < H; o++)
+        y[o] = 0.0f;
+    char done[k > 0 ? k : 1];
+    for (long r = 0; r < k; r++)
+        done[r] = 0;
+    for (long n = 0; n < k; n++) {
+        long pick = -1;
+        for (long r = 0; r < k; r++)
+            if (!done[r] && (pick < 0 || ids[r] < ids[pick]))
+                pick = r;   /* the lowest id; among equal ids the lowest rank */
+        done[pick] = 1;
+        for (long o = 0; o < H; o++)
+            y[o] = y[o] + (float)rows[pick * H + o];
+    }
+    if (has_shared)
+        for (long o = 0; o < H; o++)
+            y[o] = y[o] + (float)rows[k * H + o];
+}
+
+static double bf16(double v) { return orc_round_fmt(v, 7, -126); }
+
+/* Is the bf16 rounding of a value known to within +-err not unique? */
+static int bf16_open(double v, double err)
+{
+    return bf16(v - err) != bf16(v + err);
+}
+
+/*
+ * One slot: e4[I] (down's input) and down's rounded outputs with the
+ * rounding of v +- err for a device whose f32 sum may stray by err:
+ * d[H], d_lo[H], d_hi[H].  Returns the number of bf16 decisions before down
+ * that a device's error could flip: gate and up within gu_err * sum|w x|,
+ * the weighted activation within act_rel of its value.
+ */
+static long v4_slot(const orc_matrix *gate, const orc_matrix *up, const orc_matrix *down, const float *x,
+                    double limit, double wr, double gu_err, double act_rel, double down_err,
+                    double *e4, double *d, double *d_lo, double *d_hi)
+{
+    long I = gate->O, H = down->O, open = 0, i;
+#pragma omp parallel for schedule(static) reduction(+ : open)
+    for (i = 0; i < I; i++) {
+        double g, u, ag, au;
+        row_dot(gate, i, x, NULL, &g, &ag);
+        row_dot(up, i, x, NULL, &u, &au);
+        open += bf16_open(g, gu_err * ag) + bf16_open(u, gu_err * au);
+        double gb = bf16(g), ub = bf16(u);
+        double gc = gb > limit ? limit : gb;
+        double uc = ub > limit ? limit : (ub < -limit ? -limit : ub);
+        double hv = orc_silu(gc) * uc * wr;
+        open += bf16_open(hv, act_rel * fabs(hv));
+        e4[i] = bf16(hv);
+    }
+    for (long b0 = 0; b0 < I; b0 += 128) {
+        double m = 0.0;
+        for (long j = b0; j < b0 + 128; j++)
+            if (fabs(e4[j]) > m || isnan(e4[j]))
+                m = isnan(e4[j]) ? NAN : fabs(e4[j]);
+        double s = orc_v4_block_scale(m);
+        for (long j = b0; j < b0 + 128; j++)
+            e4[j] = orc_round_fmt(e4[j] / s, 3, -6) * s;
+    }
+    long o;
+#pragma omp parallel for schedule(static)
+    for (o = 0; o < H; o++) {
+        double sum = 0.0, mag = 0.0;
+        for (long j = 0; j < I; j++) {
+            double wk = orc_weight(down, o, j);
+            sum += wk * e4[j];
+            mag += fabs(wk * e4[j]);
+        }
+        d[o] = bf16(sum);
+        d_lo[o] = bf16(sum - down_err * mag);
+        d_hi[o] = bf16(sum + down_err * mag);
+    }
+    return open;
+}
+
+/*
+ * The expert group with DeepSeek V4's activation.  Outputs: h [S*k + S][I]
+ * (down's input per slot, in the slot order of the device scratch: t*k + r,
+ * then S*k + t for the shared expert), y [S][H] f32 and the f32 sums y_lo,
+ * y_hi of the rows' lower and upper candidates (f32 addition is monotone in
+ * each operand, so a device whose only differences are within the error
+ * bounds lands in [y_lo, y_hi]).  An id outside [0, n_experts) makes its
+ * token's y NaN.  Returns the count of open decisions before down (the h
+ * of a call with a nonzero count is not unique).
+ */
+long orc_expert_group_v4(const orc_matrix *gates, const orc_matrix *ups, const orc_matrix *downs,
+                         long n_experts, long S, long k, const int32_t *ids, const float *w, long shared,
+                         const float *x, double limit, double gu_err, double act_rel, double down_err,
+                         double *h, float *y, float *y_lo, float *y_hi)
+{
+    long H = downs[0].O, I = gates[0].O, nr = S * k, open = 0;
+    long nrow = k + (shared >= 0 ? 1 : 0);
+    double *rows = malloc(sizeof(double) * (size_t)(3 * nrow * H + 1));
+    if (!rows)
+        return -1;
+    double *lo = rows + nrow * H, *hi = lo + nrow * H;
+    for (long t = 0; t < S; t++) {
+        int bad = 0;
+        for (long j = 0; j < nrow; j++) {
+            long slot = j < k ? t * k + j : nr + t;
+            long e = j < k ? ids[t * k + j] : shared;
+            double wr = j < k ? (double)w[t * k + j] : 1.0;
+            if (e < 0 || e >= n_experts) {
+                bad = 1;
+                for (long i = 0; i < I; i++)
+                    h[slot * I + i] = NAN;
+                continue;
+            }
+            open += v4_slot(&gates[e], &ups[e], &downs[e], x + t * gates[e].K, limit, wr, gu_err, act_rel,
+                            down_err, h + slot * I, rows + j * H, lo + j * H, hi + j * H);
+        }
+        if (bad) {
+            for (long o = 0; o < H; o++)
+                y[t * H + o] = y_lo[t * H + o] = y_hi[t * H + o] = NAN;
+            continue;
+        }
+        orc_v4_combine(rows, ids + t * k, k, shared >= 0, H, y + t * H);
+        orc_v4_combine(lo, ids + t * k, k, shared >= 0, H, y_lo + t * H);
+        orc_v4_combine(hi, ids + t * k, k, shared >= 0, H, y_hi + t * H);
+    }
+    free(rows);
+    return open;
 }
 
 /* ------------------------------------------------------------------ */

@@ -97,6 +97,15 @@ class OracleLib:
         lib.orc_route.restype = None
         lib.orc_route.argtypes = [_P, _L, _L, _L, C.c_int, C.c_int, _P, C.c_double, _P, _P, _P]
         lib.orc_set_threads.restype = None
+        lib.orc_round_fmt.restype = C.c_double
+        lib.orc_round_fmt.argtypes = [C.c_double, C.c_int, C.c_int]
+        lib.orc_v4_block_scale.restype = C.c_double
+        lib.orc_v4_block_scale.argtypes = [C.c_double]
+        lib.orc_v4_combine.restype = None
+        lib.orc_v4_combine.argtypes = [_P, _P, _L, C.c_int, _L, _P]
+        lib.orc_expert_group_v4.restype = C.c_long
+        lib.orc_expert_group_v4.argtypes = [_P, _P, _P, _L, _L, _L, _P, _P, _L, _P, C.c_double, C.c_double,
+                                            C.c_double, C.c_double, _P, _P, _P, _P]
         lib.orc_set_threads.argtypes = [C.c_int]
         lib.orc_get_threads.restype = C.c_int
         lib.orc_get_threads.argtypes = []
@@ -224,6 +233,60 @@ class OracleLib:
         return y, a
 
 
+    def round_fmt(self, v: float, mbits: int, emin: int) -> float:
+        return self.lib.orc_round_fmt(float(v), int(mbits), int(emin))
+
+    def v4_block_scale(self, m: float) -> float:
+        return self.lib.orc_v4_block_scale(float(m))
+
+    def v4_combine(self, rows, ids, has_shared: bool) -> np.ndarray:
+        """One token's rows [k (+1 shared)][H] added as DeepSeek V4's path adds them (f32)."""
+        rows = np.ascontiguousarray(rows, dtype=np.float64)
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        k, H = len(ids), rows.shape[1]
+        if rows.shape[0] != k + int(bool(has_shared)):
+            raise ValueError("rows must hold k rows, then the shared row if any")
+        y = np.empty(H, dtype=np.float32)
+        self.lib.orc_v4_combine(_ptr(rows), _ptr(ids), k, int(bool(has_shared)), H, _ptr(y))
+        return y
+
+    def expert_group_v4(self, experts: Sequence, ids, w, shared: Optional[int], x, limit: float = math.inf,
+                        gu_err: float = 0.0, act_rel: float = 0.0, down_err: float = 0.0) -> dict:
+        """The expert group with DeepSeek V4's rounding activation.
+
+        Returns h [S*k + S][I] (down's input per slot), y, y_lo, y_hi (f32
+        [S][H]) and ``open``: the number of bf16 decisions before down that
+        a device within the given error bounds could take the other way.
+        """
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        w = _f32(w)
+        x = _f32(np.atleast_2d(x))
+        S, k = ids.shape
+        used = sorted({int(e) for e in ids.ravel() if 0 <= int(e) < len(experts)}
+                      | ({int(shared)} if shared is not None and shared >= 0 else set()))
+        remap = {e: i for i, e in enumerate(used)}
+        # the compact table keeps the ids' order, so the combine order is unchanged
+        cids = np.array([[remap.get(int(e), -1) for e in row] for row in ids], dtype=np.int32)
+        cshared = remap[int(shared)] if shared is not None and shared >= 0 else -1
+        n = len(used)
+        gates = (_Mat * max(n, 1))(*[_mat(experts[e].gate) for e in used])
+        ups = (_Mat * max(n, 1))(*[_mat(experts[e].up) for e in used])
+        downs = (_Mat * max(n, 1))(*[_mat(experts[e].down) for e in used])
+        H = experts[used[0]].down.O
+        I = experts[used[0]].gate.O
+        if I % 128:
+            raise ValueError("DeepSeek V4's activation rounds blocks of 128: I must be a multiple of 128")
+        h = np.empty((S * k + S, I), dtype=np.float64)
+        y, y_lo, y_hi = (np.empty((S, H), dtype=np.float32) for _ in range(3))
+        n_open = self.lib.orc_expert_group_v4(
+            C.cast(gates, C.c_void_p), C.cast(ups, C.c_void_p), C.cast(downs, C.c_void_p), n, S, k,
+            _ptr(cids), _ptr(w), cshared, _ptr(x), float(limit), float(gu_err), float(act_rel),
+            float(down_err), _ptr(h), _ptr(y), _ptr(y_lo), _ptr(y_hi))
+        if n_open < 0:
+            raise MemoryError("oracle: out of memory")
+        return {"h": h, "y": y, "y_lo": y_lo, "y_hi": y_hi, "open": int(n_open)}
+
+
 _default: Optional[OracleLib] = None
 
 
@@ -279,3 +342,19 @@ def expert_group(experts, ids, w, shared, x, limit=math.inf):
 
 def route(logits, k, mode=0, renorm=False, bias=None, w_scale=1.0):
     return load().route(logits, k, mode, renorm, bias, w_scale)
+
+
+def round_fmt(v, mbits, emin):
+    return load().round_fmt(v, mbits, emin)
+
+
+def v4_block_scale(m):
+    return load().v4_block_scale(m)
+
+
+def v4_combine(rows, ids, has_shared):
+    return load().v4_combine(rows, ids, has_shared)
+
+
+def expert_group_v4(experts, ids, w, shared, x, limit=math.inf, gu_err=0.0, act_rel=0.0, down_err=0.0):
+    return load().expert_group_v4(experts, ids, w, shared, x, limit, gu_err, act_rel, down_err)

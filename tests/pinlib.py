@@ -814,4 +814,196 @@ def pin_route_tokens_independent(lib):
         assert np.array_equal(one["w"][0], r["w"][t])
 
 
+
+# ---------------------------------------------------------------------------
+# DeepSeek V4's rounding activation
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _bf16_torch(v):
+    """f32 values rounded to bf16 by torch's cast (nearest-even)."""
+    torch = _torch()
+    return torch.from_numpy(np.asarray(v, np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def _e4m3_torch(v):
+    """f32 values rounded to E4M3 (the fn variant: no infinities) by torch's cast."""
+    torch = _torch()
+    return torch.from_numpy(np.asarray(v, np.float32)).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _f32_ties(rng, n, low_bits, exp_lo, exp_hi):
+    """f32 values whose low ``low_bits`` bits are exactly half a unit of the
+    shorter format (a tie), the rest random, exponents in [exp_lo, exp_hi)."""
+    mant = rng.integers(0, 1 << 23, size=n, dtype=np.int64)
+    mant = (mant >> low_bits << low_bits) | (1 << (low_bits - 1))
+    e = rng.integers(exp_lo, exp_hi, size=n)
+    bits = (rng.integers(0, 2, size=n) << 31) | ((e + 127) << 23) | mant
+    return bits.astype(np.uint32).view(np.float32)
+
+
+def pin_bf16_rounding_is_library_cast(lib):
+    """bf16 nearest-even on f32 values (random, exact ties, bf16 subnormals) is torch's cast."""
+    rng = np.random.default_rng(7300)
+    vals = np.concatenate([
+        (rng.standard_normal(600) * np.exp2(rng.integers(-30, 30, 600))).astype(np.float32),
+        _f32_ties(rng, 400, 16, -20, 20),
+        (rng.uniform(-1, 1, 100) * 2.0 ** -128).astype(np.float32),   # below bf16's smallest normal
+        np.array([0.0, -0.0, 1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8)], np.float32)])
+    want = _bf16_torch(vals)
+    got = np.array([lib.round_fmt(float(v), 7, -126) for v in vals])
+    assert np.array_equal(got, want), np.flatnonzero(got != want)[:5]
+
+
+def pin_e4m3_rounding_is_library_cast(lib):
+    """E4M3 nearest-even on f32 values below 448 (random, ties, subnormals) is torch's cast."""
+    rng = np.random.default_rng(7301)
+    vals = np.concatenate([
+        rng.uniform(-440, 440, 500).astype(np.float32),
+        (rng.standard_normal(400) * np.exp2(rng.integers(-9, 6, 400))).astype(np.float32),
+        _f32_ties(rng, 300, 20, -6, 8),            # ties between normal E4M3 values
+        (rng.integers(-32, 33, 100) * 2.0 ** -10).astype(np.float32),   # ties in the subnormal range
+        np.array([448.0, 447.9, 0.0, 2 ** -6, 2 ** -9, 2 ** -10, 3 * 2 ** -11, 0.0625 * 1.0625], np.float32)])
+    vals = vals[np.abs(vals) <= 448.0]
+    want = _e4m3_torch(vals)
+    got = np.array([lib.round_fmt(float(v), 3, -6) for v in vals])
+    assert np.array_equal(got, want), [(float(v), a, b) for v, a, b in zip(vals, got, want) if a != b][:5]
+
+
+def pin_v4_block_scale(lib):
+    """The scale is the smallest power of two that takes the block's maximum below 448."""
+    hand = {448.0: 2.0, 447.0: 1.0, 224.0: 1.0, 223.9: 0.5, 1.0: 2.0 ** -8, 0.0: 1.0,
+            896.0: 4.0, 2.0 ** -20: 2.0 ** -28, 1000.0: 4.0}
+    for m, s in hand.items():
+        assert lib.v4_block_scale(m) == s, (m, lib.v4_block_scale(m), s)
+    rng = np.random.default_rng(7302)
+    for m in np.exp2(rng.uniform(-40, 40, 300)):
+        s = lib.v4_block_scale(float(m))
+        assert math.frexp(s)[0] == 0.5            # a power of two
+        assert m / s < 448.0 <= m / (s / 2.0)
+
+
+def pin_v4_combine_order(lib):
+    """Rows join in ascending expert id, equal ids in rank order, the shared row last, in f32:
+    1 + 1 + 2^24 is 2^24 + 2 in f32 while 2^24 + 1 + 1 is 2^24 (1 is half an ulp there)."""
+    big = 2.0 ** 24
+    rows = np.array([[big], [1.0], [1.0]])
+    assert lib.v4_combine(rows, [7, 3, 5], False)[0] == big + 2      # ids 3, 5 before 7
+    assert lib.v4_combine(rows, [1, 3, 5], False)[0] == big
+    rows = np.array([[1.0], [big], [1.0]])
+    assert lib.v4_combine(rows, [4, 4, 2], False)[0] == big + 2      # id 2, then id 4's ranks 0, 1
+    rows = np.array([[1.0], [1.0], [big]])
+    assert lib.v4_combine(rows, [1, 2], True)[0] == big + 2          # the shared row after the routed ones
+    rows = np.array([[1.0, -3.0], [2.0, 0.5]])
+    assert lib.v4_combine(rows, [9, 8], False).tolist() == [3.0, -2.5]
+
+
+def _f32_expert(H, I, seed, gate_rows):
+    """An expert of f32 rows (format 10): gate row i all gate_rows[i]; up rows all 1/H; down random."""
+    rng = np.random.default_rng(seed)
+
+    def mat(v, O, K):
+        return _qm(10, O, K, K, np.ascontiguousarray(v, np.float32), None)
+
+    class Ex:
+        pass
+    ex = Ex()
+    ex.gate = mat(np.repeat(np.asarray(gate_rows, np.float32)[:, None], H, axis=1), I, H)
+    ex.up = mat(np.full((I, H), 1.0 / H, np.float32), I, H)
+    ex.down = mat(rng.standard_normal((H, I)).astype(np.float32), H, I)
+    return ex
+
+
+def pin_v4_group_closed_form(lib):
+    """x all ones and constant gate and up rows make g[i] = H * gate_rows[i] and u[i] = 1 exactly;
+    every later step is then a library cast, a closed-form scale or an exact rational sum."""
+    H, I = 64, 256
+    rng = np.random.default_rng(7303)
+    gate_rows = (rng.choice([-1, 1], I) * np.exp2(rng.uniform(-16, 3, I))).astype(np.float32)
+    gate_rows[:128] = gate_rows[:128] * np.float32(2.0 ** -9)   # block 0: |g| < 1
+    gate_rows[200] = 0.12    # block 1's largest activation sits in its second half
+    gate_rows[130] = 0.02
+    # block 0's largest: g just under a limit of 6.99 whose bf16 rounding (7) is above it; a
+    # route weight for which clamping before the rounding would change its E4M3 value
+    L = 6.99
+    gate_rows[17] = np.float32(6.986 / H)
+    g17 = float(_bf16_torch(H * np.float64(gate_rows[17])))
+
+    def e4_of(gc, wr):
+        a = float(_bf16_torch(gc / (1.0 + math.exp(-gc)) * float(wr)))
+        s = 2.0 ** (math.floor(math.log2(a / 448.0)) + 1)
+        return float(_e4m3_torch(a / s)) * s
+    wr = next(w for w in (np.float32(0.7 + j / 4096) for j in range(400))
+              if e4_of(min(g17, L), w) != e4_of(g17, w))
+    ex = _f32_expert(H, I, 7304, gate_rows)
+    x = np.ones((1, H), np.float32)
+    for limit in (math.inf, L):
+        r = lib.expert_group_v4([ex], np.array([[0]], np.int32), np.array([[wr]], np.float32), None, x, limit)
+        assert r["open"] == 0
+        _v4_closed_form_check(r, ex, gate_rows, H, I, wr, limit)
+
+
+def _v4_closed_form_check(r, ex, gate_rows, H, I, wr, limit):
+    g = np.minimum(_bf16_torch(H * gate_rows.astype(np.float64)), limit)   # clamped after the rounding
+    hv = np.array([gi / (1.0 + math.exp(-gi)) for gi in g]) * float(wr)   # u = 1 exactly
+    a = _bf16_torch(hv)
+    e4 = np.empty(I)
+    for b0 in range(0, I, 128):
+        blk = a[b0:b0 + 128]
+        m = np.max(np.abs(blk))
+        s = 2.0 ** (math.floor(math.log2(m / 448.0)) + 1)
+        e4[b0:b0 + 128] = _e4m3_torch(blk / s) * s
+    assert np.array_equal(r["h"][0], e4)
+    Wd = ex.down.q.astype(np.float64)
+    d = np.array([float(sum(Fraction(float(Wd[o, k])) * Fraction(float(e4[k])) for k in range(I)))
+                  for o in range(H)])
+    assert np.array_equal(r["y"][0].astype(np.float64), _bf16_torch(d))
+
+
+def pin_v4_zero_weight_slot_adds_nothing(lib):
+    """A routed slot of weight 0 leaves every row of y as the group without it (bit for bit)."""
+    ex = _tiny_experts(3, fmt=7, gs=32, H=64, I=128)
+    x = synth.activations(2, 64, 7305)
+    ids = np.array([[0, 1], [2, 1]], np.int32)
+    r2 = lib.expert_group_v4(ex, ids, np.array([[0.0, 0.6], [0.3, 0.0]], np.float32), 2, x)
+    for t, keep in ((0, 1), (1, 0)):
+        r1 = lib.expert_group_v4(ex, ids[t:t + 1, keep:keep + 1],
+                                 np.array([[(0.6, 0.3)[t]]], np.float32), 2, x[t:t + 1])
+        assert np.array_equal(r2["y"][t], r1["y"][0])
+
+
+def pin_v4_group_near_plain_group(lib):
+    """The roundings move y by at most a few percent of the plain group's normaliser
+    (E4M3 keeps 4 significant bits), and the weights, the shared expert and the limit act
+    as in the plain group."""
+    ex = _tiny_experts(4, fmt=7, gs=32, H=64, I=256)
+    x = synth.activations(3, 64, 7306) * np.float32(8.0)
+    ids = np.array([[0, 1], [2, 0], [1, 2]], np.int32)
+    w = np.array([[0.6, 0.4], [0.9, 0.1], [0.5, 0.5]], np.float32)
+    for limit in (math.inf, 0.02):
+        y, a = lib.expert_group(ex, ids, w, 3, x, limit)
+        r = lib.expert_group_v4(ex, ids, w, 3, x, limit)
+        err = np.abs(r["y"].astype(np.float64) - y)
+        assert np.all(err <= 0.08 * a + 1e-30), float(np.max(err / a))
+        assert np.max(np.abs(y)) > 0 and np.mean(err) < 0.02 * np.mean(a)
+
+
+def pin_v4_h_rows_are_e4m3_blocks(lib):
+    """Each block of 128 in a slot's h is a power of two times E4M3 values, the largest under 448."""
+    ex = _tiny_experts(2, fmt=7, gs=32, H=64, I=256)
+    x = synth.activations(2, 64, 7307) * np.float32(8.0)
+    r = lib.expert_group_v4(ex, np.array([[0], [1]], np.int32), np.array([[0.8], [0.25]], np.float32), 0, x)
+    for row in r["h"]:
+        for b0 in range(0, row.size, 128):
+            blk = row[b0:b0 + 128]
+            m = np.max(np.abs(blk))
+            assert m > 0
+            s = lib.v4_block_scale(m)
+            assert np.array_equal(_e4m3_torch(blk / s), blk / s) and m / s < 448.0
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

@@ -94,6 +94,19 @@ MUTANTS = {
                                  "return (double)m->scales[(o / 128) * blocks];"),
     "no_scale_formats_take_f16_scale": ("if (m->fmt == 10 || m->fmt == 11 || m->fmt == 14)\n        return 1.0;",
                                         "if (m->fmt == 10 || m->fmt == 11 || m->fmt == 14)\n        return m->fmt == 14 ? 0.5 : 1.0;"),
+    "v4_ties_away_from_zero": ("return nearbyint(v / quantum) * quantum;", "return round(v / quantum) * quantum;"),
+    "v4_round_truncates": ("return nearbyint(v / quantum) * quantum;", "return trunc(v / quantum) * quantum;"),
+    "v4_subnormal_quantum": ("int lead = e - 1 < emin ? emin : e - 1;", "int lead = e - 1;"),
+    "v4_scale_allows_448": ("while (m / (s / 2.0) < 448.0)", "while (m / (s / 2.0) <= 448.0)"),
+    "v4_scale_not_restored": ("e4[j] = orc_round_fmt(e4[j] / s, 3, -6) * s;", "e4[j] = orc_round_fmt(e4[j] / s, 3, -6);"),
+    "v4_e4m3_as_e5m2": ("e4[j] = orc_round_fmt(e4[j] / s, 3, -6) * s;", "e4[j] = orc_round_fmt(e4[j] / s, 2, -14) * s;"),
+    "v4_block_max_half": ("        for (long j = b0; j < b0 + 128; j++)\n            if (fabs(e4[j]) > m",
+                          "        for (long j = b0; j < b0 + 64; j++)\n            if (fabs(e4[j]) > m"),
+    "v4_weight_dropped": ("double hv = orc_silu(gc) * uc * wr;", "double hv = orc_silu(gc) * uc;"),
+    "v4_gate_not_rounded": ("double gb = bf16(g), ub = bf16(u);", "double gb = g, ub = bf16(u);"),
+    "v4_clamp_before_rounding": ("double gc = gb > limit ? limit : gb;", "double gc = g > limit ? limit : bf16(g);"),
+    "v4_down_not_rounded": ("        d[o] = bf16(sum);", "        d[o] = sum;"),
+    "v4_combine_rank_order": ("if (!done[r] && (pick < 0 || ids[r] < ids[pick]))", "if (!done[r] && pick < 0)"),
     "token_x_not_advanced": ("mlp_one(&gates[e], &ups[e], &downs[e], x + t * gates[e].K,",
                              "mlp_one(&gates[e], &ups[e], &downs[e], x,"),
 }
