@@ -23,6 +23,7 @@ STATUS = {0: "DQG_OK", -1: "DQG_EINVAL", -2: "DQG_EFORMAT", -3: "DQG_ESHAPE", -4
 DQG_I8_ROW, DQG_I4_ROW, DQG_I4_GS, DQG_I3_G64, DQG_MXFP4 = 1, 2, 4, 5, 7
 DQG_F32, DQG_BF16, DQG_FP8_BLOCK, DQG_I8_GS, DQG_F16 = 10, 11, 12, 13, 14
 DQG_ROUTE_SOFTMAX, DQG_ROUTE_SIGMOID = 0, 1
+DQG_ACT_SWIGLU, DQG_ACT_SWIGLU_V4 = 0, 1
 
 
 class DqgError(RuntimeError):
@@ -68,6 +69,7 @@ SIGNATURES = {
     "dqg_expert_table_create": (C.c_int, [C.POINTER(dqg_expert), _I32, C.POINTER(C.c_void_p)]),
     "dqg_expert_table_destroy": (None, [_P]),
     "dqg_expert_table_set_swiglu_limit": (C.c_int, [_P, C.c_float]),
+    "dqg_expert_table_set_activation": (C.c_int, [_P, C.c_int32]),
     "dqg_expert_group_scratch_bytes": (_SZ, [_P, _I32, _I32]),
     "dqg_expert_group": (C.c_int, [_P, _I32, _I32, _P, _P, _I32, _P, _P, _P, _SZ, _P]),
     "dqg_expert_group_issue": (C.c_int, [_P, _I32, _I32, _P, _P, _I32, _P, _P, _P, _SZ, _P,
@@ -237,6 +239,10 @@ class ExpertTable:
     def set_swiglu_limit(self, limit: float) -> None:
         """dqg_expert_table_set_swiglu_limit (math.inf: the plain SwiGLU)."""
         _check(load().dqg_expert_table_set_swiglu_limit(self.handle, float(limit)))
+
+    def set_activation(self, act: int) -> None:
+        """dqg_expert_table_set_activation: DQG_ACT_SWIGLU or DQG_ACT_SWIGLU_V4."""
+        _check(load().dqg_expert_table_set_activation(self.handle, int(act)))
 
     def scratch_bytes(self, S: int, k: int) -> int:
         return load().dqg_expert_group_scratch_bytes(self.handle, S, k)

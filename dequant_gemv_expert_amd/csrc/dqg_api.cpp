@@ -23,6 +23,7 @@ struct dqg_expert_table {
     int codec_gu, codec_down;
     int32_t H, I;
     float swiglu_limit;   // +inf: plain SwiGLU
+    int32_t act;          // DQG_ACT_SWIGLU or DQG_ACT_SWIGLU_V4
 };
 
 namespace {
@@ -250,6 +251,7 @@ int group_common(const dqg_expert_table *t, int32_t S, int32_t k, const int32_t 
     a.H = t->H;
     a.I = t->I;
     a.limit = t->swiglu_limit;
+    a.act = t->act == DQG_ACT_SWIGLU_V4 ? ACT_SWIGLU_V4 : ACT_SWIGLU;
     int nl = 0;
     const hipError_t e = launch_group(t->codec_gu, t->codec_down, a, static_cast<hipStream_t>(stream), &nl);
     g_launches += nl;
@@ -438,6 +440,17 @@ int dqg_expert_table_set_swiglu_limit(dqg_expert_table *t, float limit) {
     return DQG_OK;
 }
 
+int dqg_expert_table_set_activation(dqg_expert_table *t, int32_t act) {
+    if (!t) return fail(DQG_EINVAL, "expert_table_set_activation: table is NULL");
+    if (act != DQG_ACT_SWIGLU && act != DQG_ACT_SWIGLU_V4)
+        return fail(DQG_EINVAL, "expert_table_set_activation: unknown activation %d", act);
+    if (act == DQG_ACT_SWIGLU_V4 && t->I % 128)
+        return fail(DQG_EINVAL, "expert_table_set_activation: DeepSeek V4's activation rounds blocks of 128, "
+                                "I=%d is not a multiple of 128", t->I);
+    t->act = act;
+    return DQG_OK;
+}
+
 int dqg_dequant(const dqg_matrix *W, float *out, void *stream) {
     ++g_calls_dequant;
     prof_call();
@@ -516,6 +529,7 @@ int dqg_expert_table_create(const dqg_expert *experts, int32_t n, dqg_expert_tab
     t->H = e0.gate.K;
     t->I = e0.gate.O;
     t->swiglu_limit = INFINITY;
+    t->act = DQG_ACT_SWIGLU;
     hipError_t e = hipGetDevice(&t->device);
     if (e == hipSuccess) e = hipMalloc(reinterpret_cast<void **>(&t->dev), (size_t)n * sizeof(ExpertDev));
     if (e == hipSuccess) e = hipMemcpy(t->dev, host, (size_t)n * sizeof(ExpertDev), hipMemcpyHostToDevice);

@@ -37,6 +37,10 @@ struct ExpertDev {
 enum Codec : int { C_I8 = 1, C_I4 = 4, C_I3 = 5, C_FP4 = 7, C_F32 = 10, C_BF16 = 11, C_FP8 = 12, C_F16 = 14 };
 
 // Launch parameters of the grouped expert call.
+// The experts' activation: the (clamped) SwiGLU, or DeepSeek V4's rounding
+// form of it (I a multiple of 128).
+constexpr int32_t ACT_SWIGLU = 0, ACT_SWIGLU_V4 = 1;
+
 struct GroupArgs {
     const ExpertDev *table;
     int32_t n_experts;
@@ -51,6 +55,7 @@ struct GroupArgs {
                          // when an id is out of range
     int32_t H, I;
     float limit;         // swiglu_limit of the experts' SwiGLU, +inf for none
+    int32_t act;         // ACT_SWIGLU or ACT_SWIGLU_V4
 };
 
 // Launch parameters of the router.

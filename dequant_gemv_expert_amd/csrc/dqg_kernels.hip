@@ -29,6 +29,7 @@
 
 #include <hip/hip_ext.h>
 
+#include <climits>
 #include <mutex>
 #include <type_traits>
 
@@ -424,6 +425,53 @@ __device__ __forceinline__ float swiglu(float g, float u, float L) {
     const float gc = g > L ? L : g;
     const float uc = u > L ? L : (u < -L ? -L : u);
     return silu(gc) * uc;
+}
+
+// DeepSeek V4's rounding activation ("colibri -- Vulkan backend
+// (docs/vulkan.md)", the paragraph on DeepSeek V4's CPU expert and the
+// tier's third activation): bf16 and E4M3 roundings, to nearest, ties to
+// even, on the bits.
+//
+// bf16: add 0x7FFF plus the lowest kept bit, then clear the low 16 bits (a
+// carry out of the fraction steps the exponent, as rounding up should).
+__device__ __forceinline__ float round_bf16(float v) {
+    uint32_t b = __float_as_uint(v);
+    if ((b & 0x7F800000u) == 0x7F800000u) return v;   // inf and NaN unchanged
+    b += 0x7FFFu + ((b >> 16) & 1u);
+    return __uint_as_float(b & 0xFFFF0000u);
+}
+
+// E4M3 (1.4.3, bias 7, no infinities) for |v| < 464, where no value rounds
+// past 448.  From 2^-6 up: 3 fraction bits, the same carry trick at bit 20;
+// below: the subnormal quantum 2^-9 (v * 512 is exact, rintf ties to even).
+__device__ __forceinline__ float round_e4m3(float v) {
+    const float a = fabsf(v);
+    float r;
+    if (a < 0x1p-6f) {
+        r = rintf(a * 512.f) * 0x1p-9f;
+    } else {
+        uint32_t b = __float_as_uint(a);
+        b += 0x7FFFFu + ((b >> 20) & 1u);
+        r = __uint_as_float(b & 0xFFF00000u);
+    }
+    return copysignf(r, v);
+}
+
+// The exponent j of the block scale 2^j: the smallest power of two that
+// takes m (the block's largest magnitude) below 448; 0 for m = 0.  With
+// m = f 2^e, f in [1/2, 1): m / 2^(e-9) = 512 f lies in [256, 512), so j is
+// e - 9 when 512 f < 448 and e - 8 otherwise.
+__device__ __forceinline__ int v4_scale_exp(float m) {
+    if (!(m > 0.f)) return 0;
+    int e;
+    const float f = frexpf(m, &e);
+    return f * 512.f < 448.f ? e - 9 : e - 8;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 1; o < WAVE; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
 }
 
 // ---------------------------------------------------------------------------
@@ -1013,7 +1061,14 @@ __device__ __forceinline__ void group_gu_batch(const GroupArgs &a, const ExpertD
 #pragma unroll
         for (int j = 1; j < SM; ++j)
             if (s == j) slot = b.slot[j];
-        a.h[(size_t)slot * a.I + row0 + r] = swiglu(gv, uv, a.limit);
+        float hv;
+        if (a.act == ACT_SWIGLU_V4) {   // bf16 gate and up; the weighted activation to bf16
+            const float wr = slot < a.S * a.k ? a.w[slot] : 1.f;
+            hv = round_bf16(swiglu(round_bf16(gv), round_bf16(uv), a.limit) * wr);
+        } else {
+            hv = swiglu(gv, uv, a.limit);
+        }
+        a.h[(size_t)slot * a.I + row0 + r] = hv;
     }
 }
 
@@ -1082,7 +1137,7 @@ __device__ __forceinline__ void group_down_batch(const GroupArgs &a, const Exper
 #pragma unroll
         for (int j = 1; j < SM; ++j)
             if (s == j) slot = b.slot[j];
-        d[slot * R + r] = out;
+        d[slot * R + r] = a.act == ACT_SWIGLU_V4 ? round_bf16(out) : out;
     }
 }
 
@@ -1125,10 +1180,42 @@ __global__ void __launch_bounds__(WAVE * down_max_waves<CAP>()) k_group_down(Gro
         const int t = j / R, r = j % R;
         if (row0 + r >= a.H) continue;
         float acc = 0.f;
-        for (int rk = 0; rk < a.k; ++rk) acc = fmaf(a.w[t * a.k + rk], d[(t * a.k + rk) * R + r], acc);
+        if (a.act == ACT_SWIGLU_V4) {
+            // the weights were applied before down; rows join in ascending
+            // (expert id, rank): each step takes the least pair above the last
+            int last_id = INT_MIN, last_rk = -1;
+            for (int n = 0; n < a.k; ++n) {
+                int pick = -1, pick_id = 0;
+                for (int rk = 0; rk < a.k; ++rk) {
+                    const int id = a.ids[t * a.k + rk];
+                    const bool after = id > last_id || (id == last_id && rk > last_rk);
+                    if (after && (pick < 0 || id < pick_id)) { pick = rk; pick_id = id; }
+                }
+                acc += d[(t * a.k + pick) * R + r];
+                last_id = pick_id;
+                last_rk = pick;
+            }
+        } else {
+            for (int rk = 0; rk < a.k; ++rk) acc = fmaf(a.w[t * a.k + rk], d[(t * a.k + rk) * R + r], acc);
+        }
         if (a.shared >= 0) acc += d[(nr + t) * R + r];
         a.y[(size_t)t * a.H + row0 + r] = acc;
     }
+}
+
+// DeepSeek V4's pass between the activation and down: every block of 128
+// consecutive values of a slot's h becomes E4M3 values times the block's
+// power-of-two scale.  One wave per block; lane l holds values l and l + 64.
+// Multiplying by 2^-j and by 2^j is exact.
+__global__ void __launch_bounds__(256) k_group_act_v4(float *__restrict__ h, int nblk) {
+    const int blk = blockIdx.x * 4 + wave_id();
+    if (blk >= nblk) return;
+    const int lane = threadIdx.x & (WAVE - 1);
+    float *p = h + (size_t)blk * 128;
+    const float v0 = p[lane], v1 = p[lane + 64];
+    const int j = v4_scale_exp(wave_max(fmaxf(fabsf(v0), fabsf(v1))));
+    p[lane] = ldexpf(round_e4m3(ldexpf(v0, -j)), j);
+    p[lane + 64] = ldexpf(round_e4m3(ldexpf(v1, -j)), j);
 }
 
 // ---------------------------------------------------------------------------
@@ -1510,12 +1597,6 @@ __device__ __forceinline__ uint32_t float_order(float f) {
     return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 1; m < WAVE; m <<= 1) v = fmaxf(v, __shfl_xor(v, m));
-    return v;
-}
-
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
     for (int m = 1; m < WAVE; m <<= 1) {
@@ -1891,6 +1972,13 @@ hipError_t launch_group(int codec_gu, int codec_down, const GroupArgs &a, hipStr
     hipError_t e = with_codec(codec_gu, [&](auto c) { return group_a<decltype(c)::value>(a, st); });
     if (e != hipSuccess) return e;
     ++*launches;
+    if (a.act == ACT_SWIGLU_V4) {
+        const int slots = a.S * a.k + (a.shared >= 0 ? a.S : 0);
+        const int nblk = slots * (a.I / 128);
+        launch("group_act_v4", k_group_act_v4, dim3((nblk + 3) / 4), dim3(256), 0, st, a.h, nblk);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        ++*launches;
+    }
     e = with_codec(codec_down, [&](auto c) { return group_b<decltype(c)::value>(a, st); });
     if (e == hipSuccess) ++*launches;
     return e;

@@ -215,6 +215,33 @@ void dqg_expert_table_destroy(dqg_expert_table *table);
  * was.  Applies to calls issued after it returns. */
 int dqg_expert_table_set_swiglu_limit(dqg_expert_table *table, float limit);
 
+/*
+ * The experts' activation in dqg_expert_group:
+ *   DQG_ACT_SWIGLU (the default at creation): h = SwiGLU(g, u) with the
+ *     table's limit; y[t] adds w[t][r] * down(h) in rank order, then the
+ *     shared expert.
+ *   DQG_ACT_SWIGLU_V4: DeepSeek V4's rounding form ("colibri -- Vulkan
+ *     backend (docs/vulkan.md)", the paragraph on DeepSeek V4's CPU expert
+ *     and the tier's third activation).  g and u are rounded to bf16 before
+ *     the (clamped) SwiGLU; the activation times the slot's route weight
+ *     (1 for the shared expert) is rounded to bf16; each block of 128
+ *     consecutive values of a slot's h is rounded to E4M3 after division
+ *     by the block's scale, the smallest power of two that takes the
+ *     block's largest magnitude below 448, and multiplied back; down's
+ *     output is rounded to bf16; y[t] is the f32 sum from 0 of the token's
+ *     routed rows in ascending (expert id, rank), then the shared row, with
+ *     no further weight.  Every rounding is to nearest, ties to even.  The
+ *     scratch's h then holds down's input (the scaled E4M3 values).  x is
+ *     used as given: the pages' engine rounds it to E4M3 per 128 on the host
+ *     before the call.  Needs I to be a multiple of 128 (DQG_EINVAL
+ *     otherwise); adds one launch ("group_act_v4") between gate/up and down.
+ * Other values give DQG_EINVAL and leave the table as it was.  Applies to
+ * calls issued after it returns.
+ */
+#define DQG_ACT_SWIGLU 0
+#define DQG_ACT_SWIGLU_V4 1
+int dqg_expert_table_set_activation(dqg_expert_table *table, int32_t act);
+
 /* Scratch bytes dqg_expert_group needs for S tokens of top-k routing: a
  * header of DQG_SCRATCH_H_OFFSET bytes (the error flag at byte 0), then the
  * hidden state h of every (token, rank) and shared slot.  The scratch needs
@@ -294,7 +321,7 @@ int dqg_route(const float *logits, int32_t S, int32_t E, int32_t k, int32_t mode
  * (one per kernel name, in first-launch order), stores their count in *n
  * and releases the events.  Kernel names: "matmul", "gate_up", "gemm",
  * "gemm_gate_up", "gemm_reduce", "dequant", "route", "group_gate_up",
- * "group_down". */
+ * "group_act_v4", "group_down". */
 typedef struct {
     char kernel[32];
     int64_t launches;

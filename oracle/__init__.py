@@ -6,7 +6,9 @@ path: it shares no code with it and neither imports the other.  Inputs come
 from the ``synth`` generators; the arithmetic is in ``oracle.c``.
 """
 from .oracle import (OracleLib, load, dequant, code_values, gemv, gate_up, expert_group, route,
-                     e2m1, minifloat, silu, set_threads, get_threads)
+                     e2m1, minifloat, silu, set_threads, get_threads, round_fmt, v4_block_scale,
+                     v4_combine, expert_group_v4)
 
 __all__ = ["OracleLib", "load", "dequant", "code_values", "gemv", "gate_up", "expert_group", "route",
-           "e2m1", "minifloat", "silu", "set_threads", "get_threads"]
+           "e2m1", "minifloat", "silu", "set_threads", "get_threads", "round_fmt", "v4_block_scale",
+           "v4_combine", "expert_group_v4"]

@@ -128,6 +128,11 @@ def rng_for(*key: int) -> np.random.Generator:
 
 
 def _scales(rng: np.random.Generator, fmt: int, shape, kind: str) -> np.ndarray:
+    if kind == "pow2_small":
+        # powers of two 2^-5 and 2^-4 (with activations on a coarse grid,
+        # products and sums that stay exact in f32)
+        e = rng.integers(-5, -3, size=shape)
+        return np.ldexp(np.ones(shape, dtype=np.float32), e).astype(np.float32)
     if kind == "pow2":
         # e8m0 scales pre-expanded to f32: 2^e with e uniform in {-10..-6}
         e = rng.integers(-10, -5, size=shape)
@@ -198,6 +203,20 @@ def activations(S: int, K: int, *key: int) -> np.ndarray:
     return rng_for(*key).standard_normal(size=(S, K)).astype(np.float32)
 
 
+def activations_e4m3_grid(S: int, K: int, *key: int) -> np.ndarray:
+    """x[S][K] f32 on the E4M3 grid: a uniform sign, fraction 1.000b .. 1.111b
+    and exponent 2^-3 .. 2^1 (so |x| in [1/8, 3.75], multiples of 2^-6), and
+    one entry in ten zero: activations as an engine hands them over after
+    rounding them to E4M3 itself."""
+    rng = rng_for(*key)
+    mant = rng.integers(8, 16, size=(S, K))
+    expo = rng.integers(-3, 2, size=(S, K))
+    sign = rng.choice([-1.0, 1.0], size=(S, K))
+    x = sign * np.ldexp(mant.astype(np.float64), expo - 3)
+    x[rng.random((S, K)) < 0.1] = 0.0
+    return x.astype(np.float32)
+
+
 def routing(S: int, n_experts: int, k: int, *key: int):
     """Top-k routing of S tokens.
 
@@ -237,15 +256,16 @@ class Expert:
 
 
 def expert(fmt: int, H: int, I: int, gs: Optional[int], seed: int, index: int,
-           down_fmt: Optional[int] = None, down_gs: Optional[int] = None) -> Expert:
+           down_fmt: Optional[int] = None, down_gs: Optional[int] = None,
+           scale_kind: Optional[str] = None) -> Expert:
     """Expert ``index`` of a seeded set: gate, up [I x H] and down [H x I]."""
     dfmt = fmt if down_fmt is None else down_fmt
     dgs = gs if down_gs is None else down_gs
     if dfmt in (FMT_I8_ROW, FMT_I4_ROW) or dfmt in NO_SCALE_FORMATS or dfmt == FMT_FP8_BLOCK:
         dgs = None
-    return Expert(matrix(fmt, I, H, gs, seed, index, 0),
-                  matrix(fmt, I, H, gs, seed, index, 1),
-                  matrix(dfmt, H, I, dgs, seed, index, 2))
+    return Expert(matrix(fmt, I, H, gs, seed, index, 0, scale_kind=scale_kind),
+                  matrix(fmt, I, H, gs, seed, index, 1, scale_kind=scale_kind),
+                  matrix(dfmt, H, I, dgs, seed, index, 2, scale_kind=scale_kind))
 
 
 def experts(fmt: int, H: int, I: int, gs: Optional[int], seed: int, n: int,

@@ -138,6 +138,11 @@ def test_swiglu_limit_validation(lib, limit):
     assert lib.dqg_expert_table_set_swiglu_limit(None, 1.0) == -1
 
 
+def test_activation_validation(lib):
+    assert lib.dqg_expert_table_set_activation(None, L.DQG_ACT_SWIGLU_V4) == -1
+    assert "NULL" in lib.dqg_last_error().decode()
+
+
 def test_table_validation(lib):
     e = L.dqg_expert(_mat(O=32, K=64), _mat(O=32, K=64), _mat(O=64, K=64))   # down must be [64 x 32]
     out = C.c_void_p()
