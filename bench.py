@@ -24,6 +24,7 @@ themselves add about 8 us a call to the wall clock;
 """
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -140,6 +141,9 @@ def main():
                     help="dense workloads: time dqg_gate_up on two matrices of the workload's shape")
     ap.add_argument("--swiglu-limit", type=float, default=None,
                     help="clamp the experts' SwiGLU at this limit (expert-group workloads)")
+    ap.add_argument("--activation", choices=("swiglu", "v4"), default="swiglu",
+                    help="the experts' activation: the (clamped) SwiGLU, or DeepSeek V4's rounding form "
+                         "(expert-group workloads)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (torch) 5 times, the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -198,6 +202,8 @@ def main():
     table = dq.ExpertTable(experts)
     if args.swiglu_limit is not None:
         table.set_swiglu_limit(args.swiglu_limit)
+    if args.activation == "v4":
+        table.set_activation(dq.DQG_ACT_SWIGLU_V4)
     torch.cuda.synchronize()
     log(f"[bench] {dev_name}: {n_total} experts resident ({n_total * exp_bytes / 1e9:.2f} GB) "
         f"in {time.time() - t0:.1f}s")
@@ -263,9 +269,10 @@ def main():
     #    on the launch's stream (the events add about 8 us a call to the wall
     #    clock, which is why value comes from region 1) ---------------------
     clocks = gpu_clocks()
-    dq.dqg_prof_begin(2 * K)
+    per_call = 3 if args.activation == "v4" else 2   # DeepSeek V4's pass is a launch of its own
+    dq.dqg_prof_begin(per_call * K)
     t_wall_events = run_steps()
-    pstats = launch_stats(dq.dqg_prof_end_launches(2 * K))
+    pstats = launch_stats(dq.dqg_prof_end_launches(per_call * K))
     prof = {name: v[:2] for name, v in pstats.items()}
 
     total_bytes = sum(step_bytes(i) for i in range(args.warmup, args.warmup + K))
@@ -304,6 +311,13 @@ def main():
             def __getitem__(self, e):
                 return host_expert(int(e))
 
+        limit = math.inf if args.swiglu_limit is None else args.swiglu_limit
+
+        def oracle_group(*a):
+            if args.activation == "v4":
+                return oracle.expert_group_v4(*a, limit)
+            return oracle.expert_group(*a, limit)
+
         threads = oracle.get_threads()
         spent, calls, cbytes = 0.0, 0, 0
         while spent < args.cpu_seconds and calls < P:
@@ -312,8 +326,7 @@ def main():
             for e in set(ids[p].ravel().tolist()) | ({shared_of(i)} if n_shared else set()):
                 host_expert(e)   # drawn before the clock starts
             t = time.perf_counter()
-            oracle.expert_group(View(), ids[p], w[p], shared_of(i), x[p],
-                                *([] if args.swiglu_limit is None else [args.swiglu_limit]))
+            oracle_group(View(), ids[p], w[p], shared_of(i), x[p])
             spent += time.perf_counter() - t
             calls += 1
             cbytes += step_bytes(i)
@@ -333,8 +346,7 @@ def main():
 
         def one_call(j):   # the same calls again, on one host thread
             i = args.warmup + (j % calls)
-            oracle.expert_group(View(), ids[i % P], w[i % P], shared_of(i), x[i % P],
-                                *([] if args.swiglu_limit is None else [args.swiglu_limit]))
+            oracle_group(View(), ids[i % P], w[i % P], shared_of(i), x[i % P])
 
         c1, s1 = oracle_one_core(one_call, max(1.0, args.cpu_seconds / 3), draw)
         cpu["value_1core"] = round(sum(step_bytes(args.warmup + (j % calls)) for j in range(c1)) / s1 / 1e9, 3)
@@ -360,7 +372,8 @@ def main():
         "config": {"workload": args.workload, "tokens": S, "top_k": k, "experts": E,
                    "shared_expert": bool(n_sh), "H": H, "I": I, "format": f"fmt {fmt}, gs {gs}",
                    "routing_pool": P, "shared_copies": n_shared, "device": dev_name,
-                   **({} if args.swiglu_limit is None else {"swiglu_limit": args.swiglu_limit})},
+                   **({} if args.swiglu_limit is None else {"swiglu_limit": args.swiglu_limit}),
+                   **({} if args.activation == "swiglu" else {"activation": "deepseek_v4_rounding"})},
         "roofline": {"kernel": dom, "bound": "hbm",
                      "achieved": round(achieved, 1) if achieved else None, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
@@ -375,6 +388,9 @@ def main():
                            "bytes_per_launch": round(down_total / max(n_b, 1)),
                            "median_us": pstats["group_down"][2], "p10_us": pstats["group_down"][3],
                            "p90_us": pstats["group_down"][4]} if ms_b else None),
+        **({"act_v4_pass": {"kernel": "group_act_v4", "launches": pstats["group_act_v4"][0],
+                            "avg_us": round(pstats["group_act_v4"][1] / pstats["group_act_v4"][0] * 1e3, 2),
+                            "median_us": pstats["group_act_v4"][2]}} if "group_act_v4" in pstats else {}),
         "gpu_clocks": clocks,
         "cpu_baseline": cpu,
     }

@@ -29,7 +29,6 @@
 
 #include <hip/hip_ext.h>
 
-#include <climits>
 #include <mutex>
 #include <type_traits>
 
@@ -1175,26 +1174,31 @@ __global__ void __launch_bounds__(WAVE * down_max_waves<CAP>()) k_group_down(Gro
             else group_down_batch<C, R, 4>(a, ex, row0, b, d);
         });
     }
+    // DeepSeek V4's combine order, after the slots' outputs in LDS: each
+    // routed slot's place among its token's (expert id, rank) pairs
+    const bool v4 = a.act == ACT_SWIGLU_V4;
+    int *sid = reinterpret_cast<int *>(d + (size_t)(nr + (a.shared >= 0 ? a.S : 0)) * R), *ord = sid + nr;
+    if (v4)
+        for (int q = threadIdx.x; q < nr; q += blockDim.x) sid[q] = a.ids[q];
     __syncthreads();
+    if (v4) {
+        for (int q = threadIdx.x; q < nr; q += blockDim.x) {
+            const int t = q / a.k, rk = q - t * a.k, id = sid[q];
+            int pos = 0;
+            for (int j = 0; j < a.k; ++j) {
+                const int o = sid[t * a.k + j];
+                pos += o < id || (o == id && j < rk);
+            }
+            ord[t * a.k + pos] = rk;
+        }
+        __syncthreads();
+    }
     for (int j = threadIdx.x; j < a.S * R; j += blockDim.x) {
         const int t = j / R, r = j % R;
         if (row0 + r >= a.H) continue;
         float acc = 0.f;
-        if (a.act == ACT_SWIGLU_V4) {
-            // the weights were applied before down; rows join in ascending
-            // (expert id, rank): each step takes the least pair above the last
-            int last_id = INT_MIN, last_rk = -1;
-            for (int n = 0; n < a.k; ++n) {
-                int pick = -1, pick_id = 0;
-                for (int rk = 0; rk < a.k; ++rk) {
-                    const int id = a.ids[t * a.k + rk];
-                    const bool after = id > last_id || (id == last_id && rk > last_rk);
-                    if (after && (pick < 0 || id < pick_id)) { pick = rk; pick_id = id; }
-                }
-                acc += d[(t * a.k + pick) * R + r];
-                last_id = pick_id;
-                last_rk = pick;
-            }
+        if (v4) {   // the weights were applied before down
+            for (int n = 0; n < a.k; ++n) acc += d[(t * a.k + ord[t * a.k + n]) * R + r];
         } else {
             for (int rk = 0; rk < a.k; ++rk) acc = fmaf(a.w[t * a.k + rk], d[(t * a.k + rk) * R + r], acc);
         }
@@ -1904,7 +1908,9 @@ hipError_t group_b_cap(const GroupArgs &a, hipStream_t st) {
     const int slots = a.S * a.k + (a.shared >= 0 ? a.S : 0);
     const int waves = units < down_max_waves<CAP>() ? units : down_max_waves<CAP>();
     dim3 grid((a.H + RB - 1) / RB);
-    const size_t lds = (size_t)slots * RB * sizeof(float);
+    // the slots' outputs; DeepSeek V4's combine adds the ids and their order
+    const size_t lds = (size_t)slots * RB * sizeof(float) +
+                       (a.act == ACT_SWIGLU_V4 ? 2 * (size_t)a.S * a.k * sizeof(int) : 0);
     launch("group_down", (k_group_down<C, RB, CAP>), grid, dim3(WAVE * waves), lds, st, a);
     return hipGetLastError();
 }
