@@ -46,7 +46,9 @@ constexpr int WAVE = 64;
 #define DQG_WPB_A 4
 #endif
 #ifndef DQG_RB
-#define DQG_RB 8
+// 12 rows: 6144 rows make 512 blocks, one round at two 8-wave blocks per CU
+// (8 rows took 1.5 rounds, 6 rows two)
+#define DQG_RB 12
 #endif
 #ifndef DQG_CAP_A
 #define DQG_CAP_A 2   // largest token batch of the gate/up launch (x rows staged in LDS)
