@@ -476,15 +476,19 @@ static int bf16_open(double v, double err)
 }
 
 /*
- * One slot: e4[I] (down's input) and down's rounded outputs with the
- * rounding of v +- err for a device whose f32 sum may stray by err:
- * d[H], d_lo[H], d_hi[H].  Returns the number of bf16 decisions before down
- * that a device's error could flip: gate and up within gu_err * sum|w x|,
- * the weighted activation within act_rel of its value.
+ * One slot: e4[I] (down's input) and down's rounded outputs d[H].  A device
+ * whose weighted activation may stray by act_rel of its value can take an
+ * open bf16 decision either way; e4_lo, e4_hi bound what it then holds
+ * (both candidates under both block scales those candidates allow: E4M3
+ * rounding is monotone for a fixed scale, and the scale in the block's
+ * maximum).  d_lo, d_hi bound down's rounded outputs for such an e4 and an
+ * f32 sum that strays by down_err * sum|w e4|.  Returns the number of open
+ * bf16 decisions before down: gate and up within gu_err * sum|w x|, the
+ * weighted activation within act_rel of its value.
  */
 static long v4_slot(const orc_matrix *gate, const orc_matrix *up, const orc_matrix *down, const float *x,
                     double limit, double wr, double gu_err, double act_rel, double down_err,
-                    double *e4, double *d, double *d_lo, double *d_hi)
+                    double *e4, double *e4_lo, double *e4_hi, double *d, double *d_lo, double *d_hi)
 {
     long I = gate->O, H = down->O, open = 0, i;
 #pragma omp parallel for schedule(static) reduction(+ : open)
@@ -499,28 +503,50 @@ static long v4_slot(const orc_matrix *gate, const orc_matrix *up, const orc_matr
         double hv = orc_silu(gc) * uc * wr;
         open += bf16_open(hv, act_rel * fabs(hv));
         e4[i] = bf16(hv);
+        e4_lo[i] = bf16(hv - act_rel * fabs(hv));
+        e4_hi[i] = bf16(hv + act_rel * fabs(hv));
     }
     for (long b0 = 0; b0 < I; b0 += 128) {
-        double m = 0.0;
-        for (long j = b0; j < b0 + 128; j++)
+        double m = 0.0, m_lo = 0.0, m_hi = 0.0;
+        for (long j = b0; j < b0 + 128; j++) {
             if (fabs(e4[j]) > m || isnan(e4[j]))
                 m = isnan(e4[j]) ? NAN : fabs(e4[j]);
-        double s = orc_v4_block_scale(m);
-        for (long j = b0; j < b0 + 128; j++)
+            double a = fabs(e4_lo[j]), b = fabs(e4_hi[j]);
+            double small = a < b ? a : b, big = a < b ? b : a;
+            if (small > m_lo)
+                m_lo = small;
+            if (big > m_hi)
+                m_hi = big;
+        }
+        double s = orc_v4_block_scale(m), s_lo = orc_v4_block_scale(m_lo), s_hi = orc_v4_block_scale(m_hi);
+        for (long j = b0; j < b0 + 128; j++) {
+            double c[4] = {orc_round_fmt(e4_lo[j] / s_lo, 3, -6) * s_lo, orc_round_fmt(e4_lo[j] / s_hi, 3, -6) * s_hi,
+                           orc_round_fmt(e4_hi[j] / s_lo, 3, -6) * s_lo, orc_round_fmt(e4_hi[j] / s_hi, 3, -6) * s_hi};
             e4[j] = orc_round_fmt(e4[j] / s, 3, -6) * s;
+            e4_lo[j] = e4_hi[j] = c[0];
+            for (int q = 1; q < 4; q++) {
+                if (c[q] < e4_lo[j])
+                    e4_lo[j] = c[q];
+                if (c[q] > e4_hi[j])
+                    e4_hi[j] = c[q];
+            }
+        }
     }
     long o;
 #pragma omp parallel for schedule(static)
     for (o = 0; o < H; o++) {
-        double sum = 0.0, mag = 0.0;
+        double sum = 0.0, lo = 0.0, hi = 0.0, mag = 0.0;
         for (long j = 0; j < I; j++) {
             double wk = orc_weight(down, o, j);
+            double p = wk * e4_lo[j], q = wk * e4_hi[j];
             sum += wk * e4[j];
-            mag += fabs(wk * e4[j]);
+            lo += p < q ? p : q;
+            hi += p < q ? q : p;
+            mag += fabs(p) > fabs(q) ? fabs(p) : fabs(q);
         }
         d[o] = bf16(sum);
-        d_lo[o] = bf16(sum - down_err * mag);
-        d_hi[o] = bf16(sum + down_err * mag);
+        d_lo[o] = bf16(lo - down_err * mag);
+        d_hi[o] = bf16(hi + down_err * mag);
     }
     return open;
 }
@@ -528,17 +554,18 @@ static long v4_slot(const orc_matrix *gate, const orc_matrix *up, const orc_matr
 /*
  * The expert group with DeepSeek V4's activation.  Outputs: h [S*k + S][I]
  * (down's input per slot, in the slot order of the device scratch: t*k + r,
- * then S*k + t for the shared expert), y [S][H] f32 and the f32 sums y_lo,
- * y_hi of the rows' lower and upper candidates (f32 addition is monotone in
- * each operand, so a device whose only differences are within the error
- * bounds lands in [y_lo, y_hi]).  An id outside [0, n_experts) makes its
- * token's y NaN.  Returns the count of open decisions before down (the h
- * of a call with a nonzero count is not unique).
+ * then S*k + t for the shared expert) with its bounds h_lo, h_hi, y [S][H]
+ * f32 and the f32 sums y_lo, y_hi of the rows' lower and upper candidates
+ * (f32 addition is monotone in each operand, so a device whose only
+ * differences are within the error bounds lands in [y_lo, y_hi]).  An id
+ * outside [0, n_experts) makes its token's y NaN.  Returns the count of open
+ * decisions before down.  The bounds assume gate and up themselves exact
+ * (gu_err = 0, or no open decision there).
  */
 long orc_expert_group_v4(const orc_matrix *gates, const orc_matrix *ups, const orc_matrix *downs,
                          long n_experts, long S, long k, const int32_t *ids, const float *w, long shared,
                          const float *x, double limit, double gu_err, double act_rel, double down_err,
-                         double *h, float *y, float *y_lo, float *y_hi)
+                         double *h, double *h_lo, double *h_hi, float *y, float *y_lo, float *y_hi)
 {
     long H = downs[0].O, I = gates[0].O, nr = S * k, open = 0;
     long nrow = k + (shared >= 0 ? 1 : 0);
@@ -555,11 +582,12 @@ long orc_expert_group_v4(const orc_matrix *gates, const orc_matrix *ups, const o
             if (e < 0 || e >= n_experts) {
                 bad = 1;
                 for (long i = 0; i < I; i++)
-                    h[slot * I + i] = NAN;
+                    h[slot * I + i] = h_lo[slot * I + i] = h_hi[slot * I + i] = NAN;
                 continue;
             }
             open += v4_slot(&gates[e], &ups[e], &downs[e], x + t * gates[e].K, limit, wr, gu_err, act_rel,
-                            down_err, h + slot * I, rows + j * H, lo + j * H, hi + j * H);
+                            down_err, h + slot * I, h_lo + slot * I, h_hi + slot * I, rows + j * H, lo + j * H,
+                            hi + j * H);
         }
         if (bad) {
             for (long o = 0; o < H; o++)

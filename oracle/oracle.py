@@ -105,7 +105,7 @@ class OracleLib:
         lib.orc_v4_combine.argtypes = [_P, _P, _L, C.c_int, _L, _P]
         lib.orc_expert_group_v4.restype = C.c_long
         lib.orc_expert_group_v4.argtypes = [_P, _P, _P, _L, _L, _L, _P, _P, _L, _P, C.c_double, C.c_double,
-                                            C.c_double, C.c_double, _P, _P, _P, _P]
+                                            C.c_double, C.c_double, _P, _P, _P, _P, _P, _P]
         lib.orc_set_threads.argtypes = [C.c_int]
         lib.orc_get_threads.restype = C.c_int
         lib.orc_get_threads.argtypes = []
@@ -254,9 +254,10 @@ class OracleLib:
                         gu_err: float = 0.0, act_rel: float = 0.0, down_err: float = 0.0) -> dict:
         """The expert group with DeepSeek V4's rounding activation.
 
-        Returns h [S*k + S][I] (down's input per slot), y, y_lo, y_hi (f32
-        [S][H]) and ``open``: the number of bf16 decisions before down that
-        a device within the given error bounds could take the other way.
+        Returns h [S*k + S][I] (down's input per slot) with its bounds h_lo,
+        h_hi, then y, y_lo, y_hi (f32 [S][H]) and ``open``: the number of
+        bf16 decisions before down that a device within the given error
+        bounds could take the other way.
         """
         ids = np.ascontiguousarray(ids, dtype=np.int32)
         w = _f32(w)
@@ -276,15 +277,15 @@ class OracleLib:
         I = experts[used[0]].gate.O
         if I % 128:
             raise ValueError("DeepSeek V4's activation rounds blocks of 128: I must be a multiple of 128")
-        h = np.empty((S * k + S, I), dtype=np.float64)
+        h, h_lo, h_hi = (np.full((S * k + S, I), np.nan) for _ in range(3))
         y, y_lo, y_hi = (np.empty((S, H), dtype=np.float32) for _ in range(3))
         n_open = self.lib.orc_expert_group_v4(
             C.cast(gates, C.c_void_p), C.cast(ups, C.c_void_p), C.cast(downs, C.c_void_p), n, S, k,
             _ptr(cids), _ptr(w), cshared, _ptr(x), float(limit), float(gu_err), float(act_rel),
-            float(down_err), _ptr(h), _ptr(y), _ptr(y_lo), _ptr(y_hi))
+            float(down_err), _ptr(h), _ptr(h_lo), _ptr(h_hi), _ptr(y), _ptr(y_lo), _ptr(y_hi))
         if n_open < 0:
             raise MemoryError("oracle: out of memory")
-        return {"h": h, "y": y, "y_lo": y_lo, "y_hi": y_hi, "open": int(n_open)}
+        return {"h": h, "h_lo": h_lo, "h_hi": h_hi, "y": y, "y_lo": y_lo, "y_hi": y_hi, "open": int(n_open)}
 
 
 _default: Optional[OracleLib] = None

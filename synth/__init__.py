@@ -203,14 +203,14 @@ def activations(S: int, K: int, *key: int) -> np.ndarray:
     return rng_for(*key).standard_normal(size=(S, K)).astype(np.float32)
 
 
-def activations_e4m3_grid(S: int, K: int, *key: int) -> np.ndarray:
+def activations_e4m3_grid(S: int, K: int, *key: int, max_exp: int = 1) -> np.ndarray:
     """x[S][K] f32 on the E4M3 grid: a uniform sign, fraction 1.000b .. 1.111b
-    and exponent 2^-3 .. 2^1 (so |x| in [1/8, 3.75], multiples of 2^-6), and
-    one entry in ten zero: activations as an engine hands them over after
-    rounding them to E4M3 itself."""
+    and exponent 2^-3 .. 2^max_exp (so |x| in [1/8, 1.875 * 2^max_exp],
+    multiples of 2^-6), and one entry in ten zero: activations as an engine
+    hands them over after rounding them to E4M3 itself."""
     rng = rng_for(*key)
     mant = rng.integers(8, 16, size=(S, K))
-    expo = rng.integers(-3, 2, size=(S, K))
+    expo = rng.integers(-3, max_exp + 1, size=(S, K))
     sign = rng.choice([-1.0, 1.0], size=(S, K))
     x = sign * np.ldexp(mant.astype(np.float64), expo - 3)
     x[rng.random((S, K)) < 0.1] = 0.0

@@ -1006,4 +1006,22 @@ def pin_v4_h_rows_are_e4m3_blocks(lib):
             assert np.array_equal(_e4m3_torch(blk / s), blk / s) and m / s < 448.0
 
 
+
+def pin_v4_bounds(lib):
+    """The bounds for a device's error hold the exact-arithmetic result and collapse onto it
+    when the allowed errors are zero; a draw of this size has open decisions to bound."""
+    ex = _tiny_experts(3, fmt=7, gs=32, H=256, I=512)
+    x = synth.activations(2, 256, 7308) * np.float32(4.0)
+    ids = np.array([[0, 1], [2, 0]], np.int32)
+    w = np.array([[0.7, 0.3], [0.45, 0.55]], np.float32)
+    exact = lib.expert_group_v4(ex, ids, w, 2, x)
+    for key in ("h", "y"):
+        assert np.array_equal(exact[key + "_lo"], exact[key]) and np.array_equal(exact[key + "_hi"], exact[key])
+    r = lib.expert_group_v4(ex, ids, w, 2, x, math.inf, 0.0, 2.0 ** -12, 2.0 ** -14)
+    assert r["open"] > 0
+    assert np.array_equal(r["h"], exact["h"]) and np.array_equal(r["y"], exact["y"])
+    assert np.all(r["h_lo"] <= r["h"]) and np.all(r["h"] <= r["h_hi"]) and np.any(r["h_lo"] < r["h_hi"])
+    assert np.all(r["y_lo"] <= r["y"]) and np.all(r["y"] <= r["y_hi"]) and np.any(r["y_lo"] < r["y_hi"])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_") and callable(v)]

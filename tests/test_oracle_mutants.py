@@ -100,13 +100,14 @@ MUTANTS = {
     "v4_scale_allows_448": ("while (m / (s / 2.0) < 448.0)", "while (m / (s / 2.0) <= 448.0)"),
     "v4_scale_not_restored": ("e4[j] = orc_round_fmt(e4[j] / s, 3, -6) * s;", "e4[j] = orc_round_fmt(e4[j] / s, 3, -6);"),
     "v4_e4m3_as_e5m2": ("e4[j] = orc_round_fmt(e4[j] / s, 3, -6) * s;", "e4[j] = orc_round_fmt(e4[j] / s, 2, -14) * s;"),
-    "v4_block_max_half": ("        for (long j = b0; j < b0 + 128; j++)\n            if (fabs(e4[j]) > m",
-                          "        for (long j = b0; j < b0 + 64; j++)\n            if (fabs(e4[j]) > m"),
+    "v4_block_max_half": ("        for (long j = b0; j < b0 + 128; j++) {\n            if (fabs(e4[j]) > m",
+                          "        for (long j = b0; j < b0 + 64; j++) {\n            if (fabs(e4[j]) > m"),
     "v4_weight_dropped": ("double hv = orc_silu(gc) * uc * wr;", "double hv = orc_silu(gc) * uc;"),
     "v4_gate_not_rounded": ("double gb = bf16(g), ub = bf16(u);", "double gb = g, ub = bf16(u);"),
     "v4_clamp_before_rounding": ("double gc = gb > limit ? limit : gb;", "double gc = g > limit ? limit : bf16(g);"),
     "v4_down_not_rounded": ("        d[o] = bf16(sum);", "        d[o] = sum;"),
     "v4_combine_rank_order": ("if (!done[r] && (pick < 0 || ids[r] < ids[pick]))", "if (!done[r] && pick < 0)"),
+    "v4_bound_ignores_sign": ("            lo += p < q ? p : q;", "            lo += p;"),
     "token_x_not_advanced": ("mlp_one(&gates[e], &ups[e], &downs[e], x + t * gates[e].K,",
                              "mlp_one(&gates[e], &ups[e], &downs[e], x,"),
 }
