@@ -51,8 +51,13 @@ def launch_stats(launches):
 
 
 def gpu_clocks():
-    """The GPU's current clock levels as rocm-smi reports them (a child process), or None."""
+    """The GPU's current clock levels as rocm-smi reports them (a child process), or None.
+
+    None under a profiler that preloads itself into child processes: rocm-smi
+    starts through an interpreter hop, an exec the preloaded child may not do."""
     import subprocess
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+        return None
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=30)
         d = json.loads(r.stdout)
