@@ -97,11 +97,17 @@ TRAFFIC_PROFILE = "profiles/group_int4g32_s1_traffic.md"
 
 
 def kernel_sources_sha256() -> str:
+    """SHA-256 of the kernel sources' code: comments and whitespace removed,
+    so that only a change to the code itself voids a recorded profile."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f)) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)   # block comments
+        src = re.sub(r"//[^\n]*", " ", src)                  # line comments
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()
 
 

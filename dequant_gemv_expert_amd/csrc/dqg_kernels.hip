@@ -1221,7 +1221,9 @@ __global__ void __launch_bounds__(WAVE * down_max_waves<CAP>()) k_group_down(Gro
 // DeepSeek V4's pass between the activation and down: every block of 128
 // consecutive values of a slot's h becomes E4M3 values times the block's
 // power-of-two scale.  One wave per block; lane l holds values l and l + 64.
-// Multiplying by 2^-j and by 2^j is exact.
+// Multiplying by 2^-j and by 2^j is exact while E4M3's quantum 2^-9 times 2^j
+// stays on f32's grid (j >= -140: a block whose largest magnitude is at least
+// about 2^-131).
 __global__ void __launch_bounds__(256) k_group_act_v4(float *__restrict__ h, int nblk) {
     const int blk = blockIdx.x * 4 + wave_id();
     if (blk >= nblk) return;
