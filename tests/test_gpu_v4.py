@@ -187,3 +187,36 @@ def test_v4_group_full_size():
         f"{int(np.sum(hdev == r['h']))} equal to the nearest; y: {int(np.sum(r['y_lo'] == r['y_hi']))} of {y.size} "
         f"pinned")
     table.close()
+
+
+@pytest.mark.parametrize("act", ["swiglu", "v4"])
+def test_group_graph_capture_replays(act):
+    """A captured dqg_expert_group (two launches; three with DeepSeek V4's activation, none of them
+    a memset) replays with the eager call's bits, with new routings and activations copied in and
+    eager calls between the replays."""
+    E, H, I, S, k = 10, 512, 256, 2, 4
+    hs = [synth.expert(synth.FMT_MXFP4, H, I, 32, 9960, i) for i in range(E)]
+    table = dq.ExpertTable([dq.Expert.upload(h) for h in hs])
+    if act == "v4":
+        table.set_activation(dq.DQG_ACT_SWIGLU_V4)
+    draws = [synth.routing(S, E - 1, k, 9961, r) for r in range(3)]
+    xs = [synth.activations(S, H, 9962, r) for r in range(3)]
+    ids, w, x = dev_i32(draws[0][0]), dev_f32(draws[0][1]), dev_f32(xs[0])
+    y = torch.empty((S, H), dtype=torch.float32, device="cuda")
+    scratch = table.scratch(S, k)
+    dq.dqg_expert_group(table, ids, w, E - 1, x, y=y, scratch=scratch)   # warm the library
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        dq.dqg_expert_group(table, ids, w, E - 1, x, y=y, scratch=scratch)
+    for r in range(3):
+        ids.copy_(dev_i32(draws[r][0]))
+        w.copy_(dev_f32(draws[r][1]))
+        x.copy_(dev_f32(xs[r]))
+        want = host(dq.dqg_expert_group(table, ids, w, E - 1, x))   # eager, its own scratch
+        y.zero_()
+        g.replay()
+        dq.dqg_expert_group(table, ids, w, 0, x)                    # eager work between replays
+        torch.cuda.synchronize()
+        assert host(y).tobytes() == want.tobytes(), r
+    table.close()
