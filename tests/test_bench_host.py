@@ -1,0 +1,36 @@
+"""Host logic of bench.py (CPU): the kernel-source hash that keys the committed
+traffic profile changes with the code and not with its comments."""
+import importlib.util
+import os
+import shutil
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _bench():
+    spec = importlib.util.spec_from_file_location("bench_host", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    argv = sys.argv
+    try:
+        sys.argv = ["bench.py"]
+        spec.loader.exec_module(mod)
+    finally:
+        sys.argv = argv
+    return mod
+
+
+def test_source_hash_ignores_comments_only(tmp_path):
+    b = _bench()
+    for f in b.KERNEL_SOURCES:
+        os.makedirs(tmp_path / os.path.dirname(f), exist_ok=True)
+        shutil.copy(os.path.join(ROOT, f), tmp_path / f)
+    b.ROOT = str(tmp_path)
+    base = b.kernel_sources_sha256()
+    target = tmp_path / b.KERNEL_SOURCES[0]
+    src = target.read_text()
+    target.write_text("// a comment\n/* and a\n   block */\n" + src.replace("\n", "\n\n", 3))
+    assert b.kernel_sources_sha256() == base
+    target.write_text(src.replace("constexpr int RB = DQG_RB;", "constexpr int RB = DQG_RB + 0;", 1))
+    assert b.kernel_sources_sha256() != base
+
