@@ -125,6 +125,46 @@ def _dev(t: Optional[torch.Tensor], name: str, dtype=None):
     return t.data_ptr()
 
 
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
+
+
+def _need(cond: bool, msg: str) -> None:
+    if not cond:
+        raise ValueError(msg)
+
+
+def _same_device(name: str, t: Optional[torch.Tensor], dev: torch.device) -> None:
+    if t is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+_CODE_BYTES_X8 = {1: 8, 13: 8, 12: 8, 2: 4, 4: 4, 7: 4, 5: 2, 10: 32, 11: 16, 14: 16}   # code bytes per input, x8
+_NO_SCALES = (10, 11, 14)
+
+
+def storage_sizes(fmt: int, O: int, K: int, gs: int):
+    """(code bytes, high-plane bytes, scale count) of an [O x K] matrix in format
+    ``fmt`` (include/dqg.h's storage table); ValueError for shapes the format
+    cannot hold.  fmt 5's code bytes are its 2-bit plane."""
+    _need(fmt in _CODE_BYTES_X8, f"unknown format {fmt}")
+    _need(O >= 1 and K >= 1, f"O={O} and K={K} must be positive")
+    _need(K * _CODE_BYTES_X8[fmt] % 8 == 0, f"K={K} does not fill whole bytes in format {fmt}")
+    q = O * K * _CODE_BYTES_X8[fmt] // 8
+    if fmt == 5:
+        _need(K % 64 == 0, f"K={K} is not a multiple of 64 for format 5")
+        return q, O * K // 8, O * (K // 64)
+    if fmt in _NO_SCALES:
+        return q, 0, 0
+    if fmt in (1, 2):
+        return q, 0, O
+    if fmt == 12:
+        _need(K % 128 == 0, f"K={K} is not a multiple of 128 for format 12")
+        return q, 0, -(-O // 128) * (K // 128)
+    _need(gs >= 1 and K % gs == 0, f"K={K} is not a multiple of gs={gs}")
+    return q, 0, O * (K // gs)
+
+
 def _stream(stream) -> int:
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
@@ -141,6 +181,20 @@ class Matrix:
                  scales: Optional[torch.Tensor], q2: Optional[torch.Tensor] = None):
         self.fmt, self.O, self.K, self.gs = int(fmt), int(O), int(K), int(gs)
         self.q, self.q2, self.scales = q, q2, scales
+        # the kernels read O x K codes through raw pointers: every buffer must hold them
+        nq, nq2, ns = storage_sizes(self.fmt, self.O, self.K, self.gs)
+        _need(isinstance(q, torch.Tensor) and _nbytes(q) >= nq,
+              f"q holds {_nbytes(q) if isinstance(q, torch.Tensor) else 0} bytes, format {fmt} [{O} x {K}] needs {nq}")
+        if nq2:
+            _need(q2 is not None and _nbytes(q2) >= nq2,
+                  f"q2 holds {0 if q2 is None else _nbytes(q2)} bytes, format 5 [{O} x {K}] needs {nq2}")
+            _same_device("q2", q2, q.device)
+        if ns:
+            _need(scales is not None and scales.numel() >= ns,
+                  f"scales hold {0 if scales is None else scales.numel()} values, format {fmt} needs {ns}")
+            _same_device("scales", scales, q.device)
+        else:
+            _need(scales is None, f"format {fmt} has no scales (scales must be None)")
         self.struct = dqg_matrix(self.fmt, self.O, self.K, self.gs, _dev(q, "q"),
                                  _dev(q2, "q2"), _dev(scales, "scales", torch.float32))
 
@@ -163,8 +217,23 @@ class Matrix:
         return n
 
 
+def _tokens(x: torch.Tensor, K: int, name: str = "x") -> int:
+    """S of an activation tensor x [S][K] (S >= 1)."""
+    _need(isinstance(x, torch.Tensor) and x.dim() == 2 and x.shape[0] >= 1 and x.shape[1] == K,
+          f"{name} must be [S][{K}] with S >= 1, got {tuple(x.shape) if isinstance(x, torch.Tensor) else type(x)}")
+    return int(x.shape[0])
+
+
+def _out(t: Optional[torch.Tensor], n: int, name: str, dev: torch.device) -> None:
+    if t is not None:
+        _need(isinstance(t, torch.Tensor) and t.numel() >= n, f"{name} holds {t.numel()} values, {n} needed")
+        _same_device(name, t, dev)
+
+
 def dqg_matmul(W: Matrix, x: torch.Tensor, y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    S = x.shape[0]
+    S = _tokens(x, W.K)
+    _same_device("x", x, W.q.device)
+    _out(y, S * W.O, "y", x.device)
     if y is None:
         y = torch.empty((S, W.O), dtype=torch.float32, device=x.device)
     _check(load().dqg_matmul(C.byref(W.struct), _dev(x, "x", torch.float32), S,
@@ -172,9 +241,18 @@ def dqg_matmul(W: Matrix, x: torch.Tensor, y: Optional[torch.Tensor] = None, str
     return y
 
 
+def _gate_up_shapes(G: Matrix, U: Matrix, x: torch.Tensor, h: Optional[torch.Tensor]) -> int:
+    _need((G.O, G.K) == (U.O, U.K), f"gate [{G.O} x {G.K}] and up [{U.O} x {U.K}] differ")
+    S = _tokens(x, G.K)
+    _same_device("x", x, G.q.device)
+    _same_device("up", U.q, G.q.device)
+    _out(h, S * G.O, "h", x.device)
+    return S
+
+
 def dqg_gate_up(G: Matrix, U: Matrix, x: torch.Tensor, h: Optional[torch.Tensor] = None,
                 stream=None) -> torch.Tensor:
-    S = x.shape[0]
+    S = _gate_up_shapes(G, U, x, h)
     if h is None:
         h = torch.empty((S, G.O), dtype=torch.float32, device=x.device)
     _check(load().dqg_gate_up(C.byref(G.struct), C.byref(U.struct), _dev(x, "x", torch.float32), S,
@@ -184,7 +262,7 @@ def dqg_gate_up(G: Matrix, U: Matrix, x: torch.Tensor, h: Optional[torch.Tensor]
 
 def dqg_gate_up_clamped(G: Matrix, U: Matrix, x: torch.Tensor, limit: float, h: Optional[torch.Tensor] = None,
                         stream=None) -> torch.Tensor:
-    S = x.shape[0]
+    S = _gate_up_shapes(G, U, x, h)
     if h is None:
         h = torch.empty((S, G.O), dtype=torch.float32, device=x.device)
     _check(load().dqg_gate_up_clamped(C.byref(G.struct), C.byref(U.struct), _dev(x, "x", torch.float32), S,
@@ -193,6 +271,7 @@ def dqg_gate_up_clamped(G: Matrix, U: Matrix, x: torch.Tensor, limit: float, h: 
 
 
 def dqg_dequant(W: Matrix, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    _out(out, W.O * W.K, "out", W.q.device)
     if out is None:
         out = torch.empty((W.O, W.K), dtype=torch.float32, device=W.q.device)
     _check(load().dqg_dequant(C.byref(W.struct), _dev(out, "out", torch.float32), _stream(stream)))
@@ -253,7 +332,17 @@ class ExpertTable:
 
 
 def _group_args(table: ExpertTable, ids, w, shared, x, y, scratch):
-    S, k = ids.shape
+    _need(isinstance(ids, torch.Tensor) and ids.dim() == 2 and ids.shape[0] >= 1 and ids.shape[1] >= 1,
+          "ids must be [S][k] with S, k >= 1")
+    S, k = (int(v) for v in ids.shape)
+    _need(isinstance(w, torch.Tensor) and tuple(w.shape) == (S, k), f"w must be [{S}][{k}] like ids")
+    _need(_tokens(x, table.H) == S, f"x must hold S={S} tokens (one per row of ids)")
+    dev = x.device
+    for name, t in (("ids", ids), ("w", w)):
+        _same_device(name, t, dev)
+    _out(y, S * table.H, "y", dev)
+    if scratch is not None:
+        _same_device("scratch", scratch, dev)
     if y is None:
         y = torch.empty((S, table.H), dtype=torch.float32, device=x.device)
     if scratch is None:
@@ -291,7 +380,14 @@ def dqg_route(logits: torch.Tensor, k: int, mode: int = DQG_ROUTE_SOFTMAX, renor
               bias: Optional[torch.Tensor] = None, w_scale: float = 1.0,
               ids: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None, stream=None):
     """Router on the device: returns (ids int32 [S][k], w f32 [S][k])."""
-    S, E = logits.shape
+    _need(isinstance(logits, torch.Tensor) and logits.dim() == 2, "logits must be [S][E]")
+    S, E = (int(v) for v in logits.shape)
+    dev = logits.device
+    if bias is not None:
+        _need(bias.numel() == E, f"bias must hold E={E} values")
+        _same_device("bias", bias, dev)
+    _out(ids, S * int(k), "ids", dev)
+    _out(w, S * int(k), "w", dev)
     if ids is None:
         ids = torch.empty((S, k), dtype=torch.int32, device=logits.device)
     if w is None:

@@ -394,6 +394,50 @@ void orc_expert_group(const orc_matrix *gates, const orc_matrix *ups, const orc_
                              h_work, nh_work, dy_work, dabs_work);
 }
 
+/*
+ * The expert group's second half on hidden states given from outside
+ * (steps 4 and 5 of the group's definition: down, then the combine in rank
+ * order, then the shared expert with weight 1):
+ *   y[t]    = sum_{r<k} w[t][r] * (D_{ids[t][r]} . h[t*k + r])  + D_shared . h[S*k + t]
+ *   absn[t] = sum_{r<k} |w[t][r]| * A(D_{ids[t][r]}, h[t*k + r]) + A(D_shared, h[S*k + t])
+ * with A(D, v)[o] = sum_i |D[o][i] * v[i]|, the GEMV's own per-row
+ * normaliser.  h is f32 [S*k + S][I] in the slot order of the device's
+ * scratch (slot t*k + r for token t's rank r, slot S*k + t for its shared
+ * expert), so that a device's down and combine can be checked on the hidden
+ * states the device itself computed.  An id outside [0, n_experts) makes its
+ * token's row of y NaN.  shared < 0: no shared expert.
+ */
+void orc_expert_group_down(const orc_matrix *downs, long n_experts, long S, long k, const int32_t *ids,
+                           const float *w, long shared, const float *h, double *y, double *absn)
+{
+    long H = downs[0].O, I = downs[0].K, idx;
+#pragma omp parallel for schedule(static)
+    for (idx = 0; idx < S * H; idx++) {
+        long t = idx / H, o = idx % H;
+        double sum = 0.0, mag = 0.0;
+        int bad = 0;
+        for (long r = 0; r < k; r++) {
+            long e = ids[t * k + r];
+            if (e < 0 || e >= n_experts) {
+                bad = 1;
+                continue;
+            }
+            double d, a, wr = (double)w[t * k + r];
+            row_dot(&downs[e], o, h + (t * k + r) * I, NULL, &d, &a);
+            sum += wr * d;
+            mag += fabs(wr) * a;
+        }
+        if (shared >= 0) {
+            double ds, as;
+            row_dot(&downs[shared], o, h + (S * k + t) * I, NULL, &ds, &as);
+            sum += ds;
+            mag += as;
+        }
+        y[idx] = bad ? NAN : sum;
+        absn[idx] = mag;
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* DeepSeek V4's rounding activation.                                   */
 /* ------------------------------------------------------------------ */

@@ -88,6 +88,8 @@ class OracleLib:
         lib.orc_gate_up.argtypes = [C.POINTER(_Mat), C.POINTER(_Mat), _P, _L, _P, _P, _P, _P, _P, _P]
         lib.orc_expert_group.restype = None
         lib.orc_expert_group.argtypes = [_P, _P, _P, _L, _L, _L, _P, _P, _L, _P, _P, _P, _P, _P, _P, _P]
+        lib.orc_expert_group_down.restype = None
+        lib.orc_expert_group_down.argtypes = [_P, _L, _L, _L, _P, _P, _L, _P, _P, _P]
         lib.orc_gate_up_clamped.restype = None
         lib.orc_gate_up_clamped.argtypes = [C.POINTER(_Mat), C.POINTER(_Mat), _P, _L, C.c_double,
                                             _P, _P, _P, _P, _P, _P]
@@ -232,6 +234,32 @@ class OracleLib:
             self.lib.orc_expert_group_clamped(*args, float(limit), *work)
         return y, a
 
+    def expert_group_down(self, experts: Sequence, ids, w, shared: Optional[int], h) -> tuple:
+        """The group's down and combine on given hidden states h, f32
+        [S*k + S][I] in the device scratch's slot order (slot t*k + r, then
+        S*k + t for token t's shared expert).  Returns y [S][H] and its
+        normaliser sum_r |w| * sum_i |D[o][i] h[i]| (+ the shared row's)."""
+        ids = np.ascontiguousarray(ids, dtype=np.int32)
+        w = _f32(w)
+        S, k = ids.shape
+        h = _f32(h)
+        used = sorted({int(e) for e in ids.ravel() if 0 <= int(e) < len(experts)}
+                      | ({int(shared)} if shared is not None and shared >= 0 else set()))
+        if not used:
+            raise ValueError("no valid expert id")
+        I = experts[used[0]].down.K
+        H = experts[used[0]].down.O
+        if h.ndim != 2 or h.shape[1] != I or h.shape[0] < S * k + S:
+            raise ValueError(f"h must be [S*k + S][I] = [{S * k + S}][{I}], got {h.shape}")
+        remap = {e: i for i, e in enumerate(used)}
+        cids = np.array([[remap.get(int(e), -1) for e in row] for row in ids], dtype=np.int32)
+        cshared = remap[int(shared)] if shared is not None and shared >= 0 else -1
+        downs = (_Mat * len(used))(*[_mat(experts[e].down) for e in used])
+        y = np.empty((S, H), dtype=np.float64)
+        a = np.empty((S, H), dtype=np.float64)
+        self.lib.orc_expert_group_down(C.cast(downs, C.c_void_p), len(used), S, k, _ptr(cids), _ptr(w), cshared,
+                                       _ptr(h), _ptr(y), _ptr(a))
+        return y, a
 
     def round_fmt(self, v: float, mbits: int, emin: int) -> float:
         return self.lib.orc_round_fmt(float(v), int(mbits), int(emin))
@@ -339,6 +367,10 @@ def gate_up(G, U, x, limit=math.inf):
 
 def expert_group(experts, ids, w, shared, x, limit=math.inf):
     return load().expert_group(experts, ids, w, shared, x, limit)
+
+
+def expert_group_down(experts, ids, w, shared, h):
+    return load().expert_group_down(experts, ids, w, shared, h)
 
 
 def route(logits, k, mode=0, renorm=False, bias=None, w_scale=1.0):

@@ -622,6 +622,115 @@ def pin_group_normaliser(lib):
     assert np.all(a >= np.abs(y)) and np.all(a > 0)
 
 
+def pin_gate_up_error_reach(lib):
+    """nh is the first-order reach of errors eps * A_g in g and eps * A_u in u:
+    the largest change of silu(g) * u over the four sign corners, over eps
+    (a spare factor, a dropped term or a wrong silu slope moves it)."""
+    from scipy.special import expit
+    G = synth.matrix(4, 96, 256, 32, 7200, 0)
+    U = synth.matrix(4, 96, 256, 32, 7200, 1)
+    G.scales = (G.scales * 40).astype(np.float32)   # g over silu's curved range
+    x = synth.activations(3, 256, 7200, 2)
+    r = lib.gate_up(G, U, x)
+    g, u, ag, au, nh = r["g"], r["u"], r["ag"], r["au"], r["nh"]
+    assert np.ptp(g) > 4, "g should span silu's curved range"
+    eps = 1e-7
+
+    def swiglu(gv, uv):
+        return gv * expit(gv) * uv
+
+    h0 = swiglu(g, u)
+    reach = np.zeros_like(h0)
+    for sg in (-1.0, 1.0):
+        for su in (-1.0, 1.0):
+            reach = np.maximum(reach, np.abs(swiglu(g + sg * eps * ag, u + su * eps * au) - h0))
+    reach /= eps
+    assert np.allclose(reach, nh, rtol=1e-3, atol=1e-9 * float(nh.max())), float(np.max(np.abs(reach - nh) / nh))
+
+
+def pin_group_normaliser_decomposes(lib):
+    """The group's propagated normaliser is, per row, |w| times the down row's
+    own sum |D h| plus sum |D| nh (the reach of h's errors), summed over the
+    ranks, plus the shared expert's (weight 1)."""
+    exs = _tiny_experts(5)
+    x = synth.activations(1, 64, 44)
+    ids = np.array([[1, 3]], np.int32)
+    w = np.array([[0.75, -0.5]], np.float32)
+    _, a = lib.expert_group(exs, ids, w, 4, x)
+    want = np.zeros(64)
+    for e, wr in ((1, 0.75), (3, -0.5), (4, 1.0)):
+        r = lib.gate_up(exs[e].gate, exs[e].up, x)
+        _, ah = lib.gemv(exs[e].down, r["h"])    # sum_i |D[o][i] h[i]|, h in f64
+        _, an = lib.gemv(exs[e].down, r["nh"])   # sum_i |D[o][i]| nh[i], nh >= 0
+        want += abs(wr) * (ah[0] + an[0])
+    assert np.allclose(a[0], want, rtol=1e-12, atol=0)
+
+
+def pin_group_down_brute_force(lib):
+    """Down and combine on given hidden states: within f64 rounding of the exact
+    rational sum, slot t*k + r for (token t, rank r), the shared slot S*k + t
+    last with weight 1, signed weights, an expert twice in one token."""
+    exs = _tiny_experts(6)   # down [64 x 32], int4-g32
+    S, k, H, I = 2, 3, 64, 32
+    ids = np.array([[0, 3, 0], [2, 1, 4]], np.int32)
+    w = np.array([[0.5, -0.25, 0.125], [-1.0, 0.75, 0.3]], np.float32)
+    h = synth.activations(S * k + S, I, 41)
+    y, a = lib.expert_group_down(exs, ids, w, 5, h)
+    dec = {e: (numpy_values(exs[e].down), numpy_scales(exs[e].down)) for e in range(6)}
+
+    def row(e, o, slot):
+        v, sc = dec[e]
+        terms = [Fraction(v[o, i]) * Fraction(float(sc[o, i])) * Fraction(float(h[slot, i])) for i in range(I)]
+        return sum(terms), sum(abs(t) for t in terms)
+
+    for t in range(S):
+        for o in range(H):
+            exact, mag = Fraction(0), Fraction(0)
+            for r in range(k):
+                d, m = row(int(ids[t, r]), o, t * k + r)
+                exact += Fraction(float(w[t, r])) * d
+                mag += abs(Fraction(float(w[t, r]))) * m
+            d, m = row(5, o, S * k + t)
+            exact += d
+            mag += m
+            tol = mag * Fraction(4 * (I + k + 1), 2**53)
+            assert abs(Fraction(y[t, o]) - exact) <= tol, (t, o)
+            assert abs(Fraction(a[t, o]) - mag) <= tol, (t, o)
+
+
+def pin_group_down_edge_cases(lib):
+    """No shared expert and zero weights give 0 exactly; a bad id makes only its
+    token's row NaN."""
+    exs = _tiny_experts(4)
+    h = synth.activations(6, 32, 42)
+    ids = np.array([[0, 2], [1, 3]], np.int32)
+    y, a = lib.expert_group_down(exs, ids, np.zeros((2, 2), np.float32), None, h)
+    assert np.all(y == 0) and np.all(a == 0)
+    ids[0, 1] = 9
+    y, _ = lib.expert_group_down(exs, ids, np.full((2, 2), 0.5, np.float32), 3, h)
+    assert np.all(np.isnan(y[0])) and np.all(np.isfinite(y[1]))
+
+
+def pin_group_down_matches_group(lib):
+    """On the oracle's own hidden states, rounded to f32, the two-stage form is
+    the one-stage group within that rounding; the propagated normaliser is at
+    least the strict one."""
+    exs = _tiny_experts(9)
+    S, k, I = 2, 4, 32
+    ids, w = synth.routing(S, 8, k, 43)
+    x = synth.activations(S, 64, 43)
+    y, a = lib.expert_group(exs, ids, w, 8, x)
+    h = np.zeros((S * k + S, I), np.float32)
+    for t in range(S):
+        for r in range(k):
+            e = exs[int(ids[t, r])]
+            h[t * k + r] = lib.gate_up(e.gate, e.up, x[t:t + 1])["h"][0]
+        h[S * k + t] = lib.gate_up(exs[8].gate, exs[8].up, x[t:t + 1])["h"][0]
+    y2, a2 = lib.expert_group_down(exs, ids, w, 8, h)
+    assert np.all(np.abs(y2 - y) <= 2.0**-23 * a2 + 1e-300)
+    assert np.all(a >= a2 * (1 - 2.0**-20))
+
+
 # ---------------------------------------------------------------------------
 # clamped SwiGLU (swiglu_limit)
 # ---------------------------------------------------------------------------

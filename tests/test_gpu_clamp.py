@@ -14,7 +14,7 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import assert_close, dev_f32, dev_i32, host, log
+from gpu_helpers import assert_close, check_group, dev_f32, dev_i32, host, log
 
 pytestmark = pytest.mark.gpu
 
@@ -74,13 +74,9 @@ def test_group_with_table_limit(S):
     x = synth.activations(S, H, 9602, S)
     for limit in (0.3, 1.0):
         table.set_swiglu_limit(limit)
-        y = host(dq.dqg_expert_group(table, dev_i32(ids), dev_f32(w), E, dev_f32(x)))
-        yr, a = oracle.expert_group(hs, ids, w, E, x, limit)
-        assert_close(y, yr, a, f"group S={S} L={limit}")
+        check_group(hs, table, ids, w, E, x, f"group S={S} L={limit}", limit=limit)
     table.set_swiglu_limit(math.inf)
-    y = host(dq.dqg_expert_group(table, dev_i32(ids), dev_f32(w), E, dev_f32(x)))
-    yr, a = oracle.expert_group(hs, ids, w, E, x)
-    assert_close(y, yr, a, f"group S={S} back to the plain SwiGLU")
+    check_group(hs, table, ids, w, E, x, f"group S={S} back to the plain SwiGLU")
     with pytest.raises(dq.DqgError):
         table.set_swiglu_limit(0.0)
     table.close()

@@ -244,9 +244,7 @@ def test_full_size_fp8_group_256top8_shared():
     dev, hosts = upload_experts(c["fmt"], c["H"], c["I"], c["gs"], c["seed"], c["E"] + 1, keep=keep)
     table = dq.ExpertTable(dev)
     x = synth.activations(S, c["H"], c["seed"], 300)
-    y = host(dq.dqg_expert_group(table, dev_i32(ids), dev_f32(w), c["E"], dev_f32(x)))
-    yr, a = oracle.expert_group(HostExperts(c["E"] + 1, hosts), ids, w, c["E"], x)
-    log(f"  worst normalised error {assert_close(y, yr, a, 'fp8 group S=2'):.2e}")
+    check_group(HostExperts(c["E"] + 1, hosts), table, ids, w, c["E"], x, "fp8 group S=2")
     table.close()
     del dev, table
     gc.collect()

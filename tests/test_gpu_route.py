@@ -20,7 +20,7 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import assert_close, dev_f32, dev_i32, host, log
+from gpu_helpers import assert_close, dev_f32, dev_i32, host, log, scratch_h
 
 pytestmark = pytest.mark.gpu
 
@@ -148,10 +148,13 @@ def test_route_then_expert_group_on_device():
     lg = synth.router_logits(S, E, 8401)
     x = synth.activations(S, H, 8402)
     ids_d, w_d = dq.dqg_route(dev_f32(lg), k, dq.DQG_ROUTE_SOFTMAX, True)
-    y = host(dq.dqg_expert_group(table, ids_d, w_d, E, dev_f32(x)))
+    scratch = table.scratch(S, k)
+    y = host(dq.dqg_expert_group(table, ids_d, w_d, E, dev_f32(x), scratch=scratch))
     r = oracle.route(lg, k, 0, True)
     assert np.array_equal(host(ids_d), r["ids"])
     # the oracle's group on the device's f32 weights (the weights' own check is above)
+    yd, ad = oracle.expert_group_down(hs, r["ids"], host(w_d), E, scratch_h(scratch, S, k, I))
+    assert_close(y, yd, ad, "route then group: down and combine on the device's h")
     yr, a = oracle.expert_group(hs, r["ids"], host(w_d), E, x)
     assert_close(y, yr, a, "route then group")
     table.close()

@@ -108,6 +108,21 @@ MUTANTS = {
     "v4_down_not_rounded": ("        d[o] = bf16(sum);", "        d[o] = sum;"),
     "v4_combine_rank_order": ("if (!done[r] && (pick < 0 || ids[r] < ids[pick]))", "if (!done[r] && pick < 0)"),
     "v4_bound_ignores_sign": ("            lo += p < q ? p : q;", "            lo += p;"),
+    "group_down_weight_dropped": ("            sum += wr * d;\n            mag += fabs(wr) * a;",
+                                  "            sum += d;\n            mag += fabs(wr) * a;"),
+    "group_down_slot_by_rank": ("row_dot(&downs[e], o, h + (t * k + r) * I, NULL, &d, &a);",
+                                "row_dot(&downs[e], o, h + r * I, NULL, &d, &a);"),
+    "group_down_shared_slot_fixed": ("h + (S * k + t) * I", "h + (S * k) * I"),
+    "group_down_shared_dropped": ("            sum += ds;", "            sum += 0.0 * ds;"),
+    "group_down_norm_signed_weight": ("            mag += fabs(wr) * a;", "            mag += wr * a;"),
+    "group_down_bad_id_ignored": ("y[idx] = bad ? NAN : sum;", "y[idx] = sum;"),
+    "nh_spare_factor_k": ("nh[idx] = fabs(silu_slope(gc)) * ag * fabs(uc) + fabs(orc_silu(gc)) * au;",
+                          "nh[idx] = (fabs(silu_slope(gc)) * ag * fabs(uc) + fabs(orc_silu(gc)) * au) * G->K;"),
+    "nh_up_term_dropped": ("nh[idx] = fabs(silu_slope(gc)) * ag * fabs(uc) + fabs(orc_silu(gc)) * au;",
+                           "nh[idx] = fabs(silu_slope(gc)) * ag * fabs(uc);"),
+    "nh_slope_is_sigmoid": ("return sig * (1.0 + z * (1.0 - sig));", "return sig;"),
+    "group_norm_nh_dropped": ("mag += fabs(wk) * (fabs(h[k]) + nh[k]);", "mag += fabs(wk) * fabs(h[k]);"),
+    "group_norm_weight_dropped": ("at[o] += fabs(wr) * dabs_work[o];", "at[o] += dabs_work[o];"),
     "token_x_not_advanced": ("mlp_one(&gates[e], &ups[e], &downs[e], x + t * gates[e].K,",
                              "mlp_one(&gates[e], &ups[e], &downs[e], x,"),
 }
