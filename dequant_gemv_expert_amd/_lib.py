@@ -75,6 +75,7 @@ SIGNATURES = {
     "dqg_expert_group_issue": (C.c_int, [_P, _I32, _I32, _P, _P, _I32, _P, _P, _P, _SZ, _P,
                                          C.POINTER(dqg_ticket)]),
     "dqg_expert_group_take": (C.c_int, [C.POINTER(dqg_ticket)]),
+    "dqg_expert_group_noalloc": (C.c_int, [_P, _I32, _I32, _P, _P, _I32, _P, _P, _P]),
     "dqg_route": (C.c_int, [_P, _I32, _I32, _I32, _I32, _I32, _P, C.c_float, _P, _P, _P]),
     "dqg_prof_begin": (C.c_int, [_I32]),
     "dqg_prof_begin_sampled": (C.c_int, [_I32, _I32]),
@@ -359,6 +360,16 @@ def dqg_expert_group(table: ExpertTable, ids: torch.Tensor, w: torch.Tensor, sha
                      scratch: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
     args, y, _ = _group_args(table, ids, w, shared, x, y, scratch)
     _check(load().dqg_expert_group(*args, _stream(stream)))
+    return y
+
+
+def dqg_expert_group_noalloc(table: ExpertTable, ids: torch.Tensor, w: torch.Tensor, shared: Optional[int],
+                             x: torch.Tensor, y: torch.Tensor, stream=None) -> torch.Tensor:
+    """dqg_expert_group on the library's static per-device scratch: y must be given
+    (nothing is allocated on the path)."""
+    _need(y is not None, "y must be given: this call allocates nothing")
+    args, y, _ = _group_args(table, ids, w, shared, x, y, torch.empty(0, dtype=torch.uint8, device=x.device))
+    _check(load().dqg_expert_group_noalloc(*args[:8], _stream(stream)))
     return y
 
 

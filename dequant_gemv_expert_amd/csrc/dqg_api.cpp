@@ -215,9 +215,11 @@ size_t group_h_bytes(int32_t S, int32_t k, int32_t I) {
 }
 constexpr size_t FLAG_OFFSET = 0;
 
+// scratch == nullptr with use_static: the library's static per-device
+// scratch (dqg_expert_group_noalloc), resolved after every argument check.
 int group_common(const dqg_expert_table *t, int32_t S, int32_t k, const int32_t *ids,
                  const float *w, int32_t shared, const float *x, float *y, void *scratch,
-                 size_t scratch_bytes, void *stream, int32_t **flag_out) {
+                 size_t scratch_bytes, void *stream, int32_t **flag_out, bool use_static = false) {
     ++g_calls_group;
     prof_call();
     if (!t) return fail(DQG_EINVAL, "expert_group: table is NULL");
@@ -229,9 +231,18 @@ int group_common(const dqg_expert_table *t, int32_t S, int32_t k, const int32_t 
     if (!w || !aligned(w, 4)) return fail(DQG_EINVAL, "expert_group: w must be a 4-byte aligned device pointer");
     int rc;
     if ((rc = check_vec(x, "expert_group: x")) || (rc = check_vec(y, "expert_group: y")) ||
-        (rc = check_vec(scratch, "expert_group: scratch")))
+        (!use_static && (rc = check_vec(scratch, "expert_group: scratch"))))
         return rc;
     const size_t need = dqg_expert_group_scratch_bytes(t, S, k);
+    if (use_static) {
+        if (need > STATIC_SCRATCH_BYTES)
+            return fail(DQG_ENOMEM, "expert_group_noalloc: S=%d, k=%d, I=%d need %zu bytes of scratch, more than "
+                                    "the %zu the library holds", S, k, t->I, need, STATIC_SCRATCH_BYTES);
+        const hipError_t e = static_scratch(&scratch);
+        if (e != hipSuccess)
+            return fail(DQG_EDEVICE, "expert_group_noalloc: the scratch's device address: %s", hipGetErrorString(e));
+        scratch_bytes = STATIC_SCRATCH_BYTES;
+    }
     if (scratch_bytes < need)
         return fail(DQG_ENOMEM, "expert_group: scratch holds %zu bytes, %zu needed", scratch_bytes, need);
     if (inject_fault()) return fail(DQG_ELAUNCH, "expert_group: injected launch failure (DQG_FAULT)");
@@ -564,6 +575,12 @@ int dqg_expert_group(const dqg_expert_table *t, int32_t S, int32_t k, const int3
                      const float *w, int32_t shared, const float *x, float *y, void *scratch,
                      size_t scratch_bytes, void *stream) {
     return group_common(t, S, k, ids, w, shared, x, y, scratch, scratch_bytes, stream, nullptr);
+}
+
+int dqg_expert_group_noalloc(const dqg_expert_table *t, int32_t S, int32_t k, const int32_t *ids,
+                             const float *w, int32_t shared, const float *x, float *y, void *stream) {
+    static_assert(STATIC_SCRATCH_BYTES == DQG_NOALLOC_SCRATCH_BYTES, "dqg.h states the static scratch's size");
+    return group_common(t, S, k, ids, w, shared, x, y, nullptr, 0, stream, nullptr, true);
 }
 
 int dqg_expert_group_issue(const dqg_expert_table *t, int32_t S, int32_t k, const int32_t *ids,

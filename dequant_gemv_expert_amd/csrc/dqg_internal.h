@@ -77,6 +77,14 @@ struct RouteArgs {
 // otherwise it returns false and the launch carries no events.
 bool prof_slot(const char *kernel, hipEvent_t *start, hipEvent_t *stop);
 
+// Bytes of the per-device scratch that dqg_expert_group_noalloc uses (a
+// static device array in dqg_kernels.hip; DQG_NOALLOC_SCRATCH_BYTES in dqg.h).
+constexpr size_t STATIC_SCRATCH_BYTES = size_t(16) << 20;
+
+// The current device's copy of that array (its address taken once per
+// device with hipGetSymbolAddress, on the first call made there).
+hipError_t static_scratch(void **ptr);
+
 // Host launchers (dqg_kernels.hip).  Return hipSuccess or the launch error.
 hipError_t launch_matmul(int codec, const MatDev &m, const float *x, int S, float *y,
                          hipStream_t st);

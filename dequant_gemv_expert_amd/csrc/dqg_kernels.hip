@@ -1970,7 +1970,32 @@ hipError_t with_codec(int codec, F &&f) {
     return hipErrorInvalidValue;
 }
 
+// The library-held expert-group scratch of dqg_expert_group_noalloc, one
+// copy per device for the life of the process.  In host code `scratch` is
+// only a stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress, taken once per device with that device current.
+static __device__ __align__(256) uint8_t scratch[STATIC_SCRATCH_BYTES];
+
+struct StaticScratch {
+    std::once_flag once;
+    hipError_t err = hipSuccess;
+    void *ptr = nullptr;
+};
+StaticScratch g_static[64];
+
 }  // namespace
+
+hipError_t static_scratch(void **ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    StaticScratch &s = g_static[dev];
+    std::call_once(s.once, [&] { s.err = hipGetSymbolAddress(&s.ptr, HIP_SYMBOL(scratch)); });
+    if (s.err != hipSuccess) return s.err;
+    *ptr = s.ptr;
+    return hipSuccess;
+}
 
 hipError_t launch_matmul(int codec, const MatDev &m, const float *x, int S, float *y, hipStream_t st) {
     return with_codec(codec, [&](auto c) { return matmul_c<decltype(c)::value>(m, x, S, y, st); });

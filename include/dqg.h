@@ -271,6 +271,25 @@ int dqg_expert_group(const dqg_expert_table *table, int32_t S, int32_t k, const 
                      const float *w, int32_t shared, const float *x, float *y, void *scratch,
                      size_t scratch_bytes, void *stream);
 
+/*
+ * dqg_expert_group with no scratch argument and no allocation, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc).  The call uses a scratch
+ * that the library holds in a static device array of
+ * DQG_NOALLOC_SCRATCH_BYTES on each GPU it runs on (until the process ends);
+ * the first call on a device takes the array's address there.  It makes no
+ * hipMalloc, hipFree or other allocating call; the caller still passes ids,
+ * w, x and y.  Calls whose dqg_expert_group_scratch_bytes(table, S, k)
+ * exceeds DQG_NOALLOC_SCRATCH_BYTES give DQG_ENOMEM (at I = 2048: up to
+ * 2047 slots, S*k + S).  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (other streams, other threads) race, and h
+ * and the bad-id flag are not returned.  Runs on the current device, which
+ * must be the table's and the stream's.  Otherwise as dqg_expert_group.
+ */
+#define DQG_NOALLOC_SCRATCH_BYTES (16u << 20)
+int dqg_expert_group_noalloc(const dqg_expert_table *table, int32_t S, int32_t k, const int32_t *ids,
+                             const float *w, int32_t shared, const float *x, float *y, void *stream);
+
 /* As dqg_expert_group, then records an event in `ticket` (the async form,
  * coli_vk_expert_group_issue in the guide's API-contract section).  The
  * scratch must stay untouched until the ticket is taken. */

@@ -95,6 +95,8 @@ def test_vector_validation(lib):
 
 def test_expert_group_validation(lib):
     assert lib.dqg_expert_group(None, 1, 8, 0x1000, 0x2000, -1, FAKE_X, FAKE_Y, 0x50000, 1 << 20, None) == -1
+    assert lib.dqg_expert_group_noalloc(None, 1, 8, 0x1000, 0x2000, -1, FAKE_X, FAKE_Y, None) == -1
+    assert b"table is NULL" in lib.dqg_last_error()
     assert lib.dqg_expert_group_scratch_bytes(None, 1, 8) == 0
     t = L.dqg_ticket()
     assert lib.dqg_expert_group_take(C.byref(t)) == -1
