@@ -15,11 +15,13 @@ weights from the previous steps.
 
 Prints one JSON line: the metric is weight-stream GB/s (algorithmic bytes:
 codes + scales of each distinct expert the step needs, once, plus x and
-y) over wall time; `roofline` is the dominant kernel (the gate/up launch)
-timed with HIP events on its stream.  The steps run twice back to back:
-first with the wall clock only (value, ms_per_step), then with events on
-every launch (roofline; ms_per_step_with_events), because the events
-themselves add about 8 us a call to the wall clock;
+y) over wall time; `roofline` is the whole call (one launch at one token,
+two or three otherwise) timed with HIP events on its stream, its bytes
+over the summed kernel time, with a per-launch breakdown in `launches`.
+The steps run twice back to back: first with the wall clock only (value,
+ms_per_step), then with events on every launch (roofline;
+ms_per_step_with_events), because the events themselves add several us a
+call to the wall clock;
 `cpu_baseline` is the CPU oracle on a bounded sample of the same steps.
 """
 import argparse
@@ -280,28 +282,45 @@ def main():
     #    on the launch's stream (the events add about 8 us a call to the wall
     #    clock, which is why value comes from region 1) ---------------------
     clocks = gpu_clocks()
-    per_call = 3 if args.activation == "v4" else 2   # DeepSeek V4's pass is a launch of its own
-    dq.dqg_prof_begin(per_call * K)
+    dq.dqg_prof_begin(3 * K)   # at most three launches a call (DeepSeek V4's activation)
     t_wall_events = run_steps()
-    pstats = launch_stats(dq.dqg_prof_end_launches(per_call * K))
+    launches = dq.dqg_prof_end_launches(3 * K)
+    pstats = launch_stats(launches)
     prof = {name: v[:2] for name, v in pstats.items()}
+    per_call = len(launches) // K
+    if per_call * K != len(launches) or per_call not in (1, 2, 3):
+        raise RuntimeError(f"{len(launches)} launches timed for {K} calls")
+    # kernel time of each call: the sum of its launches' durations
+    call_us = [sum(ms for _, ms in launches[j * per_call:(j + 1) * per_call]) * 1e3 for j in range(K)]
 
     total_bytes = sum(step_bytes(i) for i in range(args.warmup, args.warmup + K))
     timed = range(args.warmup, args.warmup + K)   # region 2 times every call's launches
     ms_per_step = t_wall * 1e3 / K
     value = total_bytes / t_wall / 1e9
-    # the dominant kernel: the gate/up launch, its bytes summed over the timed calls
-    dom, dom_total = "group_gate_up", sum(step_bytes_gate_up(i) for i in timed)
-    n_dom, ms_dom = prof.get(dom, (0, 0.0))
-    if n_dom != len(timed):
-        raise RuntimeError(f"{n_dom} gate/up launches timed, {len(timed)} expected")
-    achieved = dom_total / (ms_dom * 1e-3) / 1e9 if ms_dom > 0 else None
-    n_b, ms_b = prof.get("group_down", (0, 0.0))
-    down_total = sum((union[i % P] + n_sh) * down_bytes + h_bytes + S * H * 4 for i in timed)
-    log(f"[bench] {K} steps: {ms_per_step * 1e3:.1f} us/step wall, {value:.0f} GB/s; "
-        f"{dom} kernel {ms_dom / max(n_dom, 1) * 1e3:.1f} us avg ({achieved or 0:.0f} GB/s)"
-        + (f", down kernel {ms_b / max(n_b, 1) * 1e3:.1f} us avg "
-           f"({down_total / (ms_b * 1e-3) / 1e9:.0f} GB/s)" if ms_b else "")
+    kernel_ms = sum(call_us) * 1e-3
+    achieved = total_bytes / (kernel_ms * 1e-3) / 1e9
+    kernels = [name for name, _ in launches[:per_call]]
+    group_kernel = "+".join(kernels)
+    # per-launch breakdown: the gate/up launch moves its weights, x and h; down its weights, h and y
+    breakdown = {}
+    for name in kernels:
+        n_k, ms_k = prof[name]
+        if name == "group_gate_up":
+            b = sum(step_bytes_gate_up(i) for i in timed)
+        elif name == "group_down":
+            b = sum((union[i % P] + n_sh) * down_bytes + h_bytes + S * H * 4 for i in timed)
+        elif name == "group_fused":
+            b = total_bytes
+        else:
+            b = None
+        breakdown[name] = {"avg_us": round(ms_k / n_k * 1e3, 2), "median_us": pstats[name][2],
+                           "p10_us": pstats[name][3], "p90_us": pstats[name][4],
+                           **({"bytes_per_launch": round(b / n_k), "achieved": round(b / (ms_k * 1e-3) / 1e9, 1)}
+                              if b else {})}
+    pc = np.asarray(call_us)
+    log(f"[bench] {K} steps: {ms_per_step * 1e3:.1f} us/step wall, {value:.0f} GB/s; kernel time "
+        f"{np.mean(pc):.1f} us a call ({achieved:.0f} GB/s, {achieved / HBM_PEAK_GBS:.3f} of peak) over "
+        + ", ".join(f"{k} {v['avg_us']} us" for k, v in breakdown.items())
         + f"; mean union {union.mean():.2f} experts + {n_sh} shared")
 
     # -- CPU oracle on a bounded sample -------------------------------------
@@ -385,23 +404,19 @@ def main():
                    "routing_pool": P, "shared_copies": n_shared, "device": dev_name,
                    **({} if args.swiglu_limit is None else {"swiglu_limit": args.swiglu_limit}),
                    **({} if args.activation == "swiglu" else {"activation": "deepseek_v4_rounding"})},
-        "roofline": {"kernel": dom, "bound": "hbm",
-                     "achieved": round(achieved, 1) if achieved else None, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4) if achieved else None,
-                     "traffic": profiled_traffic(dom) if (S == 1 and args.workload ==
+        "roofline": {"kernel": group_kernel, "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": profiled_traffic(group_kernel) if (S == 1 and args.workload ==
                                 "int4g32_expert_group_256top8_shared") else None,
-                     "avg_us": round(ms_dom / max(n_dom, 1) * 1e3, 2),
-                     "bytes_per_launch": round(dom_total / max(n_dom, 1)),
-                     "timed_launches": n_dom, "median_us": pstats[dom][2], "p10_us": pstats[dom][3],
-                     "p90_us": pstats[dom][4]},
-        "roofline_down": ({"kernel": "group_down", "avg_us": round(ms_b / max(n_b, 1) * 1e3, 2),
-                           "achieved": round(down_total / (ms_b * 1e-3) / 1e9, 1),
-                           "bytes_per_launch": round(down_total / max(n_b, 1)),
-                           "median_us": pstats["group_down"][2], "p10_us": pstats["group_down"][3],
-                           "p90_us": pstats["group_down"][4]} if ms_b else None),
-        **({"act_v4_pass": {"kernel": "group_act_v4", "launches": pstats["group_act_v4"][0],
-                            "avg_us": round(pstats["group_act_v4"][1] / pstats["group_act_v4"][0] * 1e3, 2),
-                            "median_us": pstats["group_act_v4"][2]}} if "group_act_v4" in pstats else {}),
+                     "scope": "the whole call: every launch of it, algorithmic bytes over summed kernel time",
+                     "avg_us": round(float(np.mean(pc)), 2), "median_us": round(float(np.median(pc)), 2),
+                     "p10_us": round(float(np.percentile(pc, 10)), 2), "p90_us": round(float(np.percentile(pc, 90)), 2),
+                     "bytes_per_call": round(total_bytes / K), "timed_calls": K, "launches_per_call": per_call},
+        "roofline_group": {"kernel_time_frac": round(achieved / HBM_PEAK_GBS, 4),
+                           "wall_frac": round(value / HBM_PEAK_GBS, 4),
+                           "kernel_us_per_call": round(float(np.mean(pc)), 2),
+                           "wall_us_per_call": round(ms_per_step * 1e3, 2)},
+        "launches": breakdown,
         "gpu_clocks": clocks,
         "cpu_baseline": cpu,
     }

@@ -189,12 +189,13 @@ def test_v4_group_full_size():
     table.close()
 
 
+@pytest.mark.parametrize("S", [1, 2])
 @pytest.mark.parametrize("act", ["swiglu", "v4"])
-def test_group_graph_capture_replays(act):
+def test_group_graph_capture_replays(act, S):
     """A captured dqg_expert_group (two launches; three with DeepSeek V4's activation, none of them
     a memset) replays with the eager call's bits, with new routings and activations copied in and
-    eager calls between the replays."""
-    E, H, I, S, k = 10, 512, 256, 2, 4
+    eager calls between the replays, at one token (the one-token gate/up kernel) and two."""
+    E, H, I, k = 10, 512, 256, 4
     hs = [synth.expert(synth.FMT_MXFP4, H, I, 32, 9960, i) for i in range(E)]
     table = dq.ExpertTable([dq.Expert.upload(h) for h in hs])
     if act == "v4":
