@@ -582,6 +582,35 @@ __device__ __forceinline__ void step_compute(const Step<C, NR, SM> &st, float (&
             acc[r][s] = fmaf(st.sc[r] * Cd::VMUL, fmaf(-Cd::OFFS, xs[s], p[r][s]), acc[r][s]);
 }
 
+// One row of step_compute for one token: the same operations in the same
+// order for that row (xs is step_compute's sum of x over the chunk, 0 for
+// offset-free codes), so that a caller can compute rows one by one as their
+// loads land.
+template <int C>
+__device__ __forceinline__ float row_dot(const typename Codec<C>::Chunk &ch, float sc,
+                                         const float (&xv)[Codec<C>::CW], float xs, float acc) {
+    using Cd = Codec<C>;
+    float p = 0.f;
+#pragma unroll
+    for (int u = 0; u < Cd::UNITS; ++u) {
+        if constexpr (Cd::WIDE) {
+            float v[Cd::UW];
+            Cd::decode_f(ch, u, v);
+#pragma unroll
+            for (int i = 0; i < Cd::UW; ++i) p = fmaf(v[i], xv[u * Cd::UW + i], p);
+        } else {
+            uint32_t pr[Cd::UW / 2];
+            Cd::decode(ch, u, pr);
+#pragma unroll
+            for (int q = 0; q < Cd::UW / 2; ++q) {
+                p = fma_lo(pr[q], xv[u * Cd::UW + Cd::IDX[2 * q]], p);
+                p = fma_hi(pr[q], xv[u * Cd::UW + Cd::IDX[2 * q + 1]], p);
+            }
+        }
+    }
+    return fmaf(sc * Cd::VMUL, fmaf(-Cd::OFFS, xs, p), acc);
+}
+
 #ifndef DQG_PIPE
 #define DQG_PIPE 0
 #endif
@@ -1160,6 +1189,9 @@ __device__ __forceinline__ void group_down_batch(const GroupArgs &a, const Exper
     }
 }
 
+template <int R>
+__device__ __forceinline__ void group_combine(const GroupArgs &a, float *d, int row0);
+
 // Kernel B: one block per R rows of H.  Waves share the units; each unit's
 // outputs go to LDS d[slot][R]; then y[t][row] = sum_r w[t][r] * d[t*k+r]
 // in rank order, plus the shared slot.  Sets the flag for a bad id.
@@ -1172,7 +1204,7 @@ template <int CAP>
 constexpr int down_max_waves() { return CAP == 1 ? DQG_BW1 : 8; }
 
 template <int C, int R, int CAP>
-__global__ void __launch_bounds__(WAVE * down_max_waves<CAP>()) k_group_down(GroupArgs a) {
+__device__ __forceinline__ void group_down(const GroupArgs &a) {
     extern __shared__ float d[];
     const int row0 = blockIdx.x * R;
     const int nr = a.S * a.k;
@@ -1194,6 +1226,16 @@ __global__ void __launch_bounds__(WAVE * down_max_waves<CAP>()) k_group_down(Gro
             else group_down_batch<C, R, 4>(a, ex, row0, b, d);
         });
     }
+    group_combine<R>(a, d, row0);
+}
+
+// The end of kernel B, after every slot's outputs for rows row0..row0+R-1
+// are in d[slot][R] (LDS): y[t][row] = sum_r w[t][r] * d[t*k+r] in rank
+// order, plus the shared slot; DeepSeek V4's weights were applied before
+// down and its slots are summed in (expert id, rank) order.  All threads.
+template <int R>
+__device__ __forceinline__ void group_combine(const GroupArgs &a, float *d, int row0) {
+    const int nr = a.S * a.k;
     // DeepSeek V4's combine order, after the slots' outputs in LDS: each
     // routed slot's place among its token's (expert id, rank) pairs
     const bool v4 = a.act == ACT_SWIGLU_V4;
@@ -1225,6 +1267,124 @@ __global__ void __launch_bounds__(WAVE * down_max_waves<CAP>()) k_group_down(Gro
         if (a.shared >= 0) acc += d[(nr + t) * R + r];
         a.y[(size_t)t * a.H + row0 + r] = acc;
     }
+}
+
+template <int C, int R, int CAP>
+__global__ void __launch_bounds__(WAVE * down_max_waves<CAP>()) k_group_down(GroupArgs a) { group_down<C, R, CAP>(a); }
+
+// Kernel B for one token with a shared expert and 6 to 8 routed ones (a
+// decode step): wave w computes the R rows of routed rank w, and the shared
+// expert's R rows are dealt over the waves (row j to wave j % W, at most
+// SPLIT_NX a wave), so that no wave streams a second unit after its first.
+// Each wave issues all its loads (its rank's codes, scales and h, then its
+// shared rows' codes and scales) before any arithmetic; the shared slot's h
+// is staged once per block in LDS, its loads issued ahead of the weights.
+// The per-row arithmetic is step_compute's (step_compute_lds reads the same
+// x in the same order), so the bits are those of k_group_down.  The
+// launcher checks: S == 1, shared >= 0, k == W in [6, 8], and I of 64
+// chunks (one a lane; I = 2048 for the 32-value chunks of int4 and MXFP4).
+constexpr int SPLIT_NX = 2;
+// Rows a wave keeps in flight (measured on MI355X for the int4-g32 group at
+// one token: depth 2, 3, 4, 6 -> 19.1, 18.6, 18.3, 18.0 us; every row's loads
+// issued at once 18.2 us).
+constexpr int SPLIT_DEPTH = 6;
+
+template <int C, int R>
+__global__ void __launch_bounds__(WAVE * 8) __attribute__((amdgpu_waves_per_eu(4))) k_group_down_split(GroupArgs a) {
+    using Cd = Codec<C>;
+    constexpr int NX = SPLIT_NX;
+    extern __shared__ float lds[];
+    lfloats_w xsh = (lfloats_w)lds;   // the shared slot's h (a.I floats, unpadded)
+    float *d = lds + a.I;          // the slots' outputs, d[slot][R]
+    const int W = blockDim.x / WAVE, w = wave_id(), lane = threadIdx.x & (WAVE - 1);
+    const int row0 = blockIdx.x * R;
+    const int nr = a.k;            // one token: slot q is rank q, the shared slot is nr
+    // the shared slot's h, at most two 16-byte loads a thread (clamped
+    // duplicates write the same value twice)
+    const uint32_t n4 = (uint32_t)a.I / 4, nt = blockDim.x;
+    const GLOBAL f32x4 *hsrc = (const GLOBAL f32x4 *)gf(a.h + (size_t)nr * a.I);
+    const uint32_t i0 = min((uint32_t)threadIdx.x, n4 - 1), i1 = min((uint32_t)threadIdx.x + nt, n4 - 1);
+    const f32x4 hv0 = hsrc[i0], hv1 = hsrc[i1];
+    const int e = __builtin_amdgcn_readfirstlane(a.ids[w]);
+    const bool ok = e >= 0 && e < a.n_experts;
+    const ExpertDev &ex = a.table[ok ? e : a.shared];   // a bad id reads the shared expert, then writes NaN
+    const ExpertDev &exs = a.table[a.shared];
+    // the wave's rows in order: R of its rank, then NX of the shared expert
+    constexpr int NT = R + NX, D = SPLIT_DEPTH;
+    GRow rows[NT];
+#pragma unroll
+    for (int r = 0; r < R; ++r) rows[r] = row_ptrs(ex.down, min(row0 + r, a.H - 1));
+#pragma unroll
+    for (int j = 0; j < NX; ++j) rows[R + j] = row_ptrs(exs.down, min(row0 + min(w + j * W, R - 1), a.H - 1));
+    const int shift = ex.down.shift;
+    const uint32_t c = opaque((uint32_t)lane);   // one chunk a lane
+    const uint32_t si = c >> shift;
+    float acc[NT];
+    typename Cd::Chunk ch[D];
+    float sc[D];
+    // h of the wave's rank first, then a ring of D rows in flight: row i's
+    // codes and scale are issued when row i - D has been computed
+    float xv[Cd::CW];
+    {
+        const gfloats hp = gf(a.h + (size_t)w * a.I);
+#pragma unroll
+        for (int i = 0; i < Cd::CW / 4; ++i) {
+            const float4 t = ldf4(hp, c * Cd::CW + 4 * i);
+            xv[4 * i] = t.x; xv[4 * i + 1] = t.y; xv[4 * i + 2] = t.z; xv[4 * i + 3] = t.w;
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+        ch[i] = Cd::load(rows[i], c);
+        sc[i] = Cd::SCALED ? ld_scale(rows[i].s, si) : 1.f;
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    *(LDS f32x4 *)(xsh + 4 * i0) = hv0;
+    *(LDS f32x4 *)(xsh + 4 * i1) = hv1;
+    float xs = 0.f;
+    if (Cd::OFFS != 0.f) {
+#pragma unroll
+        for (int i = 0; i < Cd::CW; ++i) xs += xv[i];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+        if (i == R) {
+            // the shared rows: x of the shared slot from the block's LDS copy
+            __syncthreads();   // xsh staged
+            xs = 0.f;
+#pragma unroll
+            for (int q = 0; q < Cd::CW / 4; ++q) {
+                const f32x4 t = *(const LDS f32x4 *)(xsh + c * Cd::CW + 4 * q);
+                xv[4 * q] = t.x; xv[4 * q + 1] = t.y; xv[4 * q + 2] = t.z; xv[4 * q + 3] = t.w;
+            }
+            if (Cd::OFFS != 0.f) {
+#pragma unroll
+                for (int q = 0; q < Cd::CW; ++q) xs += xv[q];
+            }
+        }
+        acc[i] = row_dot<C>(ch[i % D], sc[i % D], xv, xs, 0.f);
+        if (i + D < NT) {
+            ch[i % D] = Cd::load(rows[i + D], c);
+            sc[i % D] = Cd::SCALED ? ld_scale(rows[i + D].s, si) : 1.f;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    const bool v4 = a.act == ACT_SWIGLU_V4;
+    float out = 0.f;
+#pragma unroll
+    for (int r = 0; r < NT; ++r) {
+        const float t = wave_sum(acc[r]);
+        if (lane == r) out = t;
+    }
+    if (lane < R) d[w * R + lane] = ok ? (v4 ? round_bf16(out) : out) : __int_as_float(0x7FC00000);
+    if (lane >= R && lane < R + NX) {
+        const int xr = w + (lane - R) * W;
+        if (xr < R) d[nr * R + xr] = v4 ? round_bf16(out) : out;
+    }
+    if (!ok && lane == 0) *a.flag = 1;
+    group_combine<R>(a, d, row0);
 }
 
 // DeepSeek V4's pass between the activation and down: every block of 128
@@ -1928,11 +2088,19 @@ template <int C, int CAP>
 hipError_t group_b_cap(const GroupArgs &a, hipStream_t st) {
     const int units = a.S * a.k + (a.shared >= 0 ? 1 : 0);
     const int slots = a.S * a.k + (a.shared >= 0 ? a.S : 0);
+    const size_t v4_lds = a.act == ACT_SWIGLU_V4 ? 2 * (size_t)a.S * a.k * sizeof(int) : 0;
+    if constexpr (CAP == 1 && C != C_I3) {
+        if (a.S == 1 && a.shared >= 0 && a.k >= 6 && a.k <= 8 && a.I == WAVE * Codec<C>::CW) {
+            dim3 grid((a.H + RB - 1) / RB);
+            const size_t lds = ((size_t)a.I + (size_t)slots * RB) * sizeof(float) + v4_lds;
+            launch("group_down", (k_group_down_split<C, RB>), grid, dim3(WAVE * a.k), lds, st, a);
+            return hipGetLastError();
+        }
+    }
     const int waves = units < down_max_waves<CAP>() ? units : down_max_waves<CAP>();
     dim3 grid((a.H + RB - 1) / RB);
     // the slots' outputs; DeepSeek V4's combine adds the ids and their order
-    const size_t lds = (size_t)slots * RB * sizeof(float) +
-                       (a.act == ACT_SWIGLU_V4 ? 2 * (size_t)a.S * a.k * sizeof(int) : 0);
+    const size_t lds = (size_t)slots * RB * sizeof(float) + v4_lds;
     launch("group_down", (k_group_down<C, RB, CAP>), grid, dim3(WAVE * waves), lds, st, a);
     return hipGetLastError();
 }

@@ -216,6 +216,40 @@ def test_group_batch_invariant():
         assert bits_equal(yb[t], y1[0]), t
 
 
+# One token with k routed experts (6 to 8) and a shared one, I of 64 code
+# chunks: the down launch that deals the shared expert's rows over the
+# waves.  H is ragged against its 12-row blocks.
+SPLIT_CASES = [(8, 160, 4, 32, 2048), (7, 224, 7, 32, 2048), (6, 64, 4, 32, 2048), (8, 80, 1, None, 1024)]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES)
+def test_group_one_token_split_down(case):
+    k, H, fmt, gs, I = case
+    E = k + 2
+    seed = 4800 + SPLIT_CASES.index(case)
+    hs, table = _small_group(E, fmt=fmt, gs=gs, H=H, I=I, seed=seed)
+    ids, w = synth.routing(3, E - 1, k, seed)
+    ids[1, k - 1] = ids[1, 0]   # an expert twice in one token
+    x = synth.activations(3, H, seed)
+    for t in range(3):
+        check_group(hs, table, ids[t:t + 1], w[t:t + 1], E - 1, x[t:t + 1], f"split down {case} token {t}")
+    # batch invariance: three tokens (the general down launch) against one at a time
+    yb = host(dq.dqg_expert_group(table, dev_i32(ids), dev_f32(w), E - 1, dev_f32(x)))
+    for t in range(3):
+        y1 = host(dq.dqg_expert_group(table, dev_i32(ids[t:t + 1]), dev_f32(w[t:t + 1]), E - 1,
+                                      dev_f32(x[t:t + 1])))
+        assert bits_equal(yb[t], y1[0]), (case, t)
+    # a bad id: the token's outputs are NaN and the call reports it
+    bad = ids[:1].copy()
+    bad[0, k // 2] = E + 5
+    ticket, y, _ = dq.dqg_expert_group_issue(table, dev_i32(bad), dev_f32(w[:1]), E - 1, dev_f32(x[:1]))
+    with pytest.raises(dq.DqgError) as ei:
+        dq.dqg_expert_group_take(ticket)
+    assert ei.value.code == -7
+    assert np.all(np.isnan(host(y)))
+    table.close()
+
+
 def test_group_bad_id_is_reported():
     hs, table = _small_group(6)
     ids = np.array([[0, 1, 2], [1, 99, 4]], np.int32)
