@@ -881,6 +881,113 @@ __global__ void __launch_bounds__(256) k_rows_lds(MatDev m0, MatDev m1, const fl
     }
 }
 
+// The same products for 1-2 tokens and K of 1-4 whole 64-chunk steps (NS),
+// shaped to fill the chip at one token: blocks of 12 waves x 2 rows (6144
+// rows make 256 blocks, one a CU), x staged once per block, and every load
+// of a wave issued before its first arithmetic.  x's loads go out first and
+// wait in registers while the weights' loads are issued (step by step, rows
+// in order), so that copying x to LDS waits for x alone; then each row of
+// each step is computed as its codes land (one token: the step's x in
+// registers; two: step_compute_lds).  The per-row arithmetic and the order
+// of steps are k_rows_lds's, so the bits are the same.
+constexpr int GX_W = 12, GX_R = 2;
+
+template <int C, int SM, bool GU, int NS>
+__global__ void __launch_bounds__(WAVE * GX_W) k_rows_x(MatDev m0, MatDev m1, const float *__restrict__ x, int S,
+                                                       float *__restrict__ y, float L) {
+    extern __shared__ float xl_raw[];
+    lfloats_w xs = (lfloats_w)xl_raw;
+    using Cd = Codec<C>;
+    constexpr int R = GX_R, NR = GU ? 2 * R : R;
+    constexpr int K = NS * WAVE * Cd::CW;                     // m0.K (checked by the launcher)
+    constexpr uint32_t k4n = K / 4, n4 = SM * k4n, nt = WAVE * GX_W, XN = (n4 + nt - 1) / nt;
+    constexpr uint32_t xl = (uint32_t)x_lds_len<Cd::CW>(K);
+    const MatDev &m = m0;
+    const int lane = threadIdx.x & (WAVE - 1);
+    const int row0 = (blockIdx.x * GX_W + wave_id()) * R;
+    // x of every token (a second token past S repeats the first; its outputs are dropped)
+    f32x4 xv4[XN];
+#pragma unroll
+    for (uint32_t u = 0; u < XN; ++u) {
+        const uint32_t i = min((uint32_t)threadIdx.x + u * nt, n4 - 1), sl = i / k4n, k4 = i - sl * k4n;
+        xv4[u] = *(const GLOBAL f32x4 *)(gf(x) + (size_t)min((int)sl, S - 1) * K + 4 * k4);
+    }
+    GRow rows[NR];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        rows[r] = row_ptrs(m0, min(row0 + r, m.O - 1));
+        if (GU) rows[R + r] = row_ptrs(m1, min(row0 + r, m.O - 1));
+    }
+    Step<C, NR, SM> st[NS];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        step_load_w(st[j], rows, m.shift, opaque((uint32_t)(j * WAVE + lane)));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (uint32_t u = 0; u < XN; ++u) {
+        const uint32_t i = min((uint32_t)threadIdx.x + u * nt, n4 - 1), sl = i / k4n, k4 = i - sl * k4n;
+        *(LDS f32x4 *)(xs + sl * xl + x_lds_at<Cd::CW>(4 * k4)) = xv4[u];
+    }
+    __syncthreads();
+    // one token, codes with an offset: each chunk's sum of x, summed once per
+    // block in step_compute's order, after the row
+    constexpr bool XSUM = SM == 1 && Cd::OFFS != 0.f;
+    lfloats_w xsums = xs + xl;
+    if constexpr (XSUM) {
+        for (uint32_t t = threadIdx.x; t < (uint32_t)(K / Cd::CW); t += nt) {
+            float a = 0.f;
+#pragma unroll
+            for (int q = 0; q < Cd::CW / 4; ++q) {
+                const f32x4 v = *(const LDS f32x4 *)(xs + x_lds_at<Cd::CW>(t * Cd::CW) + 4 * q);
+                a += v.x;
+                a += v.y;
+                a += v.z;
+                a += v.w;
+            }
+            xsums[t] = a;
+        }
+        __syncthreads();
+    }
+    float acc[NR][SM];
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+        for (int s = 0; s < SM; ++s) acc[r][s] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+        const uint32_t cu = (uint32_t)(j * WAVE + lane);
+        if constexpr (SM == 1) {
+            float xv[Cd::CW];
+#pragma unroll
+            for (int q = 0; q < Cd::CW / 4; ++q) {
+                const f32x4 t = *(const LDS f32x4 *)(xs + x_lds_at<Cd::CW>(cu * Cd::CW) + 4 * q);
+                xv[4 * q] = t.x; xv[4 * q + 1] = t.y; xv[4 * q + 2] = t.z; xv[4 * q + 3] = t.w;
+            }
+            const float xsum = XSUM ? xsums[cu] : 0.f;
+#pragma unroll
+            for (int r = 0; r < NR; ++r) acc[r][0] = row_dot<C>(st[j].ch[r], st[j].sc[r], xv, xsum, acc[r][0]);
+            __builtin_amdgcn_sched_barrier(0);
+        } else {
+            step_compute_lds(st[j], (lfloats)xs, xl, cu, acc);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    float out = 0.f, outu = 0.f;
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int s = 0; s < SM; ++s) {
+            const float t = wave_sum(acc[r][s]);
+            const float tu = GU ? wave_sum(acc[R + r][s]) : 0.f;
+            if (lane == r * SM + s) { out = t; outu = tu; }
+        }
+    const int r = lane / SM, s = lane % SM;
+    if (lane < R * SM && row0 + r < m.O && s < S)
+        y[(size_t)s * m.O + row0 + r] = GU ? swiglu(out, outu, L) : out;
+}
+
 // ---------------------------------------------------------------------------
 // dqg_dequant: out[o][k] = value * scale with value = (pattern - OFFS) *
 // VMUL exactly, then one rounding.  One thread per chunk.
@@ -2025,10 +2132,49 @@ hipError_t go_gemm(const MatDev &m0, const MatDev &m1, const float *x, int S, fl
     return go_gemm_nc<C, GU, 4>(m0, m1, x, S, y, L, st, name);
 }
 
+// k_rows_x for 1-2 tokens and K of 1-4 whole 64-chunk steps (not int3,
+// whose 64-input chunks would spill).
+template <int C>
+bool rows_x_fits(int K, int S) {
+    const int unit = WAVE * Codec<C>::CW;
+    return C != C_I3 && S <= 2 && K % unit == 0 && K / unit <= 4;
+}
+
+template <int C, int SM, bool GU, int NS>
+hipError_t go_rows_x(const MatDev &g, const MatDev &u, const float *x, int S, float *y, float L, hipStream_t st,
+                     const char *name) {
+    dim3 grid((g.O + GX_W * GX_R - 1) / (GX_W * GX_R));
+    const size_t lds = ((size_t)SM * x_lds_len<Codec<C>::CW>(g.K) + (SM == 1 ? g.K / Codec<C>::CW : 0)) * 4;
+    launch(name, (k_rows_x<C, SM, GU, NS>), grid, dim3(WAVE * GX_W), lds, st, g, u, x, S, y, L);
+    return hipGetLastError();
+}
+
+template <int C, bool GU, int SM>
+hipError_t rows_x_sm(const MatDev &g, const MatDev &u, const float *x, int S, float *y, float L, hipStream_t st,
+                     const char *name) {
+    switch (g.K / (WAVE * Codec<C>::CW)) {
+    case 1: return go_rows_x<C, SM, GU, 1>(g, u, x, S, y, L, st, name);
+    case 2: return go_rows_x<C, SM, GU, 2>(g, u, x, S, y, L, st, name);
+    case 3: return go_rows_x<C, SM, GU, 3>(g, u, x, S, y, L, st, name);
+    default: return go_rows_x<C, SM, GU, 4>(g, u, x, S, y, L, st, name);
+    }
+}
+
+template <int C, bool GU>
+hipError_t rows_x(const MatDev &g, const MatDev &u, const float *x, int S, float *y, float L, hipStream_t st,
+                  const char *name) {
+    if constexpr (C != C_I3) {
+        if (S == 1) return rows_x_sm<C, GU, 1>(g, u, x, S, y, L, st, name);
+        return rows_x_sm<C, GU, 2>(g, u, x, S, y, L, st, name);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <int C>
 hipError_t matmul_c(const MatDev &m, const float *x, int S, float *y, hipStream_t st) {
     if constexpr (gemm_codec<C>())
         if (S >= gemm_min_s<C>() && m.K % 32 == 0) return go_gemm<C, false>(m, m, x, S, y, INFINITY, st);
+    if (rows_x_fits<C>(m.K, S)) return rows_x<C, false>(m, m, x, S, y, INFINITY, st, "matmul");
     // int3's 64-input chunks: 8 tokens at a time would spill, 4 fit with x in LDS
     if constexpr (C != C_I3)
         if (S >= 8) return go_matmul<C, DQG_MM_R8, 8>(m, x, S, y, st);
@@ -2052,6 +2198,7 @@ template <int C>
 hipError_t gate_up_c(const MatDev &g, const MatDev &u, const float *x, int S, float *h, float L, hipStream_t st) {
     if constexpr (gemm_codec<C>())
         if (S >= gemm_min_s_gu<C>() && g.K % 32 == 0) return go_gemm<C, true>(g, u, x, S, h, L, st);
+    if (rows_x_fits<C>(g.K, S)) return rows_x<C, true>(g, u, x, S, h, L, st, "gate_up");
     // int3's 64-input chunks: 8 tokens at a time would spill, 4 fit with x in LDS
     if constexpr (C != C_I3)
         if (S >= 8) return go_gate_up<C, 2, 8>(g, u, x, S, h, L, st);
