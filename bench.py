@@ -93,6 +93,25 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def host_cpu() -> dict:
+    """The host's CPU model (/proc/cpuinfo), its logical CPU count (nproc)
+    and the CPUs this process may run on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = None
+    return {"cpu_model": model, "nproc": os.cpu_count(), "cpus_usable": usable}
+
+
 KERNEL_SOURCES = ["dequant_gemv_expert_amd/csrc/dqg_kernels.hip", "dequant_gemv_expert_amd/csrc/dqg_api.cpp",
                   "dequant_gemv_expert_amd/csrc/dqg_internal.h"]
 TRAFFIC_PROFILE = "profiles/group_int4g32_s1_traffic.md"
@@ -157,6 +176,9 @@ def main():
     ap.add_argument("--activation", choices=("swiglu", "v4"), default="swiglu",
                     help="the experts' activation: the (clamped) SwiGLU, or DeepSeek V4's rounding form "
                          "(expert-group workloads)")
+    ap.add_argument("--stream-ceiling", action="store_true",
+                    help="only measure the plain streaming read (dqg_read_bytes): one pass over a 4.25 GiB "
+                         "buffer, and reads the size of this library's launches")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (torch) 5 times, the reference "
                          "kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
@@ -185,11 +207,15 @@ def main():
     import dequant_gemv_expert_amd as dq
     from dequant_gemv_expert_amd import _lib as L
 
+    if args.stream_ceiling:
+        return bench_stream(args)
     c = synth.WORKLOADS[args.workload]
     if c["kind"] == "gemv":
         return bench_gemv(args, c)
+    if c["kind"] == "expert":
+        return bench_expert(args, c)
     if c["kind"] != "group":
-        raise SystemExit("bench.py times the expert-group and dense GEMV workloads")
+        raise SystemExit("bench.py times the expert-group, single-expert and dense GEMV workloads")
     S = args.tokens or c["S"][0]
     E, k, H, I, fmt, gs, seed = c["E"], c["k"], c["H"], c["I"], c["fmt"], c["gs"], c["seed"]
     n_shared = args.shared_copies if c["shared"] else 0
@@ -365,7 +391,7 @@ def main():
         cpu = {"value": round(cbytes / spent / 1e9, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
                "sample": f"{calls} expert-group calls ({S} token(s), top-{k} of {E}"
                          f"{' + shared' if n_sh else ''}) from the same routing pool, {spent:.1f} s",
-               "us_per_call": round(spent / calls * 1e6, 1)}
+               "us_per_call": round(spent / calls * 1e6, 1), **host_cpu()}
 
         def draw(j):   # the call's experts, drawn before the clock starts
             i = args.warmup + (j % calls)
@@ -560,7 +586,7 @@ def bench_gemv(args, c):
         cpu = {"value": rate(per_call),
                "unit": "GB/s" if not gemm else "TFLOP/s", "cores": oracle.get_threads(), "kind": "oracle",
                "sample": f"{calls} oracle {'gate_up calls' if gu else 'GEMVs'} of the first {rows} of {O} rows "
-                         f"at S = {S}, {spent:.1f} s, scaled to the whole matrix"}
+                         f"at S = {S}, {spent:.1f} s, scaled to the whole matrix", **host_cpu()}
 
         def one_call(j):   # the same sample on one host thread
             if gu:
@@ -589,6 +615,169 @@ def bench_gemv(args, c):
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def bench_stream(args):
+    """The plain streaming read (dqg_read_bytes) on one MI355X.
+
+    One pass over a 4.25 GiB buffer per launch (the long-stream ceiling),
+    then reads of the byte counts of this library's launches (the dense
+    int4-g32 6144 x 6144 matrix, and the int4-g32 group's down launch,
+    gate/up launch and whole call at one token), each launch at its own
+    offset so that the Infinity Cache cannot serve it.  HIP events on every
+    launch give its duration.
+    """
+    import numpy as np
+    import torch
+    import dequant_gemv_expert_amd as dq
+
+    torch.cuda.set_device(0)
+    dev_name = torch.cuda.get_device_name(0)
+    total = 4352 << 20
+    buf = torch.empty(total, dtype=torch.uint8, device="cuda").fill_(1)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    sizes = {"whole_buffer": total, "gemv_int4g32_6144x6144": 23642112, "group_int4g32_down": 70778880,
+             "group_int4g32_gate_up": 141557760, "group_int4g32_call": 212336640}
+    results = {}
+    for name, n in sizes.items():
+        n = n // 1024 * 1024
+        launches = 10 if n == total else args.steps
+        offsets = [0] if n == total else [(i * n) % (total - n) // 4096 * 4096 for i in range(launches + args.warmup)]
+        for i in range(args.warmup if n != total else 2):
+            dq.dqg_read_bytes(buf, sink, n, offsets[i % len(offsets)])
+        torch.cuda.synchronize()
+        dq.dqg_prof_begin(launches)
+        for i in range(launches):
+            dq.dqg_read_bytes(buf, sink, n, offsets[(i + args.warmup) % len(offsets)] if n != total else 0)
+        torch.cuda.synchronize()
+        ms = [m for _, m in dq.dqg_prof_end_launches(launches)]
+        avg = float(np.mean(ms)) * 1e-3
+        results[name] = {"bytes": n, "launches": len(ms), "avg_us": round(avg * 1e6, 2),
+                         "median_us": round(float(np.median(ms)) * 1e3, 2), "GB/s": round(n / avg / 1e9, 1),
+                         "frac": round(n / avg / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"[bench] read {n / 1e6:.1f} MB: {avg * 1e6:.2f} us a launch, {n / avg / 1e9:.0f} GB/s")
+    whole = results["whole_buffer"]
+    out = {"metric": "plain streaming read GB/s (the weight streams' ceiling)", "value": whole["GB/s"],
+           "unit": "GB/s", "n_gpus": 1, "steps": whole["launches"], "warmup": 2, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
+           "config": {"workload": "stream_read", "bytes": total, "device": dev_name},
+           "roofline": {"kernel": "read", "bound": "hbm", "achieved": whole["GB/s"], "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": whole["frac"], "traffic": None, "avg_us": whole["avg_us"]},
+           "by_size": results, "gpu_clocks": gpu_clocks(), "cpu_baseline": None}
+    print(json.dumps(out), flush=True)
+
+
+def bench_expert(args, c):
+    """One expert MLP at one token: dqg_expert_group with a single routed
+    expert of weight 1 and no shared expert, so y = down(SwiGLU(gate x, up x)).
+
+    Distinct device copies of the expert (about 2 GB in all) rotate so that
+    the Infinity Cache cannot serve a step's weights.  Reported in us per
+    call and as weight-stream GB/s over the summed kernel time of the call's
+    two launches.
+    """
+    import numpy as np
+    import torch
+    import synth
+    import dequant_gemv_expert_amd as dq
+    from dequant_gemv_expert_amd import _lib as L
+
+    S, k = 1, 1
+    fmt, H, I, gs, seed = c["fmt"], c["H"], c["I"], c["gs"], c["seed"]
+    torch.cuda.set_device(0)
+    dev_name = torch.cuda.get_device_name(0)
+    he = synth.expert(fmt, H, I, gs, seed, 0)
+    exp_bytes = matrix_bytes(he.gate) + matrix_bytes(he.up) + matrix_bytes(he.down)
+    copies = max(2, min(256, (2 << 30) // exp_bytes))
+    de = dq.Expert.upload(he)
+    table = dq.ExpertTable([de] + [dq.Expert.upload(he) for _ in range(copies - 1)])
+    x = synth.activations(S, H, seed, 9)
+    x_d = torch.from_numpy(x).cuda()
+    y_d = torch.empty((S, H), dtype=torch.float32, device="cuda")
+    ids = torch.arange(copies, dtype=torch.int32, device="cuda").reshape(copies, 1, 1)
+    w = torch.ones((1, 1), dtype=torch.float32, device="cuda")
+    scratch = table.scratch(S, k)
+    lib = L.load()
+    stream = torch.cuda.current_stream().cuda_stream
+    plan = [(table.handle, S, k, ids[i].data_ptr(), w.data_ptr(), -1, x_d.data_ptr(), y_d.data_ptr(),
+             scratch.data_ptr(), scratch.numel(), stream) for i in range(copies)]
+    log(f"[bench] {dev_name}: {copies} copies of {args.workload} ({exp_bytes / 1e6:.2f} MB each)")
+
+    def call(i):
+        rc = lib.dqg_expert_group(*plan[i % copies])
+        if rc:
+            raise RuntimeError(dq.dqg_last_error())
+
+    for i in range(args.warmup):
+        call(i)
+    K = args.steps
+
+    def run_steps():
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        for i in range(K):
+            call(args.warmup + i)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t
+
+    t_wall = run_steps()
+    clocks = gpu_clocks()
+    dq.dqg_prof_begin(2 * K)
+    t_wall_events = run_steps()
+    launches = dq.dqg_prof_end_launches(2 * K)
+    per_call = len(launches) // K
+    if per_call * K != len(launches):
+        raise RuntimeError(f"{len(launches)} launches timed for {K} calls")
+    call_us = np.asarray([sum(ms for _, ms in launches[j * per_call:(j + 1) * per_call]) * 1e3 for j in range(K)])
+    pstats = launch_stats(launches)
+    step_bytes = exp_bytes + S * H * 4 * 2 + 2 * S * I * 4   # weights, x and y, h written and read
+    kernel_s = float(np.mean(call_us)) * 1e-6
+    achieved = step_bytes / kernel_s / 1e9
+    value = step_bytes * K / t_wall / 1e9
+    breakdown = {name: {"avg_us": round(v[1] / v[0] * 1e3, 2), "median_us": v[2], "p10_us": v[3], "p90_us": v[4]}
+                 for name, v in pstats.items()}
+    log(f"[bench] {K} steps: {t_wall / K * 1e6:.1f} us/step wall; kernel time {kernel_s * 1e6:.1f} us a call "
+        f"({achieved:.0f} GB/s, {achieved / HBM_PEAK_GBS:.3f} of peak) over "
+        + ", ".join(f"{n} {v['avg_us']} us" for n, v in breakdown.items()))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        spent, calls = 0.0, 0
+        while spent < args.cpu_seconds and calls < 100000:
+            t = time.perf_counter()
+            oracle.expert_group([he], np.zeros((1, 1), np.int32), np.ones((1, 1), np.float32), None, x)
+            spent += time.perf_counter() - t
+            calls += 1
+        cpu = {"value": round(step_bytes * calls / spent / 1e9, 3), "unit": "GB/s", "cores": oracle.get_threads(),
+               "kind": "oracle", "sample": f"{calls} oracle expert MLP calls (1 token), {spent:.1f} s",
+               "us_per_call": round(spent / calls * 1e6, 1), **host_cpu()}
+
+        def one_call(j):
+            oracle.expert_group([he], np.zeros((1, 1), np.int32), np.ones((1, 1), np.float32), None, x)
+
+        c1, s1 = oracle_one_core(one_call, max(1.0, args.cpu_seconds / 3))
+        cpu["value_1core"] = round(step_bytes * c1 / s1 / 1e9, 3)
+        log(f"[bench] cpu oracle: {cpu['value']} GB/s on {cpu['cores']} threads, {cpu['value_1core']} on 1")
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(t_wall / K * 1e3, 5), "us_per_call": round(t_wall / K * 1e6, 2),
+        "ms_per_step_with_events": round(t_wall_events / K * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": S, "H": H, "I": I, "format": f"fmt {fmt}, gs {gs}",
+                   "copies": copies, "device": dev_name},
+        "roofline": {"kernel": "+".join(n for n, _ in launches[:per_call]), "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "scope": "the whole call: both launches, algorithmic bytes over summed kernel time",
+                     "avg_us": round(kernel_s * 1e6, 2), "median_us": round(float(np.median(call_us)), 2),
+                     "bytes_per_call": step_bytes, "timed_calls": K, "launches_per_call": per_call},
+        "launches": breakdown, "gpu_clocks": clocks, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    table.close()
 
 
 if __name__ == "__main__":

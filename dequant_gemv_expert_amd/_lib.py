@@ -66,6 +66,7 @@ SIGNATURES = {
     "dqg_gate_up": (C.c_int, [C.POINTER(dqg_matrix), C.POINTER(dqg_matrix), _P, _I32, _P, _P]),
     "dqg_gate_up_clamped": (C.c_int, [C.POINTER(dqg_matrix), C.POINTER(dqg_matrix), _P, _I32, C.c_float, _P, _P]),
     "dqg_dequant": (C.c_int, [C.POINTER(dqg_matrix), _P, _P]),
+    "dqg_read_bytes": (C.c_int, [_P, C.c_uint64, _P, _P]),
     "dqg_expert_table_create": (C.c_int, [C.POINTER(dqg_expert), _I32, C.POINTER(C.c_void_p)]),
     "dqg_expert_table_destroy": (None, [_P]),
     "dqg_expert_table_set_swiglu_limit": (C.c_int, [_P, C.c_float]),
@@ -277,6 +278,18 @@ def dqg_dequant(W: Matrix, out: Optional[torch.Tensor] = None, stream=None) -> t
         out = torch.empty((W.O, W.K), dtype=torch.float32, device=W.q.device)
     _check(load().dqg_dequant(C.byref(W.struct), _dev(out, "out", torch.float32), _stream(stream)))
     return out
+
+
+def dqg_read_bytes(buf: torch.Tensor, sink: torch.Tensor, nbytes: Optional[int] = None, offset: int = 0,
+                   stream=None) -> None:
+    """A plain streaming read of nbytes of buf from byte `offset` (the
+    measurement ceiling; see dqg.h).  sink: a GPU int32 tensor of one word."""
+    n = _nbytes(buf) - offset if nbytes is None else nbytes
+    if offset < 0 or n <= 0 or offset + n > _nbytes(buf):
+        raise ValueError(f"read_bytes: [{offset}, {offset + n}) outside the buffer's {_nbytes(buf)} bytes")
+    _dev(buf, "buf")
+    _check(load().dqg_read_bytes(C.c_void_p(buf.data_ptr() + offset), n, _dev(sink, "sink", torch.int32),
+                                 _stream(stream)))
 
 
 class Expert:

@@ -477,6 +477,23 @@ int dqg_dequant(const dqg_matrix *W, float *out, void *stream) {
     return DQG_OK;
 }
 
+int dqg_read_bytes(const void *p, uint64_t nbytes, uint32_t *sink, void *stream) {
+    prof_call();
+    if (!p || !aligned(p, 16)) return fail(DQG_EINVAL, "read_bytes: p must be a 16-byte aligned device pointer");
+    if (nbytes == 0 || nbytes % 1024)
+        return fail(DQG_EINVAL, "read_bytes: nbytes=%llu must be a positive multiple of 1024",
+                    (unsigned long long)nbytes);
+    if (!sink || !aligned(sink, 4)) return fail(DQG_EINVAL, "read_bytes: sink must be a 4-byte aligned device pointer");
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+        return fail(DQG_EDEVICE, "read_bytes: no device");
+    int rc;
+    if ((rc = launched(launch_read(p, nbytes, sink, cus, static_cast<hipStream_t>(stream)), "read_bytes"))) return rc;
+    ++g_launches;
+    return DQG_OK;
+}
+
 int dqg_route(const float *logits, int32_t S, int32_t E, int32_t k, int32_t mode, int32_t renorm,
               const float *bias, float w_scale, int32_t *ids, float *w, void *stream) {
     ++g_calls_route;

@@ -91,6 +91,7 @@ hipError_t launch_matmul(int codec, const MatDev &m, const float *x, int S, floa
 hipError_t launch_gate_up(int codec, const MatDev &g, const MatDev &u, const float *x, int S,
                           float *h, float limit, hipStream_t st);   // limit: swiglu_limit, +inf for none
 hipError_t launch_dequant(int codec, const MatDev &m, float *out, hipStream_t st);
+hipError_t launch_read(const void *p, uint64_t nbytes, uint32_t *sink, int cus, hipStream_t st);
 hipError_t launch_route(const RouteArgs &a, hipStream_t st);
 hipError_t launch_group(int codec_gu, int codec_down, const GroupArgs &a, hipStream_t st,
                         int *launches);

@@ -1970,6 +1970,32 @@ __global__ void __launch_bounds__(WAVE * ROUTE_WAVES) k_route(RouteArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// dqg_read_bytes: a plain streaming read, the ceiling the weight streams are
+// measured against.  Wave w reads 1 KB pieces w, w + W, w + 2W, ... with 16-B
+// non-temporal loads, two pieces in flight; blocks of 4 waves, 8 a CU (32 KB
+// a CU in flight measured best on MI355X).  The XOR of the bytes goes to
+// *sink only if it equals a value no input of a constant fill gives, so
+// nothing is written in practice and no load can be dropped.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(8)))
+k_read(const u32x4 *__restrict__ p, uint64_t npieces, uint32_t *sink) {
+    const uint32_t lane = threadIdx.x & (WAVE - 1);
+    const uint64_t nw = (uint64_t)gridDim.x * (blockDim.x / WAVE);
+    uint64_t k = (uint64_t)blockIdx.x * (blockDim.x / WAVE) + wave_id();
+    uint32_t acc = 0;
+    for (; k + nw < npieces; k += 2 * nw) {
+        const u32x4 a = __builtin_nontemporal_load((const GLOBAL u32x4 *)(p + k * WAVE + lane));
+        const u32x4 b = __builtin_nontemporal_load((const GLOBAL u32x4 *)(p + (k + nw) * WAVE + lane));
+        acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w;
+    }
+    if (k < npieces) {
+        const u32x4 a = __builtin_nontemporal_load((const GLOBAL u32x4 *)(p + k * WAVE + lane));
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    if (acc == 0x9E3779B9u) *sink = acc;
+}
+
+// ---------------------------------------------------------------------------
 // Host launchers
 // ---------------------------------------------------------------------------
 constexpr int WPB = 4;   // waves per block for the row kernels
@@ -2329,6 +2355,11 @@ hipError_t launch_route(const RouteArgs &a, hipStream_t st) {
     else if (a.E <= 512) launch("route", k_route<8>, grid, block, 0, st, a);
     else if (a.E <= ROUTE_MAX_E) launch("route", k_route<16>, grid, block, 0, st, a);
     else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_read(const void *p, uint64_t nbytes, uint32_t *sink, int cus, hipStream_t st) {
+    launch("read", k_read, dim3(8 * cus), dim3(256), 0, st, (const u32x4 *)p, nbytes / 1024, sink);
     return hipGetLastError();
 }
 

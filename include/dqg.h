@@ -366,7 +366,18 @@ typedef struct {
 } dqg_prof_launch;
 int dqg_prof_end_launches(dqg_prof_launch *out, int32_t max, int32_t *n);
 
-/* Text of the calling thread's last error (never NULL). */
+/*
+ * A plain streaming read of nbytes (a positive multiple of 1024) at the
+ * 16-byte aligned device pointer p, asynchronous on `stream`: the ceiling
+ * that the weight streams are measured against (the bench's streaming-read
+ * mode).  Nothing is computed from the bytes but their XOR, which is stored
+ * to the 4-byte aligned device word *sink only in the unlikely case that it
+ * equals one fixed value.  DQG_EINVAL on a bad argument, DQG_EDEVICE
+ * without a device, DQG_ELAUNCH if the launch fails.
+ */
+int dqg_read_bytes(const void *p, uint64_t nbytes, uint32_t *sink, void *stream);
+
+/* Text of the calling thread's last error (never NULL). *//* Text of the calling thread's last error (never NULL). */
 const char *dqg_last_error(void);
 
 /* Snapshot and reset of the process-wide counters. */

@@ -93,6 +93,16 @@ def test_vector_validation(lib):
     assert lib.dqg_gate_up(C.byref(g), C.byref(u), FAKE_X, 1, FAKE_Y, None) == -3
 
 
+def test_read_bytes_validation(lib):
+    """Argument checks of the streaming-read entry, which launch nothing."""
+    assert lib.dqg_read_bytes(None, 1024, FAKE_Y, None) == -1
+    assert lib.dqg_read_bytes(FAKE_X + 8, 1024, FAKE_Y, None) == -1      # p not 16-byte aligned
+    assert lib.dqg_read_bytes(FAKE_X, 0, FAKE_Y, None) == -1
+    assert lib.dqg_read_bytes(FAKE_X, 1000, FAKE_Y, None) == -1          # not a multiple of 1024
+    assert lib.dqg_read_bytes(FAKE_X, 1024, None, None) == -1
+    assert b"sink" in lib.dqg_last_error()
+
+
 def test_expert_group_validation(lib):
     assert lib.dqg_expert_group(None, 1, 8, 0x1000, 0x2000, -1, FAKE_X, FAKE_Y, 0x50000, 1 << 20, None) == -1
     assert lib.dqg_expert_group_noalloc(None, 1, 8, 0x1000, 0x2000, -1, FAKE_X, FAKE_Y, None) == -1
