@@ -53,8 +53,8 @@ def is_stale(lib: str = LIB) -> bool:
 
 if __name__ == "__main__":
     # python -m dequant_gemv_expert_amd.build [--out PATH] [-DNAME=VALUE ...]:
-    # the library, or a copy built with compile-time settings overridden
-    # (tile shapes, route cut-overs) for a measurement
+    # the library, or a copy at another path (with extra preprocessor
+    # definitions) that DQG_LIBRARY=PATH loads instead
     args = sys.argv[1:]
     out = LIB
     if args[:1] == ["--out"]:

@@ -37,28 +37,13 @@ namespace {
 
 constexpr int WAVE = 64;
 
-// Tile shapes of the grouped launches (compile-time; the defaults are the
-// measured best on MI355X for the int4-g32 group at 1-4 tokens).
-#ifndef DQG_RA
-#define DQG_RA 4
-#endif
-#ifndef DQG_WPB_A
-#define DQG_WPB_A 4
-#endif
-#ifndef DQG_RB
-// 12 rows: 6144 rows make 512 blocks, one round at two 8-wave blocks per CU
-// (8 rows took 1.5 rounds, 6 rows two)
-#define DQG_RB 12
-#endif
-#ifndef DQG_CAP_A
-#define DQG_CAP_A 2   // largest token batch of the gate/up launch (x rows staged in LDS)
-#endif
-#ifndef DQG_CAP_B
-#define DQG_CAP_B 1   // largest slot batch of the down launch
-#endif
-constexpr int RA = DQG_RA;        // rows of gate (and of up) per wave in kernel A
-constexpr int WPB_A = DQG_WPB_A;  // waves per block in kernel A
-constexpr int RB = DQG_RB;        // rows of down per block in kernel B
+// Tile shapes of the grouped launches (the measured best on MI355X for the
+// int4-g32 group at 1-4 tokens).  Kernel B's 12 rows: 6144 rows make 512
+// blocks, one round at two 8-wave blocks per CU (8 rows took 1.5 rounds, 6
+// rows two).
+constexpr int RA = 4;      // rows of gate (and of up) per wave in kernel A
+constexpr int WPB_A = 4;   // waves per block in kernel A
+constexpr int RB = 12;     // rows of down per block in kernel B
 
 // Global-memory loads: base pointers are wave-uniform, offsets 32-bit, so
 // the address is one SGPR pair plus one VGPR (no per-row 64-bit math).
@@ -70,16 +55,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-#ifndef DQG_NT
-#define DQG_NT 1
-#endif
 // Weight codes are read once per call, so their loads are non-temporal:
 // they do not displace x, h and the descriptors in the caches (measured on
 // MI355X: the int4-g32 group's gate/up launch 29.3 -> 28.2 us at 1 token;
 // a plain read of the same bytes 24.0 -> 22.3 us).
 __device__ __forceinline__ uint4 ld16(gbytes base, uint32_t off) {
     const GLOBAL u32x4 *p = (const GLOBAL u32x4 *)(base + off);
-    const u32x4 v = DQG_NT ? __builtin_nontemporal_load(p) : *p;
+    const u32x4 v = __builtin_nontemporal_load(p);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ uint2 ld8(gbytes base, uint32_t off) {
@@ -96,12 +78,8 @@ __device__ __forceinline__ float ldf(gfloats base, uint32_t idx) {
 }
 // A weight scale: read once per call, like the codes (measured on MI355X:
 // the int4-g32 group's gate/up launch 28.5 -> 28.0 us at 1 token).
-#ifndef DQG_NT_SCALES
-#define DQG_NT_SCALES 1
-#endif
 __device__ __forceinline__ float ld_scale(gfloats base, uint32_t idx) {
-    const GLOBAL float *p = (const GLOBAL float *)((gbytes)base + (idx << 2));
-    return DQG_NT_SCALES ? __builtin_nontemporal_load(p) : *p;
+    return __builtin_nontemporal_load((const GLOBAL float *)((gbytes)base + (idx << 2)));
 }
 
 // Where a step reads x from: global memory (L2) or the block's LDS copy.
@@ -495,8 +473,7 @@ __device__ __forceinline__ float wave_max(float v) {
 // then x) before any arithmetic, held ahead by a scheduling barrier, so a
 // wave has all its requests in flight before it waits.  The chunk index
 // is hidden from loop strength reduction so that each load is one SGPR
-// base plus a 32-bit lane offset.  With DQG_PIPE the next chunk's loads
-// are issued before the current chunk is computed.
+// base plus a 32-bit lane offset.
 // ---------------------------------------------------------------------------
 template <int C, int NR, int SM>
 struct Step {
@@ -611,11 +588,7 @@ __device__ __forceinline__ float row_dot(const typename Codec<C>::Chunk &ch, flo
     return fmaf(sc * Cd::VMUL, fmaf(-Cd::OFFS, xs, p), acc);
 }
 
-#ifndef DQG_PIPE
-#define DQG_PIPE 0
-#endif
-
-template <int C, int NR, int SM, bool PIPE = DQG_PIPE, typename XP = XGlobal>
+template <int C, int NR, int SM, typename XP = XGlobal>
 __device__ __forceinline__ void dot_rows(const GRow (&rows)[NR], int nch, int shift,
                                          const XP (&xp)[SM], float (&acc)[NR][SM]) {
     const int lane = threadIdx.x & (WAVE - 1);
@@ -623,25 +596,11 @@ __device__ __forceinline__ void dot_rows(const GRow (&rows)[NR], int nch, int sh
     for (int r = 0; r < NR; ++r)
 #pragma unroll
         for (int s = 0; s < SM; ++s) acc[r][s] = 0.f;
-    if (!PIPE) {
-        for (int c = lane; c < nch; c += WAVE) {
-            Step<C, NR, SM> st;
-            step_load(st, rows, shift, xp, opaque((uint32_t)c));
-            __builtin_amdgcn_sched_barrier(0);
-            step_compute(st, acc);
-        }
-        return;
-    }
-    int c = lane;
-    Step<C, NR, SM> cur, nxt;
-    if (c < nch) step_load(cur, rows, shift, xp, opaque((uint32_t)c));
-    while (c < nch) {
-        const int cn = c + WAVE;
-        if (cn < nch) step_load(nxt, rows, shift, xp, opaque((uint32_t)cn));
+    for (int c = lane; c < nch; c += WAVE) {
+        Step<C, NR, SM> st;
+        step_load(st, rows, shift, xp, opaque((uint32_t)c));
         __builtin_amdgcn_sched_barrier(0);
-        step_compute(cur, acc);
-        cur = nxt;
-        c = cn;
+        step_compute(st, acc);
     }
 }
 
@@ -752,13 +711,10 @@ __device__ __forceinline__ void step_compute_lds_pairs(const Step<C, NR, 1> &st,
     }
 }
 
-#ifndef DQG_GU1_PAIRS
-#define DQG_GU1_PAIRS 1
-#endif
 // Whether the one-token group path takes its rows in pairs (and so stages
-// the chunk sums of x): codes with an offset, rows in pairs.
+// the chunk sums of x): an even row count.
 template <int C, int NR>
-constexpr bool gu1_pairs() { return DQG_GU1_PAIRS && NR % 2 == 0; }
+constexpr bool gu1_pairs() { return NR % 2 == 0; }
 
 // dot_rows for one token with x in LDS, when the caller has already issued
 // the codes and scales of this lane's first chunk into st (have: this lane
@@ -768,9 +724,6 @@ constexpr bool gu1_pairs() { return DQG_GU1_PAIRS && NR % 2 == 0; }
 // have arrived finishes the step and requests its next one ahead of waves
 // still waiting (measured on MI355X: the int4-g32 group's gate/up launch
 // 28.1-28.2 -> 27.4-27.5 us at 1 token).
-#ifndef DQG_GU1_PRIO
-#define DQG_GU1_PRIO 1
-#endif
 template <int C, int NR>
 __device__ __forceinline__ void dot_rows_lds1(Step<C, NR, 1> &st, bool have, const GRow (&rows)[NR], int nch,
                                               int shift, lfloats x, lfloats xsum, float (&acc)[NR][1]) {
@@ -781,12 +734,12 @@ __device__ __forceinline__ void dot_rows_lds1(Step<C, NR, 1> &st, bool have, con
         const uint32_t cu = opaque((uint32_t)c);
         if (!(have && c == lane)) step_load_w(st, rows, shift, cu);
         __builtin_amdgcn_sched_barrier(0);
-        if (DQG_GU1_PRIO) __builtin_amdgcn_s_setprio(1);
+        __builtin_amdgcn_s_setprio(1);
         if constexpr (gu1_pairs<C, NR>())
             step_compute_lds_pairs<C, NR, GROUP_XPAD>(st, x, Codec<C>::OFFS != 0.f ? xsum[cu] : 0.f, cu, acc);
         else
             step_compute_lds<C, NR, 1, GROUP_XPAD>(st, x, 0u, cu, acc);
-        if (DQG_GU1_PRIO) __builtin_amdgcn_s_setprio(0);
+        __builtin_amdgcn_s_setprio(0);
     }
 }
 
@@ -1199,7 +1152,7 @@ __device__ __forceinline__ void group_gu_batch(const GroupArgs &a, const ExpertD
     } else {
         stage_x<SM, Codec<C>::CW>(a, b, xs);
         row_set(rows);
-        dot_rows<C, 2 * R, SM, DQG_PIPE, XLdsT<GROUP_XPAD>>(rows, nch, ex.gate.shift, xp, acc);
+        dot_rows<C, 2 * R, SM, XLdsT<GROUP_XPAD>>(rows, nch, ex.gate.shift, xp, acc);
     }
     float gv = 0.f, uv = 0.f;
 #pragma unroll
@@ -1258,11 +1211,8 @@ __global__ void __launch_bounds__(WAVE * WPB_A) k_group_gate_up(GroupArgs a) { g
 
 // The one-token form with a register budget of 5 waves per SIMD, so that a
 // 9-unit group (1152 blocks of 4 waves) is resident in one round on 256 CUs.
-#ifndef DQG_GU1_WAVES
-#define DQG_GU1_WAVES 5
-#endif
 template <int C, int R>
-__global__ void __launch_bounds__(WAVE * WPB_A) __attribute__((amdgpu_waves_per_eu(DQG_GU1_WAVES)))
+__global__ void __launch_bounds__(WAVE * WPB_A) __attribute__((amdgpu_waves_per_eu(5)))
 k_group_gate_up1(GroupArgs a) { group_gate_up<C, R, 1>(a); }
 
 // down rows row0.. of expert e applied to a batch of slots' h -> d (LDS)
@@ -1277,7 +1227,7 @@ __device__ __forceinline__ void group_down_batch(const GroupArgs &a, const Exper
 #pragma unroll
     for (int s = 0; s < SM; ++s) xp[s] = {gf(a.h + (size_t)b.slot[s] * a.I)};
     float acc[R][SM];
-    dot_rows<C, R, SM, false>(rows, ex.down.K / Codec<C>::CW, ex.down.shift, xp, acc);
+    dot_rows<C, R, SM>(rows, ex.down.K / Codec<C>::CW, ex.down.shift, xp, acc);
     float out = 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -1304,11 +1254,7 @@ __device__ __forceinline__ void group_combine(const GroupArgs &a, float *d, int 
 // in rank order, plus the shared slot.  Sets the flag for a bad id.
 // Block size: one wave per unit, at most 8 waves (2 per SIMD, so that two
 // blocks share a CU; blocks of 9 or more waves were measured to hold one).
-#ifndef DQG_BW1
-#define DQG_BW1 8
-#endif
-template <int CAP>
-constexpr int down_max_waves() { return CAP == 1 ? DQG_BW1 : 8; }
+constexpr int DOWN_MAX_WAVES = 8;
 
 template <int C, int R, int CAP>
 __device__ __forceinline__ void group_down(const GroupArgs &a) {
@@ -1377,7 +1323,7 @@ __device__ __forceinline__ void group_combine(const GroupArgs &a, float *d, int 
 }
 
 template <int C, int R, int CAP>
-__global__ void __launch_bounds__(WAVE * down_max_waves<CAP>()) k_group_down(GroupArgs a) { group_down<C, R, CAP>(a); }
+__global__ void __launch_bounds__(WAVE * DOWN_MAX_WAVES) k_group_down(GroupArgs a) { group_down<C, R, CAP>(a); }
 
 // Kernel B for one token with a shared expert and 6 to 8 routed ones (a
 // decode step): wave w computes the R rows of routed rank w, and the shared
@@ -2010,18 +1956,7 @@ void launch(const char *name, K kernel, dim3 grid, dim3 block, size_t lds, hipSt
         hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
 }
 
-#ifndef DQG_MM_R1
-#define DQG_MM_R1 4
-#endif
-#ifndef DQG_MM_R4
-#define DQG_MM_R4 4
-#endif
-#ifndef DQG_MM_R8
-#define DQG_MM_R8 4
-#endif
-#ifndef DQG_MM_R2
-#define DQG_MM_R2 4
-#endif
+constexpr int MM_R = 4;   // rows per wave of the general per-row kernel
 // Inputs of x per K-chunk: the largest multiple of 64 code chunks that keeps
 // SM tokens within 64 KB of LDS, or the whole of K.  (Every format's batch
 // size keeps at least 64 code chunks within it: int3's 64-input chunks take
@@ -2054,21 +1989,9 @@ hipError_t go_matmul(const MatDev &m, const float *x, int S, float *y, hipStream
 // matrices) at 8 tokens: int4 53 us per row against 48 GEMM, E4M3 49
 // against 41, f16 58 against 51, int8 57 against 61.
 template <int C>
-constexpr int gemm_min_s() {
-#ifdef DQG_GEMM_MIN_S
-    return DQG_GEMM_MIN_S;
-#else
-    return 9;
-#endif
-}
+constexpr int gemm_min_s() { return 9; }
 template <int C>
-constexpr int gemm_min_s_gu() {
-#ifdef DQG_GEMM_MIN_S_GU
-    return DQG_GEMM_MIN_S_GU;
-#else
-    return C == C_I8 ? 9 : 8;
-#endif
-}
+constexpr int gemm_min_s_gu() { return C == C_I8 ? 9 : 8; }
 
 template <int C>
 constexpr bool gemm_codec() { return C == C_I8 || C == C_I4 || C == C_FP4 || C == C_FP8 || C == C_F16; }
@@ -2080,9 +2003,7 @@ template <int C>
 constexpr int gemm_min_nc() { return (int)(sizeof(typename GemmCodec<C>::Raw) / 4); }
 
 // A grid of fewer blocks than this takes one block per K chunk (split-K).
-#ifndef DQG_GEMM_SPLIT_BELOW
-#define DQG_GEMM_SPLIT_BELOW 1024
-#endif
+constexpr size_t GEMM_SPLIT_BELOW = 1024;
 
 // The split-K partials live in one buffer per device that the library keeps
 // and grows on demand, up to WS_MAX bytes (larger needs take the unsplit
@@ -2112,7 +2033,7 @@ hipError_t go_gemm_nc(const MatDev &m0, const MatDev &m1, const float *x, int S,
         launch(name, (k_gemm<C, GU, NC>), grid, dim3(256), 0, st, m0, m1, x, S, y, L, (float *)nullptr, 0);
         return hipGetLastError();
     };
-    if (nch == 1 || (size_t)grid.x * grid.y >= DQG_GEMM_SPLIT_BELOW) return plain();
+    if (nch == 1 || (size_t)grid.x * grid.y >= GEMM_SPLIT_BELOW) return plain();
     const int op = grid.x * rows_per_block;
     const size_t bytes = (size_t)nch * (GU ? 2 : 1) * S * op * sizeof(float);
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -2203,10 +2124,10 @@ hipError_t matmul_c(const MatDev &m, const float *x, int S, float *y, hipStream_
     if (rows_x_fits<C>(m.K, S)) return rows_x<C, false>(m, m, x, S, y, INFINITY, st, "matmul");
     // int3's 64-input chunks: 8 tokens at a time would spill, 4 fit with x in LDS
     if constexpr (C != C_I3)
-        if (S >= 8) return go_matmul<C, DQG_MM_R8, 8>(m, x, S, y, st);
-    if (S >= 4) return go_matmul<C, DQG_MM_R4, 4>(m, x, S, y, st);
-    if (S >= 2) return go_matmul<C, DQG_MM_R2, 2>(m, x, S, y, st);
-    return go_matmul<C, DQG_MM_R1, 1>(m, x, S, y, st);
+        if (S >= 8) return go_matmul<C, MM_R, 8>(m, x, S, y, st);
+    if (S >= 4) return go_matmul<C, MM_R, 4>(m, x, S, y, st);
+    if (S >= 2) return go_matmul<C, MM_R, 2>(m, x, S, y, st);
+    return go_matmul<C, MM_R, 1>(m, x, S, y, st);
 }
 
 template <int C, int R, int SM>
@@ -2270,7 +2191,7 @@ hipError_t group_b_cap(const GroupArgs &a, hipStream_t st) {
             return hipGetLastError();
         }
     }
-    const int waves = units < down_max_waves<CAP>() ? units : down_max_waves<CAP>();
+    const int waves = units < DOWN_MAX_WAVES ? units : DOWN_MAX_WAVES;
     dim3 grid((a.H + RB - 1) / RB);
     // the slots' outputs; DeepSeek V4's combine adds the ids and their order
     const size_t lds = (size_t)slots * RB * sizeof(float) + v4_lds;
@@ -2278,22 +2199,17 @@ hipError_t group_b_cap(const GroupArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Batch capacity: one token needs single-slot batches only.  Tokens that
-// share an expert beyond the capacity take further passes over its rows,
-// which the caches then serve.
+// Batch capacity: one token needs single-slot batches only; gate/up takes
+// slots in batches of up to 2 (x rows staged in LDS), down one slot at a
+// time.  Tokens that share an expert beyond the capacity take further
+// passes over its rows, which the caches then serve.
 template <int C>
 hipError_t group_a(const GroupArgs &a, hipStream_t st) {
-    if constexpr (DQG_CAP_A == 1) return group_a_cap<C, 1>(a, st);
-    else if constexpr (DQG_CAP_A == 2) return a.S == 1 ? group_a_cap<C, 1>(a, st) : group_a_cap<C, 2>(a, st);
-    else return a.S == 1 ? group_a_cap<C, 1>(a, st) : a.S == 2 ? group_a_cap<C, 2>(a, st) : group_a_cap<C, 4>(a, st);
+    return a.S == 1 ? group_a_cap<C, 1>(a, st) : group_a_cap<C, 2>(a, st);
 }
 
 template <int C>
-hipError_t group_b(const GroupArgs &a, hipStream_t st) {
-    if constexpr (DQG_CAP_B == 1) return group_b_cap<C, 1>(a, st);
-    else if constexpr (DQG_CAP_B == 2) return a.S == 1 ? group_b_cap<C, 1>(a, st) : group_b_cap<C, 2>(a, st);
-    else return a.S == 1 ? group_b_cap<C, 1>(a, st) : a.S == 2 ? group_b_cap<C, 2>(a, st) : group_b_cap<C, 4>(a, st);
-}
+hipError_t group_b(const GroupArgs &a, hipStream_t st) { return group_b_cap<C, 1>(a, st); }
 
 // Calls f(std::integral_constant<int, C>) for the codec of a run-time id.
 template <typename F>

@@ -31,6 +31,7 @@ def test_source_hash_ignores_comments_only(tmp_path):
     src = target.read_text()
     target.write_text("// a comment\n/* and a\n   block */\n" + src.replace("\n", "\n\n", 3))
     assert b.kernel_sources_sha256() == base
-    target.write_text(src.replace("constexpr int RB = DQG_RB;", "constexpr int RB = DQG_RB + 0;", 1))
+    assert "constexpr int RB = 12;" in src
+    target.write_text(src.replace("constexpr int RB = 12;", "constexpr int RB = 12 + 0;", 1))
     assert b.kernel_sources_sha256() != base
 
