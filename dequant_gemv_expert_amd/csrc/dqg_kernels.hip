@@ -1326,66 +1326,65 @@ template <int C, int R, int CAP>
 __global__ void __launch_bounds__(WAVE * DOWN_MAX_WAVES) k_group_down(GroupArgs a) { group_down<C, R, CAP>(a); }
 
 // Kernel B for one token with a shared expert and 6 to 8 routed ones (a
-// decode step): wave w computes the R rows of routed rank w, and the shared
+// decode step), on blocks of R = 24 rows and 2k waves: waves 2r and 2r + 1
+// compute the first and second 12 rows of routed rank r, and the shared
 // expert's R rows are dealt over the waves (row j to wave j % W, at most
 // SPLIT_NX a wave), so that no wave streams a second unit after its first.
-// Each wave issues all its loads (its rank's codes, scales and h, then its
-// shared rows' codes and scales) before any arithmetic; the shared slot's h
-// is staged once per block in LDS, its loads issued ahead of the weights.
-// The per-row arithmetic is step_compute's (step_compute_lds reads the same
-// x in the same order), so the bits are those of k_group_down.  The
-// launcher checks: S == 1, shared >= 0, k == W in [6, 8], and I of 64
-// chunks (one a lane; I = 2048 for the 32-value chunks of int4 and MXFP4).
-constexpr int SPLIT_NX = 2;
+// The h of every slot (the k ranks, then the shared slot) is staged once per
+// block in LDS, its loads (SPLIT_HN 16-byte loads a thread, clamped
+// duplicates writing the same value twice) issued ahead of the weights, so
+// that a block reads h from L2 once for 24 rows (measured on MI355X, int4-g32
+// group at one token: 17.1-17.2 us against 18.1-18.3 with one wave a rank on
+// 12-row blocks, each wave reading its rank's h from L2).  A wave's rows go
+// through a ring of SPLIT_DEPTH rows in flight, each row computed as it
+// lands.  The per-row arithmetic is step_compute's, so the bits are those of
+// k_group_down.  The launcher checks: S == 1, shared >= 0, k in [6, 8], and
+// I of 64 chunks (one a lane; I = 2048 for the 32-value chunks of int4 and
+// MXFP4).
+constexpr int SPLIT_NX = 2, SPLIT_R = 24, SPLIT_HN = 5;
 // Rows a wave keeps in flight (measured on MI355X for the int4-g32 group at
 // one token: depth 2, 3, 4, 6 -> 19.1, 18.6, 18.3, 18.0 us; every row's loads
 // issued at once 18.2 us).
 constexpr int SPLIT_DEPTH = 6;
 
-template <int C, int R>
-__global__ void __launch_bounds__(WAVE * 8) __attribute__((amdgpu_waves_per_eu(4))) k_group_down_split(GroupArgs a) {
+template <int C>
+__global__ void __launch_bounds__(WAVE * 16) __attribute__((amdgpu_waves_per_eu(4)))
+k_group_down_split(GroupArgs a) {
     using Cd = Codec<C>;
-    constexpr int NX = SPLIT_NX;
+    constexpr int NX = SPLIT_NX, R = SPLIT_R, RW = R / 2, HN = SPLIT_HN;
     extern __shared__ float lds[];
-    lfloats_w xsh = (lfloats_w)lds;   // the shared slot's h (a.I floats, unpadded)
-    float *d = lds + a.I;          // the slots' outputs, d[slot][R]
-    const int W = blockDim.x / WAVE, w = wave_id(), lane = threadIdx.x & (WAVE - 1);
-    const int row0 = blockIdx.x * R;
     const int nr = a.k;            // one token: slot q is rank q, the shared slot is nr
-    // the shared slot's h, at most two 16-byte loads a thread (clamped
-    // duplicates write the same value twice)
-    const uint32_t n4 = (uint32_t)a.I / 4, nt = blockDim.x;
-    const GLOBAL f32x4 *hsrc = (const GLOBAL f32x4 *)gf(a.h + (size_t)nr * a.I);
-    const uint32_t i0 = min((uint32_t)threadIdx.x, n4 - 1), i1 = min((uint32_t)threadIdx.x + nt, n4 - 1);
-    const f32x4 hv0 = hsrc[i0], hv1 = hsrc[i1];
-    const int e = __builtin_amdgcn_readfirstlane(a.ids[w]);
+    // LDS: h of slots 0..nr (unpadded), then the slots' outputs d[slot][R]
+    lfloats_w hl = (lfloats_w)lds;
+    float *d = lds + (size_t)(nr + 1) * a.I;
+    const int W = blockDim.x / WAVE, w = wave_id(), lane = threadIdx.x & (WAVE - 1);
+    const int rank = w / 2, part = w % 2;
+    const int row0 = blockIdx.x * R;
+    const uint32_t n4 = (uint32_t)((nr + 1) * a.I / 4), nt = blockDim.x;
+    const GLOBAL f32x4 *hsrc = (const GLOBAL f32x4 *)gf(a.h);
+    f32x4 hv[HN];
+#pragma unroll
+    for (int u = 0; u < HN; ++u) hv[u] = hsrc[min((uint32_t)threadIdx.x + u * nt, n4 - 1)];
+    const int e = __builtin_amdgcn_readfirstlane(a.ids[rank]);
     const bool ok = e >= 0 && e < a.n_experts;
     const ExpertDev &ex = a.table[ok ? e : a.shared];   // a bad id reads the shared expert, then writes NaN
     const ExpertDev &exs = a.table[a.shared];
-    // the wave's rows in order: R of its rank, then NX of the shared expert
-    constexpr int NT = R + NX, D = SPLIT_DEPTH;
+    // the wave's rows in order: RW of its rank, then NX of the shared expert
+    constexpr int NT = RW + NX, D = SPLIT_DEPTH;
     GRow rows[NT];
 #pragma unroll
-    for (int r = 0; r < R; ++r) rows[r] = row_ptrs(ex.down, min(row0 + r, a.H - 1));
+    for (int r = 0; r < RW; ++r) rows[r] = row_ptrs(ex.down, min(row0 + part * RW + r, a.H - 1));
 #pragma unroll
-    for (int j = 0; j < NX; ++j) rows[R + j] = row_ptrs(exs.down, min(row0 + min(w + j * W, R - 1), a.H - 1));
+    for (int j = 0; j < NX; ++j) rows[RW + j] = row_ptrs(exs.down, min(row0 + min(w + j * W, R - 1), a.H - 1));
     const int shift = ex.down.shift;
     const uint32_t c = opaque((uint32_t)lane);   // one chunk a lane
     const uint32_t si = c >> shift;
     float acc[NT];
     typename Cd::Chunk ch[D];
     float sc[D];
-    // h of the wave's rank first, then a ring of D rows in flight: row i's
-    // codes and scale are issued when row i - D has been computed
+    // then a ring of D rows in flight: row i's codes and scale are issued
+    // when row i - D has been computed
     float xv[Cd::CW];
-    {
-        const gfloats hp = gf(a.h + (size_t)w * a.I);
-#pragma unroll
-        for (int i = 0; i < Cd::CW / 4; ++i) {
-            const float4 t = ldf4(hp, c * Cd::CW + 4 * i);
-            xv[4 * i] = t.x; xv[4 * i + 1] = t.y; xv[4 * i + 2] = t.z; xv[4 * i + 3] = t.w;
-        }
-    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < D; ++i) {
@@ -1393,8 +1392,21 @@ __global__ void __launch_bounds__(WAVE * 8) __attribute__((amdgpu_waves_per_eu(4
         sc[i] = Cd::SCALED ? ld_scale(rows[i].s, si) : 1.f;
         __builtin_amdgcn_sched_barrier(0);
     }
-    *(LDS f32x4 *)(xsh + 4 * i0) = hv0;
-    *(LDS f32x4 *)(xsh + 4 * i1) = hv1;
+#pragma unroll
+    for (int u = 0; u < HN; ++u) {
+        const uint32_t i = min((uint32_t)threadIdx.x + u * nt, n4 - 1);
+        *(LDS f32x4 *)(hl + 4 * i) = hv[u];
+    }
+    // x of a slot from the block's LDS copy, and its chunk sum
+    const auto x_from_lds = [&](int slot_in_lds) {
+#pragma unroll
+        for (int q = 0; q < Cd::CW / 4; ++q) {
+            const f32x4 t = *(const LDS f32x4 *)(hl + (size_t)slot_in_lds * a.I + c * Cd::CW + 4 * q);
+            xv[4 * q] = t.x; xv[4 * q + 1] = t.y; xv[4 * q + 2] = t.z; xv[4 * q + 3] = t.w;
+        }
+    };
+    __syncthreads();   // h staged
+    x_from_lds(rank);
     float xs = 0.f;
     if (Cd::OFFS != 0.f) {
 #pragma unroll
@@ -1403,15 +1415,10 @@ __global__ void __launch_bounds__(WAVE * 8) __attribute__((amdgpu_waves_per_eu(4
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < NT; ++i) {
-        if (i == R) {
-            // the shared rows: x of the shared slot from the block's LDS copy
-            __syncthreads();   // xsh staged
+        if (i == RW) {
+            // the shared rows
+            x_from_lds(nr);
             xs = 0.f;
-#pragma unroll
-            for (int q = 0; q < Cd::CW / 4; ++q) {
-                const f32x4 t = *(const LDS f32x4 *)(xsh + c * Cd::CW + 4 * q);
-                xv[4 * q] = t.x; xv[4 * q + 1] = t.y; xv[4 * q + 2] = t.z; xv[4 * q + 3] = t.w;
-            }
             if (Cd::OFFS != 0.f) {
 #pragma unroll
                 for (int q = 0; q < Cd::CW; ++q) xs += xv[q];
@@ -1431,9 +1438,9 @@ __global__ void __launch_bounds__(WAVE * 8) __attribute__((amdgpu_waves_per_eu(4
         const float t = wave_sum(acc[r]);
         if (lane == r) out = t;
     }
-    if (lane < R) d[w * R + lane] = ok ? (v4 ? round_bf16(out) : out) : __int_as_float(0x7FC00000);
-    if (lane >= R && lane < R + NX) {
-        const int xr = w + (lane - R) * W;
+    if (lane < RW) d[rank * R + part * RW + lane] = ok ? (v4 ? round_bf16(out) : out) : __int_as_float(0x7FC00000);
+    if (lane >= RW && lane < RW + NX) {
+        const int xr = w + (lane - RW) * W;
         if (xr < R) d[nr * R + xr] = v4 ? round_bf16(out) : out;
     }
     if (!ok && lane == 0) *a.flag = 1;
@@ -2184,10 +2191,11 @@ hipError_t group_b_cap(const GroupArgs &a, hipStream_t st) {
     const int slots = a.S * a.k + (a.shared >= 0 ? a.S : 0);
     const size_t v4_lds = a.act == ACT_SWIGLU_V4 ? 2 * (size_t)a.S * a.k * sizeof(int) : 0;
     if constexpr (CAP == 1 && C != C_I3) {
-        if (a.S == 1 && a.shared >= 0 && a.k >= 6 && a.k <= 8 && a.I == WAVE * Codec<C>::CW) {
-            dim3 grid((a.H + RB - 1) / RB);
-            const size_t lds = ((size_t)a.I + (size_t)slots * RB) * sizeof(float) + v4_lds;
-            launch("group_down", (k_group_down_split<C, RB>), grid, dim3(WAVE * a.k), lds, st, a);
+        if (a.S == 1 && a.shared >= 0 && a.k >= 6 && a.k <= 8 && a.I == WAVE * Codec<C>::CW &&
+            (long)(a.k + 1) * a.I / 4 <= (long)SPLIT_HN * WAVE * 2 * a.k) {
+            dim3 grid((a.H + SPLIT_R - 1) / SPLIT_R);
+            const size_t lds = ((size_t)(a.k + 1) * a.I + (size_t)slots * SPLIT_R) * sizeof(float) + v4_lds;
+            launch("group_down", (k_group_down_split<C>), grid, dim3(WAVE * 2 * a.k), lds, st, a);
             return hipGetLastError();
         }
     }
