@@ -834,14 +834,14 @@ __global__ void __launch_bounds__(256) k_rows_lds(MatDev m0, MatDev m1, const fl
     }
 }
 
-// The same products for 1-2 tokens and K of 1-4 whole 64-chunk steps (NS),
+// The same products for 1-4 tokens and K of 1-4 whole 64-chunk steps (NS),
 // shaped to fill the chip at one token: blocks of 12 waves x 2 rows (6144
 // rows make 256 blocks, one a CU), x staged once per block, and every load
 // of a wave issued before its first arithmetic.  x's loads go out first and
 // wait in registers while the weights' loads are issued (step by step, rows
 // in order), so that copying x to LDS waits for x alone; then each row of
 // each step is computed as its codes land (one token: the step's x in
-// registers; two: step_compute_lds).  The per-row arithmetic and the order
+// registers; more: step_compute_lds).  The per-row arithmetic and the order
 // of steps are k_rows_lds's, so the bits are the same.
 constexpr int GX_W = 12, GX_R = 2;
 
@@ -2086,12 +2086,12 @@ hipError_t go_gemm(const MatDev &m0, const MatDev &m1, const float *x, int S, fl
     return go_gemm_nc<C, GU, 4>(m0, m1, x, S, y, L, st, name);
 }
 
-// k_rows_x for 1-2 tokens and K of 1-4 whole 64-chunk steps (not int3,
+// k_rows_x for 1-4 tokens and K of 1-4 whole 64-chunk steps (not int3,
 // whose 64-input chunks would spill).
 template <int C>
 bool rows_x_fits(int K, int S) {
     const int unit = WAVE * Codec<C>::CW;
-    return C != C_I3 && S <= 2 && K % unit == 0 && K / unit <= 4;
+    return C != C_I3 && S <= 4 && K % unit == 0 && K / unit <= 4;
 }
 
 template <int C, int SM, bool GU, int NS>
@@ -2119,7 +2119,8 @@ hipError_t rows_x(const MatDev &g, const MatDev &u, const float *x, int S, float
                   const char *name) {
     if constexpr (C != C_I3) {
         if (S == 1) return rows_x_sm<C, GU, 1>(g, u, x, S, y, L, st, name);
-        return rows_x_sm<C, GU, 2>(g, u, x, S, y, L, st, name);
+        if (S == 2) return rows_x_sm<C, GU, 2>(g, u, x, S, y, L, st, name);
+        return rows_x_sm<C, GU, 4>(g, u, x, S, y, L, st, name);
     }
     return hipErrorInvalidValue;
 }

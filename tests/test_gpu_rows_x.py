@@ -1,4 +1,4 @@
-"""Parity of the one- and two-token row kernel (x staged once per block,
+"""Parity of the one- to four-token row kernel (x staged once per block,
 every load of a wave issued before its arithmetic) with the CPU oracle,
 through the C ABI.
 
@@ -54,7 +54,7 @@ def test_rows_x_matmul(case):
     W = dq.Matrix.upload(m)
     x = synth.activations(8, K, 7100 + i)
     yb = host(dq.dqg_matmul(W, dev_f32(x)))
-    for S in (1, 2):
+    for S in (1, 2, 3, 4):
         y = host(dq.dqg_matmul(W, dev_f32(x[:S])))
         yr, a = oracle.gemv(m, x[:S])
         assert_close(y, yr, a, f"rows_x matmul {case} S={S}")
@@ -70,8 +70,8 @@ def test_rows_x_gate_up(case):
     i = CASES.index(case)
     G = synth.matrix(fmt, O, K, gs, 7200 + i, 0)
     U = synth.matrix(fmt, O, K, gs, 7200 + i, 1)
-    x = synth.activations(2, K, 7300 + i)
-    for S in (1, 2):
+    x = synth.activations(4, K, 7300 + i)
+    for S in (1, 2, 4):
         h = host(dq.dqg_gate_up(dq.Matrix.upload(G), dq.Matrix.upload(U), dev_f32(x[:S])))
         r = oracle.gate_up(G, U, x[:S])
         assert_close(h, r["h"], r["nh"], f"rows_x gate_up {case} S={S}")
