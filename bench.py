@@ -133,8 +133,9 @@ def kernel_sources_sha256() -> str:
 
 
 def profiled_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None when the kernel sources changed since it was taken."""
+    """HBM bytes per launch of `kernel` (or per call of "a+b", the sum over its
+    launches) from the committed rocprofv3 counter summary, or None when the
+    kernel sources changed since it was taken."""
     path = os.path.join(ROOT, TRAFFIC_PROFILE)
     if not os.path.exists(path):
         return None
@@ -146,8 +147,13 @@ def profiled_traffic(kernel: str):
                 fields[key.strip()] = val.strip()
     if fields.get("kernel_sources_sha256") != kernel_sources_sha256():
         return None
-    v = fields.get(f"bytes_per_launch.{kernel}")
-    return int(float(v)) if v else None
+    total = 0
+    for name in kernel.split("+"):   # a call's launches, joined by "+": their sum
+        v = fields.get(f"bytes_per_launch.{name}")
+        if not v:
+            return None
+        total += int(float(v))
+    return total
 
 
 def matrix_bytes(m) -> int:
@@ -341,6 +347,8 @@ def main():
             b = None
         breakdown[name] = {"avg_us": round(ms_k / n_k * 1e3, 2), "median_us": pstats[name][2],
                            "p10_us": pstats[name][3], "p90_us": pstats[name][4],
+                           "traffic": profiled_traffic(name) if (S == 1 and args.workload ==
+                                      "int4g32_expert_group_256top8_shared") else None,
                            **({"bytes_per_launch": round(b / n_k), "achieved": round(b / (ms_k * 1e-3) / 1e9, 1)}
                               if b else {})}
     pc = np.asarray(call_us)
