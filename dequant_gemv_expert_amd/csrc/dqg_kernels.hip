@@ -834,14 +834,14 @@ __global__ void __launch_bounds__(256) k_rows_lds(MatDev m0, MatDev m1, const fl
     }
 }
 
-// The same products for 1-4 tokens and K of 1-4 whole 64-chunk steps (NS),
+// The same products for 1-4 tokens (int3: 1) and K of 1-4 whole 64-chunk steps (NS),
 // shaped to fill the chip at one token: blocks of 12 waves x 2 rows (6144
 // rows make 256 blocks, one a CU), x staged once per block, and every load
 // of a wave issued before its first arithmetic.  x's loads go out first and
 // wait in registers while the weights' loads are issued (step by step, rows
 // in order), so that copying x to LDS waits for x alone; then each row of
 // each step is computed as its codes land (one token: the step's x in
-// registers; more: step_compute_lds).  The per-row arithmetic and the order
+// registers; more, or int3: step_compute_lds).  The per-row arithmetic and the order
 // of steps are k_rows_lds's, so the bits are the same.
 constexpr int GX_W = 12, GX_R = 2;
 
@@ -886,7 +886,11 @@ __global__ void __launch_bounds__(WAVE * GX_W) k_rows_x(MatDev m0, MatDev m1, co
     __syncthreads();
     // one token, codes with an offset: each chunk's sum of x, summed once per
     // block in step_compute's order, after the row
-    constexpr bool XSUM = SM == 1 && Cd::OFFS != 0.f;
+    // one token with a chunk of at most 32 inputs takes the step's x in
+    // registers (and the chunk sums of x once per block); int3's 64-input
+    // chunks read x per decode unit from LDS like several tokens do
+    constexpr bool XREG = SM == 1 && Cd::CW <= 32;
+    constexpr bool XSUM = XREG && Cd::OFFS != 0.f;
     lfloats_w xsums = xs + xl;
     if constexpr (XSUM) {
         for (uint32_t t = threadIdx.x; t < (uint32_t)(K / Cd::CW); t += nt) {
@@ -911,7 +915,7 @@ __global__ void __launch_bounds__(WAVE * GX_W) k_rows_x(MatDev m0, MatDev m1, co
 #pragma unroll
     for (int j = 0; j < NS; ++j) {
         const uint32_t cu = (uint32_t)(j * WAVE + lane);
-        if constexpr (SM == 1) {
+        if constexpr (XREG) {
             float xv[Cd::CW];
 #pragma unroll
             for (int q = 0; q < Cd::CW / 4; ++q) {
@@ -2086,12 +2090,12 @@ hipError_t go_gemm(const MatDev &m0, const MatDev &m1, const float *x, int S, fl
     return go_gemm_nc<C, GU, 4>(m0, m1, x, S, y, L, st, name);
 }
 
-// k_rows_x for 1-4 tokens and K of 1-4 whole 64-chunk steps (not int3,
-// whose 64-input chunks would spill).
+// k_rows_x for 1-4 tokens and K of 1-4 whole 64-chunk steps (int3, whose
+// 64-input chunks would spill a wider batch, at one token only).
 template <int C>
 bool rows_x_fits(int K, int S) {
     const int unit = WAVE * Codec<C>::CW;
-    return C != C_I3 && S <= 4 && K % unit == 0 && K / unit <= 4;
+    return S <= (C == C_I3 ? 1 : 4) && K % unit == 0 && K / unit <= 4;
 }
 
 template <int C, int SM, bool GU, int NS>
@@ -2099,6 +2103,7 @@ hipError_t go_rows_x(const MatDev &g, const MatDev &u, const float *x, int S, fl
                      const char *name) {
     dim3 grid((g.O + GX_W * GX_R - 1) / (GX_W * GX_R));
     const size_t lds = ((size_t)SM * x_lds_len<Codec<C>::CW>(g.K) + (SM == 1 ? g.K / Codec<C>::CW : 0)) * 4;
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
     launch(name, (k_rows_x<C, SM, GU, NS>), grid, dim3(WAVE * GX_W), lds, st, g, u, x, S, y, L);
     return hipGetLastError();
 }
@@ -2117,8 +2122,8 @@ hipError_t rows_x_sm(const MatDev &g, const MatDev &u, const float *x, int S, fl
 template <int C, bool GU>
 hipError_t rows_x(const MatDev &g, const MatDev &u, const float *x, int S, float *y, float L, hipStream_t st,
                   const char *name) {
+    if (S == 1) return rows_x_sm<C, GU, 1>(g, u, x, S, y, L, st, name);
     if constexpr (C != C_I3) {
-        if (S == 1) return rows_x_sm<C, GU, 1>(g, u, x, S, y, L, st, name);
         if (S == 2) return rows_x_sm<C, GU, 2>(g, u, x, S, y, L, st, name);
         return rows_x_sm<C, GU, 4>(g, u, x, S, y, L, st, name);
     }

@@ -3,8 +3,8 @@ every load of a wave issued before its arithmetic) with the CPU oracle,
 through the C ABI.
 
 It takes K of one to four whole steps of 64 code chunks, so the shapes below
-set K = n * 64 * (inputs per chunk) for n = 1..4 in every format but int3,
-with row counts ragged against its 24-row blocks.  Bars as for the other
+set K = n * 64 * (inputs per chunk) for n = 1..4 in every format (int3 at one
+token only), with row counts ragged against its 24-row blocks.  Bars as for the other
 matmul tests: every output within 1e-5 of its row's normaliser, and a
 token's bits the same alone and inside a batch of 8 (which takes the
 general per-row kernel).
@@ -34,7 +34,7 @@ def _announce(request):
 
 
 # inputs per code chunk, and a group size where the format has one
-CHUNK = {1: (16, None), 2: (32, None), 4: (32, 32), 7: (32, 32), 10: (4, None), 11: (8, None),
+CHUNK = {1: (16, None), 2: (32, None), 4: (32, 32), 5: (64, 64), 7: (32, 32), 10: (4, None), 11: (8, None),
          12: (16, None), 13: (16, 64), 14: (8, None)}
 CASES = [(fmt, n, O) for fmt in CHUNK for n, O in ((1, 37), (2, 24), (3, 61), (4, 5))]
 IDS = [f"fmt{f}_steps{n}_O{o}" for f, n, o in CASES]
