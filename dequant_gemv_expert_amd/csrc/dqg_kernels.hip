@@ -1383,7 +1383,7 @@ k_group_down_split(GroupArgs a) {
     const int shift = ex.down.shift;
     const uint32_t c = opaque((uint32_t)lane);   // one chunk a lane
     const uint32_t si = c >> shift;
-    float acc[NT];
+    float out = 0.f;   // lane r: row r's sum
     typename Cd::Chunk ch[D];
     float sc[D];
     // then a ring of D rows in flight: row i's codes and scale are issued
@@ -1428,20 +1428,18 @@ k_group_down_split(GroupArgs a) {
                 for (int q = 0; q < Cd::CW; ++q) xs += xv[q];
             }
         }
-        acc[i] = row_dot<C>(ch[i % D], sc[i % D], xv, xs, 0.f);
+        const float acc = row_dot<C>(ch[i % D], sc[i % D], xv, xs, 0.f);
         if (i + D < NT) {
             ch[i % D] = Cd::load(rows[i + D], c);
             sc[i % D] = Cd::SCALED ? ld_scale(rows[i + D].s, si) : 1.f;
         }
+        // the row's sum over the wave right away, so that only the last
+        // rows' reductions remain after the last bytes land
+        const float t = wave_sum(acc);
+        if (lane == i) out = t;
         __builtin_amdgcn_sched_barrier(0);
     }
     const bool v4 = a.act == ACT_SWIGLU_V4;
-    float out = 0.f;
-#pragma unroll
-    for (int r = 0; r < NT; ++r) {
-        const float t = wave_sum(acc[r]);
-        if (lane == r) out = t;
-    }
     if (lane < RW) d[rank * R + part * RW + lane] = ok ? (v4 ? round_bf16(out) : out) : __int_as_float(0x7FC00000);
     if (lane >= RW && lane < RW + NX) {
         const int xr = w + (lane - RW) * W;
