@@ -1195,7 +1195,9 @@ __device__ __forceinline__ void group_gate_up(const GroupArgs &a) {
     extern __shared__ float x_lds_raw[];
     lfloats_w xs = (lfloats_w)x_lds_raw;
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.flag = 0;
-    const int q = blockIdx.y;
+    // the shared expert's blocks (row y = 0) go first: with several tokens
+    // it serves a batch per token, and started last it would set the tail
+    const int q = a.shared >= 0 ? (blockIdx.y == 0 ? (int)gridDim.y - 1 : (int)blockIdx.y - 1) : (int)blockIdx.y;
     const int nr = a.S * a.k;
     const int e = __builtin_amdgcn_readfirstlane(q < nr ? a.ids[q] : a.shared);
     if (e < 0 || e >= a.n_experts) return;         // reported by kernel B
@@ -1265,7 +1267,10 @@ __device__ __forceinline__ void group_down(const GroupArgs &a) {
     extern __shared__ float d[];
     const int row0 = blockIdx.x * R;
     const int nr = a.S * a.k;
-    const int nunits = nr + (a.shared >= 0 ? 1 : 0);
+    // units: the routed slots (each expert once, by its first slot), then
+    // each token's shared slot on its own, so that the shared expert's S
+    // slots spread over the waves instead of one wave's serial passes
+    const int nunits = nr + (a.shared >= 0 ? a.S : 0);
     const int nw = blockDim.x / WAVE;
     const int lane = threadIdx.x & (WAVE - 1);
     for (int q = wave_id(); q < nunits; q += nw) {
@@ -1275,8 +1280,19 @@ __device__ __forceinline__ void group_down(const GroupArgs &a) {
             if (lane == 0) *a.flag = 1;
             continue;
         }
-        if (q < nr && !owns(a.ids, q, e)) continue;
         const ExpertDev &ex = a.table[e];
+        if (q >= nr) {   // token q - nr's shared slot
+            SlotBatch b;
+            b.n = 1;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                b.slot[j] = q;
+                b.token[j] = q - nr;
+            }
+            group_down_batch<C, R, 1>(a, ex, row0, b, d);
+            continue;
+        }
+        if (!owns(a.ids, q, e)) continue;
         for_slots<CAP>(a, q, e, [&](const SlotBatch &b) {
             if (CAP == 1 || b.n == 1) group_down_batch<C, R, 1>(a, ex, row0, b, d);
             else if (CAP == 2 || b.n == 2) group_down_batch<C, R, 2>(a, ex, row0, b, d);
@@ -2191,7 +2207,7 @@ hipError_t group_a_cap(const GroupArgs &a, hipStream_t st) {
 
 template <int C, int CAP>
 hipError_t group_b_cap(const GroupArgs &a, hipStream_t st) {
-    const int units = a.S * a.k + (a.shared >= 0 ? 1 : 0);
+    const int units = a.S * a.k + (a.shared >= 0 ? a.S : 0);   // each shared slot a unit
     const int slots = a.S * a.k + (a.shared >= 0 ? a.S : 0);
     const size_t v4_lds = a.act == ACT_SWIGLU_V4 ? 2 * (size_t)a.S * a.k * sizeof(int) : 0;
     if constexpr (CAP == 1 && C != C_I3) {
@@ -2211,14 +2227,15 @@ hipError_t group_b_cap(const GroupArgs &a, hipStream_t st) {
     return hipGetLastError();
 }
 
-// Batch capacity: one token needs single-slot batches only; gate/up takes
-// slots in batches of up to 2 (x rows staged in LDS), down one slot at a
-// time.  Tokens that share an expert beyond the capacity take further
-// passes over its rows, which the caches then serve.
+// Batch capacity: one slot at a time in both launches, at every S.  Tokens
+// that share an expert take further passes over its rows, which the caches
+// then serve.  (Beyond one token most units serve one slot; 2-slot batches
+// cost the gate/up launch its one-token register and LDS budget, 3 waves a
+// SIMD against 5: measured on MI355X, int4-g32 group, gate/up 54.2 -> 51.2 us
+// at 2 tokens and 108.8 -> 93.6 us at 4 with the shared expert's blocks
+// first.)
 template <int C>
-hipError_t group_a(const GroupArgs &a, hipStream_t st) {
-    return a.S == 1 ? group_a_cap<C, 1>(a, st) : group_a_cap<C, 2>(a, st);
-}
+hipError_t group_a(const GroupArgs &a, hipStream_t st) { return group_a_cap<C, 1>(a, st); }
 
 template <int C>
 hipError_t group_b(const GroupArgs &a, hipStream_t st) { return group_b_cap<C, 1>(a, st); }
