@@ -250,6 +250,41 @@ def test_group_one_token_split_down(case):
     table.close()
 
 
+# Several tokens with at least 8 units and I of 64 code chunks, H ragged
+# against the down launch's 12-row blocks, one expert named by two tokens.
+MULTI_CASES = [(2, 8, True, 4, 32, 2048, 416), (3, 4, False, 4, 32, 2048, 224),
+              (2, 6, True, 7, 32, 2048, 6176), (5, 3, True, 1, None, 1024, 160)]
+
+
+@pytest.mark.parametrize("case", MULTI_CASES)
+def test_group_multi_token_down(case):
+    S, k, with_shared, fmt, gs, I, H = case
+    E = 2 * k + 3
+    seed = 4900 + MULTI_CASES.index(case)
+    hs, table = _small_group(E, fmt=fmt, gs=gs, H=H, I=I, seed=seed)
+    ids, w = synth.routing(S, E - 1, k, seed)
+    ids[S - 1, k - 1] = ids[0, 0]   # one expert named by two tokens
+    shared = E - 1 if with_shared else None
+    x = synth.activations(S, H, seed)
+    check_group(hs, table, ids, w, shared, x, f"multi-token down {case}")
+    # batch invariance: the batch against one token at a time
+    yb = host(dq.dqg_expert_group(table, dev_i32(ids), dev_f32(w), shared, dev_f32(x)))
+    for t in range(S):
+        y1 = host(dq.dqg_expert_group(table, dev_i32(ids[t:t + 1]), dev_f32(w[t:t + 1]), shared,
+                                      dev_f32(x[t:t + 1])))
+        assert bits_equal(yb[t], y1[0]), (case, t)
+    # a bad id: that token's outputs are NaN, the others finite, and the call reports it
+    bad = ids.copy()
+    bad[S - 1, 1] = E + 9
+    ticket, y, _ = dq.dqg_expert_group_issue(table, dev_i32(bad), dev_f32(w), shared, dev_f32(x))
+    with pytest.raises(dq.DqgError) as ei:
+        dq.dqg_expert_group_take(ticket)
+    assert ei.value.code == -7
+    yh = host(y)
+    assert np.all(np.isnan(yh[S - 1])) and np.all(np.isfinite(yh[:S - 1]))
+    table.close()
+
+
 def test_group_bad_id_is_reported():
     hs, table = _small_group(6)
     ids = np.array([[0, 1, 2], [1, 99, 4]], np.int32)
