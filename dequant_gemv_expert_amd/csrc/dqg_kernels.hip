@@ -115,15 +115,6 @@ struct XGlobal {
     template <int CW>
     __device__ __forceinline__ float4 load4(uint32_t cu, uint32_t off) const { return ldf4(p, cu * CW + off); }
 };
-template <bool P>
-struct XLdsT {
-    lfloats p;   // the token's row, laid out by x_lds_at<CW, P>
-    template <int CW>
-    __device__ __forceinline__ float4 load4(uint32_t cu, uint32_t off) const {
-        const f32x4 v = *(const LDS f32x4 *)(p + x_lds_at<CW, P>(cu * CW) + off);
-        return make_float4(v.x, v.y, v.z, v.w);
-    }
-};
 
 // A wave-uniform global pointer, held in SGPRs.
 __device__ __forceinline__ uint64_t uniform_bits(const void *p) {
@@ -988,16 +979,17 @@ __global__ void __launch_bounds__(256) k_dequant(MatDev m, float *__restrict__ o
 // ---------------------------------------------------------------------------
 // Routed expert group.
 //
-// Units: routed slot q = t*k + r (q < S*k) and, with a shared expert, unit
-// S*k.  A routed unit whose expert appears at an earlier slot is skipped;
-// the first slot of an expert (its owner) serves every slot that names it,
-// so each distinct expert's rows are read once per call.  Slot lists come
+// Units: routed slot q = t*k + r (q < S*k) and, with a shared expert, the
+// gate/up launch's unit S*k (which serves every token's shared slot) or the
+// down launch's units S*k + t (token t's shared slot each).  A routed unit
+// whose expert appears at an earlier slot is skipped; the first slot of an
+// expert (its owner) serves every slot that names it, one after another, so
+// each distinct expert's rows come from HBM once per call.  Slot lists come
 // from wave ballots over ids; no host round trip.
 // ---------------------------------------------------------------------------
 struct SlotBatch {
-    int n;          // 1..4 valid entries; unused entries repeat entry 0
-    int slot[4];
-    int token[4];
+    int slot;       // the h row it fills: t*k + r for token t's rank r, S*k + t for its shared expert
+    int token;
 };
 
 // Is unit q the first slot naming expert e?  (wave-uniform)
@@ -1011,100 +1003,48 @@ __device__ __forceinline__ bool owns(const int32_t *ids, int q, int e) {
     return true;
 }
 
-// Calls f(batch) for batches of up to CAP (<= 4) (slot, token) pairs that
-// use unit q's expert e: every slot >= q naming e, or every token's shared
-// slot.  All indexes into a batch are compile-time constants.
-template <int CAP, typename F>
+// Calls f(batch) for each (slot, token) that uses unit q's expert e, one at
+// a time: every slot >= q naming e, or every token's shared slot.
+template <typename F>
 __device__ __forceinline__ void for_slots(const GroupArgs &a, int q, int e, F &&f) {
     const int lane = threadIdx.x & (WAVE - 1);
     const int nr = a.S * a.k;
     if (q >= nr) {   // shared expert: token t's slot is nr + t
-        for (int t0 = 0; t0 < a.S; t0 += CAP) {
-            SlotBatch b;
-            b.n = min(CAP, a.S - t0);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int t = t0 + (j < b.n ? j : 0);
-                b.slot[j] = nr + t;
-                b.token[j] = t;
-            }
-            f(b);
-        }
+        for (int t = 0; t < a.S; ++t) f(SlotBatch{nr + t, t});
         return;
     }
     for (int base = q; base < nr; base += WAVE) {
         const int i = base + lane;
         uint64_t mask = __ballot(i < nr && a.ids[i] == e);
         while (mask) {
-            SlotBatch b;
-            b.n = 0;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (j < CAP && mask) {
-                    const int slot = base + __builtin_ctzll(mask);
-                    mask &= mask - 1;
-                    b.slot[j] = slot;
-                    b.token[j] = slot / a.k;
-                    b.n = j + 1;
-                } else {
-                    b.slot[j] = b.slot[0];
-                    b.token[j] = b.token[0];
-                }
-            }
-            f(b);
+            const int slot = base + __builtin_ctzll(mask);
+            mask &= mask - 1;
+            f(SlotBatch{slot, slot / a.k});
         }
     }
 }
 
-// Copies the batch's token rows of x into the block's LDS (all threads).
-// Each thread issues up to 8 loads (4 for batches of several tokens, whose
-// kernels hold more registers) before its first LDS write, so the copy
-// costs one round trip per batch of loads, not one per load.
-template <int SM, int CW>
+// Copies the batch's token row of x into the block's LDS (all threads).
+// Each thread issues up to 8 loads before its first LDS write, so the copy
+// costs one round trip per 8 loads, not one per load.
+template <int CW>
 __device__ __forceinline__ void stage_x(const GroupArgs &a, const SlotBatch &b, lfloats_w xs, bool sums = false) {
-    constexpr int U = SM == 1 ? 8 : 4;
+    constexpr int U = 8;
     constexpr uint32_t NT = WAVE * WPB_A;   // the gate/up launch's block size
     __syncthreads();   // the previous batch's readers are done
     const uint32_t n4 = a.H / 4;
-    if constexpr (SM == 1) {
-        const GLOBAL f32x4 *src = (const GLOBAL f32x4 *)(gf(a.x) + (size_t)b.token[0] * a.H);
-        for (uint32_t i0 = threadIdx.x; i0 < n4; i0 += U * NT) {
-            f32x4 v[U];
+    const GLOBAL f32x4 *src = (const GLOBAL f32x4 *)(gf(a.x) + (size_t)b.token * a.H);
+    for (uint32_t i0 = threadIdx.x; i0 < n4; i0 += U * NT) {
+        f32x4 v[U];
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (i0 + u * NT < n4) v[u] = src[i0 + u * NT];
+        for (int u = 0; u < U; ++u)
+            if (i0 + u * NT < n4) v[u] = src[i0 + u * NT];
 #pragma unroll
-            for (int u = 0; u < U; ++u)
-                if (i0 + u * NT < n4) *(LDS f32x4 *)(xs + x_lds_at<CW, GROUP_XPAD>(4 * (i0 + u * NT))) = v[u];
-        }
-    } else {
-        const int total = SM * (int)n4;
-        for (int i0 = threadIdx.x; i0 < total; i0 += U * (int)NT) {
-            f32x4 v[U];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int i = i0 + u * (int)NT;
-                if (i < total) {
-                    const int s = i / (int)n4, k4 = i - s * (int)n4;
-                    int t = b.token[0];
-#pragma unroll
-                    for (int j = 1; j < SM; ++j)
-                        if (s == j) t = b.token[j];
-                    v[u] = *(const GLOBAL f32x4 *)(gf(a.x) + (size_t)t * a.H + 4 * k4);
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int i = i0 + u * (int)NT;
-                if (i < total) {
-                    const int s = i / (int)n4, k4 = i - s * (int)n4;
-                    *(LDS f32x4 *)(xs + (size_t)s * x_lds_len<CW, GROUP_XPAD>(a.H) + x_lds_at<CW, GROUP_XPAD>(4 * k4)) = v[u];
-                }
-            }
-        }
+        for (int u = 0; u < U; ++u)
+            if (i0 + u * NT < n4) *(LDS f32x4 *)(xs + x_lds_at<CW, GROUP_XPAD>(4 * (i0 + u * NT))) = v[u];
     }
     __syncthreads();
-    if (SM == 1 && sums) {
+    if (sums) {
         // the sum of each chunk of x, in input order, after the row
         lfloats_w xsum = xs + x_lds_len<CW, GROUP_XPAD>(a.H);
         for (int t = threadIdx.x; t < a.H / CW; t += (int)NT) {
@@ -1123,80 +1063,57 @@ __device__ __forceinline__ void stage_x(const GroupArgs &a, const SlotBatch &b, 
     }
 }
 
-// gate_up of R rows (row0..) of expert e for a batch of SM slots, x from LDS.
-template <int C, int R, int SM>
+// gate_up of R rows (row0..) of expert e for one slot, x from LDS.  The
+// first chunk's weights are requested before x is staged.
+template <int C, int R>
 __device__ __forceinline__ void group_gu_batch(const GroupArgs &a, const ExpertDev &ex, int row0,
                                                const SlotBatch &b, lfloats_w xs) {
     const int lane = threadIdx.x & (WAVE - 1);
     const int nch = ex.gate.K / Codec<C>::CW;
-    const auto row_set = [&](GRow (&rows)[2 * R]) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) {
-            rows[r] = row_ptrs(ex.gate, min(row0 + r, a.I - 1));
-            rows[R + r] = row_ptrs(ex.up, min(row0 + r, a.I - 1));
-        }
-    };
-    XLdsT<GROUP_XPAD> xp[SM];
-#pragma unroll
-    for (int s = 0; s < SM; ++s) xp[s] = {xs + (size_t)s * x_lds_len<Codec<C>::CW, GROUP_XPAD>(a.H)};
-    float acc[2 * R][SM];
     GRow rows[2 * R];
-    if constexpr (SM == 1) {
-        // one token: the first chunk's weights are requested before x is
-        // staged (with several tokens the registers this holds cost more
-        // than it saves)
-        row_set(rows);
-        Step<C, 2 * R, SM> st;
-        const bool have = lane < nch;
-        if (have) step_load_w(st, rows, ex.gate.shift, opaque((uint32_t)lane));
-        constexpr bool sums = gu1_pairs<C, 2 * R>() && Codec<C>::OFFS != 0.f;
-        stage_x<SM, Codec<C>::CW>(a, b, xs, sums);
-        dot_rows_lds1<C, 2 * R>(st, have, rows, nch, ex.gate.shift, xs, xs + x_lds_len<Codec<C>::CW, GROUP_XPAD>(a.H),
-                                acc);
-    } else {
-        stage_x<SM, Codec<C>::CW>(a, b, xs);
-        row_set(rows);
-        dot_rows<C, 2 * R, SM, XLdsT<GROUP_XPAD>>(rows, nch, ex.gate.shift, xp, acc);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        rows[r] = row_ptrs(ex.gate, min(row0 + r, a.I - 1));
+        rows[R + r] = row_ptrs(ex.up, min(row0 + r, a.I - 1));
     }
+    float acc[2 * R][1];
+    Step<C, 2 * R, 1> st;
+    const bool have = lane < nch;
+    if (have) step_load_w(st, rows, ex.gate.shift, opaque((uint32_t)lane));
+    constexpr bool sums = gu1_pairs<C, 2 * R>() && Codec<C>::OFFS != 0.f;
+    stage_x<Codec<C>::CW>(a, b, xs, sums);
+    dot_rows_lds1<C, 2 * R>(st, have, rows, nch, ex.gate.shift, xs, xs + x_lds_len<Codec<C>::CW, GROUP_XPAD>(a.H),
+                            acc);
     float gv = 0.f, uv = 0.f;
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int s = 0; s < SM; ++s) {
-            const float tg = wave_sum(acc[r][s]);
-            const float tu = wave_sum(acc[R + r][s]);
-            if (lane == r * SM + s) { gv = tg; uv = tu; }
-        }
-    const int r = lane / SM, s = lane % SM;
-    if (lane < R * SM && row0 + r < a.I && s < b.n) {
-        int slot = b.slot[0];
-#pragma unroll
-        for (int j = 1; j < SM; ++j)
-            if (s == j) slot = b.slot[j];
+    for (int r = 0; r < R; ++r) {
+        const float tg = wave_sum(acc[r][0]);
+        const float tu = wave_sum(acc[R + r][0]);
+        if (lane == r) { gv = tg; uv = tu; }
+    }
+    if (lane < R && row0 + lane < a.I) {
         float hv;
         if (a.act == ACT_SWIGLU_V4) {   // bf16 gate and up; the weighted activation to bf16
-            const float wr = slot < a.S * a.k ? a.w[slot] : 1.f;
+            const float wr = b.slot < a.S * a.k ? a.w[b.slot] : 1.f;
             hv = round_bf16(swiglu(round_bf16(gv), round_bf16(uv), a.limit) * wr);
         } else {
             hv = swiglu(gv, uv, a.limit);
         }
-        a.h[(size_t)slot * a.I + row0 + r] = hv;
+        a.h[(size_t)b.slot * a.I + row0 + lane] = hv;
     }
 }
 
-// Kernel A: grid (row blocks of I, units).  Clears the error flag.  CAP is
-// the largest token batch the launch needs (1 when S = 1), so that a
-// launch only carries the register footprint of the batches it can see.
-// The block stages each batch's x rows in LDS (CAP * H floats) once; its
-// waves read their slices from there.  Every wave of a block stays to the
-// end (block barriers), with rows past I clamped and their outputs dropped.
-template <int C, int R, int CAP>
+// Kernel A: grid (row blocks of I, units).  Clears the error flag.  The
+// block stages each slot's x row in LDS once; its waves read their slices
+// from there.  Every wave of a block stays to the end (block barriers),
+// with rows past I clamped and their outputs dropped.
+template <int C, int R>
 __device__ __forceinline__ void group_gate_up(const GroupArgs &a) {
     extern __shared__ float x_lds_raw[];
     lfloats_w xs = (lfloats_w)x_lds_raw;
     if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *a.flag = 0;
     // the shared expert's blocks (row y = 0) go first: with several tokens
-    // it serves a batch per token, and started last it would set the tail
+    // it serves a slot per token, and started last it would set the tail
     const int q = a.shared >= 0 ? (blockIdx.y == 0 ? (int)gridDim.y - 1 : (int)blockIdx.y - 1) : (int)blockIdx.y;
     const int nr = a.S * a.k;
     const int e = __builtin_amdgcn_readfirstlane(q < nr ? a.ids[q] : a.shared);
@@ -1205,51 +1122,37 @@ __device__ __forceinline__ void group_gate_up(const GroupArgs &a) {
     const int wave = blockIdx.x * (blockDim.x / WAVE) + wave_id();
     const int row0 = wave * R;   // rows past I are clamped in row_ptrs, outputs dropped
     const ExpertDev &ex = a.table[e];
-    for_slots<CAP>(a, q, e, [&](const SlotBatch &b) {
-        if (CAP == 1 || b.n == 1) group_gu_batch<C, R, 1>(a, ex, row0, b, xs);
-        else if (CAP == 2 || b.n == 2) group_gu_batch<C, R, 2>(a, ex, row0, b, xs);
-        else group_gu_batch<C, R, 4>(a, ex, row0, b, xs);
-    });
+    for_slots(a, q, e, [&](const SlotBatch &b) { group_gu_batch<C, R>(a, ex, row0, b, xs); });
 }
 
-template <int C, int R, int CAP>
-__global__ void __launch_bounds__(WAVE * WPB_A) k_group_gate_up(GroupArgs a) { group_gate_up<C, R, CAP>(a); }
+template <int C, int R>
+__global__ void __launch_bounds__(WAVE * WPB_A) k_group_gate_up(GroupArgs a) { group_gate_up<C, R>(a); }
 
-// The one-token form with a register budget of 5 waves per SIMD, so that a
-// 9-unit group (1152 blocks of 4 waves) is resident in one round on 256 CUs.
+// The same with a register budget of 5 waves per SIMD (every codec but
+// int3), so that a one-token 9-unit group (1152 blocks of 4 waves) is
+// resident in one round on 256 CUs.
 template <int C, int R>
 __global__ void __launch_bounds__(WAVE * WPB_A) __attribute__((amdgpu_waves_per_eu(5)))
-k_group_gate_up1(GroupArgs a) { group_gate_up<C, R, 1>(a); }
+k_group_gate_up1(GroupArgs a) { group_gate_up<C, R>(a); }
 
-// down rows row0.. of expert e applied to a batch of slots' h -> d (LDS)
-template <int C, int R, int SM>
+// down rows row0.. of expert e applied to one slot's h -> d (LDS)
+template <int C, int R>
 __device__ __forceinline__ void group_down_batch(const GroupArgs &a, const ExpertDev &ex, int row0,
                                                  const SlotBatch &b, float *d) {
     const int lane = threadIdx.x & (WAVE - 1);
     GRow rows[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) rows[r] = row_ptrs(ex.down, min(row0 + r, a.H - 1));
-    XGlobal xp[SM];
-#pragma unroll
-    for (int s = 0; s < SM; ++s) xp[s] = {gf(a.h + (size_t)b.slot[s] * a.I)};
-    float acc[R][SM];
-    dot_rows<C, R, SM>(rows, ex.down.K / Codec<C>::CW, ex.down.shift, xp, acc);
+    const XGlobal xp[1] = {{gf(a.h + (size_t)b.slot * a.I)}};
+    float acc[R][1];
+    dot_rows<C, R, 1>(rows, ex.down.K / Codec<C>::CW, ex.down.shift, xp, acc);
     float out = 0.f;
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int s = 0; s < SM; ++s) {
-            const float t = wave_sum(acc[r][s]);
-            if (lane == r * SM + s) out = t;
-        }
-    const int r = lane / SM, s = lane % SM;
-    if (lane < R * SM && s < b.n) {
-        int slot = b.slot[0];
-#pragma unroll
-        for (int j = 1; j < SM; ++j)
-            if (s == j) slot = b.slot[j];
-        d[slot * R + r] = a.act == ACT_SWIGLU_V4 ? round_bf16(out) : out;
+    for (int r = 0; r < R; ++r) {
+        const float t = wave_sum(acc[r][0]);
+        if (lane == r) out = t;
     }
+    if (lane < R) d[b.slot * R + lane] = a.act == ACT_SWIGLU_V4 ? round_bf16(out) : out;
 }
 
 template <int R>
@@ -1262,7 +1165,7 @@ __device__ __forceinline__ void group_combine(const GroupArgs &a, float *d, int 
 // blocks share a CU; blocks of 9 or more waves were measured to hold one).
 constexpr int DOWN_MAX_WAVES = 8;
 
-template <int C, int R, int CAP>
+template <int C, int R>
 __device__ __forceinline__ void group_down(const GroupArgs &a) {
     extern __shared__ float d[];
     const int row0 = blockIdx.x * R;
@@ -1282,22 +1185,11 @@ __device__ __forceinline__ void group_down(const GroupArgs &a) {
         }
         const ExpertDev &ex = a.table[e];
         if (q >= nr) {   // token q - nr's shared slot
-            SlotBatch b;
-            b.n = 1;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                b.slot[j] = q;
-                b.token[j] = q - nr;
-            }
-            group_down_batch<C, R, 1>(a, ex, row0, b, d);
+            group_down_batch<C, R>(a, ex, row0, SlotBatch{q, q - nr}, d);
             continue;
         }
         if (!owns(a.ids, q, e)) continue;
-        for_slots<CAP>(a, q, e, [&](const SlotBatch &b) {
-            if (CAP == 1 || b.n == 1) group_down_batch<C, R, 1>(a, ex, row0, b, d);
-            else if (CAP == 2 || b.n == 2) group_down_batch<C, R, 2>(a, ex, row0, b, d);
-            else group_down_batch<C, R, 4>(a, ex, row0, b, d);
-        });
+        for_slots(a, q, e, [&](const SlotBatch &b) { group_down_batch<C, R>(a, ex, row0, b, d); });
     }
     group_combine<R>(a, d, row0);
 }
@@ -1342,8 +1234,8 @@ __device__ __forceinline__ void group_combine(const GroupArgs &a, float *d, int 
     }
 }
 
-template <int C, int R, int CAP>
-__global__ void __launch_bounds__(WAVE * DOWN_MAX_WAVES) k_group_down(GroupArgs a) { group_down<C, R, CAP>(a); }
+template <int C, int R>
+__global__ void __launch_bounds__(WAVE * DOWN_MAX_WAVES) k_group_down(GroupArgs a) { group_down<C, R>(a); }
 
 // Kernel B for one token with a shared expert and 6 to 8 routed ones (a
 // decode step), on blocks of R = 24 rows and 2k waves: waves 2r and 2r + 1
@@ -2190,27 +2082,32 @@ hipError_t dequant_c(const MatDev &m, float *out, hipStream_t st) {
 }
 
 
-template <int C, int CAP>
-hipError_t group_a_cap(const GroupArgs &a, hipStream_t st) {
+// Both launches take one slot at a time, at every S: tokens that share an
+// expert take further passes over its rows, which the caches then serve.
+// (Beyond one token most units serve one slot; 2-slot batches cost the
+// gate/up launch its one-token register and LDS budget, 3 waves a SIMD
+// against 5: measured on MI355X, int4-g32 group, gate/up 54.2 -> 51.2 us at
+// 2 tokens and 108.8 -> 93.6 us at 4 with the shared expert's blocks first.)
+template <int C>
+hipError_t group_a(const GroupArgs &a, hipStream_t st) {
     const int units = a.S * a.k + (a.shared >= 0 ? 1 : 0);
     const int rows_per_block = RA * WPB_A;
-    // CAP rows of x; a one-token batch keeps the chunk sums of x after its row
-    const size_t lds = ((size_t)CAP * x_lds_len<Codec<C>::CW, GROUP_XPAD>(a.H) +
-                        (CAP == 1 ? (size_t)a.H / Codec<C>::CW : 0)) * sizeof(float);
+    // the slot's row of x, and the chunk sums of x after it
+    const size_t lds = ((size_t)x_lds_len<Codec<C>::CW, GROUP_XPAD>(a.H) + (size_t)a.H / Codec<C>::CW) * sizeof(float);
     dim3 grid((a.I + rows_per_block - 1) / rows_per_block, units);
-    if constexpr (CAP == 1 && C != C_I3)
+    if constexpr (C != C_I3)
         launch("group_gate_up", (k_group_gate_up1<C, RA>), grid, dim3(WAVE * WPB_A), lds, st, a);
     else
-        launch("group_gate_up", (k_group_gate_up<C, RA, CAP>), grid, dim3(WAVE * WPB_A), lds, st, a);
+        launch("group_gate_up", (k_group_gate_up<C, RA>), grid, dim3(WAVE * WPB_A), lds, st, a);
     return hipGetLastError();
 }
 
-template <int C, int CAP>
-hipError_t group_b_cap(const GroupArgs &a, hipStream_t st) {
+template <int C>
+hipError_t group_b(const GroupArgs &a, hipStream_t st) {
     const int units = a.S * a.k + (a.shared >= 0 ? a.S : 0);   // each shared slot a unit
     const int slots = a.S * a.k + (a.shared >= 0 ? a.S : 0);
     const size_t v4_lds = a.act == ACT_SWIGLU_V4 ? 2 * (size_t)a.S * a.k * sizeof(int) : 0;
-    if constexpr (CAP == 1 && C != C_I3) {
+    if constexpr (C != C_I3) {
         if (a.S == 1 && a.shared >= 0 && a.k >= 6 && a.k <= 8 && a.I == WAVE * Codec<C>::CW &&
             (long)(a.k + 1) * a.I / 4 <= (long)SPLIT_HN * WAVE * 2 * a.k) {
             dim3 grid((a.H + SPLIT_R - 1) / SPLIT_R);
@@ -2223,22 +2120,9 @@ hipError_t group_b_cap(const GroupArgs &a, hipStream_t st) {
     dim3 grid((a.H + RB - 1) / RB);
     // the slots' outputs; DeepSeek V4's combine adds the ids and their order
     const size_t lds = (size_t)slots * RB * sizeof(float) + v4_lds;
-    launch("group_down", (k_group_down<C, RB, CAP>), grid, dim3(WAVE * waves), lds, st, a);
+    launch("group_down", (k_group_down<C, RB>), grid, dim3(WAVE * waves), lds, st, a);
     return hipGetLastError();
 }
-
-// Batch capacity: one slot at a time in both launches, at every S.  Tokens
-// that share an expert take further passes over its rows, which the caches
-// then serve.  (Beyond one token most units serve one slot; 2-slot batches
-// cost the gate/up launch its one-token register and LDS budget, 3 waves a
-// SIMD against 5: measured on MI355X, int4-g32 group, gate/up 54.2 -> 51.2 us
-// at 2 tokens and 108.8 -> 93.6 us at 4 with the shared expert's blocks
-// first.)
-template <int C>
-hipError_t group_a(const GroupArgs &a, hipStream_t st) { return group_a_cap<C, 1>(a, st); }
-
-template <int C>
-hipError_t group_b(const GroupArgs &a, hipStream_t st) { return group_b_cap<C, 1>(a, st); }
 
 // Calls f(std::integral_constant<int, C>) for the codec of a run-time id.
 template <typename F>
