@@ -630,8 +630,9 @@ def bench_stream(args):
 
     One pass over a 4.25 GiB buffer per launch (the long-stream ceiling),
     then reads of the byte counts of this library's launches (the dense
-    int4-g32 6144 x 6144 matrix, and the int4-g32 group's down launch,
-    gate/up launch and whole call at one token), each launch at its own
+    int4-g32 6144 x 6144 matrix, the int4-g32 group's down launch, gate/up
+    launch and whole call at one token, and the two launches of one int4-g32
+    expert of H 6144, I 2048), each launch at its own
     offset so that the Infinity Cache cannot serve it.  HIP events on every
     launch give its duration.
     """
@@ -646,7 +647,8 @@ def bench_stream(args):
     sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     torch.cuda.synchronize()
     sizes = {"whole_buffer": total, "gemv_int4g32_6144x6144": 23642112, "group_int4g32_down": 70778880,
-             "group_int4g32_gate_up": 141557760, "group_int4g32_call": 212336640}
+             "group_int4g32_gate_up": 141557760, "group_int4g32_call": 212336640,
+             "expert_int4g32_gate_up": 15728640, "expert_int4g32_down": 7864320}
     results = {}
     for name, n in sizes.items():
         n = n // 1024 * 1024

@@ -835,20 +835,27 @@ __global__ void __launch_bounds__(256) k_rows_lds(MatDev m0, MatDev m1, const fl
 // registers; more, or int3: step_compute_lds).  The per-row arithmetic and the order
 // of steps are k_rows_lds's, so the bits are the same.
 constexpr int GX_W = 12, GX_R = 2;
+// Matrices of fewer rows take blocks of 8 waves x 1 row, so that 2048 rows
+// still make 256 blocks.
+constexpr int GXS_W = 8, GXS_R = 1;
+constexpr int GX_WIDE_ROWS = 256 * GX_W * GX_R;   // the wide shape from this many rows up
 
-template <int C, int SM, bool GU, int NS>
-__global__ void __launch_bounds__(WAVE * GX_W) k_rows_x(MatDev m0, MatDev m1, const float *__restrict__ x, int S,
-                                                       float *__restrict__ y, float L) {
+// The body of k_rows_x for blocks of W waves x R rows (GU: R rows of m0 and
+// the same rows of m1).  epi(s, row, v, vu) takes token s's dot product of
+// row (and of m1's row with GU), for rows below m0.O and s below S.
+template <int C, int SM, bool GU, int NS, int W, int R, typename Epi>
+__device__ __forceinline__ void rows_x_body(const MatDev &m0, const MatDev &m1, const float *__restrict__ x, int S,
+                                            Epi &&epi) {
     extern __shared__ float xl_raw[];
     lfloats_w xs = (lfloats_w)xl_raw;
     using Cd = Codec<C>;
-    constexpr int R = GX_R, NR = GU ? 2 * R : R;
+    constexpr int NR = GU ? 2 * R : R;
     constexpr int K = NS * WAVE * Cd::CW;                     // m0.K (checked by the launcher)
-    constexpr uint32_t k4n = K / 4, n4 = SM * k4n, nt = WAVE * GX_W, XN = (n4 + nt - 1) / nt;
+    constexpr uint32_t k4n = K / 4, n4 = SM * k4n, nt = WAVE * W, XN = (n4 + nt - 1) / nt;
     constexpr uint32_t xl = (uint32_t)x_lds_len<Cd::CW>(K);
     const MatDev &m = m0;
     const int lane = threadIdx.x & (WAVE - 1);
-    const int row0 = (blockIdx.x * GX_W + wave_id()) * R;
+    const int row0 = (blockIdx.x * W + wave_id()) * R;
     // x of every token (a second token past S repeats the first; its outputs are dropped)
     f32x4 xv4[XN];
 #pragma unroll
@@ -875,11 +882,10 @@ __global__ void __launch_bounds__(WAVE * GX_W) k_rows_x(MatDev m0, MatDev m1, co
         *(LDS f32x4 *)(xs + sl * xl + x_lds_at<Cd::CW>(4 * k4)) = xv4[u];
     }
     __syncthreads();
-    // one token, codes with an offset: each chunk's sum of x, summed once per
-    // block in step_compute's order, after the row
     // one token with a chunk of at most 32 inputs takes the step's x in
-    // registers (and the chunk sums of x once per block); int3's 64-input
-    // chunks read x per decode unit from LDS like several tokens do
+    // registers (and, for codes with an offset, each chunk's sum of x, summed
+    // once per block in step_compute's order, after the row); int3's
+    // 64-input chunks read x per decode unit from LDS like several tokens do
     constexpr bool XREG = SM == 1 && Cd::CW <= 32;
     constexpr bool XSUM = XREG && Cd::OFFS != 0.f;
     lfloats_w xsums = xs + xl;
@@ -932,8 +938,15 @@ __global__ void __launch_bounds__(WAVE * GX_W) k_rows_x(MatDev m0, MatDev m1, co
             if (lane == r * SM + s) { out = t; outu = tu; }
         }
     const int r = lane / SM, s = lane % SM;
-    if (lane < R * SM && row0 + r < m.O && s < S)
-        y[(size_t)s * m.O + row0 + r] = GU ? swiglu(out, outu, L) : out;
+    if (lane < R * SM && row0 + r < m.O && s < S) epi(s, row0 + r, out, outu);
+}
+
+template <int C, int SM, bool GU, int NS, int W, int R>
+__global__ void __launch_bounds__(WAVE * W) k_rows_x(MatDev m0, MatDev m1, const float *__restrict__ x, int S,
+                                                     float *__restrict__ y, float L) {
+    rows_x_body<C, SM, GU, NS, W, R>(m0, m1, x, S, [&](int s, int row, float v, float vu) {
+        y[(size_t)s * m0.O + row] = GU ? swiglu(v, vu, L) : v;
+    });
 }
 
 // ---------------------------------------------------------------------------
@@ -1063,6 +1076,16 @@ __device__ __forceinline__ void stage_x(const GroupArgs &a, const SlotBatch &b, 
     }
 }
 
+// The experts' activation of one slot's gate and up outputs, as the gate/up
+// launch writes it to h.
+__device__ __forceinline__ float group_act(const GroupArgs &a, int slot, float gv, float uv) {
+    if (a.act == ACT_SWIGLU_V4) {   // bf16 gate and up; the weighted activation to bf16
+        const float wr = slot < a.S * a.k ? a.w[slot] : 1.f;
+        return round_bf16(swiglu(round_bf16(gv), round_bf16(uv), a.limit) * wr);
+    }
+    return swiglu(gv, uv, a.limit);
+}
+
 // gate_up of R rows (row0..) of expert e for one slot, x from LDS.  The
 // first chunk's weights are requested before x is staged.
 template <int C, int R>
@@ -1091,16 +1114,7 @@ __device__ __forceinline__ void group_gu_batch(const GroupArgs &a, const ExpertD
         const float tu = wave_sum(acc[R + r][0]);
         if (lane == r) { gv = tg; uv = tu; }
     }
-    if (lane < R && row0 + lane < a.I) {
-        float hv;
-        if (a.act == ACT_SWIGLU_V4) {   // bf16 gate and up; the weighted activation to bf16
-            const float wr = b.slot < a.S * a.k ? a.w[b.slot] : 1.f;
-            hv = round_bf16(swiglu(round_bf16(gv), round_bf16(uv), a.limit) * wr);
-        } else {
-            hv = swiglu(gv, uv, a.limit);
-        }
-        a.h[(size_t)b.slot * a.I + row0 + lane] = hv;
-    }
+    if (lane < R && row0 + lane < a.I) a.h[(size_t)b.slot * a.I + row0 + lane] = group_act(a, b.slot, gv, uv);
 }
 
 // Kernel A: grid (row blocks of I, units).  Clears the error flag.  The
@@ -1236,6 +1250,39 @@ __device__ __forceinline__ void group_combine(const GroupArgs &a, float *d, int 
 
 template <int C, int R>
 __global__ void __launch_bounds__(WAVE * DOWN_MAX_WAVES) k_group_down(GroupArgs a) { group_down<C, R>(a); }
+
+// One token routed to one expert, no shared expert (a single expert MLP):
+// the group's two launches on k_rows_x's block shape, whose blocks fill the
+// chip where one unit's group blocks (I/16 of them) leave most CUs idle.
+// The per-row arithmetic, the activation and the combine (the one slot's
+// weight times its output, or with DeepSeek V4's activation 0 plus the
+// output rounded to bf16) are the group kernels', so the bits are theirs.
+template <int C, int NS, int W, int R>
+__global__ void __launch_bounds__(WAVE * W) k_unit_gate_up(GroupArgs a) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) *a.flag = 0;
+    const int e = __builtin_amdgcn_readfirstlane(a.ids[0]);
+    if (e < 0 || e >= a.n_experts) return;   // reported by the down launch
+    const MatDev g = a.table[e].gate, u = a.table[e].up;
+    rows_x_body<C, 1, true, NS, W, R>(g, u, a.x, 1,
+                                      [&](int, int row, float gv, float uv) { a.h[row] = group_act(a, 0, gv, uv); });
+}
+
+template <int C, int NS, int W, int R>
+__global__ void __launch_bounds__(WAVE * W) k_unit_down(GroupArgs a) {
+    const int e = __builtin_amdgcn_readfirstlane(a.ids[0]);
+    if (e < 0 || e >= a.n_experts) {   // NaN outputs, and the call reports the id
+        const int row = blockIdx.x * W * R + (int)threadIdx.x;
+        if ((int)threadIdx.x < W * R && row < a.H) a.y[row] = __int_as_float(0x7FC00000);
+        if (threadIdx.x == 0) *a.flag = 1;
+        return;
+    }
+    const MatDev d = a.table[e].down;
+    const float w0 = a.w[0];
+    const bool v4 = a.act == ACT_SWIGLU_V4;
+    rows_x_body<C, 1, false, NS, W, R>(d, d, a.h, 1, [&](int, int row, float v, float) {
+        a.y[row] = v4 ? 0.f + round_bf16(v) : fmaf(w0, v, 0.f);
+    });
+}
 
 // Kernel B for one token with a shared expert and 6 to 8 routed ones (a
 // decode step), on blocks of R = 24 rows and 2k waves: waves 2r and 2r + 1
@@ -2004,13 +2051,25 @@ bool rows_x_fits(int K, int S) {
     return S <= (C == C_I3 ? 1 : 4) && K % unit == 0 && K / unit <= 4;
 }
 
+// Bytes of LDS k_rows_x takes: x of SM tokens, and with one token the
+// chunk sums of x.
+template <int C, int SM>
+size_t rows_x_lds(int K) {
+    return ((size_t)SM * x_lds_len<Codec<C>::CW>(K) + (SM == 1 ? K / Codec<C>::CW : 0)) * 4;
+}
+
 template <int C, int SM, bool GU, int NS>
 hipError_t go_rows_x(const MatDev &g, const MatDev &u, const float *x, int S, float *y, float L, hipStream_t st,
                      const char *name) {
-    dim3 grid((g.O + GX_W * GX_R - 1) / (GX_W * GX_R));
-    const size_t lds = ((size_t)SM * x_lds_len<Codec<C>::CW>(g.K) + (SM == 1 ? g.K / Codec<C>::CW : 0)) * 4;
+    const size_t lds = rows_x_lds<C, SM>(g.K);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
-    launch(name, (k_rows_x<C, SM, GU, NS>), grid, dim3(WAVE * GX_W), lds, st, g, u, x, S, y, L);
+    if (g.O >= GX_WIDE_ROWS) {
+        launch(name, (k_rows_x<C, SM, GU, NS, GX_W, GX_R>), dim3((g.O + GX_W * GX_R - 1) / (GX_W * GX_R)),
+               dim3(WAVE * GX_W), lds, st, g, u, x, S, y, L);
+    } else {
+        launch(name, (k_rows_x<C, SM, GU, NS, GXS_W, GXS_R>), dim3((g.O + GXS_W * GXS_R - 1) / (GXS_W * GXS_R)),
+               dim3(WAVE * GXS_W), lds, st, g, u, x, S, y, L);
+    }
     return hipGetLastError();
 }
 
@@ -2082,6 +2141,40 @@ hipError_t dequant_c(const MatDev &m, float *out, hipStream_t st) {
 }
 
 
+// One token, one routed expert, no shared expert, and K (H for gate/up, I
+// for down) of k_rows_x's shapes: the unit kernels.
+template <int C>
+bool unit_fits(const GroupArgs &a, int K) {
+    return a.S == 1 && a.k == 1 && a.shared < 0 && rows_x_fits<C>(K, 1) && rows_x_lds<C, 1>(K) <= 160 * 1024;
+}
+
+template <int C, bool GU, int NS, int W, int R>
+hipError_t go_unit(const GroupArgs &a, hipStream_t st) {
+    const int O = GU ? a.I : a.H, K = GU ? a.H : a.I;
+    const dim3 grid((O + W * R - 1) / (W * R)), block(WAVE * W);
+    if constexpr (GU)
+        launch("group_gate_up", (k_unit_gate_up<C, NS, W, R>), grid, block, rows_x_lds<C, 1>(K), st, a);
+    else
+        launch("group_down", (k_unit_down<C, NS, W, R>), grid, block, rows_x_lds<C, 1>(K), st, a);
+    return hipGetLastError();
+}
+
+template <int C, bool GU, int NS>
+hipError_t unit_shape(const GroupArgs &a, hipStream_t st) {
+    if ((GU ? a.I : a.H) >= GX_WIDE_ROWS) return go_unit<C, GU, NS, GX_W, GX_R>(a, st);
+    return go_unit<C, GU, NS, GXS_W, GXS_R>(a, st);
+}
+
+template <int C, bool GU>
+hipError_t unit_launch(const GroupArgs &a, hipStream_t st) {
+    switch ((GU ? a.H : a.I) / (WAVE * Codec<C>::CW)) {
+    case 1: return unit_shape<C, GU, 1>(a, st);
+    case 2: return unit_shape<C, GU, 2>(a, st);
+    case 3: return unit_shape<C, GU, 3>(a, st);
+    default: return unit_shape<C, GU, 4>(a, st);
+    }
+}
+
 // Both launches take one slot at a time, at every S: tokens that share an
 // expert take further passes over its rows, which the caches then serve.
 // (Beyond one token most units serve one slot; 2-slot batches cost the
@@ -2090,6 +2183,7 @@ hipError_t dequant_c(const MatDev &m, float *out, hipStream_t st) {
 // 2 tokens and 108.8 -> 93.6 us at 4 with the shared expert's blocks first.)
 template <int C>
 hipError_t group_a(const GroupArgs &a, hipStream_t st) {
+    if (unit_fits<C>(a, a.H)) return unit_launch<C, true>(a, st);
     const int units = a.S * a.k + (a.shared >= 0 ? 1 : 0);
     const int rows_per_block = RA * WPB_A;
     // the slot's row of x, and the chunk sums of x after it
@@ -2104,6 +2198,7 @@ hipError_t group_a(const GroupArgs &a, hipStream_t st) {
 
 template <int C>
 hipError_t group_b(const GroupArgs &a, hipStream_t st) {
+    if (unit_fits<C>(a, a.I)) return unit_launch<C, false>(a, st);
     const int units = a.S * a.k + (a.shared >= 0 ? a.S : 0);   // each shared slot a unit
     const int slots = a.S * a.k + (a.shared >= 0 ? a.S : 0);
     const size_t v4_lds = a.act == ACT_SWIGLU_V4 ? 2 * (size_t)a.S * a.k * sizeof(int) : 0;

@@ -8,6 +8,7 @@ h itself within 1e-5 of its first-order error reach; and, as a second check,
 the oracle's whole group with that reach carried through down.
 """
 import gc
+import math
 
 import numpy as np
 import pytest
@@ -282,6 +283,49 @@ def test_group_multi_token_down(case):
     assert ei.value.code == -7
     yh = host(y)
     assert np.all(np.isnan(yh[S - 1])) and np.all(np.isfinite(yh[:S - 1]))
+    table.close()
+
+
+# One token routed to one expert with no shared expert (a single expert
+# MLP), H and I whole multiples of 64 code chunks (1 to 4 of them per lane):
+# the group's unit launches, whose bits must be those of the general group
+# launches (a batch of two tokens, one expert each).  H = 8192 leaves the
+# down launch's last 24-row block ragged; int4 down at I = 1024 takes the
+# general down launch after the unit gate/up launch.
+UNIT_CASES = [  # gate/up format and group size, down's, H, I
+    (4, 32, 4, 32, 2048, 2048), (4, 32, 4, 32, 8192, 2048), (4, 32, 4, 32, 6144, 1024),
+    (7, 32, 7, 32, 6144, 2048), (5, 64, 4, 32, 4096, 2048), (1, None, 12, None, 3072, 1024),
+    (13, 64, 13, 64, 4096, 1024), (11, None, 14, None, 1024, 512), (10, None, 10, None, 1024, 256),
+]
+
+
+@pytest.mark.parametrize("case", UNIT_CASES, ids=lambda c: f"fmt{c[0]}_down{c[2]}_H{c[4]}_I{c[5]}")
+def test_group_single_expert(case):
+    fmt, gs, dfmt, dgs, H, I = case
+    seed = 5100 + UNIT_CASES.index(case)
+    hs, table = _small_group(3, fmt=fmt, gs=gs, H=H, I=I, seed=seed, down_fmt=dfmt, down_gs=dgs)
+    ids = np.array([[2], [0]], np.int32)
+    w = np.array([[0.6180339], [1.0]], np.float32)
+    x = synth.activations(2, H, seed)
+    y1 = [check_group(hs, table, ids[t:t + 1], w[t:t + 1], None, x[t:t + 1], f"single expert {case} token {t}")[0]
+          for t in range(2)]
+    yb = host(dq.dqg_expert_group(table, dev_i32(ids), dev_f32(w), None, dev_f32(x)))
+    for t in range(2):
+        assert bits_equal(yb[t], y1[t][0]), (case, t)
+    if case == UNIT_CASES[0]:
+        table.set_swiglu_limit(0.5)
+        check_group(hs, table, ids[:1], w[:1], None, x[:1], f"single expert {case} limit 0.5", limit=0.5)
+        table.set_swiglu_limit(math.inf)
+    # a bad id: every output NaN, and the call reports it; the next call clears the flag
+    ticket, y, _ = dq.dqg_expert_group_issue(table, dev_i32(np.array([[7]], np.int32)), dev_f32(w[:1]), None,
+                                             dev_f32(x[:1]))
+    with pytest.raises(dq.DqgError) as ei:
+        dq.dqg_expert_group_take(ticket)
+    assert ei.value.code == -7
+    assert np.all(np.isnan(host(y)))
+    ticket, y, _ = dq.dqg_expert_group_issue(table, dev_i32(ids[:1]), dev_f32(w[:1]), None, dev_f32(x[:1]))
+    dq.dqg_expert_group_take(ticket)
+    assert bits_equal(host(y)[0], y1[0][0])
     table.close()
 
 

@@ -4,7 +4,8 @@ through the C ABI.
 
 It takes K of one to four whole steps of 64 code chunks, so the shapes below
 set K = n * 64 * (inputs per chunk) for n = 1..4 in every format (int3 at one
-token only), with row counts ragged against its 24-row blocks.  Bars as for the other
+token only), with row counts ragged against its blocks (8 rows below 6144
+rows, 24 from there up).  Bars as for the other
 matmul tests: every output within 1e-5 of its row's normaliser, and a
 token's bits the same alone and inside a batch of 8 (which takes the
 general per-row kernel).
@@ -37,6 +38,8 @@ def _announce(request):
 CHUNK = {1: (16, None), 2: (32, None), 4: (32, 32), 5: (64, 64), 7: (32, 32), 10: (4, None), 11: (8, None),
          12: (16, None), 13: (16, 64), 14: (8, None)}
 CASES = [(fmt, n, O) for fmt in CHUNK for n, O in ((1, 37), (2, 24), (3, 61), (4, 5))]
+# from 6144 rows up the blocks are 12 waves x 2 rows; these leave the last block ragged
+CASES += [(4, 1, 6161), (7, 2, 6150), (1, 3, 6170), (5, 1, 6151), (11, 4, 6145), (13, 4, 6157)]
 IDS = [f"fmt{f}_steps{n}_O{o}" for f, n, o in CASES]
 
 

@@ -189,6 +189,35 @@ def test_v4_group_full_size():
     table.close()
 
 
+@pytest.mark.parametrize("limit", [math.inf, 7.0])
+def test_v4_single_expert(limit):
+    """One token routed to one expert with no shared expert (the group's unit launches), H 2048,
+    I 2048, route weight 0.75: h within the oracle's bf16 bounds and bit for bit where they
+    coincide, y within [y_lo, y_hi]."""
+    E, H, I = 4, 2048, 2048
+    hs = [synth.expert(synth.FMT_MXFP4, H, I, 32, 9970, i, scale_kind="pow2_small") for i in range(E)]
+    x = synth.activations_e4m3_grid(1, H, 9971, 1)
+    ids, w = np.array([[2]], np.int32), np.array([[0.75]], np.float32)
+    _exact_inputs(hs, x, H)
+    r = oracle.expert_group_v4(hs, ids, w, None, x, limit, 0.0, ACT_REL, (48 + -(-I // 2048)) * 2.0 ** -24)
+    table = dq.ExpertTable([dq.Expert.upload(h) for h in hs])
+    table.set_activation(dq.DQG_ACT_SWIGLU_V4)
+    if not math.isinf(limit):
+        table.set_swiglu_limit(limit)
+    scratch = table.scratch(1, 1)
+    y = host(dq.dqg_expert_group(table, dev_i32(ids), dev_f32(w), None, dev_f32(x), scratch=scratch))
+    hdev = host(scratch[H_OFFSET: H_OFFSET + I * 4].view(torch.float32)).reshape(1, I).astype(np.float64)
+    lo, hi = r["h_lo"][:1], r["h_hi"][:1]
+    fixed = lo == hi
+    assert np.array_equal(hdev[fixed], r["h"][:1][fixed])
+    assert np.all((hdev >= lo) & (hdev <= hi))
+    out = (y < r["y_lo"]) | (y > r["y_hi"]) | np.isnan(y)
+    assert not out.any(), f"{int(out.sum())} of {y.size} outside [y_lo, y_hi]"
+    log(f"  {r['open']} open decisions; h: {int(fixed.sum())} of {fixed.size} fixed; "
+        f"y: {int(np.sum(r['y_lo'] == r['y_hi']))} of {y.size} pinned")
+    table.close()
+
+
 @pytest.mark.parametrize("S", [1, 2])
 @pytest.mark.parametrize("act", ["swiglu", "v4"])
 def test_group_graph_capture_replays(act, S):
