@@ -151,54 +151,75 @@ __device__ __forceinline__ float fma_hi(uint32_t pair, float x, float acc) {
 
 // ---------------------------------------------------------------------------
 // Codecs.  A chunk is the 16 bytes of codes (plus 8 of high plane for int3)
-// one lane reads per step, covering CW inputs.  decode(ch, u, pr) turns the
-// UW codes of unit u into UW/2 pairs of f16 bit patterns; half h of pair p
-// multiplies x[unit base + IDX[2p + h]].
+// one lane reads per step, covering CW inputs.  Unit u of a chunk is inputs
+// u * UW .. u * UW + UW - 1; the products of a unit are summed in the order
+// IDX gives (a codec's natural decode order), in every kernel alike.
 //
-// The f16 patterns are exact multiples of the weight values:
-//  - a non-negative integer code n below 1024 placed in the low bits of an
-//    f16 is the subnormal n * 2^-24 (int8 read as offset binary n = q + 128,
-//    int4 nibbles, int3 codes);
-//  - an e2m1 code with its three magnitude bits at f16 bits 9..11 and its
-//    sign at bit 15 is e2m1 * 2^-14, subnormal case included, because both
-//    formats put the implicit one and the exponent bias in the same places.
-// So weight = (pattern - OFF * 2^-24) * VMUL with VMUL a power of two that
-// folds into the scale; f16 and f32 denormals are kept (IEEE mode).
+// WIDE codecs decode to f32 values, decode_f(ch, u, v): v[i] multiplies
+// x[unit base + IDX[i]], with plain f32 FMAs:
+//  - int8 (read as offset binary n = q + 128) and int3 give the code
+//    itself as a float, byte by byte with v_cvt_f32_ubyte0..3 after the
+//    codes are spread one a byte;
+//  - MXFP4 converts pairs of e2m1 codes with v_cvt_scalef32_pk_f32_fp4 at
+//    scale 1, E4M3 pairs with v_cvt_pk_f32_fp8, bf16 and f32 by bit moves.
+// All of these are exact, so weight = (value - OFFS) * VMUL * scale.
+// On MI355X v_fmac_f32 issues at about 1.5 times the rate of v_fma_mix_f32
+// (an f16 operand converted inside the FMA), so converting each code once
+// and using plain FMAs pays the more tokens share a conversion.
 //
-// WIDE codecs (f32, bf16 and E4M3 rows) decode to f32 values instead,
-// decode_f(ch, u, v): v[i] multiplies x[unit base + i], with plain f32 FMAs.
+// The non-WIDE codecs hand decode(ch, u, pr) UW/2 pairs of f16s; half h of
+// pair p multiplies x[unit base + IDX[2p + h]] through v_fma_mix_f32 (exact
+// f16 -> f32 inside the FMA): f16 rows as they stand, and int4 codes as the
+// f16 subnormals n * 2^-24 at one token (a mixed FMA and a cheap pair
+// decode beat a conversion and an FMA a product there, measured on the
+// one-token expert group); int4 also has decode_f, the same values as f32,
+// for several tokens.
+//
 // SCALED is false for the formats without scales (f32, bf16, f16 rows):
-// their scale is the constant 1 and no scale is read.
+// their scale is the constant 1 and no scale is read.  f32 denormals are
+// kept (IEEE mode).
 // ---------------------------------------------------------------------------
 template <int C>
 struct Codec;
 
+// The float value of byte B of w (v_cvt_f32_ubyteB).  w must come from
+// opaque() so that the compiler does not fold a mask that made w into a
+// bit-field extract ahead of the conversion.
+template <int B>
+__device__ __forceinline__ float ubyte_f(uint32_t w) {
+    return (float)((w >> (8 * B)) & 0xFFu);
+}
+
 // int8 rows: byte = two's complement q; q ^ 0x80 = q + 128 as an unsigned
-// byte; v_perm drops bytes into the low byte of each f16 half.
+// byte (offset binary), converted byte by byte.
 template <>
 struct Codec<C_I8> {
     static constexpr int CW = 16, UNITS = 4, UW = 4;
-    static constexpr bool WIDE = false, SCALED = true;
-    static constexpr float VMUL = 16777216.f, OFFS = 128.f / 16777216.f;
+    static constexpr bool F32DEC = false, WIDE = true, SCALED = true;
+    static constexpr float VMUL = 1.f, OFFS = 128.f;
     static constexpr int IDX[UW] = {0, 2, 1, 3};
     struct Chunk { uint32_t w[4]; };
     __device__ static Chunk load(const GRow &r, uint32_t c) {
         uint4 v = ld16(r.q, c * 16u);
         return {{v.x, v.y, v.z, v.w}};
     }
-    __device__ static void decode(const Chunk &ch, int u, uint32_t (&pr)[UW / 2]) {
-        const uint32_t w = ch.w[u] ^ 0x80808080u;
-        pr[0] = __builtin_amdgcn_perm(0u, w, 0x0C020C00u);   // inputs 0, 2
-        pr[1] = __builtin_amdgcn_perm(0u, w, 0x0C030C01u);   // inputs 1, 3
+    __device__ static void decode_f(const Chunk &ch, int u, float (&v)[UW]) {
+        const uint32_t w = opaque(ch.w[u] ^ 0x80808080u);
+        v[0] = ubyte_f<0>(w); v[1] = ubyte_f<2>(w); v[2] = ubyte_f<1>(w); v[3] = ubyte_f<3>(w);
     }
 };
 
-// int4 pairs: nibble i of word u is input 8u + i; pair j = nibbles j, j+4,
-// which sit at the same offset of the two 16-bit halves.
+// int4: nibble i of word u is input 8u + i, decoded two ways with the same
+// values:
+//  - decode: pairs j = nibbles j, j+4 (they sit at the same offset of the
+//    two 16-bit halves) as f16 subnormals n * 2^-24, for v_fma_mix_f32;
+//  - decode_f: the same n * 2^-24 as f32 (one mask keeps the even nibbles,
+//    one a byte, a shift and the same mask the odd ones; v_cvt_f32_ubyte;
+//    an exact scaling), for several tokens, which share each conversion.
 template <>
 struct Codec<C_I4> {
     static constexpr int CW = 32, UNITS = 4, UW = 8;
-    static constexpr bool WIDE = false, SCALED = true;
+    static constexpr bool WIDE = false, F32DEC = true, SCALED = true;
     static constexpr float VMUL = 16777216.f, OFFS = 8.f / 16777216.f;
     static constexpr int IDX[UW] = {0, 4, 1, 5, 2, 6, 3, 7};
     struct Chunk { uint32_t w[4]; };
@@ -215,31 +236,38 @@ struct Codec<C_I4> {
         // packed 16-bit shift and no mask
         pr[3] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(u16x2, w) >> (unsigned short)12);
     }
+    __device__ static void decode_f(const Chunk &ch, int u, float (&v)[UW]) {
+        const uint32_t w = ch.w[u];
+        const uint32_t ev = opaque(w & 0x0F0F0F0Fu);          // nibbles 0, 2, 4, 6
+        const uint32_t od = opaque((w >> 4) & 0x0F0F0F0Fu);   // nibbles 1, 3, 5, 7
+        v[0] = ubyte_f<0>(ev); v[1] = ubyte_f<2>(ev); v[2] = ubyte_f<0>(od); v[3] = ubyte_f<2>(od);
+        v[4] = ubyte_f<1>(ev); v[5] = ubyte_f<3>(ev); v[6] = ubyte_f<1>(od); v[7] = ubyte_f<3>(od);
+#pragma unroll
+        for (int i = 0; i < UW; ++i) v[i] *= 0x1p-24f;
+    }
 };
 
-// MXFP4: e2m1 nibbles in int4 order.  The f16 high byte of code c is
-// ((c & 7) << 1) | ((c & 8) << 4); it is built for the four even and four
-// odd codes of a word at once, then v_perm pairs each even code with the
-// next odd one over zero low bytes.
+// MXFP4: e2m1 codes in int4 order (nibble i of word u is input 8u + i, the
+// sign in bit 3), two codes (one byte) per conversion.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 template <>
 struct Codec<C_FP4> {
     static constexpr int CW = 32, UNITS = 4, UW = 8;
-    static constexpr bool WIDE = false, SCALED = true;
-    static constexpr float VMUL = 16384.f, OFFS = 0.f;
+    static constexpr bool F32DEC = false, WIDE = true, SCALED = true;
+    static constexpr float VMUL = 1.f, OFFS = 0.f;
     static constexpr int IDX[UW] = {0, 1, 2, 3, 4, 5, 6, 7};
     struct Chunk { uint32_t w[4]; };
     __device__ static Chunk load(const GRow &r, uint32_t c) {
         uint4 v = ld16(r.q, c * 16u);
         return {{v.x, v.y, v.z, v.w}};
     }
-    __device__ static void decode(const Chunk &ch, int u, uint32_t (&pr)[UW / 2]) {
+    __device__ static void decode_f(const Chunk &ch, int u, float (&v)[UW]) {
         const uint32_t w = ch.w[u];
-        const uint32_t he = ((w << 1) & 0x0E0E0E0Eu) | ((w << 4) & 0x80808080u);   // codes 0,2,4,6
-        const uint32_t ho = ((w >> 3) & 0x0E0E0E0Eu) | (w & 0x80808080u);          // codes 1,3,5,7
-        pr[0] = __builtin_amdgcn_perm(ho, he, 0x040C000Cu);
-        pr[1] = __builtin_amdgcn_perm(ho, he, 0x050C010Cu);
-        pr[2] = __builtin_amdgcn_perm(ho, he, 0x060C020Cu);
-        pr[3] = __builtin_amdgcn_perm(ho, he, 0x070C030Cu);
+        const f32x2 a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);   // byte 0: inputs 0, 1
+        const f32x2 b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+        const f32x2 c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+        const f32x2 d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+        v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y; v[4] = c.x; v[5] = c.y; v[6] = d.x; v[7] = d.y;
     }
 };
 
@@ -248,14 +276,13 @@ struct Codec<C_FP4> {
 // inputs each).  Unit u is inputs 32u..32u+31: L(2u), L(2u+1), H(u).  For
 // m = 0..7, byte b of q_m is the 3-bit code of input 8b + m: the 2-bit
 // fields are gathered with one v_perm per four m, the high bits with a
-// shift, the two joined with a shift-or, and v_perm pairs bytes (0, 1) and
-// (2, 3) of q_m into f16 halves.
+// shift, the two joined with a shift-or, and each byte of q_m converted.
 template <>
 struct Codec<C_I3> {
     static constexpr int CW = 64, UNITS = 2, UW = 32;
-    static constexpr bool WIDE = false, SCALED = true;
-    static constexpr float VMUL = 16777216.f, OFFS = 4.f / 16777216.f;
-    // pair 2m: inputs m, 8+m; pair 2m+1: inputs 16+m, 24+m
+    static constexpr bool F32DEC = false, WIDE = true, SCALED = true;
+    static constexpr float VMUL = 1.f, OFFS = 4.f;
+    // v[4m + b] is input 8b + m
     static constexpr int IDX[UW] = {0, 8, 16, 24, 1, 9, 17, 25, 2, 10, 18, 26, 3, 11, 19, 27,
                                     4, 12, 20, 28, 5, 13, 21, 29, 6, 14, 22, 30, 7, 15, 23, 31};
     struct Chunk { uint32_t l[4]; uint32_t h[2]; };
@@ -264,7 +291,7 @@ struct Codec<C_I3> {
         uint2 hv = ld8(r.q2, c * 8u);
         return {{lv.x, lv.y, lv.z, lv.w}, {hv.x, hv.y}};
     }
-    __device__ static void decode(const Chunk &ch, int u, uint32_t (&pr)[UW / 2]) {
+    __device__ static void decode_f(const Chunk &ch, int u, float (&v)[UW]) {
         const uint32_t L0 = ch.l[2 * u], L1 = ch.l[2 * u + 1], H = ch.h[u];
         // za = [L0.b0, L0.b2, L1.b0, L1.b2]: fields of inputs m, 8+m, 16+m, 24+m (m < 4)
         // zb = [L0.b1, L0.b3, L1.b1, L1.b3]: the same for m >= 4
@@ -275,9 +302,9 @@ struct Codec<C_I3> {
             const uint32_t z = m < 4 ? za : zb;
             const uint32_t lo = (z >> (2 * (m & 3))) & 0x03030303u;
             const uint32_t hi = (H >> m) & 0x01010101u;
-            const uint32_t q = lo | (hi << 2);
-            pr[2 * m] = __builtin_amdgcn_perm(0u, q, 0x0C010C00u);
-            pr[2 * m + 1] = __builtin_amdgcn_perm(0u, q, 0x0C030C02u);
+            const uint32_t q = opaque(lo | (hi << 2));
+            v[4 * m] = ubyte_f<0>(q); v[4 * m + 1] = ubyte_f<1>(q);
+            v[4 * m + 2] = ubyte_f<2>(q); v[4 * m + 3] = ubyte_f<3>(q);
         }
     }
 };
@@ -286,7 +313,7 @@ struct Codec<C_I3> {
 template <>
 struct Codec<C_F16> {
     static constexpr int CW = 8, UNITS = 2, UW = 4;
-    static constexpr bool WIDE = false, SCALED = false;
+    static constexpr bool F32DEC = false, WIDE = false, SCALED = false;
     static constexpr float VMUL = 1.f, OFFS = 0.f;
     static constexpr int IDX[UW] = {0, 1, 2, 3};
     struct Chunk { uint32_t w[4]; };
@@ -304,8 +331,9 @@ struct Codec<C_F16> {
 template <>
 struct Codec<C_F32> {
     static constexpr int CW = 4, UNITS = 1, UW = 4;
-    static constexpr bool WIDE = true, SCALED = false;
+    static constexpr bool F32DEC = false, WIDE = true, SCALED = false;
     static constexpr float VMUL = 1.f, OFFS = 0.f;
+    static constexpr int IDX[UW] = {0, 1, 2, 3};
     struct Chunk { uint32_t w[4]; };
     __device__ static Chunk load(const GRow &r, uint32_t c) {
         uint4 v = ld16(r.q, c * 16u);
@@ -322,8 +350,9 @@ struct Codec<C_F32> {
 template <>
 struct Codec<C_BF16> {
     static constexpr int CW = 8, UNITS = 2, UW = 4;
-    static constexpr bool WIDE = true, SCALED = false;
+    static constexpr bool F32DEC = false, WIDE = true, SCALED = false;
     static constexpr float VMUL = 1.f, OFFS = 0.f;
+    static constexpr int IDX[UW] = {0, 1, 2, 3};
     struct Chunk { uint32_t w[4]; };
     __device__ static Chunk load(const GRow &r, uint32_t c) {
         uint4 v = ld16(r.q, c * 16u);
@@ -341,12 +370,12 @@ struct Codec<C_BF16> {
 
 // E4M3 (OCP FP8) with one f32 scale per 128 x 128 block: v_cvt_pk_f32_fp8
 // turns two codes into two f32 values, exactly (NaN codes stay NaN).
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 template <>
 struct Codec<C_FP8> {
     static constexpr int CW = 16, UNITS = 4, UW = 4;
-    static constexpr bool WIDE = true, SCALED = true;
+    static constexpr bool F32DEC = false, WIDE = true, SCALED = true;
     static constexpr float VMUL = 1.f, OFFS = 0.f;
+    static constexpr int IDX[UW] = {0, 1, 2, 3};
     struct Chunk { uint32_t w[4]; };
     __device__ static Chunk load(const GRow &r, uint32_t c) {
         uint4 v = ld16(r.q, c * 16u);
@@ -358,6 +387,14 @@ struct Codec<C_FP8> {
         v[0] = a.x; v[1] = a.y; v[2] = b.x; v[3] = b.y;
     }
 };
+
+// Whether a step over SM tokens multiplies f32 values (decode_f) rather than
+// f16 pairs: the WIDE codecs always, int4 from two tokens up (one
+// conversion then serves every token; at one token v_fma_mix_f32's
+// conversion inside the FMA is the cheaper form).  Both forms hold the same
+// values, so the bits do not depend on the form.
+template <int C, int SM>
+constexpr bool dec_f32() { return Codec<C>::WIDE || (Codec<C>::F32DEC && SM >= 2); }
 
 // ---------------------------------------------------------------------------
 // Wave64 sum with DPP.  Quad permutes and row rotates give every lane its
@@ -523,13 +560,13 @@ __device__ __forceinline__ void step_compute(const Step<C, NR, SM> &st, float (&
     for (int u = 0; u < Cd::UNITS; ++u) {
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            if constexpr (Cd::WIDE) {
+            if constexpr (dec_f32<C, SM>()) {
                 float v[Cd::UW];
                 Cd::decode_f(st.ch[r], u, v);
 #pragma unroll
                 for (int s = 0; s < SM; ++s)
 #pragma unroll
-                    for (int i = 0; i < Cd::UW; ++i) p[r][s] = fmaf(v[i], st.xv[s][u * Cd::UW + i], p[r][s]);
+                    for (int i = 0; i < Cd::UW; ++i) p[r][s] = fmaf(v[i], st.xv[s][u * Cd::UW + Cd::IDX[i]], p[r][s]);
             } else {
                 uint32_t pr[Cd::UW / 2];
                 Cd::decode(st.ch[r], u, pr);
@@ -565,7 +602,7 @@ __device__ __forceinline__ float row_dot(const typename Codec<C>::Chunk &ch, flo
             float v[Cd::UW];
             Cd::decode_f(ch, u, v);
 #pragma unroll
-            for (int i = 0; i < Cd::UW; ++i) p = fmaf(v[i], xv[u * Cd::UW + i], p);
+            for (int i = 0; i < Cd::UW; ++i) p = fmaf(v[i], xv[u * Cd::UW + Cd::IDX[i]], p);
         } else {
             uint32_t pr[Cd::UW / 2];
             Cd::decode(ch, u, pr);
@@ -599,15 +636,16 @@ __device__ __forceinline__ void dot_rows(const GRow (&rows)[NR], int nch, int sh
 // token) as the unit is used, so only SM * UW values of x are live at a
 // time instead of SM * CW; the operations and their order are those of
 // step_compute, so the results have the same bits.  x + s * xstride is
-// token s's row of the staged x.
-template <int C, int NR, int SM, bool P = true>
+// token s's row of the staged x.  With XSP the chunk's sums of x come in
+// xsp (summed beforehand in the same order) instead of being summed here.
+template <int C, int NR, int SM, bool P = true, bool XSP = false>
 __device__ __forceinline__ void step_compute_lds(const Step<C, NR, SM> &st, lfloats x, uint32_t xstride,
-                                                 uint32_t cu, float (&acc)[NR][SM]) {
+                                                 uint32_t cu, float (&acc)[NR][SM], const float *xsp = nullptr) {
     using Cd = Codec<C>;
     float p[NR][SM], xs[SM];
 #pragma unroll
     for (int s = 0; s < SM; ++s) {
-        xs[s] = 0.f;
+        xs[s] = XSP ? xsp[s] : 0.f;
 #pragma unroll
         for (int r = 0; r < NR; ++r) p[r][s] = 0.f;
     }
@@ -621,7 +659,7 @@ __device__ __forceinline__ void step_compute_lds(const Step<C, NR, SM> &st, lflo
                 const f32x4 t = *(const LDS f32x4 *)(x + s * xstride + x_lds_at<Cd::CW, P>(cu * Cd::CW) + u * Cd::UW + 4 * i);
                 xv[s][4 * i] = t.x; xv[s][4 * i + 1] = t.y; xv[s][4 * i + 2] = t.z; xv[s][4 * i + 3] = t.w;
             }
-        if (Cd::OFFS != 0.f) {
+        if (Cd::OFFS != 0.f && !XSP) {
 #pragma unroll
             for (int s = 0; s < SM; ++s)
 #pragma unroll
@@ -629,13 +667,13 @@ __device__ __forceinline__ void step_compute_lds(const Step<C, NR, SM> &st, lflo
         }
 #pragma unroll
         for (int r = 0; r < NR; ++r) {
-            if constexpr (Cd::WIDE) {
+            if constexpr (dec_f32<C, SM>()) {
                 float v[Cd::UW];
                 Cd::decode_f(st.ch[r], u, v);
 #pragma unroll
                 for (int s = 0; s < SM; ++s)
 #pragma unroll
-                    for (int i = 0; i < Cd::UW; ++i) p[r][s] = fmaf(v[i], xv[s][i], p[r][s]);
+                    for (int i = 0; i < Cd::UW; ++i) p[r][s] = fmaf(v[i], xv[s][Cd::IDX[i]], p[r][s]);
             } else {
                 uint32_t pr[Cd::UW / 2];
                 Cd::decode(st.ch[r], u, pr);
@@ -684,7 +722,7 @@ __device__ __forceinline__ void step_compute_lds_pairs(const Step<C, NR, 1> &st,
                     float v[Cd::UW];
                     Cd::decode_f(st.ch[r0 + rr], u, v);
 #pragma unroll
-                    for (int i = 0; i < Cd::UW; ++i) p[rr] = fmaf(v[i], xv[i], p[rr]);
+                    for (int i = 0; i < Cd::UW; ++i) p[rr] = fmaf(v[i], xv[Cd::IDX[i]], p[rr]);
                 } else {
                     uint32_t pr[Cd::UW / 2];
                     Cd::decode(st.ch[r0 + rr], u, pr);
@@ -835,10 +873,15 @@ __global__ void __launch_bounds__(256) k_rows_lds(MatDev m0, MatDev m1, const fl
 // registers; more, or int3: step_compute_lds).  The per-row arithmetic and the order
 // of steps are k_rows_lds's, so the bits are the same.
 constexpr int GX_W = 12, GX_R = 2;
+// Several tokens: 8 waves x 3 rows, so that the x of each chunk a wave reads
+// from LDS serves 3 rows (the reads of x for 2-4 tokens cost LDS bandwidth
+// on the scale of the arithmetic).
+constexpr int GXM_W = 8, GXM_R = 3;
+static_assert(GX_W * GX_R == GXM_W * GXM_R, "one block height at every batch");
 // Matrices of fewer rows take blocks of 8 waves x 1 row, so that 2048 rows
 // still make 256 blocks.
 constexpr int GXS_W = 8, GXS_R = 1;
-constexpr int GX_WIDE_ROWS = 256 * GX_W * GX_R;   // the wide shape from this many rows up
+constexpr int GX_WIDE_ROWS = 256 * GX_W * GX_R;   // the wide shapes from this many rows up
 
 // The body of k_rows_x for blocks of W waves x R rows (GU: R rows of m0 and
 // the same rows of m1).  epi(s, row, v, vu) takes token s's dot product of
@@ -883,18 +926,20 @@ __device__ __forceinline__ void rows_x_body(const MatDev &m0, const MatDev &m1, 
     }
     __syncthreads();
     // one token with a chunk of at most 32 inputs takes the step's x in
-    // registers (and, for codes with an offset, each chunk's sum of x, summed
-    // once per block in step_compute's order, after the row); int3's
-    // 64-input chunks read x per decode unit from LDS like several tokens do
+    // registers; several tokens, and int3's 64-input chunks, read x per
+    // decode unit from LDS.  Codes with an offset take each chunk's sum of x
+    // per token, summed once per block in step_compute's order, after the row.
     constexpr bool XREG = SM == 1 && Cd::CW <= 32;
-    constexpr bool XSUM = XREG && Cd::OFFS != 0.f;
-    lfloats_w xsums = xs + xl;
+    constexpr bool XSUM = Cd::OFFS != 0.f;
+    constexpr uint32_t NCH = K / Cd::CW;
+    lfloats_w xsums = xs + SM * xl;
     if constexpr (XSUM) {
-        for (uint32_t t = threadIdx.x; t < (uint32_t)(K / Cd::CW); t += nt) {
+        for (uint32_t t = threadIdx.x; t < SM * NCH; t += nt) {
+            const uint32_t sl = t / NCH, c = t - sl * NCH;
             float a = 0.f;
 #pragma unroll
             for (int q = 0; q < Cd::CW / 4; ++q) {
-                const f32x4 v = *(const LDS f32x4 *)(xs + x_lds_at<Cd::CW>(t * Cd::CW) + 4 * q);
+                const f32x4 v = *(const LDS f32x4 *)(xs + sl * xl + x_lds_at<Cd::CW>(c * Cd::CW) + 4 * q);
                 a += v.x;
                 a += v.y;
                 a += v.z;
@@ -924,7 +969,10 @@ __device__ __forceinline__ void rows_x_body(const MatDev &m0, const MatDev &m1, 
             for (int r = 0; r < NR; ++r) acc[r][0] = row_dot<C>(st[j].ch[r], st[j].sc[r], xv, xsum, acc[r][0]);
             __builtin_amdgcn_sched_barrier(0);
         } else {
-            step_compute_lds(st[j], (lfloats)xs, xl, cu, acc);
+            float xsv[SM];
+#pragma unroll
+            for (int t = 0; t < SM; ++t) xsv[t] = XSUM ? xsums[t * NCH + cu] : 0.f;
+            step_compute_lds<C, NR, SM, true, XSUM>(st[j], (lfloats)xs, xl, cu, acc, xsv);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -950,7 +998,7 @@ __global__ void __launch_bounds__(WAVE * W) k_rows_x(MatDev m0, MatDev m1, const
 }
 
 // ---------------------------------------------------------------------------
-// dqg_dequant: out[o][k] = value * scale with value = (pattern - OFFS) *
+// dqg_dequant: out[o][k] = value * scale with value = (decoded - OFFS) *
 // VMUL exactly, then one rounding.  One thread per chunk.
 // ---------------------------------------------------------------------------
 template <int C>
@@ -968,10 +1016,15 @@ __global__ void __launch_bounds__(256) k_dequant(MatDev m, float *__restrict__ o
     for (int u = 0; u < Cd::UNITS; ++u) {
         float v[Cd::UW];
         if constexpr (Cd::WIDE) {
-            Cd::decode_f(ch, u, v);
-            if constexpr (Cd::SCALED) {
+            float d[Cd::UW];
+            Cd::decode_f(ch, u, d);
 #pragma unroll
-                for (int i = 0; i < Cd::UW; ++i) v[i] *= sc;
+            for (int i = 0; i < Cd::UW; ++i) {
+                float t = d[i];   // formats without offset, power or scale pass their values through
+                if constexpr (Cd::OFFS != 0.f) t -= Cd::OFFS;
+                if constexpr (Cd::VMUL != 1.f) t *= Cd::VMUL;
+                if constexpr (Cd::SCALED) t *= sc;
+                v[Cd::IDX[i]] = t;
             }
         } else {
             uint32_t pr[Cd::UW / 2];
@@ -1248,8 +1301,11 @@ __device__ __forceinline__ void group_combine(const GroupArgs &a, float *d, int 
     }
 }
 
+// (a budget of 4 waves per SIMD, so that two 8-wave blocks share a CU; int3,
+// whose rows of 64-input chunks take more registers, has none)
 template <int C, int R>
-__global__ void __launch_bounds__(WAVE * DOWN_MAX_WAVES) k_group_down(GroupArgs a) { group_down<C, R>(a); }
+__global__ void __launch_bounds__(WAVE * DOWN_MAX_WAVES) __attribute__((amdgpu_waves_per_eu(C == C_I3 ? 1 : 4)))
+k_group_down(GroupArgs a) { group_down<C, R>(a); }
 
 // One token routed to one expert, no shared expert (a single expert MLP):
 // the group's two launches on k_rows_x's block shape, whose blocks fill the
@@ -1450,9 +1506,19 @@ typedef _Float16 h16x8 __attribute__((ext_vector_type(8)));
 template <int C>
 struct GemmCodec;
 
+//
+// The f16 operand of a code: the integer codes as f16 subnormals (a
+// non-negative integer n below 1024 in the low bits of an f16 is n * 2^-24),
+// an e2m1 code with its magnitude bits at f16 bits 9..11 and its sign at bit
+// 15 as e2m1 * 2^-14 (the two formats put the implicit one and the exponent
+// bias in the same places), E4M3 and f16 as their values.  So a code's
+// value is (operand - OFFS) * VMUL, VMUL a power of two folded into the
+// window's scale.
+
 template <>
 struct GemmCodec<C_I4> {
     static constexpr int PERM[8] = {0, 4, 1, 5, 2, 6, 3, 7};
+    static constexpr float VMUL = Codec<C_I4>::VMUL, OFFS = Codec<C_I4>::OFFS;
     using Raw = uint32_t;
     __device__ static Raw load(gbytes row, uint32_t k) { return *(const GLOBAL uint32_t *)(row + k / 2); }
     __device__ static void decode(Raw w, uint32_t (&pr)[4]) {
@@ -1460,27 +1526,40 @@ struct GemmCodec<C_I4> {
     }
 };
 
+// MXFP4: the f16 high byte of code c is ((c & 7) << 1) | ((c & 8) << 4); it
+// is built for the four even and four odd codes of a word at once, then
+// v_perm pairs each even code with the next odd one over zero low bytes.
 template <>
 struct GemmCodec<C_FP4> {
     static constexpr int PERM[8] = {0, 1, 2, 3, 4, 5, 6, 7};
+    static constexpr float VMUL = 16384.f, OFFS = 0.f;
     using Raw = uint32_t;
     __device__ static Raw load(gbytes row, uint32_t k) { return *(const GLOBAL uint32_t *)(row + k / 2); }
     __device__ static void decode(Raw w, uint32_t (&pr)[4]) {
-        Codec<C_FP4>::decode({{w, 0u, 0u, 0u}}, 0, pr);
+        const uint32_t he = ((w << 1) & 0x0E0E0E0Eu) | ((w << 4) & 0x80808080u);   // codes 0,2,4,6
+        const uint32_t ho = ((w >> 3) & 0x0E0E0E0Eu) | (w & 0x80808080u);          // codes 1,3,5,7
+        pr[0] = __builtin_amdgcn_perm(ho, he, 0x040C000Cu);
+        pr[1] = __builtin_amdgcn_perm(ho, he, 0x050C010Cu);
+        pr[2] = __builtin_amdgcn_perm(ho, he, 0x060C020Cu);
+        pr[3] = __builtin_amdgcn_perm(ho, he, 0x070C030Cu);
     }
 };
 
+// int8: q ^ 0x80 = q + 128 as an unsigned byte; v_perm drops bytes into the
+// low byte of each f16 half.
 template <>
 struct GemmCodec<C_I8> {
     static constexpr int PERM[8] = {0, 2, 1, 3, 4, 6, 5, 7};
+    static constexpr float VMUL = 16777216.f, OFFS = 128.f / 16777216.f;
     using Raw = u32x2;
     __device__ static Raw load(gbytes row, uint32_t k) { return *(const GLOBAL u32x2 *)(row + k); }
     __device__ static void decode(Raw w, uint32_t (&pr)[4]) {
-        const typename Codec<C_I8>::Chunk ch{{w.x, w.y, 0u, 0u}};
-        uint32_t a[2], b[2];
-        Codec<C_I8>::decode(ch, 0, a);
-        Codec<C_I8>::decode(ch, 1, b);
-        pr[0] = a[0]; pr[1] = a[1]; pr[2] = b[0]; pr[3] = b[1];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const uint32_t b = (j ? w.y : w.x) ^ 0x80808080u;
+            pr[2 * j] = __builtin_amdgcn_perm(0u, b, 0x0C020C00u);       // inputs 0, 2
+            pr[2 * j + 1] = __builtin_amdgcn_perm(0u, b, 0x0C030C01u);   // inputs 1, 3
+        }
     }
 };
 
@@ -1488,6 +1567,7 @@ struct GemmCodec<C_I8> {
 template <>
 struct GemmCodec<C_FP8> {
     static constexpr int PERM[8] = {0, 1, 2, 3, 4, 5, 6, 7};
+    static constexpr float VMUL = 1.f, OFFS = 0.f;
     using Raw = u32x2;
     __device__ static Raw load(gbytes row, uint32_t k) { return *(const GLOBAL u32x2 *)(row + k); }
     __device__ static void decode(Raw w, uint32_t (&pr)[4]) {
@@ -1506,6 +1586,7 @@ struct GemmCodec<C_FP8> {
 template <>
 struct GemmCodec<C_F16> {
     static constexpr int PERM[8] = {0, 1, 2, 3, 4, 5, 6, 7};
+    static constexpr float VMUL = 1.f, OFFS = 0.f;
     using Raw = u32x4;
     __device__ static Raw load(gbytes row, uint32_t k) { return *(const GLOBAL u32x4 *)(row + 2 * k); }
     __device__ static void decode(Raw w, uint32_t (&pr)[4]) {
@@ -1640,10 +1721,10 @@ k_gemm(MatDev m0, MatDev m1, const float *__restrict__ x, int S, float *__restri
             const int row = min(gemm_row<GU>(block_row, sw, st, sr), O - 1);
             const int k = k0 + 32 * j;
             if constexpr (Cd::SCALED)
-                sc_n[h] = j < nwin ? m.s[(size_t)(row >> m.srow) * m.sstride + ((uint32_t)(k / Cd::CW) >> m.shift)] * Cd::VMUL
+                sc_n[h] = j < nwin ? m.s[(size_t)(row >> m.srow) * m.sstride + ((uint32_t)(k / Cd::CW) >> m.shift)] * Gc::VMUL
                                    : 0.f;
             else
-                sc_n[h] = Cd::VMUL;
+                sc_n[h] = Gc::VMUL;
         }
     };
     fetch(kbeg);
@@ -1698,12 +1779,12 @@ k_gemm(MatDev m0, MatDev m1, const float *__restrict__ x, int S, float *__restri
             for (int t = 0; t < 2; ++t) {
                 uint32_t pr[4];
                 Gc::decode(raw[t][j], pr);
-                if constexpr (Cd::OFFS != 0.f) {
+                if constexpr (Gc::OFFS != 0.f) {
                     // offset codes to signed values: exact, the f16 patterns
                     // are integer multiples of 2^-24 far below f16's precision
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const half2_t o = half2_t{(_Float16)(-Cd::OFFS), (_Float16)(-Cd::OFFS)};
+                        const half2_t o = half2_t{(_Float16)(-Gc::OFFS), (_Float16)(-Gc::OFFS)};
                         pr[q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, pr[q]) + o);
                     }
                 }
@@ -2044,18 +2125,19 @@ hipError_t go_gemm(const MatDev &m0, const MatDev &m1, const float *x, int S, fl
 }
 
 // k_rows_x for 1-4 tokens and K of 1-4 whole 64-chunk steps (int3, whose
-// 64-input chunks would spill a wider batch, at one token only).
-template <int C>
+// 64-input chunks would spill a wider batch, at one token only, and its
+// gate/up pairs at 1-3 steps).
+template <int C, bool GU>
 bool rows_x_fits(int K, int S) {
     const int unit = WAVE * Codec<C>::CW;
-    return S <= (C == C_I3 ? 1 : 4) && K % unit == 0 && K / unit <= 4;
+    return S <= (C == C_I3 ? 1 : 4) && K % unit == 0 && K / unit <= (C == C_I3 && GU ? 3 : 4);
 }
 
-// Bytes of LDS k_rows_x takes: x of SM tokens, and with one token the
-// chunk sums of x.
+// Bytes of LDS k_rows_x takes: x of SM tokens, and for codes with an
+// offset the chunk sums of x.
 template <int C, int SM>
 size_t rows_x_lds(int K) {
-    return ((size_t)SM * x_lds_len<Codec<C>::CW>(K) + (SM == 1 ? K / Codec<C>::CW : 0)) * 4;
+    return ((size_t)SM * x_lds_len<Codec<C>::CW>(K) + (Codec<C>::OFFS != 0.f ? SM * K / Codec<C>::CW : 0)) * 4;
 }
 
 template <int C, int SM, bool GU, int NS>
@@ -2063,9 +2145,10 @@ hipError_t go_rows_x(const MatDev &g, const MatDev &u, const float *x, int S, fl
                      const char *name) {
     const size_t lds = rows_x_lds<C, SM>(g.K);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
+    constexpr int W = SM == 1 ? GX_W : GXM_W, R = SM == 1 ? GX_R : GXM_R;
     if (g.O >= GX_WIDE_ROWS) {
-        launch(name, (k_rows_x<C, SM, GU, NS, GX_W, GX_R>), dim3((g.O + GX_W * GX_R - 1) / (GX_W * GX_R)),
-               dim3(WAVE * GX_W), lds, st, g, u, x, S, y, L);
+        launch(name, (k_rows_x<C, SM, GU, NS, W, R>), dim3((g.O + W * R - 1) / (W * R)), dim3(WAVE * W), lds, st,
+               g, u, x, S, y, L);
     } else {
         launch(name, (k_rows_x<C, SM, GU, NS, GXS_W, GXS_R>), dim3((g.O + GXS_W * GXS_R - 1) / (GXS_W * GXS_R)),
                dim3(WAVE * GXS_W), lds, st, g, u, x, S, y, L);
@@ -2080,7 +2163,9 @@ hipError_t rows_x_sm(const MatDev &g, const MatDev &u, const float *x, int S, fl
     case 1: return go_rows_x<C, SM, GU, 1>(g, u, x, S, y, L, st, name);
     case 2: return go_rows_x<C, SM, GU, 2>(g, u, x, S, y, L, st, name);
     case 3: return go_rows_x<C, SM, GU, 3>(g, u, x, S, y, L, st, name);
-    default: return go_rows_x<C, SM, GU, 4>(g, u, x, S, y, L, st, name);
+    default:
+        if constexpr (C == C_I3 && GU) return hipErrorInvalidValue;   // not taken (rows_x_fits)
+        else return go_rows_x<C, SM, GU, 4>(g, u, x, S, y, L, st, name);
     }
 }
 
@@ -2099,7 +2184,7 @@ template <int C>
 hipError_t matmul_c(const MatDev &m, const float *x, int S, float *y, hipStream_t st) {
     if constexpr (gemm_codec<C>())
         if (S >= gemm_min_s<C>() && m.K % 32 == 0) return go_gemm<C, false>(m, m, x, S, y, INFINITY, st);
-    if (rows_x_fits<C>(m.K, S)) return rows_x<C, false>(m, m, x, S, y, INFINITY, st, "matmul");
+    if (rows_x_fits<C, false>(m.K, S)) return rows_x<C, false>(m, m, x, S, y, INFINITY, st, "matmul");
     // int3's 64-input chunks: 8 tokens at a time would spill, 4 fit with x in LDS
     if constexpr (C != C_I3)
         if (S >= 8) return go_matmul<C, MM_R, 8>(m, x, S, y, st);
@@ -2123,7 +2208,7 @@ template <int C>
 hipError_t gate_up_c(const MatDev &g, const MatDev &u, const float *x, int S, float *h, float L, hipStream_t st) {
     if constexpr (gemm_codec<C>())
         if (S >= gemm_min_s_gu<C>() && g.K % 32 == 0) return go_gemm<C, true>(g, u, x, S, h, L, st);
-    if (rows_x_fits<C>(g.K, S)) return rows_x<C, true>(g, u, x, S, h, L, st, "gate_up");
+    if (rows_x_fits<C, true>(g.K, S)) return rows_x<C, true>(g, u, x, S, h, L, st, "gate_up");
     // int3's 64-input chunks: 8 tokens at a time would spill, 4 fit with x in LDS
     if constexpr (C != C_I3)
         if (S >= 8) return go_gate_up<C, 2, 8>(g, u, x, S, h, L, st);
@@ -2143,9 +2228,9 @@ hipError_t dequant_c(const MatDev &m, float *out, hipStream_t st) {
 
 // One token, one routed expert, no shared expert, and K (H for gate/up, I
 // for down) of k_rows_x's shapes: the unit kernels.
-template <int C>
+template <int C, bool GU>
 bool unit_fits(const GroupArgs &a, int K) {
-    return a.S == 1 && a.k == 1 && a.shared < 0 && rows_x_fits<C>(K, 1) && rows_x_lds<C, 1>(K) <= 160 * 1024;
+    return a.S == 1 && a.k == 1 && a.shared < 0 && rows_x_fits<C, GU>(K, 1) && rows_x_lds<C, 1>(K) <= 160 * 1024;
 }
 
 template <int C, bool GU, int NS, int W, int R>
@@ -2171,7 +2256,9 @@ hipError_t unit_launch(const GroupArgs &a, hipStream_t st) {
     case 1: return unit_shape<C, GU, 1>(a, st);
     case 2: return unit_shape<C, GU, 2>(a, st);
     case 3: return unit_shape<C, GU, 3>(a, st);
-    default: return unit_shape<C, GU, 4>(a, st);
+    default:
+        if constexpr (C == C_I3 && GU) return hipErrorInvalidValue;   // not taken (unit_fits)
+        else return unit_shape<C, GU, 4>(a, st);
     }
 }
 
@@ -2183,7 +2270,7 @@ hipError_t unit_launch(const GroupArgs &a, hipStream_t st) {
 // 2 tokens and 108.8 -> 93.6 us at 4 with the shared expert's blocks first.)
 template <int C>
 hipError_t group_a(const GroupArgs &a, hipStream_t st) {
-    if (unit_fits<C>(a, a.H)) return unit_launch<C, true>(a, st);
+    if (unit_fits<C, true>(a, a.H)) return unit_launch<C, true>(a, st);
     const int units = a.S * a.k + (a.shared >= 0 ? 1 : 0);
     const int rows_per_block = RA * WPB_A;
     // the slot's row of x, and the chunk sums of x after it
@@ -2198,7 +2285,7 @@ hipError_t group_a(const GroupArgs &a, hipStream_t st) {
 
 template <int C>
 hipError_t group_b(const GroupArgs &a, hipStream_t st) {
-    if (unit_fits<C>(a, a.I)) return unit_launch<C, false>(a, st);
+    if (unit_fits<C, false>(a, a.I)) return unit_launch<C, false>(a, st);
     const int units = a.S * a.k + (a.shared >= 0 ? a.S : 0);   // each shared slot a unit
     const int slots = a.S * a.k + (a.shared >= 0 ? a.S : 0);
     const size_t v4_lds = a.act == ACT_SWIGLU_V4 ? 2 * (size_t)a.S * a.k * sizeof(int) : 0;
