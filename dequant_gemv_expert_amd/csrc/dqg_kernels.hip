@@ -1868,6 +1868,207 @@ __global__ void __launch_bounds__(256) k_gemm_reduce(const float *__restrict__ w
 }
 
 // ---------------------------------------------------------------------------
+// The GEMM route's split-K chunk for one tile of up to 16 tokens with 4-bit
+// codes and one scale per row and 32-input window (int4-g32, MXFP4), shaped
+// for batches that stream each weight once.  The products, their order and
+// the chunk sums are k_gemm's (same A and B operands in the same lanes,
+// the same two matrix-core products a window, the same scaling and order),
+// so the bits are its.  A block is 8 waves over one 512-input chunk; a wave
+// takes 2 row tiles of 16 (GU: 16 rows of gate and the same 16 of up).
+// Every code and scale load of a wave goes out at once, 16 bytes a lane:
+// load j gives lane l the 32 codes of window 4j + l / 16 of row l % 16,
+// and a 4 x 4 transpose across lane groups (v_permlane32_swap, then
+// v_permlane16_swap) leaves lane l quarter l / 16 of each window, the A
+// operand's layout.  x' of the chunk is split once a block.
+// ---------------------------------------------------------------------------
+constexpr int GV_W = 8;   // waves a block
+
+struct alignas(16) GvLds {
+    _Float16 xh[16][GEMM_KC + 8];          // x' hi, token, input (padded rows)
+    _Float16 xl[16][GEMM_KC + 8];          // x' lo
+    float xe[16][GEMM_KC / 32];            // 2^e of each token and window
+    float sc[GV_W][2][GEMM_KC / 32][16];   // per wave and tile: scale * VMUL by window, row
+};
+
+template <int C, bool GU>
+__global__ void __launch_bounds__(WAVE * GV_W) __attribute__((amdgpu_waves_per_eu(4)))
+k_gemv_mma(MatDev m0, MatDev m1, const float *__restrict__ x, int S, float *__restrict__ ws, int op) {
+    using Gc = GemmCodec<C>;
+    constexpr int GWIN = GEMM_KC / 32;
+    static_assert(GWIN == 16, "four loads of 16 bytes a row cover a chunk");
+    __shared__ GvLds L;
+    const int tid = threadIdx.x, lane = tid & (WAVE - 1), w = wave_id();
+    const int lr = lane & 15, lq = lane >> 4;
+    const int O = m0.O, K = m0.K;
+    const int block_row = blockIdx.x * (GU ? 16 * GV_W : 32 * GV_W);
+    const int kbeg = blockIdx.y * GEMM_KC;
+    // x of the chunk, 16 bytes a lane and 1 KiB a load: load i of wave w
+    // covers token (4w + i) / 2 (tokens past S repeat the last; their
+    // outputs are dropped), 16-byte units 64 ((4w + i) % 2) + lane, so lane
+    // l holds inputs 4 (l % 8) .. + 3 of window 8 ((4w + i) % 2) + l / 8
+    f32x4 xv[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int f = 4 * w + i;
+        xv[i] = *(const GLOBAL f32x4 *)(gf(x) + (size_t)min(f >> 1, S - 1) * K + kbeg + 4 * (64 * (f & 1) + lane));
+    }
+    // this lane's rows for the codes (row lr of each tile) and the scales (row lane / 4)
+    gbytes arow[2];
+    gfloats srow[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+        const MatDev &m = (GU && t == 1) ? m1 : m0;
+        const int ra = min(gemm_row<GU>(block_row, w, t, lr), O - 1);
+        const int rs = min(gemm_row<GU>(block_row, w, t, lane >> 2), O - 1);
+        arow[t] = (gbytes)(m.q + (size_t)ra * m.qstride);   // per lane: not gb / gf, which take lane 0's
+        srow[t] = (gfloats)(m.s + (size_t)rs * m.sstride);
+    }
+    // stage x' = x 2^-e as f16 hi + lo, e per token and window from the
+    // window's largest magnitude (the 8 lanes of a window share it through
+    // DPP), each value split as split_window splits it; the two lanes of a
+    // quarter swap halves so that one writes its hi and the other its lo,
+    // in the decode's order PERM
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int f = 4 * w + i, tok = f >> 1, win = 8 * (f & 1) + (lane >> 3), a = lane & 7;
+        const f32x4 v = xv[i];
+        float mx = fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w)));
+        mx = fmaxf(mx, dpp_mov<0xB1>(mx));    // quad_perm [1,0,3,2]
+        mx = fmaxf(mx, dpp_mov<0x4E>(mx));    // quad_perm [2,3,0,1]
+        mx = fmaxf(mx, dpp_mov<0x141>(mx));   // row_half_mirror: the other quad of the 8
+        int ex = 0;
+        if (mx > 0.f) { frexpf(mx, &ex); ex -= 15; }   // mx * 2^-ex < 2^15
+        _Float16 h[4], l[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const float xs = ldexpf(v[e], -ex);
+            h[e] = (_Float16)xs;
+            l[e] = (_Float16)(xs - (float)h[e]);
+        }
+        // lane a % 2 == 0 holds inputs 0..3 of quarter a / 2, the other 4..7;
+        // the first keeps its hi and takes the other's, the second its lo
+        const bool odd = a & 1;
+        const uint32_t m0 = __builtin_bit_cast(uint32_t, odd ? half2_t{l[0], l[1]} : half2_t{h[0], h[1]});
+        const uint32_t m1 = __builtin_bit_cast(uint32_t, odd ? half2_t{l[2], l[3]} : half2_t{h[2], h[3]});
+        const uint32_t s0 = __builtin_bit_cast(uint32_t, odd ? half2_t{h[0], h[1]} : half2_t{l[0], l[1]});
+        const uint32_t s1 = __builtin_bit_cast(uint32_t, odd ? half2_t{h[2], h[3]} : half2_t{l[2], l[3]});
+        const uint32_t t0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s0, 0xB1, 0xF, 0xF, false);
+        const uint32_t t1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)s1, 0xB1, 0xF, 0xF, false);
+        const half2_t q0[2] = {__builtin_bit_cast(half2_t, odd ? t0 : m0), __builtin_bit_cast(half2_t, odd ? t1 : m1)};
+        const half2_t q1[2] = {__builtin_bit_cast(half2_t, odd ? m0 : t0), __builtin_bit_cast(half2_t, odd ? m1 : t1)};
+        h16x8 o;
+#pragma unroll
+        for (int pp = 0; pp < 8; ++pp) {
+            const int in = Gc::PERM[pp];   // input of the quarter at position pp
+            const half2_t &src = in < 4 ? q0[(in & 3) >> 1] : q1[(in & 3) >> 1];
+            o[pp] = (in & 1) ? src.y : src.x;
+        }
+        _Float16(*dst)[GEMM_KC + 8] = odd ? L.xl : L.xh;
+        *(LDS h16x8 *)&dst[tok][32 * win + 8 * (a >> 1)] = o;
+        if (a == 0) L.xe[tok][win] = ldexpf(1.f, ex);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    // then the scales and the codes, in the order the windows use them:
+    // requested only now, so that x came back through an idle memory
+    // system, and each window's products wait for their own codes while
+    // the later ones stream
+    f32x4 scv[2];
+    u32x4 raw[4][2];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+        scv[t] = __builtin_nontemporal_load((const GLOBAL f32x4 *)(srow[t] + kbeg / 32 + 4 * (lane & 3)));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const uint4 v = ld16(arow[t], (uint32_t)(kbeg / 2 + 64 * j + 16 * lq));
+            raw[j][t] = u32x4{v.x, v.y, v.z, v.w};
+        }
+    __builtin_amdgcn_sched_barrier(0);
+    // the wave's own scales by window and row (no other wave reads them)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) L.sc[w][t][4 * (lane & 3) + i][lane >> 2] = scv[t][i] * Gc::VMUL;
+    float acc[2][4];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[t][i] = 0.f;
+    // window j's x operands and scales are read during window j - 1; each
+    // window's scaled sums are complete before the next window's reads
+    // (left to itself the compiler runs every product first and holds all
+    // 32 results, which spills)
+    h16x8 bh_n = *(LDS h16x8 *)&L.xh[lr][8 * lq];
+    h16x8 bl_n = *(LDS h16x8 *)&L.xl[lr][8 * lq];
+    float xe_n = L.xe[lr][0];
+    f32x4 sc_n[2] = {*(LDS f32x4 *)&L.sc[w][0][0][4 * lq], *(LDS f32x4 *)&L.sc[w][1][0][4 * lq]};
+    uint32_t a32[2][4];   // the A dwords of this load's 4 windows
+#pragma unroll
+    for (int j = 0; j < GWIN; ++j) {
+        if (j % 4 == 0) {
+            // codes of windows j .. j + 3 to the A layout: after the transpose
+            // register k of lane group g holds what register g of lane group
+            // k held
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const u32x4 r = raw[j / 4][t];
+                const auto r02 = __builtin_amdgcn_permlane32_swap(r.x, r.z, false, false);
+                const auto r13 = __builtin_amdgcn_permlane32_swap(r.y, r.w, false, false);
+                const auto r01 = __builtin_amdgcn_permlane16_swap(r02[0], r13[0], false, false);
+                const auto r23 = __builtin_amdgcn_permlane16_swap(r02[1], r13[1], false, false);
+                a32[t][0] = r01[0];
+                a32[t][1] = r01[1];
+                a32[t][2] = r23[0];
+                a32[t][3] = r23[1];
+            }
+        }
+        const h16x8 bh = bh_n, bl = bl_n;
+        const float xe = xe_n;
+        const f32x4 scj[2] = {sc_n[0], sc_n[1]};
+        if (j + 1 < GWIN) {
+            bh_n = *(LDS h16x8 *)&L.xh[lr][32 * (j + 1) + 8 * lq];
+            bl_n = *(LDS h16x8 *)&L.xl[lr][32 * (j + 1) + 8 * lq];
+            xe_n = L.xe[lr][j + 1];
+            sc_n[0] = *(LDS f32x4 *)&L.sc[w][0][j + 1][4 * lq];
+            sc_n[1] = *(LDS f32x4 *)&L.sc[w][1][j + 1][4 * lq];
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            uint32_t pr[4];
+            Gc::decode(a32[t][j % 4], pr);
+            if constexpr (Gc::OFFS != 0.f) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const half2_t o = half2_t{(_Float16)(-Gc::OFFS), (_Float16)(-Gc::OFFS)};
+                    pr[q] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2_t, pr[q]) + o);
+                }
+            }
+            const h16x8 a = __builtin_bit_cast(h16x8, u32x4{pr[0], pr[1], pr[2], pr[3]});
+            f32x4 d = {0.f, 0.f, 0.f, 0.f};
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bh, d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bl, d, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[t][i] = fmaf(scj[t][i] * xe, d[i], acc[t][i]);
+        }
+        asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]), "+v"(acc[0][2]), "+v"(acc[0][3]), "+v"(acc[1][0]),
+                     "+v"(acc[1][1]), "+v"(acc[1][2]), "+v"(acc[1][3])::"memory");
+    }
+    // the chunk's sums as k_gemm adds them up from 0; D lane layout: rows
+    // 4 lq + i of each tile, token lr
+    if (lr < S) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const int row = gemm_row<GU>(block_row, w, GU ? 0 : t, 4 * lq), mat = GU ? t : 0;
+            float *p = ws + ((size_t)(blockIdx.y * (GU ? 2 : 1) + mat) * S + lr) * op + row;
+            *(f32x4 *)p = f32x4{0.f + acc[t][0], 0.f + acc[t][1], 0.f + acc[t][2], 0.f + acc[t][3]};
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Router: logits -> scores -> top-k -> (ids, w), one wave per token.  The
 // scores are softmax (max subtracted) or sigmoid; the pick key is the logit
 // itself (both scores keep the logits' order) or, with a bias, score +
@@ -2067,18 +2268,34 @@ struct Workspace {
 };
 Workspace g_ws[64];
 
+// Whether k_gemv_mma takes the split-K chunks: one token tile, 4-bit codes
+// with one scale per row and 32-input window, whole chunks, 16-byte aligned
+// rows of codes and scales.
+template <int C, int NC>
+bool gemv_mma_fits(const MatDev &m, int S) {
+    if constexpr (NC != 1 || (C != C_I4 && C != C_FP4)) {
+        return false;
+    } else {
+        return S <= 16 && m.K % GEMM_KC == 0 && m.shift == 0 && m.srow == 0 && m.sstride % 4 == 0 &&
+               m.qstride % 16 == 0 && ((uintptr_t)m.q | (uintptr_t)m.s) % 16 == 0;
+    }
+}
+
 template <int C, bool GU, int NC>
 hipError_t go_gemm_nc(const MatDev &m0, const MatDev &m1, const float *x, int S, float *y, float L,
                       hipStream_t st, const char *name) {
     static_assert(NC >= gemm_min_nc<C>(), "a step's codes must fit 32 registers");
-    const int rows_per_block = GU ? GROWS / 2 : GROWS;
     const int O = m0.O, nch = (m0.K + GEMM_KC - 1) / GEMM_KC;
-    dim3 grid((O + rows_per_block - 1) / rows_per_block, (S + 16 * NC - 1) / (16 * NC));
+    const bool gv = gemv_mma_fits<C, NC>(m0, S) && (!GU || gemv_mma_fits<C, NC>(m1, S));
+    const int rows_plain = GU ? GROWS / 2 : GROWS;
+    const int rows_per_block = gv ? (GU ? 16 : 32) * GV_W : rows_plain;
+    dim3 grid((O + rows_plain - 1) / rows_plain, (S + 16 * NC - 1) / (16 * NC));
     const auto plain = [&]() {   // each block walks all of K
         launch(name, (k_gemm<C, GU, NC>), grid, dim3(256), 0, st, m0, m1, x, S, y, L, (float *)nullptr, 0);
         return hipGetLastError();
     };
     if (nch == 1 || (size_t)grid.x * grid.y >= GEMM_SPLIT_BELOW) return plain();
+    grid.x = (O + rows_per_block - 1) / rows_per_block;
     const int op = grid.x * rows_per_block;
     const size_t bytes = (size_t)nch * (GU ? 2 : 1) * S * op * sizeof(float);
     hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
@@ -2098,12 +2315,19 @@ hipError_t go_gemm_nc(const MatDev &m0, const MatDev &m1, const float *x, int S,
         if ((e = hipMalloc((void **)&W.buf, bytes)) != hipSuccess) return e;
         W.bytes = bytes;
     }
+    float *part = W.buf;
     if (W.used && (e = hipStreamWaitEvent(st, W.done, 0)) != hipSuccess) return e;
-    grid.z = nch;
-    launch(name, (k_gemm<C, GU, NC>), grid, dim3(256), 0, st, m0, m1, x, S, y, L, W.buf, op);
+    if constexpr (NC == 1 && (C == C_I4 || C == C_FP4)) {
+        if (gv)
+            launch(name, (k_gemv_mma<C, GU>), dim3(grid.x, nch), dim3(WAVE * GV_W), 0, st, m0, m1, x, S, part, op);
+    }
+    if (!gv) {
+        grid.z = nch;
+        launch(name, (k_gemm<C, GU, NC>), grid, dim3(256), 0, st, m0, m1, x, S, y, L, part, op);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t n = (size_t)S * O;
-    launch("gemm_reduce", (k_gemm_reduce<GU>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, W.buf, nch, S, O,
+    launch("gemm_reduce", (k_gemm_reduce<GU>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, part, nch, S, O,
            op, y, L);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if ((e = hipEventRecord(W.done, st)) != hipSuccess) return e;

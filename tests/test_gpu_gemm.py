@@ -97,6 +97,45 @@ def test_gemm_batch_invariant():
         assert yn.tobytes() == y96[lo:lo + n].tobytes(), (lo, n)
 
 
+# One tile of up to 16 tokens with 4-bit codes, a scale per 32 inputs and K
+# of whole 512-input chunks: the split-K chunks take the small-batch kernel
+# (16-byte code loads, a transpose across lane groups to the matrix cores'
+# layout), whose bits must be those of the general kernel's chunks (a
+# 48-token batch).  Row counts ragged against its 256-row (gate/up: 128) blocks.
+SMALL = [(4, 77, 1024), (4, 300, 2048), (7, 513, 1536), (7, 40, 512 * 5), (4, 6144, 6144)]
+
+
+@pytest.mark.parametrize("spec", SMALL, ids=lambda s: f"fmt{s[0]}_{s[1]}x{s[2]}")
+def test_gemm_small_batch_kernel(spec):
+    fmt, O, K = spec
+    i = SMALL.index(spec)
+    m = synth.matrix(fmt, O, K, 32, 9900 + i, fmt)
+    x = synth.activations(48, K, 9950 + i)
+    W = up(m)
+    y48 = host(dq.dqg_matmul(W, dev_f32(x)))
+    for lo, n in ((0, 9), (9, 16), (30, 13)):
+        yn = host(dq.dqg_matmul(W, dev_f32(x[lo:lo + n])))
+        assert yn.tobytes() == y48[lo:lo + n].tobytes(), (spec, lo, n)
+    rows = list(range(O)) if O <= 600 else [0, 1, 255, 256, 3000, O - 1]
+    yr, a = oracle.gemv(_sampled_rows(m, rows), x[9:25])
+    assert_close(y48[9:25][:, rows], yr, a, f"small-batch gemm {spec} S=16")
+
+
+@pytest.mark.parametrize("spec", [(4, 300, 2048), (7, 129, 1024)], ids=lambda s: f"fmt{s[0]}_{s[1]}x{s[2]}")
+def test_gemm_gate_up_small_batch_kernel(spec):
+    fmt, O, K = spec
+    G = synth.matrix(fmt, O, K, 32, 9960, 0)
+    U = synth.matrix(fmt, O, K, 32, 9960, 1)
+    x = synth.activations(48, K, 9961)
+    g, u = up(G), up(U)
+    h48 = host(dq.dqg_gate_up(g, u, dev_f32(x)))
+    for lo, n in ((0, 9), (20, 16)):
+        hn = host(dq.dqg_gate_up(g, u, dev_f32(x[lo:lo + n])))
+        assert hn.tobytes() == h48[lo:lo + n].tobytes(), (spec, lo, n)
+    r = oracle.gate_up(G, U, x[20:36])
+    assert_close(h48[20:36], r["h"], r["nh"], f"small-batch gemm gate_up {spec} S=16")
+
+
 def test_gemm_zero_scales():
     m = synth.matrix(4, 64, 1024, 32, 9400, 0)
     m.scales[:] = 0
