@@ -865,13 +865,14 @@ __global__ void __launch_bounds__(256) k_rows_lds(MatDev m0, MatDev m1, const fl
 
 // The same products for 1-4 tokens (int3: 1) and K of 1-4 whole 64-chunk steps (NS),
 // shaped to fill the chip at one token: blocks of 12 waves x 2 rows (6144
-// rows make 256 blocks, one a CU), x staged once per block, and every load
-// of a wave issued before its first arithmetic.  x's loads go out first and
-// wait in registers while the weights' loads are issued (step by step, rows
-// in order), so that copying x to LDS waits for x alone; then each row of
-// each step is computed as its codes land (one token: the step's x in
-// registers; more, or int3: step_compute_lds).  The per-row arithmetic and the order
-// of steps are k_rows_lds's, so the bits are the same.
+// rows make 256 blocks, one a CU), x staged once per block, and every
+// weight load of a wave issued before its first arithmetic.  x's loads go
+// out first; at one token the weights' loads (step by step, rows in order)
+// follow once x is in LDS, at several tokens while x is in flight; then
+// each row of each step is computed as its codes land (one token: the
+// step's x in registers; more, or int3: step_compute_lds).  The per-row
+// arithmetic and the order of steps are k_rows_lds's, so the bits are the
+// same.
 constexpr int GX_W = 12, GX_R = 2;
 // Several tokens: 8 waves x 3 rows, so that the x of each chunk a wave reads
 // from LDS serves 3 rows (the reads of x for 2-4 tokens cost LDS bandwidth
@@ -886,7 +887,13 @@ constexpr int GX_WIDE_ROWS = 256 * GX_W * GX_R;   // the wide shapes from this m
 // The body of k_rows_x for blocks of W waves x R rows (GU: R rows of m0 and
 // the same rows of m1).  epi(s, row, v, vu) takes token s's dot product of
 // row (and of m1's row with GU), for rows below m0.O and s below S.
-template <int C, int SM, bool GU, int NS, int W, int R, typename Epi>
+// XFIRST: the weights are requested only once x is staged, so that x comes
+// back through an idle memory system and the arithmetic starts while the
+// weights stream (the dense one-token launches: 6144^2 int4 7.6 -> 7.0 us,
+// its gate_up 13.2 -> 10.8, int3 6144 x 16384 15.6 -> 12.9; no gain at 4
+// tokens, and the single expert's short launches lose); otherwise they go
+// out with x and wait for it.
+template <int C, int SM, bool GU, int NS, int W, int R, bool XFIRST, typename Epi>
 __device__ __forceinline__ void rows_x_body(const MatDev &m0, const MatDev &m1, const float *__restrict__ x, int S,
                                             Epi &&epi) {
     extern __shared__ float xl_raw[];
@@ -913,12 +920,15 @@ __device__ __forceinline__ void rows_x_body(const MatDev &m0, const MatDev &m1, 
         if (GU) rows[R + r] = row_ptrs(m1, min(row0 + r, m.O - 1));
     }
     Step<C, NR, SM> st[NS];
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int j = 0; j < NS; ++j) {
-        step_load_w(st[j], rows, m.shift, opaque((uint32_t)(j * WAVE + lane)));
+    const auto load_weights = [&]() {
         __builtin_amdgcn_sched_barrier(0);
-    }
+#pragma unroll
+        for (int j = 0; j < NS; ++j) {
+            step_load_w(st[j], rows, m.shift, opaque((uint32_t)(j * WAVE + lane)));
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    if constexpr (!XFIRST) load_weights();
 #pragma unroll
     for (uint32_t u = 0; u < XN; ++u) {
         const uint32_t i = min((uint32_t)threadIdx.x + u * nt, n4 - 1), sl = i / k4n, k4 = i - sl * k4n;
@@ -949,6 +959,7 @@ __device__ __forceinline__ void rows_x_body(const MatDev &m0, const MatDev &m1, 
         }
         __syncthreads();
     }
+    if constexpr (XFIRST) load_weights();
     float acc[NR][SM];
 #pragma unroll
     for (int r = 0; r < NR; ++r)
@@ -992,7 +1003,7 @@ __device__ __forceinline__ void rows_x_body(const MatDev &m0, const MatDev &m1, 
 template <int C, int SM, bool GU, int NS, int W, int R>
 __global__ void __launch_bounds__(WAVE * W) k_rows_x(MatDev m0, MatDev m1, const float *__restrict__ x, int S,
                                                      float *__restrict__ y, float L) {
-    rows_x_body<C, SM, GU, NS, W, R>(m0, m1, x, S, [&](int s, int row, float v, float vu) {
+    rows_x_body<C, SM, GU, NS, W, R, SM == 1>(m0, m1, x, S, [&](int s, int row, float v, float vu) {
         y[(size_t)s * m0.O + row] = GU ? swiglu(v, vu, L) : v;
     });
 }
@@ -1319,7 +1330,7 @@ __global__ void __launch_bounds__(WAVE * W) k_unit_gate_up(GroupArgs a) {
     const int e = __builtin_amdgcn_readfirstlane(a.ids[0]);
     if (e < 0 || e >= a.n_experts) return;   // reported by the down launch
     const MatDev g = a.table[e].gate, u = a.table[e].up;
-    rows_x_body<C, 1, true, NS, W, R>(g, u, a.x, 1,
+    rows_x_body<C, 1, true, NS, W, R, false>(g, u, a.x, 1,
                                       [&](int, int row, float gv, float uv) { a.h[row] = group_act(a, 0, gv, uv); });
 }
 
@@ -1335,7 +1346,7 @@ __global__ void __launch_bounds__(WAVE * W) k_unit_down(GroupArgs a) {
     const MatDev d = a.table[e].down;
     const float w0 = a.w[0];
     const bool v4 = a.act == ACT_SWIGLU_V4;
-    rows_x_body<C, 1, false, NS, W, R>(d, d, a.h, 1, [&](int, int row, float v, float) {
+    rows_x_body<C, 1, false, NS, W, R, false>(d, d, a.h, 1, [&](int, int row, float v, float) {
         a.y[row] = v4 ? 0.f + round_bf16(v) : fmaf(w0, v, 0.f);
     });
 }
