@@ -1871,9 +1871,23 @@ __global__ void __launch_bounds__(256) k_gemm_reduce(const float *__restrict__ w
     const size_t plane = (size_t)S * op;   // one (chunk, matrix) slice
     const float *p = ws + (size_t)s * op + o;
     float g = 0.f, u = 0.f;
-    for (int z = 0; z < nch; ++z) {
-        g += p[(size_t)(GU ? 2 * z : z) * plane];
-        if (GU) u += p[(size_t)(2 * z + 1) * plane];
+    // 8 chunks' loads in flight at a time, added in chunk order
+    constexpr int U = 8;
+    for (int z0 = 0; z0 < nch; z0 += U) {
+        float vg[U], vu[U];
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            const int z = min(z0 + i, nch - 1);
+            vg[i] = p[(size_t)(GU ? 2 * z : z) * plane];
+            vu[i] = GU ? p[(size_t)(2 * z + 1) * plane] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            if (z0 + i < nch) {
+                g += vg[i];
+                if (GU) u += vu[i];
+            }
+        }
     }
     y[i] = GU ? swiglu(g, u, limit) : g;
 }
@@ -1886,13 +1900,27 @@ __global__ void __launch_bounds__(256) k_gemm_reduce(const float *__restrict__ w
 // the same two matrix-core products a window, the same scaling and order),
 // so the bits are its.  A block is 8 waves over one 512-input chunk; a wave
 // takes 2 row tiles of 16 (GU: 16 rows of gate and the same 16 of up).
-// Every code and scale load of a wave goes out at once, 16 bytes a lane:
-// load j gives lane l the 32 codes of window 4j + l / 16 of row l % 16,
-// and a 4 x 4 transpose across lane groups (v_permlane32_swap, then
-// v_permlane16_swap) leaves lane l quarter l / 16 of each window, the A
-// operand's layout.  x' of the chunk is split once a block.
+// Every code and scale load of a wave goes out at once, 16 bytes a lane.
+// A code load covers 8 rows x 128 bytes (pieces of 64 bytes a row stream
+// markedly slower on MI355X): load (p, t, h) gives lane l the 32 codes of
+// window 8p + l / 8 of row 8h + l % 8 of tile t.  Three exchanges of a lane
+// bit with a register bit (lane bit 5 by v_permlane32_swap, 4 by
+// v_permlane16_swap, 3 by a row_ror:8 DPP move and a select) leave lane l
+// quarter l / 16 of each window of row l % 16, the A operand's layout.
+// x' of the chunk is split once a block.
 // ---------------------------------------------------------------------------
 constexpr int GV_W = 8;   // waves a block
+
+// Exchanges lane bit 3 with the register pair's index: afterwards a holds
+// what lanes with bit 3 clear held in a and b (lane L of b's at L ^ 8), and b
+// what lanes with bit 3 set held.  hi8: this lane's bit 3.
+__device__ __forceinline__ void swap_lane_bit3(uint32_t &a, uint32_t &b, bool hi8) {
+    const uint32_t ra = (uint32_t)__builtin_amdgcn_mov_dpp((int)a, 0x128, 0xF, 0xF, false);   // row_ror:8: lane L ^ 8
+    const uint32_t rb = (uint32_t)__builtin_amdgcn_mov_dpp((int)b, 0x128, 0xF, 0xF, false);
+    const uint32_t na = hi8 ? rb : a, nb = hi8 ? b : ra;
+    a = na;
+    b = nb;
+}
 
 struct alignas(16) GvLds {
     _Float16 xh[16][GEMM_KC + 8];          // x' hi, token, input (padded rows)
@@ -1923,15 +1951,18 @@ k_gemv_mma(MatDev m0, MatDev m1, const float *__restrict__ x, int S, float *__re
         const int f = 4 * w + i;
         xv[i] = *(const GLOBAL f32x4 *)(gf(x) + (size_t)min(f >> 1, S - 1) * K + kbeg + 4 * (64 * (f & 1) + lane));
     }
-    // this lane's rows for the codes (row lr of each tile) and the scales (row lane / 4)
-    gbytes arow[2];
+    // this lane's rows for the codes (rows 8h + l % 8 of each tile) and the scales (row lane / 4)
+    gbytes arow[2][2];
     gfloats srow[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
         const MatDev &m = (GU && t == 1) ? m1 : m0;
-        const int ra = min(gemm_row<GU>(block_row, w, t, lr), O - 1);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int ra = min(gemm_row<GU>(block_row, w, t, 8 * h + (lane & 7)), O - 1);
+            arow[t][h] = (gbytes)(m.q + (size_t)ra * m.qstride);   // per lane: not gb / gf, which take lane 0's
+        }
         const int rs = min(gemm_row<GU>(block_row, w, t, lane >> 2), O - 1);
-        arow[t] = (gbytes)(m.q + (size_t)ra * m.qstride);   // per lane: not gb / gf, which take lane 0's
         srow[t] = (gfloats)(m.s + (size_t)rs * m.sstride);
     }
     // stage x' = x 2^-e as f16 hi + lo, e per token and window from the
@@ -1985,18 +2016,20 @@ k_gemv_mma(MatDev m0, MatDev m1, const float *__restrict__ x, int S, float *__re
     // system, and each window's products wait for their own codes while
     // the later ones stream
     f32x4 scv[2];
-    u32x4 raw[4][2];
+    u32x4 raw[2][2][2];   // [half of the chunk p][tile t][row half h]
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
         scv[t] = __builtin_nontemporal_load((const GLOBAL f32x4 *)(srow[t] + kbeg / 32 + 4 * (lane & 3)));
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int p = 0; p < 2; ++p)
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const uint4 v = ld16(arow[t], (uint32_t)(kbeg / 2 + 64 * j + 16 * lq));
-            raw[j][t] = u32x4{v.x, v.y, v.z, v.w};
-        }
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint4 v = ld16(arow[t][h], (uint32_t)(kbeg / 2 + 128 * p + 16 * (lane >> 3)));
+                raw[p][t][h] = u32x4{v.x, v.y, v.z, v.w};
+            }
     __builtin_amdgcn_sched_barrier(0);
     // the wave's own scales by window and row (no other wave reads them)
 #pragma unroll
@@ -2016,24 +2049,36 @@ k_gemv_mma(MatDev m0, MatDev m1, const float *__restrict__ x, int S, float *__re
     h16x8 bl_n = *(LDS h16x8 *)&L.xl[lr][8 * lq];
     float xe_n = L.xe[lr][0];
     f32x4 sc_n[2] = {*(LDS f32x4 *)&L.sc[w][0][0][4 * lq], *(LDS f32x4 *)&L.sc[w][1][0][4 * lq]};
-    uint32_t a32[2][4];   // the A dwords of this load's 4 windows
+    uint32_t a32[2][8];   // the A dwords of the 8 windows of a chunk half, by window
+    const bool hi8 = (lane >> 3) & 1;
 #pragma unroll
     for (int j = 0; j < GWIN; ++j) {
-        if (j % 4 == 0) {
-            // codes of windows j .. j + 3 to the A layout: after the transpose
-            // register k of lane group g holds what register g of lane group
-            // k held
+        if (j % 8 == 0) {
+            // codes of windows j .. j + 7 to the A layout.  Before: lane
+            // (r % 8) + 8 (w % 8) holds row r, window w, in register (row
+            // half, quarter).  Swapping lane bit 5 with the quarter's bit 1,
+            // lane bit 4 with its bit 0 and lane bit 3 with the row half
+            // leaves lane r + 16 q holding quarter q of row r, in register
+            // w % 8.
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
-                const u32x4 r = raw[j / 4][t];
-                const auto r02 = __builtin_amdgcn_permlane32_swap(r.x, r.z, false, false);
-                const auto r13 = __builtin_amdgcn_permlane32_swap(r.y, r.w, false, false);
-                const auto r01 = __builtin_amdgcn_permlane16_swap(r02[0], r13[0], false, false);
-                const auto r23 = __builtin_amdgcn_permlane16_swap(r02[1], r13[1], false, false);
-                a32[t][0] = r01[0];
-                a32[t][1] = r01[1];
-                a32[t][2] = r23[0];
-                a32[t][3] = r23[1];
+                const u32x4 r0 = raw[j / 8][t][0], r1 = raw[j / 8][t][1];
+                const auto h0q0 = __builtin_amdgcn_permlane32_swap(r0.x, r0.z, false, false);   // [window bit 2]
+                const auto h0q1 = __builtin_amdgcn_permlane32_swap(r0.y, r0.w, false, false);
+                const auto h1q0 = __builtin_amdgcn_permlane32_swap(r1.x, r1.z, false, false);
+                const auto h1q1 = __builtin_amdgcn_permlane32_swap(r1.y, r1.w, false, false);
+#pragma unroll
+                for (int w2 = 0; w2 < 2; ++w2) {
+                    const auto u0 = __builtin_amdgcn_permlane16_swap(h0q0[w2], h0q1[w2], false, false);   // [window bit 1]
+                    const auto u1 = __builtin_amdgcn_permlane16_swap(h1q0[w2], h1q1[w2], false, false);
+#pragma unroll
+                    for (int w1 = 0; w1 < 2; ++w1) {
+                        uint32_t a = u0[w1], b = u1[w1];
+                        swap_lane_bit3(a, b, hi8);   // a: window bit 0 clear, b: set
+                        a32[t][4 * w2 + 2 * w1] = a;
+                        a32[t][4 * w2 + 2 * w1 + 1] = b;
+                    }
+                }
             }
         }
         const h16x8 bh = bh_n, bl = bl_n;
@@ -2049,7 +2094,7 @@ k_gemv_mma(MatDev m0, MatDev m1, const float *__restrict__ x, int S, float *__re
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             uint32_t pr[4];
-            Gc::decode(a32[t][j % 4], pr);
+            Gc::decode(a32[t][j % 8], pr);
             if constexpr (Gc::OFFS != 0.f) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
