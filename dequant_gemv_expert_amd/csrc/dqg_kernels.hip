@@ -1877,9 +1877,12 @@ __global__ void __launch_bounds__(256) k_gemm_reduce(const float *__restrict__ w
         float vg[U], vu[U];
 #pragma unroll
         for (int i = 0; i < U; ++i) {
-            const int z = min(z0 + i, nch - 1);
-            vg[i] = p[(size_t)(GU ? 2 * z : z) * plane];
-            vu[i] = GU ? p[(size_t)(2 * z + 1) * plane] : 0.f;
+            const int z = z0 + i;
+            vg[i] = vu[i] = 0.f;
+            if (z < nch) {
+                vg[i] = p[(size_t)(GU ? 2 * z : z) * plane];
+                if (GU) vu[i] = p[(size_t)(2 * z + 1) * plane];
+            }
         }
 #pragma unroll
         for (int i = 0; i < U; ++i) {
