@@ -822,6 +822,11 @@ __global__ void __launch_bounds__(256) k_rows_lds(MatDev m0, MatDev m1, const fl
             for (int s = 0; s < SM; ++s) acc[r][s] = 0.f;
         for (int kc0 = 0; kc0 < m.K; kc0 += KC) {
             const int kn = min(KC, m.K - kc0), n4 = kn / 4;
+            const int c0 = kc0 / Cd::CW, nc = kn / Cd::CW;
+            // this lane's first step of the chunk is requested before x is
+            // staged, so that the two round trips overlap
+            Step<C, NR, SM> st;
+            if (lane < nc) step_load_w(st, rows, m.shift, opaque((uint32_t)lane) + (uint32_t)c0);
             __syncthreads();   // the previous chunk's readers are done
             for (int i0 = threadIdx.x; i0 < SM * n4; i0 += 8 * (int)blockDim.x) {
                 f32x4 v[8];
@@ -839,11 +844,9 @@ __global__ void __launch_bounds__(256) k_rows_lds(MatDev m0, MatDev m1, const fl
                 }
             }
             __syncthreads();
-            const int c0 = kc0 / Cd::CW, nc = kn / Cd::CW;
             for (int c = lane; c < nc; c += WAVE) {
                 const uint32_t cu = opaque((uint32_t)c);
-                Step<C, NR, SM> st;
-                step_load_w(st, rows, m.shift, cu + (uint32_t)c0);
+                if (c != lane) step_load_w(st, rows, m.shift, cu + (uint32_t)c0);
                 __builtin_amdgcn_sched_barrier(0);
                 step_compute_lds(st, (lfloats)xs, (uint32_t)x_lds_len<Cd::CW>(KC), cu, acc);
             }
