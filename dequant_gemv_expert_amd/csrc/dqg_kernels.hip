@@ -867,8 +867,9 @@ __global__ void __launch_bounds__(256) k_rows_lds(MatDev m0, MatDev m1, const fl
 }
 
 // The same products for 1-4 tokens (int3: 1) and K of 1-4 whole 64-chunk steps (NS),
-// shaped to fill the chip at one token: blocks of 12 waves x 2 rows (6144
-// rows make 256 blocks, one a CU), x staged once per block, and every
+// shaped to fill the chip at one token: blocks of 12 waves x 1 row (6144
+// rows make 512 blocks, two a CU; int3, and the single expert's launches,
+// 12 waves x 2 rows), x staged once per block, and every
 // weight load of a wave issued before its first arithmetic.  x's loads go
 // out first; at one token the weights' loads (step by step, rows in order)
 // follow once x is in LDS, at several tokens while x is in flight; then
@@ -877,11 +878,16 @@ __global__ void __launch_bounds__(256) k_rows_lds(MatDev m0, MatDev m1, const fl
 // arithmetic and the order of steps are k_rows_lds's, so the bits are the
 // same.
 constexpr int GX_W = 12, GX_R = 2;
+// One token with codes of at most 32 inputs a chunk: one row a wave, so that
+// the arithmetic left when a wave's last bytes land is one row's (measured on
+// MI355X, interleaved against 12 x 2: 6144^2 int4 6.75-7.07 -> 6.44-6.47 us,
+// its gate_up 11.0-11.2 -> 10.5; int3 6144 x 16384, whose rows are longer,
+// loses: 12.9-13.4 -> 14.1-14.8).
+constexpr int GX1_R = 1;
 // Several tokens: 8 waves x 3 rows, so that the x of each chunk a wave reads
 // from LDS serves 3 rows (the reads of x for 2-4 tokens cost LDS bandwidth
 // on the scale of the arithmetic).
 constexpr int GXM_W = 8, GXM_R = 3;
-static_assert(GX_W * GX_R == GXM_W * GXM_R, "one block height at every batch");
 // Matrices of fewer rows take blocks of 8 waves x 1 row, so that 2048 rows
 // still make 256 blocks.
 constexpr int GXS_W = 8, GXS_R = 1;
@@ -2431,7 +2437,7 @@ hipError_t go_rows_x(const MatDev &g, const MatDev &u, const float *x, int S, fl
                      const char *name) {
     const size_t lds = rows_x_lds<C, SM>(g.K);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
-    constexpr int W = SM == 1 ? GX_W : GXM_W, R = SM == 1 ? GX_R : GXM_R;
+    constexpr int W = SM == 1 ? GX_W : GXM_W, R = SM == 1 ? (C == C_I3 ? GX_R : GX1_R) : GXM_R;
     if (g.O >= GX_WIDE_ROWS) {
         launch(name, (k_rows_x<C, SM, GU, NS, W, R>), dim3((g.O + W * R - 1) / (W * R)), dim3(WAVE * W), lds, st,
                g, u, x, S, y, L);

@@ -38,7 +38,8 @@ def _announce(request):
 CHUNK = {1: (16, None), 2: (32, None), 4: (32, 32), 5: (64, 64), 7: (32, 32), 10: (4, None), 11: (8, None),
          12: (16, None), 13: (16, 64), 14: (8, None)}
 CASES = [(fmt, n, O) for fmt in CHUNK for n, O in ((1, 37), (2, 24), (3, 61), (4, 5))]
-# from 6144 rows up the blocks are 12 waves x 2 rows; these leave the last block ragged
+# from 6144 rows up the blocks are 12 waves x 1 row at one token (int3 and several tokens:
+# 12 x 2 and 8 x 3); these leave the last block ragged
 CASES += [(4, 1, 6161), (7, 2, 6150), (1, 3, 6170), (5, 1, 6151), (11, 4, 6145), (13, 4, 6157)]
 IDS = [f"fmt{f}_steps{n}_O{o}" for f, n, o in CASES]
 
