@@ -1378,9 +1378,10 @@ __global__ void __launch_bounds__(WAVE * W) k_unit_down(GroupArgs a) {
 // MXFP4).
 constexpr int SPLIT_NX = 2, SPLIT_R = 24, SPLIT_HN = 5;
 // Rows a wave keeps in flight (measured on MI355X for the int4-g32 group at
-// one token: depth 2, 3, 4, 6 -> 19.1, 18.6, 18.3, 18.0 us; every row's loads
-// issued at once 18.2 us).
-constexpr int SPLIT_DEPTH = 6;
+// one token, interleaved: depth 2, 3, 4, 6, 8, 10 -> 15.4-15.5, 15.5-15.7,
+// 15.2-15.7, 16.4-16.7, 17.7-18.0, 19.2 us; with 16 waves a CU, 4 rows a wave
+// keep enough bytes in flight, and fewer rows land in the wave's last stretch).
+constexpr int SPLIT_DEPTH = 4;
 
 template <int C>
 __global__ void __launch_bounds__(WAVE * 16) __attribute__((amdgpu_waves_per_eu(4)))
