@@ -44,6 +44,14 @@ constexpr int WAVE = 64;
 constexpr int RA = 4;      // rows of gate (and of up) per wave in kernel A
 constexpr int WPB_A = 4;   // waves per block in kernel A
 constexpr int RB = 12;     // rows of down per block in kernel B
+// Kernel B's blocks in one round (two a CU on 256 CUs), and its row count for
+// hidden sizes past 512 blocks of RB: 14 rows keep 6145-7168 rows in one
+// round (measured on MI355X, MXFP4 top-8 of 384, H 7168, 8 tokens,
+// interleaved: down 144.6-146.2 us in 512 blocks of 14 rows against
+// 158.5-162.6 in 598 of 12, although the 14-row kernel spills at the 4-wave
+// budget; 16 rows, 448 blocks: 210-211 us).
+constexpr int DOWN_ROUND = 512;
+constexpr int RB_WIDE = 14;
 
 // Global-memory loads: base pointers are wave-uniform, offsets 32-bit, so
 // the address is one SGPR pair plus one VGPR (no per-row 64-bit math).
@@ -2596,6 +2604,12 @@ hipError_t group_b(const GroupArgs &a, hipStream_t st) {
         }
     }
     const int waves = units < DOWN_MAX_WAVES ? units : DOWN_MAX_WAVES;
+    if (a.H > DOWN_ROUND * RB && a.H <= DOWN_ROUND * RB_WIDE) {
+        dim3 grid((a.H + RB_WIDE - 1) / RB_WIDE);
+        const size_t lds = (size_t)slots * RB_WIDE * sizeof(float) + v4_lds;
+        launch("group_down", (k_group_down<C, RB_WIDE>), grid, dim3(WAVE * waves), lds, st, a);
+        return hipGetLastError();
+    }
     dim3 grid((a.H + RB - 1) / RB);
     // the slots' outputs; DeepSeek V4's combine adds the ids and their order
     const size_t lds = (size_t)slots * RB * sizeof(float) + v4_lds;

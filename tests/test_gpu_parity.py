@@ -252,9 +252,11 @@ def test_group_one_token_split_down(case):
 
 
 # Several tokens with at least 8 units and I of 64 code chunks, H ragged
-# against the down launch's 12-row blocks, one expert named by two tokens.
+# against the down launch's 12-row blocks (14-row blocks for H of 6145 to
+# 7168: 6176 and 7008), one expert named by two tokens.
 MULTI_CASES = [(2, 8, True, 4, 32, 2048, 416), (3, 4, False, 4, 32, 2048, 224),
-              (2, 6, True, 7, 32, 2048, 6176), (5, 3, True, 1, None, 1024, 160)]
+              (2, 6, True, 7, 32, 2048, 6176), (5, 3, True, 1, None, 1024, 160),
+              (3, 4, False, 4, 32, 2048, 7008)]
 
 
 @pytest.mark.parametrize("case", MULTI_CASES)
