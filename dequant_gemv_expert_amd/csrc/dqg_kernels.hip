@@ -1253,9 +1253,10 @@ __device__ __forceinline__ void group_down_batch(const GroupArgs &a, const Exper
 template <int R>
 __device__ __forceinline__ void group_combine(const GroupArgs &a, float *d, int row0);
 
-// Kernel B: one block per R rows of H.  Waves share the units; each unit's
-// outputs go to LDS d[slot][R]; then y[t][row] = sum_r w[t][r] * d[t*k+r]
-// in rank order, plus the shared slot.  Sets the flag for a bad id.
+// Kernel B: one block per R rows of H.  Waves take the units from a block
+// counter; each unit's outputs go to LDS d[slot][R]; then y[t][row] =
+// sum_r w[t][r] * d[t*k+r] in rank order, plus the shared slot.  Sets the
+// flag for a bad id.
 // Block size: one wave per unit, at most 8 waves (2 per SIMD, so that two
 // blocks share a CU; blocks of 9 or more waves were measured to hold one).
 constexpr int DOWN_MAX_WAVES = 8;
@@ -1263,6 +1264,7 @@ constexpr int DOWN_MAX_WAVES = 8;
 template <int C, int R>
 __device__ __forceinline__ void group_down(const GroupArgs &a) {
     extern __shared__ float d[];
+    __shared__ int next_unit;   // the block's next unit that no wave has taken
     const int row0 = blockIdx.x * R;
     const int nr = a.S * a.k;
     // units: the routed slots (each expert once, by its first slot), then
@@ -1271,20 +1273,28 @@ __device__ __forceinline__ void group_down(const GroupArgs &a) {
     const int nunits = nr + (a.shared >= 0 ? a.S : 0);
     const int nw = blockDim.x / WAVE;
     const int lane = threadIdx.x & (WAVE - 1);
-    for (int q = wave_id(); q < nunits; q += nw) {
+    if (threadIdx.x == 0) next_unit = nw;
+    __syncthreads();
+    // wave w starts with unit w, then takes the next untaken one: an
+    // expert named by several slots costs its owner a pass per slot and its
+    // other slots nothing, so units dealt in turn left some waves more
+    // passes than others (measured on MI355X, interleaved: the MXFP4 group
+    // at 8 tokens, down 144.5-146.0 -> 132.2-134.3 us; the int4-g32 group at
+    // 4 tokens 63.9-64.4 -> 60.9-61.2 us, at 2 34.9-35.8 -> 33.1-34.2 us)
+    for (int q = wave_id(); q < nunits;) {
         const int e = __builtin_amdgcn_readfirstlane(q < nr ? a.ids[q] : a.shared);
         if (e < 0 || e >= a.n_experts) {
             if (lane < R) d[q * R + lane] = __int_as_float(0x7FC00000);   // quiet NaN
             if (lane == 0) *a.flag = 1;
-            continue;
+        } else if (q >= nr) {   // token q - nr's shared slot
+            group_down_batch<C, R>(a, a.table[e], row0, SlotBatch{q, q - nr}, d);
+        } else if (owns(a.ids, q, e)) {
+            const ExpertDev &ex = a.table[e];
+            for_slots(a, q, e, [&](const SlotBatch &b) { group_down_batch<C, R>(a, ex, row0, b, d); });
         }
-        const ExpertDev &ex = a.table[e];
-        if (q >= nr) {   // token q - nr's shared slot
-            group_down_batch<C, R>(a, ex, row0, SlotBatch{q, q - nr}, d);
-            continue;
-        }
-        if (!owns(a.ids, q, e)) continue;
-        for_slots(a, q, e, [&](const SlotBatch &b) { group_down_batch<C, R>(a, ex, row0, b, d); });
+        int t = 0;
+        if (lane == 0) t = atomicAdd(&next_unit, 1);
+        q = __builtin_amdgcn_readfirstlane(t);
     }
     group_combine<R>(a, d, row0);
 }
