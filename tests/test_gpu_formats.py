@@ -152,6 +152,22 @@ def test_matmul_batch_invariant(fmt):
         assert yb[t].tobytes() == y1[0].tobytes(), (spec, t)
 
 
+@pytest.mark.parametrize("fmt", [1, 11, 12, 13, 14])
+def test_matmul_6144_one_token_in_batch(fmt):
+    """K = 6144 of 16-input chunks (int8, E4M3, int8-gs) or 8-input ones (bf16, f16): one token
+    alone takes the one-row kernel (6 or 12 steps), a batch of 8 the general row kernel; each token
+    has the same bits either way, and each token alone matches the oracle."""
+    m = synth.matrix(fmt, 300, 6144, 64 if fmt == 13 else None, 6950, fmt)
+    W = up(m)
+    x = synth.activations(8, 6144, 6951, fmt)
+    yb = host(dq.dqg_matmul(W, dev_f32(x)))
+    yr, a = oracle.gemv(m, x)
+    for t in range(8):
+        y1 = host(dq.dqg_matmul(W, dev_f32(x[t:t + 1])))
+        assert yb[t].tobytes() == y1[0].tobytes(), (fmt, t)
+        assert_close(y1, yr[t:t + 1], a[t:t + 1], f"fmt {fmt} 6144 token {t}")
+
+
 # ---------------------------------------------------------------------------
 # gate_up and the expert group
 # ---------------------------------------------------------------------------
