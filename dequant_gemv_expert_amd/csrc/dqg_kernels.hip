@@ -2444,13 +2444,16 @@ bool rows_x_fits(int K, int S) {
     return S <= (C == C_I3 ? 1 : 4) && K % unit == 0 && K / unit <= (C == C_I3 && GU ? 3 : 4);
 }
 
-// Also one token's matmul over 6144 inputs in 6 steps of 16-input chunks
-// (int8, E4M3 and int8-gs rows) or 12 of 8-input chunks (f16 and bf16 rows):
-// measured on MI355X, interleaved against the general row kernel, 6144^2
-// E4M3 10.39-10.64 -> 8.81-8.84 us, int8-gs 10.10-10.27 -> 8.68-8.88 us, f16
-// 14.89-15.04 -> 12.86-13.17 us, bf16 14.88 -> 12.96-12.99 us.
+// Also one token's matmul and gate_up over 6144 inputs in 6 steps of
+// 16-input chunks (int8, E4M3 and int8-gs rows) or 12 of 8-input chunks (f16
+// and bf16 rows): measured on MI355X, interleaved against the general row
+// kernel, 6144^2 matmul E4M3 10.39-10.64 -> 8.81-8.84 us, int8-gs
+// 10.10-10.27 -> 8.68-8.88, f16 14.89-15.04 -> 12.86-13.17, bf16 14.88 ->
+// 12.96-12.99; gate_up on two such matrices E4M3 17.4-17.6 -> 14.0-14.6,
+// int8-gs 16.5-17.1 -> 15.2-15.5, f16 27.8 -> 23.4.  (Not the single
+// expert's launches, whose switch stops at 4 steps.)
 template <int C>
-bool rows_x_fits_matmul1(int K, int S) {
+bool rows_x_fits_wide1(int K, int S) {
     return S == 1 && ((Codec<C>::CW == 16 && K == 6 * WAVE * Codec<C>::CW) ||
                       (Codec<C>::CW == 8 && K == 12 * WAVE * Codec<C>::CW));
 }
@@ -2486,11 +2489,11 @@ hipError_t rows_x_sm(const MatDev &g, const MatDev &u, const float *x, int S, fl
     case 2: return go_rows_x<C, SM, GU, 2>(g, u, x, S, y, L, st, name);
     case 3: return go_rows_x<C, SM, GU, 3>(g, u, x, S, y, L, st, name);
     case 6:
-        if constexpr (SM == 1 && !GU && Codec<C>::CW == 16) return go_rows_x<C, SM, GU, 6>(g, u, x, S, y, L, st, name);
-        else return hipErrorInvalidValue;   // not taken (rows_x_fits_matmul1)
+        if constexpr (SM == 1 && Codec<C>::CW == 16) return go_rows_x<C, SM, GU, 6>(g, u, x, S, y, L, st, name);
+        else return hipErrorInvalidValue;   // not taken (rows_x_fits_wide1)
     case 12:
-        if constexpr (SM == 1 && !GU && Codec<C>::CW == 8) return go_rows_x<C, SM, GU, 12>(g, u, x, S, y, L, st, name);
-        else return hipErrorInvalidValue;   // not taken (rows_x_fits_matmul1)
+        if constexpr (SM == 1 && Codec<C>::CW == 8) return go_rows_x<C, SM, GU, 12>(g, u, x, S, y, L, st, name);
+        else return hipErrorInvalidValue;   // not taken (rows_x_fits_wide1)
     default:
         if constexpr (C == C_I3 && GU) return hipErrorInvalidValue;   // not taken (rows_x_fits)
         else return go_rows_x<C, SM, GU, 4>(g, u, x, S, y, L, st, name);
@@ -2512,7 +2515,7 @@ template <int C>
 hipError_t matmul_c(const MatDev &m, const float *x, int S, float *y, hipStream_t st) {
     if constexpr (gemm_codec<C>())
         if (S >= gemm_min_s<C>() && m.K % 32 == 0) return go_gemm<C, false>(m, m, x, S, y, INFINITY, st);
-    if (rows_x_fits<C, false>(m.K, S) || rows_x_fits_matmul1<C>(m.K, S))
+    if (rows_x_fits<C, false>(m.K, S) || rows_x_fits_wide1<C>(m.K, S))
         return rows_x<C, false>(m, m, x, S, y, INFINITY, st, "matmul");
     // int3's 64-input chunks: 8 tokens at a time would spill, 4 fit with x in LDS
     if constexpr (C != C_I3)
@@ -2541,7 +2544,7 @@ template <int C>
 hipError_t gate_up_c(const MatDev &g, const MatDev &u, const float *x, int S, float *h, float L, hipStream_t st) {
     if constexpr (gemm_codec<C>())
         if (S >= gemm_min_s_gu<C>() && g.K % 32 == 0) return go_gemm<C, true>(g, u, x, S, h, L, st);
-    if (rows_x_fits<C, true>(g.K, S)) return rows_x<C, true>(g, u, x, S, h, L, st, "gate_up");
+    if (rows_x_fits<C, true>(g.K, S) || rows_x_fits_wide1<C>(g.K, S)) return rows_x<C, true>(g, u, x, S, h, L, st, "gate_up");
     // int3's 64-input chunks: 8 tokens at a time would spill, 4 fit with x in LDS
     if constexpr (C != C_I3)
         if (S >= 8) return go_gate_up<C, 2, 8>(g, u, x, S, h, L, st);

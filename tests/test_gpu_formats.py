@@ -188,6 +188,23 @@ def test_gate_up_matches_oracle(spec, S):
     assert_close(h, r["h"], r["nh"], f"gate_up {spec} S={S}")
 
 
+@pytest.mark.parametrize("fmt", [11, 12, 13, 14])
+def test_gate_up_6144_one_token_in_batch(fmt):
+    """gate_up over 6144 inputs: one token alone takes the one-row kernel (6 or 12 steps), a batch
+    of 4 the general row kernel (from 8 tokens E4M3 and f16 take the matrix cores); each token has
+    the same bits either way and matches the oracle."""
+    gs = 64 if fmt == 13 else None
+    G = synth.matrix(fmt, 200, 6144, gs, 6960, fmt, 0)
+    U = synth.matrix(fmt, 200, 6144, gs, 6960, fmt, 1)
+    x = synth.activations(4, 6144, 6961, fmt)
+    hb = host(dq.dqg_gate_up(up(G), up(U), dev_f32(x)))
+    r = oracle.gate_up(G, U, x)
+    for t in range(4):
+        h1 = host(dq.dqg_gate_up(up(G), up(U), dev_f32(x[t:t + 1])))
+        assert hb[t].tobytes() == h1[0].tobytes(), (fmt, t)
+        assert_close(h1, r["h"][t:t + 1], r["nh"][t:t + 1], f"gate_up fmt {fmt} 6144 token {t}")
+
+
 @pytest.mark.parametrize("S", [1, 40])
 @pytest.mark.parametrize("fmt", [11, 12])
 def test_gate_up_clamped(fmt, S):
