@@ -2444,17 +2444,19 @@ bool rows_x_fits(int K, int S) {
     return S <= (C == C_I3 ? 1 : 4) && K % unit == 0 && K / unit <= (C == C_I3 && GU ? 3 : 4);
 }
 
-// Also one token's matmul and gate_up over 6144 inputs in 6 steps of
+// Also 1-4 tokens' matmul and gate_up over 6144 inputs in 6 steps of
 // 16-input chunks (int8, E4M3 and int8-gs rows) or 12 of 8-input chunks (f16
 // and bf16 rows): measured on MI355X, interleaved against the general row
-// kernel, 6144^2 matmul E4M3 10.39-10.64 -> 8.81-8.84 us, int8-gs
+// kernel, 6144^2 matmul at 1 token E4M3 10.39-10.64 -> 8.81-8.84 us, int8-gs
 // 10.10-10.27 -> 8.68-8.88, f16 14.89-15.04 -> 12.86-13.17, bf16 14.88 ->
-// 12.96-12.99; gate_up on two such matrices E4M3 17.4-17.6 -> 14.0-14.6,
-// int8-gs 16.5-17.1 -> 15.2-15.5, f16 27.8 -> 23.4.  (Not the single
-// expert's launches, whose switch stops at 4 steps.)
+// 12.96-12.99, at 2 and 4 tokens E4M3 12.3-13.2 -> 11.6-11.8 and 17.8-18.2
+// -> 15.5-15.6, f16 16.1-16.7 -> 15.9-16.3 and 20.3-20.5 -> 19.7; gate_up on
+// two such matrices at 1 token E4M3 17.4-17.6 -> 14.0-14.6, int8-gs
+// 16.5-17.1 -> 15.2-15.5, f16 27.8 -> 23.4.  (Not the single expert's
+// launches, whose switch stops at 4 steps.)
 template <int C>
 bool rows_x_fits_wide1(int K, int S) {
-    return S == 1 && ((Codec<C>::CW == 16 && K == 6 * WAVE * Codec<C>::CW) ||
+    return S <= 4 && ((Codec<C>::CW == 16 && K == 6 * WAVE * Codec<C>::CW) ||
                       (Codec<C>::CW == 8 && K == 12 * WAVE * Codec<C>::CW));
 }
 
@@ -2489,10 +2491,10 @@ hipError_t rows_x_sm(const MatDev &g, const MatDev &u, const float *x, int S, fl
     case 2: return go_rows_x<C, SM, GU, 2>(g, u, x, S, y, L, st, name);
     case 3: return go_rows_x<C, SM, GU, 3>(g, u, x, S, y, L, st, name);
     case 6:
-        if constexpr (SM == 1 && Codec<C>::CW == 16) return go_rows_x<C, SM, GU, 6>(g, u, x, S, y, L, st, name);
+        if constexpr (Codec<C>::CW == 16) return go_rows_x<C, SM, GU, 6>(g, u, x, S, y, L, st, name);
         else return hipErrorInvalidValue;   // not taken (rows_x_fits_wide1)
     case 12:
-        if constexpr (SM == 1 && Codec<C>::CW == 8) return go_rows_x<C, SM, GU, 12>(g, u, x, S, y, L, st, name);
+        if constexpr (Codec<C>::CW == 8) return go_rows_x<C, SM, GU, 12>(g, u, x, S, y, L, st, name);
         else return hipErrorInvalidValue;   // not taken (rows_x_fits_wide1)
     default:
         if constexpr (C == C_I3 && GU) return hipErrorInvalidValue;   // not taken (rows_x_fits)
