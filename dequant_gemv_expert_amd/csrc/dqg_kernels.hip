@@ -2452,8 +2452,8 @@ bool rows_x_fits(int K, int S) {
 // 12.96-12.99, at 2 and 4 tokens E4M3 12.3-13.2 -> 11.6-11.8 and 17.8-18.2
 // -> 15.5-15.6, f16 16.1-16.7 -> 15.9-16.3 and 20.3-20.5 -> 19.7; gate_up on
 // two such matrices at 1 token E4M3 17.4-17.6 -> 14.0-14.6, int8-gs
-// 16.5-17.1 -> 15.2-15.5, f16 27.8 -> 23.4.  (Not the single expert's
-// launches, whose switch stops at 4 steps.)
+// 16.5-17.1 -> 15.2-15.5, f16 27.8 -> 23.4.  The single expert's launches
+// take the same step counts (unit_launch).
 template <int C>
 bool rows_x_fits_wide1(int K, int S) {
     return S <= 4 && ((Codec<C>::CW == 16 && K == 6 * WAVE * Codec<C>::CW) ||
@@ -2568,7 +2568,8 @@ hipError_t dequant_c(const MatDev &m, float *out, hipStream_t st) {
 // for down) of k_rows_x's shapes: the unit kernels.
 template <int C, bool GU>
 bool unit_fits(const GroupArgs &a, int K) {
-    return a.S == 1 && a.k == 1 && a.shared < 0 && rows_x_fits<C, GU>(K, 1) && rows_x_lds<C, 1>(K) <= 160 * 1024;
+    return a.S == 1 && a.k == 1 && a.shared < 0 && (rows_x_fits<C, GU>(K, 1) || rows_x_fits_wide1<C>(K, 1)) &&
+           rows_x_lds<C, 1>(K) <= 160 * 1024;
 }
 
 template <int C, bool GU, int NS, int W, int R>
@@ -2594,6 +2595,12 @@ hipError_t unit_launch(const GroupArgs &a, hipStream_t st) {
     case 1: return unit_shape<C, GU, 1>(a, st);
     case 2: return unit_shape<C, GU, 2>(a, st);
     case 3: return unit_shape<C, GU, 3>(a, st);
+    case 6:
+        if constexpr (Codec<C>::CW == 16) return unit_shape<C, GU, 6>(a, st);
+        else return hipErrorInvalidValue;   // not taken (unit_fits)
+    case 12:
+        if constexpr (Codec<C>::CW == 8) return unit_shape<C, GU, 12>(a, st);
+        else return hipErrorInvalidValue;   // not taken (unit_fits)
     default:
         if constexpr (C == C_I3 && GU) return hipErrorInvalidValue;   // not taken (unit_fits)
         else return unit_shape<C, GU, 4>(a, st);

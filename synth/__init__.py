@@ -296,4 +296,6 @@ WORKLOADS = {
     # E4M3 experts in 128 x 128 blocks on the expert-group shape
     "fp8b128_expert_group_256top8_shared": dict(kind="group", fmt=FMT_FP8_BLOCK, H=6144, I=2048, gs=None, E=256,
                                                 k=8, shared=True, S=(1, 2, 4), seed=BASE_SEED + 11),
+    "fp8b128_expert_6144x2048": dict(kind="expert", fmt=FMT_FP8_BLOCK, H=6144, I=2048, gs=None, S=(1,),
+                                     seed=BASE_SEED + 12),
 }

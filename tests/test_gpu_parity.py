@@ -289,7 +289,8 @@ def test_group_multi_token_down(case):
 
 
 # One token routed to one expert with no shared expert (a single expert
-# MLP), H and I whole multiples of 64 code chunks (1 to 4 of them per lane):
+# MLP), H and I whole multiples of 64 code chunks (1 to 4 of them per lane, or
+# 6 and 12 for 6144 inputs of 16- and 8-input chunks):
 # the group's unit launches, whose bits must be those of the general group
 # launches (a batch of two tokens, one expert each).  H = 8192 leaves the
 # down launch's last 24-row block ragged; int4 down at I = 1024 takes the
@@ -298,6 +299,7 @@ UNIT_CASES = [  # gate/up format and group size, down's, H, I
     (4, 32, 4, 32, 2048, 2048), (4, 32, 4, 32, 8192, 2048), (4, 32, 4, 32, 6144, 1024),
     (7, 32, 7, 32, 6144, 2048), (5, 64, 4, 32, 4096, 2048), (1, None, 12, None, 3072, 1024),
     (13, 64, 13, 64, 4096, 1024), (11, None, 14, None, 1024, 512), (10, None, 10, None, 1024, 256),
+    (12, None, 12, None, 6144, 2048), (14, None, 14, None, 6144, 1024),
 ]
 
 
